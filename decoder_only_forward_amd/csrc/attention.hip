@@ -1,0 +1,408 @@
+// Causal grouped-query attention over the KV cache.
+//
+// Definition ([P3] "GQA 注意力" formula; [P1] sections 9-10): for q head h of a
+// sequence, query row at absolute position p, kv head h / (nq / nkv):
+//     o = sum_{j <= p} softmax_j(q . k_j / sqrt(hd)) v_j
+//
+// Operands: q arrives in fp16; the bf16 K/V cache tiles are converted to fp16 (exact in
+// fp16's normal range) as they are staged, and P is rounded to fp16, so both products run
+// on v_mfma_f32_16x16x32_f16 with 8x finer operand rounding than bf16 for q and P.
+// Prefill (flash-style, matrix cores):
+//   one block = 128 query rows of one q head, 4 waves x 32 rows; K tiles of 64 keys
+//   [64][128] and the matching V^T tile [128][64] are staged in LDS (double buffered).
+//   Scores are formed transposed, S^T = K . Q^T, so each lane owns one query column:
+//   the row max needs only two cross-lane steps and the rescale is per lane.  The
+//   probabilities P^T then sit in registers exactly in the B-operand order of
+//   O^T = V^T . P^T (k-slots permuted consistently with the V^T reads), so P never
+//   leaves registers; this is why the cache keeps V transposed.  Tiles entirely above
+//   a wave's rows are skipped; heavy row blocks are dispatched first.
+// Decode (bandwidth bound): split-K over the cache positions, one block per
+// (sequence, kv head, 256-position chunk) serving all q heads of the group from one
+// read of K and V; a second kernel merges the partial (max, sum, output) triples.
+#include "launch.h"
+
+namespace q3 {
+namespace {
+
+constexpr int HD = 128;
+constexpr int BQ = 128;  // query rows per block
+constexpr int BKV = 64;  // keys per tile
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+DEV int k_off(int row, int chunk) { return row * HD + ((chunk ^ (row & 7)) << 3); }
+// V^T tile row = 64 keys = 16 chunks of 8 bytes, chunk index XOR (row & 15)
+DEV int vt_off8(int row, int chunk8) { return row * BKV + ((chunk8 ^ (row & 15)) << 2); }
+
+DEV float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__global__ void __launch_bounds__(256) attn_prefill_kernel(AttnPrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t sK[2][BKV * HD];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[2][HD * BKV];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q4 = lane >> 4, c16 = lane & 15;
+  const int nmb = (a.S + BQ - 1) / BQ;
+  const int nblocks = nmb * a.B * a.nq;
+  // contiguous work ranges per XCD; heavy (late) row blocks first
+  int wid;
+  {
+    int q = nblocks >> 3, r = nblocks & 7, x = blockIdx.x & 7, i = blockIdx.x >> 3;
+    wid = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+  }
+  const int mb = nmb - 1 - wid / (a.B * a.nq);
+  const int rem = wid % (a.B * a.nq);
+  const int b = rem / a.nq, h = rem % a.nq;
+  const int g = a.nq / a.nkv, kvh = h / g;
+
+  const int row0 = mb * BQ;                       // first query row (token index)
+  const int kv_len = a.pos0 + min(a.S, row0 + BQ);  // keys this block may need
+  const int ntiles = (kv_len + BKV - 1) / BKV;
+  const int wrow0 = row0 + wave * 32;
+  const int wave_max_pos = a.pos0 + min(a.S - 1, wrow0 + 31);
+  const int wave_min_pos = a.pos0 + wrow0;
+
+  const bf16_t* kbase = a.k_cache + ((int64_t)b * a.nkv + kvh) * a.cap * HD;
+  const bf16_t* vbase = a.vt_cache + ((int64_t)b * a.nkv + kvh) * HD * a.cap;
+
+  // Q^T fragments (B operand): column = query row, k = head dims
+  f16x8_t qf[2][4];
+  int qpos[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    int s = wrow0 + nt * 16 + c16;
+    bool valid = s < a.S;
+    int sc = valid ? s : a.S - 1;
+    qpos[nt] = valid ? a.pos0 + s : kv_len - 1;
+    const f16_t* qp = a.q + (((int64_t)b * a.S + sc) * a.nq + h) * HD;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[nt][ks] = as_f16x8(ld16(qp + ks * 32 + q4 * 8));
+  }
+
+  f32x4_t acc_o[8][2];
+#pragma unroll
+  for (int md = 0; md < 8; ++md)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc_o[md][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  const float sl2 = 0.08838834764831845f * kLog2e;  // log2(e) / sqrt(128)
+
+  u32x4_t rk[4], rv[4];
+  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+  auto gload = [&](int t) {
+    const int j0 = t * BKV;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int c = tid & 15, r = (tid >> 4) + 16 * i;
+      int key = j0 + r;
+      rk[i] = key < kv_len ? ld16(kbase + (int64_t)key * HD + c * 8) : zero4;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int c = tid & 7, d = (tid >> 3) + 32 * i;
+      int key = j0 + c * 8;
+      u32x4_t v = zero4;
+      if (key + 8 <= kv_len) {
+        v = ld16(vbase + (int64_t)d * a.cap + key);
+      } else if (key < kv_len) {
+        v = ld16(vbase + (int64_t)d * a.cap + key);
+        int nvalid = kv_len - key;  // 1..7 keys valid in this chunk
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t keep = (2 * e + 1 < nvalid) ? 0xFFFFFFFFu : (2 * e < nvalid ? 0xFFFFu : 0u);
+          v[e] &= keep;
+        }
+      }
+      rv[i] = v;
+    }
+  };
+  auto sstore = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int c = tid & 15, r = (tid >> 4) + 16 * i;
+      st16(&sK[st][k_off(r, c)], bf16x8_to_f16x8(rk[i]));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int c = tid & 7, d = (tid >> 3) + 32 * i;
+      int x = d & 15;
+      int base8 = (2 * c) ^ (x & ~1);
+      u32x4_t v = bf16x8_to_f16x8(rv[i]);
+      if (x & 1) v = u32x4_t{v[2], v[3], v[0], v[1]};
+      st16(&sV[st][d * BKV + (base8 << 2)], v);
+    }
+  };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int st = t & 1;
+    if (t + 1 < ntiles) gload(t + 1);
+    const int j0 = t * BKV;
+    if (j0 <= wave_max_pos) {
+      // S^T[key][qrow] for 64 keys x 32 query rows
+      f32x4_t sacc[4][2];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f16x8_t kf = as_f16x8(ld16(&sK[st][k_off(mt * 16 + c16, ks * 4 + q4)]));
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            sacc[mt][nt] =
+                __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[nt][ks], sacc[mt][nt], 0, 0, 0);
+        }
+      }
+      const bool need_mask = j0 + BKV - 1 > wave_min_pos;
+      f16x8_t pf[2][2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x = sacc[mt][nt][i] * sl2;
+            if (need_mask) {
+              int key = j0 + mt * 16 + q4 * 4 + i;
+              if (key > qpos[nt]) x = -INFINITY;
+            }
+            sacc[mt][nt][i] = x;
+            tmax = fmaxf(tmax, x);
+          }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float m_new = fmaxf(m_run[nt], tmax);
+        const float alpha = exp2_fast(m_run[nt] - m_new);
+        m_run[nt] = m_new;
+        float psum = 0.f;
+        float p[4][4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p[mt][i] = exp2_fast(sacc[mt][nt][i] - m_new);
+            psum += p[mt][i];
+          }
+        l_run[nt] = l_run[nt] * alpha + psum;
+#pragma unroll
+        for (int md = 0; md < 8; ++md)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc_o[md][nt][i] *= alpha;
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2) {
+          u32x4_t u;
+          u[0] = pack_f16x2(p[2 * ks2][0], p[2 * ks2][1]);
+          u[1] = pack_f16x2(p[2 * ks2][2], p[2 * ks2][3]);
+          u[2] = pack_f16x2(p[2 * ks2 + 1][0], p[2 * ks2 + 1][1]);
+          u[3] = pack_f16x2(p[2 * ks2 + 1][2], p[2 * ks2 + 1][3]);
+          pf[nt][ks2] = as_f16x8(u);
+        }
+      }
+      // O^T[d][qrow] += V^T[d][keys] . P^T[keys][qrow]
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+#pragma unroll
+        for (int md = 0; md < 8; ++md) {
+          const int d = md * 16 + c16;
+          const int c8a = ks2 * 8 + q4, c8b = ks2 * 8 + 4 + q4;
+          u32x2_t lo = *(const u32x2_t*)&sV[st][vt_off8(d, c8a)];
+          u32x2_t hi = *(const u32x2_t*)&sV[st][vt_off8(d, c8b)];
+          f16x8_t vf = as_f16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            acc_o[md][nt] =
+                __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[nt][ks2], acc_o[md][nt], 0, 0, 0);
+        }
+      }
+    }
+    if (t + 1 < ntiles) sstore(st ^ 1);
+    __syncthreads();
+  }
+
+  // normalise and store: lane owns query column c16 of n-tile nt, dims 16md + 4q4 + i
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    float l = l_run[nt];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float inv = 1.0f / l;
+    const int s = wrow0 + nt * 16 + c16;
+    if (s >= a.S) continue;
+    f16_t* op = a.out + (((int64_t)b * a.S + s) * a.nq + h) * HD;
+#pragma unroll
+    for (int md = 0; md < 8; ++md) {
+      u32x2_t v;
+      v[0] = pack_f16x2(acc_o[md][nt][0] * inv, acc_o[md][nt][1] * inv);
+      v[1] = pack_f16x2(acc_o[md][nt][2] * inv, acc_o[md][nt][3] * inv);
+      *(u32x2_t*)(op + md * 16 + q4 * 4) = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ decode
+constexpr int kDecChunk = 256;
+constexpr int kMaxGroup = 8;
+
+__global__ void __launch_bounds__(256) attn_decode_kernel(AttnDecodeArgs a) {
+  __shared__ float sp[kMaxGroup][kDecChunk];
+  __shared__ float sm[kMaxGroup], sl[kMaxGroup];
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = a.nq / a.nkv;
+  const int pos = a.pos[b];
+  const bool ok = pos >= 0 && pos < a.cap && pos < a.max_pos;
+  const int kv_len = ok ? pos + 1 : 0;
+  const int j0 = split * kDecChunk;
+  const int n = max(0, min(kDecChunk, kv_len - j0));
+  float* part = a.part + (((int64_t)b * a.nq + kvh * g) * a.splits + split) * (HD + 2);
+  const int64_t hstride = (int64_t)a.splits * (HD + 2);
+
+  if (n == 0) {
+    for (int i = tid; i < g * (HD + 2); i += 256) {
+      int hh = i / (HD + 2), e = i % (HD + 2);
+      part[hh * hstride + e] = e == HD ? -INFINITY : 0.f;
+    }
+    return;
+  }
+  const bf16_t* kbase = a.k_cache + (((int64_t)b * a.nkv + kvh) * a.cap + j0) * HD;
+  const bf16_t* vbase = a.vt_cache + ((int64_t)b * a.nkv + kvh) * HD * a.cap + j0;
+
+  // phase 1: scores (log2 domain).  16 lanes per key row, 4 keys per wave step.
+  const int kg = lane >> 4, dc = lane & 15;
+  const float sl2 = 0.08838834764831845f * kLog2e;
+  float qv[kMaxGroup][8];
+#pragma unroll
+  for (int hh = 0; hh < kMaxGroup; ++hh) {
+    if (hh < g) {
+      float f[8];
+      unpack8_f16(ld16(a.q + ((int64_t)b * a.nq + kvh * g + hh) * HD + dc * 8), f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[hh][e] = f[e] * sl2;
+    }
+  }
+  for (int j = wave * 4 + kg; j < n; j += 16) {
+    float kf[8];
+    unpack8(ld16(kbase + (int64_t)j * HD + dc * 8), kf);
+#pragma unroll
+    for (int hh = 0; hh < kMaxGroup; ++hh) {
+      if (hh < g) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d += qv[hh][e] * kf[e];
+        d += __shfl_xor(d, 1, 64);
+        d += __shfl_xor(d, 2, 64);
+        d += __shfl_xor(d, 4, 64);
+        d += __shfl_xor(d, 8, 64);
+        if (dc == 0) sp[hh][j] = d;
+      }
+    }
+  }
+  __syncthreads();
+  // phase 2: per-head max and exponentials
+  for (int hh = wave; hh < g; hh += 4) {
+    float m = -INFINITY;
+    for (int j = lane; j < n; j += 64) m = fmaxf(m, sp[hh][j]);
+    m = warp_max(m);
+    float s = 0.f;
+    for (int j = lane; j < kDecChunk; j += 64) {
+      float p = j < n ? exp2_fast(sp[hh][j] - m) : 0.f;
+      sp[hh][j] = p;
+      s += p;
+    }
+    s = warp_sum(s);
+    if (lane == 0) { sm[hh] = m; sl[hh] = s; }
+  }
+  __syncthreads();
+  // phase 3: o[hh][d] = sum_j p[hh][j] vt[d][j]; 16 lanes per d row, 16 keys per lane
+  const int rg = tid >> 4, kl = tid & 15;
+  float pv[kMaxGroup][16];
+#pragma unroll
+  for (int hh = 0; hh < kMaxGroup; ++hh)
+    if (hh < g)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) pv[hh][e] = sp[hh][kl * 16 + e];
+  for (int r = 0; r < HD / 16; ++r) {
+    const int d = rg + 16 * r;
+    const int key = kl * 16;
+    float vf[16];
+    if (key + 16 <= n) {
+      unpack8(ld16(vbase + (int64_t)d * a.cap + key), vf);
+      unpack8(ld16(vbase + (int64_t)d * a.cap + key + 8), vf + 8);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        vf[e] = key + e < n ? bf2f(vbase[(int64_t)d * a.cap + key + e]) : 0.f;
+    }
+#pragma unroll
+    for (int hh = 0; hh < kMaxGroup; ++hh) {
+      if (hh < g) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc += pv[hh][e] * vf[e];
+        acc += __shfl_xor(acc, 1, 64);
+        acc += __shfl_xor(acc, 2, 64);
+        acc += __shfl_xor(acc, 4, 64);
+        acc += __shfl_xor(acc, 8, 64);
+        if (kl == 0) part[hh * hstride + d] = acc;
+      }
+    }
+  }
+  if (tid < g) {
+    part[tid * hstride + HD] = sm[tid];
+    part[tid * hstride + HD + 1] = sl[tid];
+  }
+}
+
+__global__ void __launch_bounds__(128) attn_decode_combine_kernel(AttnDecodeArgs a) {
+  const int bh = blockIdx.x;
+  const int b = bh / a.nq;
+  const int d = threadIdx.x;
+  const int pos = a.pos[b];
+  const bool ok = pos >= 0 && pos < a.cap && pos < a.max_pos;
+  const float* part = a.part + (int64_t)bh * a.splits * (HD + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, part[s * (HD + 2) + HD]);
+  float L = 0.f, O = 0.f;
+  for (int s = 0; s < a.splits; ++s) {
+    const float* p = part + s * (HD + 2);
+    float m = p[HD];
+    if (m == -INFINITY) continue;
+    float f = exp2_fast(m - M);
+    L += p[HD + 1] * f;
+    O += p[d] * f;
+  }
+  float o = ok ? O / L : __int_as_float(0x7FC00000);
+  a.out[(int64_t)bh * HD + d] = f2h(o);
+}
+
+}  // namespace
+
+hipError_t attn_prefill(const AttnPrefillArgs& a, hipStream_t s) {
+  if (a.B <= 0 || a.S <= 0) return hipSuccess;
+  const int nmb = (a.S + BQ - 1) / BQ;
+  hipLaunchKernelGGL(attn_prefill_kernel, dim3(nmb * a.B * a.nq), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+void attn_decode_plan(int cap, int& splits, int& chunk) {
+  chunk = kDecChunk;
+  splits = (cap + kDecChunk - 1) / kDecChunk;
+}
+
+hipError_t attn_decode(const AttnDecodeArgs& a, hipStream_t s) {
+  if (a.B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_decode_kernel, dim3(a.splits, a.nkv, a.B), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(a.B * a.nq), dim3(128), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace q3

@@ -1,0 +1,87 @@
+// Device helpers shared by the gfx950 kernels of libqwen3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;  // bfloat16 bits
+typedef uint16_t f16_t;   // IEEE binary16 bits (transient activations)
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+#define DEV static __device__ __forceinline__
+
+DEV float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest even; a NaN input stays a (quiet) NaN.
+DEV bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// fp16 <-> fp32 (round to nearest even)
+DEV float h2f(f16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+DEV f16_t f2h(float f) { return __builtin_bit_cast(f16_t, (_Float16)f); }
+DEV uint32_t pack_f16x2(float lo, float hi) {
+  return (uint32_t)f2h(lo) | ((uint32_t)f2h(hi) << 16);
+}
+DEV void unpack8_f16(const u32x4_t v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = h2f((f16_t)(v[i] & 0xFFFFu));
+    f[2 * i + 1] = h2f((f16_t)(v[i] >> 16));
+  }
+}
+// Two bf16 -> two fp16.  Exact for magnitudes in fp16's normal range
+// [6.1e-5, 65504]; smaller values become fp16 subnormals (error <= 6e-8).
+DEV uint32_t bf16x2_to_f16x2(uint32_t v) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v << 16),
+                                                                 __uint_as_float(v & 0xFFFF0000u)));
+}
+DEV u32x4_t bf16x8_to_f16x8(u32x4_t v) {
+  return u32x4_t{bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]),
+                 bf16x2_to_f16x2(v[3])};
+}
+
+// Unpack 8 bf16 held in a 16-byte vector into floats.
+DEV void unpack8(const u32x4_t v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(v[i] << 16);
+    f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+  }
+}
+
+DEV float warp_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+DEV float warp_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+DEV float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// Reinterpret 4 dwords as 8 bf16 / 8 fp16 for the MFMA builtins.
+DEV bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+DEV f16x8_t as_f16x8(u32x4_t v) { return __builtin_bit_cast(f16x8_t, v); }
+
+DEV u32x4_t ld16(const void* p) { return *(const u32x4_t*)p; }
+DEV void st16(void* p, u32x4_t v) { *(u32x4_t*)p = v; }
+
+constexpr float kLog2e = 1.4426950408889634f;

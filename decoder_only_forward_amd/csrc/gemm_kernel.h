@@ -1,0 +1,305 @@
+// GEMM on the gfx950 matrix cores: C[M, N] = A[M, K] . B[N, K]^T, fp32 accumulate.
+//
+// Both operands are K-contiguous (activations [tokens, in], weights in the HF
+// [out, in] layout), which is the operand order of v_mfma_f32_32x32x16_{bf16,f16}.
+// Operand precision: weights are always bf16 in memory.  When the activations are
+// bf16 exactly (a caller's bf16 input) the bf16 MFMA is used; when they are computed
+// activations they are kept in fp16 (8x finer rounding than bf16) and the weight tile
+// is converted bf16 -> fp16 on its way into LDS (exact in fp16's normal range), so the
+// fp16 MFMA runs at the same rate.
+// Block tile BM x BN x 64 staged through LDS, double buffered (one barrier per
+// k-step).  Each 128-byte tile row is stored with its eight 16-byte chunks XOR-swizzled
+// by (row & 7), so the 16-byte fragment reads of 8 consecutive lanes (8 rows, same
+// chunk) hit 8 distinct bank groups, and so do the row-contiguous tile stores.
+// Every wave owns a WM x WN sub-tile made of 32x32 MFMA tiles.
+//
+// Fused epilogues (one per projection of the decoder block):
+//   E_F32       fp32 store                               (QKV, LM head, router, MoE down)
+//   E_RES_F32   out_f32 = res_f32 + acc (in place ok)    (o_proj / down in the stack)
+//   E_RESB_F32  out_f32 = float(res_bf16) + acc          (o_proj in the block API)
+//   E_RESF_B16  out_bf16 = bf16(res_f32 + acc)           (down in the block API)
+//   E_SWIGLU    out_f16[:, c] = f16(silu(g) * u)         (gate|up with SwiGLU)
+//   E_PARTIAL   fp32 partial sums of one K split         (skinny decode GEMMs)
+// B row sources:
+//   B_DENSE   one matrix;  B_QKV  q/k/v weights stacked along N without a copy;
+//   B_SWIGLU  gate and up rows interleaved per wave so that a lane holds the gate and
+//             up accumulators of the same output element.
+// Grouped mode (routed MoE): the m-tile index selects (expert, first row) from a
+// device tile table; A rows may be gathered through a row-index list.
+#pragma once
+
+#include "common.h"
+
+namespace gemm {
+
+enum BMode { B_DENSE = 0, B_QKV = 1, B_SWIGLU = 2 };
+enum EpiMode { E_F32 = 1, E_RES_F32, E_RESB_F32, E_RESF_B16, E_SWIGLU, E_PARTIAL };
+
+struct Args {
+  int M, N, K;  // N counts virtual columns (gate|up: 2 * I)
+  const uint16_t* A;  // bf16 or fp16 bits (see F16)
+  int64_t lda;
+  const int32_t* a_rows;  // optional: A row of output row r is a_rows[r]
+  const bf16_t* B0;
+  const bf16_t* B1;
+  const bf16_t* B2;
+  int64_t ldb;
+  int seg1, seg2;  // B_QKV: virtual columns [0,seg1) from B0, [seg1,seg2) B1, rest B2
+  void* C;
+  int64_t ldc;
+  const void* R;  // residual input
+  int64_t ldr;
+  float* partial;  // E_PARTIAL: [k_splits][M][N]
+  int k_splits;
+  int m_tiles, n_tiles;
+  // grouped mode
+  const int32_t* g_offsets;      // [E + 1] first output row of each expert
+  const int32_t* g_tile_expert;  // [m_tiles] expert of each m tile (-1: idle)
+  const int32_t* g_tile_row0;    // [m_tiles] first row within the expert
+  int64_t g_b_stride;            // elements between experts' B matrices
+};
+
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, BK = 64;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int TM = WM / 32, TN = WN / 32;
+  static constexpr int THREADS = WAVES_M * WAVES_N * 64;
+  static constexpr int A_LOADS = BM * 8 / THREADS;  // 16-byte chunks per thread per stage
+  static constexpr int B_LOADS = BN * 8 / THREADS;
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1, "tile too small for the thread count");
+  static_assert((BM * 8) % THREADS == 0 && (BN * 8) % THREADS == 0, "load split");
+};
+
+// Blocks are dispatched round-robin over the 8 XCDs; give each XCD a contiguous run of
+// tile ids so neighbouring tiles (which share A row panels / B column panels) share an
+// L2.  Then order tiles in groups of 8 m-tiles for panel reuse.
+DEV int xcd_remap(int b, int nblocks) {
+  int q = nblocks >> 3, r = nblocks & 7;
+  int xcd = b & 7, idx = b >> 3;
+  int base = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
+  return base + idx;
+}
+
+DEV void tile_coords(int t, int m_tiles, int n_tiles, int& tm, int& tn) {
+  const int G = 8;
+  int group = t / (G * n_tiles);
+  int first_m = group * G;
+  int gm = min(G, m_tiles - first_m);
+  int rem = t - group * G * n_tiles;
+  tm = first_m + rem % gm;
+  tn = rem / gm;
+}
+
+DEV int lds_off(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
+
+template <class T, bool F16, int BMODE, int EPI, bool GROUPED, bool SPLITK>
+__global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
+  __shared__ __attribute__((aligned(16))) bf16_t sA[2][T::BM * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t sB[2][T::BN * 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+
+  const int nblocks_mn = p.m_tiles * p.n_tiles;
+  const int t = xcd_remap(blockIdx.x, nblocks_mn);
+  int tm, tn;
+  tile_coords(t, p.m_tiles, p.n_tiles, tm, tn);
+
+  // rows handled by this block
+  int out_row0, rows_valid;
+  const bf16_t* B0 = p.B0;
+  const bf16_t* B1 = p.B1;
+  if (GROUPED) {
+    int e = p.g_tile_expert[tm];
+    if (e < 0) return;
+    int r0 = p.g_tile_row0[tm];
+    int ne = p.g_offsets[e + 1] - p.g_offsets[e];
+    out_row0 = p.g_offsets[e] + r0;
+    rows_valid = min(T::BM, ne - r0);
+    B0 += (int64_t)e * p.g_b_stride;
+    B1 += (int64_t)e * p.g_b_stride;
+  } else {
+    out_row0 = tm * T::BM;
+    rows_valid = min(T::BM, p.M - out_row0);
+  }
+  const int n0 = tn * T::BN;
+
+  // K range of this block (split-K over gridDim.y)
+  const int nk_total = p.K / 64;
+  int kt0 = 0, kt1 = nk_total;
+  if (SPLITK) {
+    int per = (nk_total + p.k_splits - 1) / p.k_splits;
+    kt0 = blockIdx.y * per;
+    kt1 = min(nk_total, kt0 + per);
+  }
+  const int nk = kt1 - kt0;
+
+  // per-thread global row pointers (fixed across k)
+  const int lchunk = tid & 7;
+  const uint16_t* aptr[T::A_LOADS];
+  const bf16_t* bptr[T::B_LOADS];
+#pragma unroll
+  for (int i = 0; i < T::A_LOADS; ++i) {
+    int r = (tid >> 3) + i * (T::THREADS / 8);
+    const uint16_t* ptr = nullptr;
+    if (r < rows_valid) {
+      int orow = out_row0 + r;
+      int64_t arow = p.a_rows ? (int64_t)p.a_rows[orow] : (int64_t)orow;
+      ptr = p.A + arow * p.lda + lchunk * 8;
+    }
+    aptr[i] = ptr;
+  }
+#pragma unroll
+  for (int i = 0; i < T::B_LOADS; ++i) {
+    int r = (tid >> 3) + i * (T::THREADS / 8);
+    const bf16_t* ptr = nullptr;
+    if (BMODE == B_SWIGLU) {
+      const int half = T::WN / 2;
+      int w = r / T::WN, j = r % T::WN;
+      int col = tn * (T::BN / 2) + w * half + (j % half);
+      if (col < p.N / 2) ptr = (j < half ? B0 : B1) + (int64_t)col * p.ldb;
+    } else {
+      int n = n0 + r;
+      if (n < p.N) {
+        if (BMODE == B_QKV) {
+          if (n < p.seg1) ptr = B0 + (int64_t)n * p.ldb;
+          else if (n < p.seg2) ptr = B1 + (int64_t)(n - p.seg1) * p.ldb;
+          else ptr = p.B2 + (int64_t)(n - p.seg2) * p.ldb;
+        } else {
+          ptr = B0 + (int64_t)n * p.ldb;
+        }
+      }
+    }
+    bptr[i] = ptr ? ptr + lchunk * 8 : nullptr;
+  }
+
+  f32x16_t acc[T::TM][T::TN];
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  u32x4_t ra[T::A_LOADS], rb[T::B_LOADS];
+  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+
+  auto gload = [&](int kt) {
+    const int koff = kt * 64;
+#pragma unroll
+    for (int i = 0; i < T::A_LOADS; ++i) ra[i] = aptr[i] ? ld16(aptr[i] + koff) : zero4;
+#pragma unroll
+    for (int i = 0; i < T::B_LOADS; ++i) rb[i] = bptr[i] ? ld16(bptr[i] + koff) : zero4;
+  };
+  auto sstore = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < T::A_LOADS; ++i) {
+      int r = (tid >> 3) + i * (T::THREADS / 8);
+      st16(&sA[s][lds_off(r, lchunk)], ra[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < T::B_LOADS; ++i) {
+      int r = (tid >> 3) + i * (T::THREADS / 8);
+      st16(&sB[s][lds_off(r, lchunk)], F16 ? bf16x8_to_f16x8(rb[i]) : rb[i]);
+    }
+  };
+
+  if (nk > 0) {
+    gload(kt0);
+    sstore(0);
+  }
+  __syncthreads();
+
+  const int frow = lane & 31, fhalf = lane >> 5;
+  for (int it = 0; it < nk; ++it) {
+    const int s = it & 1;
+    if (it + 1 < nk) gload(kt0 + it + 1);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int c = 2 * kk + fhalf;
+      u32x4_t fa[T::TM], fb[T::TN];
+#pragma unroll
+      for (int i = 0; i < T::TM; ++i) {
+        int r = wm * T::WM + i * 32 + frow;
+        fa[i] = ld16(&sA[s][lds_off(r, c)]);
+      }
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j) {
+        int r = wn * T::WN + j * 32 + frow;
+        fb[j] = ld16(&sB[s][lds_off(r, c)]);
+      }
+#pragma unroll
+      for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) {
+          if (F16)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(fa[i]), as_f16x8(fb[j]),
+                                                               acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[i]), as_bf16x8(fb[j]),
+                                                                acc[i][j], 0, 0, 0);
+        }
+    }
+    if (it + 1 < nk) sstore(s ^ 1);
+    __syncthreads();
+  }
+
+  // ---------------- epilogue
+  // 32x32 accumulator layout: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4,
+  // column l%32 of the MFMA tile.
+  const int ccol = lane & 31;
+  const int rsub = (lane >> 5) * 4;
+  if (EPI == E_SWIGLU) {
+    constexpr int HALF_TN = T::TN / 2;
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < HALF_TN; ++j) {
+        int col = tn * (T::BN / 2) + wn * (T::WN / 2) + j * 32 + ccol;
+        if (col >= p.N / 2) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          int lr = wm * T::WM + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
+          if (lr >= rows_valid) continue;
+          float g = acc[i][j][r], u = acc[i][j + HALF_TN][r];
+          f16_t* out = (f16_t*)p.C + (int64_t)(out_row0 + lr) * p.ldc + col;
+          *out = f2h(silu(g) * u);
+        }
+      }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) {
+      int col = n0 + wn * T::WN + j * 32 + ccol;
+      if (col >= p.N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        int lr = wm * T::WM + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
+        if (lr >= rows_valid) continue;
+        int64_t row = out_row0 + lr;
+        float v = acc[i][j][r];
+        if (EPI == E_PARTIAL) {
+          p.partial[((int64_t)blockIdx.y * p.M + row) * p.N + col] = v;
+        } else if (EPI == E_F32) {
+          ((float*)p.C)[row * p.ldc + col] = v;
+        } else if (EPI == E_RES_F32) {
+          float res = ((const float*)p.R)[row * p.ldr + col];
+          ((float*)p.C)[row * p.ldc + col] = res + v;
+        } else if (EPI == E_RESB_F32) {
+          float res = bf2f(((const bf16_t*)p.R)[row * p.ldr + col]);
+          ((float*)p.C)[row * p.ldc + col] = res + v;
+        } else if (EPI == E_RESF_B16) {
+          float res = ((const float*)p.R)[row * p.ldr + col];
+          ((bf16_t*)p.C)[row * p.ldc + col] = f2bf(res + v);
+        }
+      }
+    }
+}
+
+}  // namespace gemm

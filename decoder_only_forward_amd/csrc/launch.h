@@ -1,0 +1,103 @@
+// Internal launch interface of libqwen3 (host side).  Every launcher enqueues on `s`
+// and returns hipSuccess or the launch error; none allocates or synchronises.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_kernel.h"
+
+namespace q3 {
+
+// ---- GEMM (gemm.hip)
+// Tile families; kAuto picks by problem size.
+enum GemmTile { kAuto = 0, kBig = 1, kMid = 2, kSkinny = 3 };
+
+struct GemmPlan {
+  int tile;      // GemmTile actually used
+  int k_splits;  // > 1: split-K with fp32 partials + reduce kernel
+  size_t partial_bytes;
+};
+
+// Chooses tile family and split count for an (M, N, K) problem; partial_bytes is the
+// split-K scratch it needs (0 without split-K).
+GemmPlan gemm_plan(int M, int N, int K, int bmode, int epi, bool grouped);
+
+// Runs C = A . B^T with the given B source and epilogue.  `partial` must hold
+// plan.partial_bytes when plan.k_splits > 1.
+// f16: A holds fp16 activations and the bf16 weights are converted to fp16 (otherwise
+// both operands are bf16).
+hipError_t gemm_run(const gemm::Args& a, bool f16, int bmode, int epi, bool grouped,
+                    const GemmPlan& plan, float* partial, hipStream_t s);
+
+// ---- norms, embedding, RoPE (norm_rope.hip)
+// out[r] = f16(rmsnorm(in[r_in])) with r_in = r * in_row_stride + in_row_offset.
+hipError_t rmsnorm_f32(const float* in, int64_t in_row_stride, int64_t in_row_offset,
+                       const bf16_t* w, f16_t* out, int rows, int H, float eps, hipStream_t s);
+hipError_t rmsnorm_bf16(const bf16_t* in, int64_t in_row_stride, int64_t in_row_offset,
+                        const bf16_t* w, f16_t* out, int rows, int H, float eps, hipStream_t s);
+hipError_t embed_gather(const int32_t* ids, const bf16_t* table, float* out, int T, int H, int V,
+                        hipStream_t s);
+hipError_t rope_table(float* rope, int max_pos, int hd, double theta, hipStream_t s);
+
+struct RopeCacheArgs {
+  const float* qkv;  // [T][(nq + 2 nkv) * hd] fp32 projections, token t = b * S + s
+  const float* rope;  // [2][max_pos][hd/2]
+  const bf16_t* q_norm;
+  const bf16_t* k_norm;
+  f16_t* q_out;  // [T][nq][hd] fp16
+  bf16_t* k_cache;  // [B][nkv][cap][hd]
+  bf16_t* vt_cache; // [B][nkv][hd][cap]
+  const int32_t* pos;  // decode: device [B] (S == 1); prefill: nullptr
+  int pos0, B, S, nq, nkv, cap, max_pos, qk_norm;
+  float eps;
+};
+hipError_t qkv_rope_cache(const RopeCacheArgs& a, hipStream_t s);
+
+// ---- attention (attention.hip)
+struct AttnPrefillArgs {
+  const f16_t* q;        // [B][S][nq][hd] fp16
+  const bf16_t* k_cache; // [B][nkv][cap][hd]
+  const bf16_t* vt_cache;// [B][nkv][hd][cap]
+  f16_t* out;            // [B][S][nq][hd] fp16
+  int B, S, pos0, nq, nkv, cap;
+};
+hipError_t attn_prefill(const AttnPrefillArgs& a, hipStream_t s);
+
+struct AttnDecodeArgs {
+  const f16_t* q;   // [B][nq][hd] fp16
+  const bf16_t* k_cache;
+  const bf16_t* vt_cache;
+  const int32_t* pos;  // device [B]
+  f16_t* out;          // [B][nq][hd] fp16
+  float* part;         // [B][nq][splits][hd + 2]
+  int B, nq, nkv, cap, max_pos, splits, chunk;
+};
+void attn_decode_plan(int cap, int& splits, int& chunk);
+hipError_t attn_decode(const AttnDecodeArgs& a, hipStream_t s);
+
+// ---- sampling (argmax.hip)
+hipError_t argmax_rows(const float* logits, int64_t row_stride, int rows, int V, int32_t* out,
+                       float* part_val, int32_t* part_idx, int chunks, hipStream_t s);
+
+// ---- MoE (moe.hip)
+struct MoeRouteArgs {
+  const float* logits;  // [T][E]
+  int T, E, k, norm_topk;
+  int32_t* idx;   // [T][k]
+  float* w;       // [T][k]
+  int32_t* chunk_counts;  // [nchunks][E]
+  int32_t* counts;        // [E]
+  int32_t* offsets;       // [E + 1]
+  int32_t* perm_token;    // [T*k]
+  int32_t* inv_row;       // [T][k]
+  int32_t* tile_expert;   // [max_tiles]
+  int32_t* tile_row0;     // [max_tiles]
+  int max_tiles, tile_m;
+};
+int moe_route_chunks(int T);
+hipError_t moe_route(const MoeRouteArgs& a, hipStream_t s);
+hipError_t moe_combine(const float* y_rows, const int32_t* inv_row, const float* w, bf16_t* y,
+                       int T, int k, int H, hipStream_t s);
+
+}  // namespace q3

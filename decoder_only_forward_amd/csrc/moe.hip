@@ -1,0 +1,210 @@
+// Routed MoE: top-k routing, deterministic dispatch order, weighted combine
+// ([P3] "MoE": fp32 router softmax, top-k, renormalisation, hit experts only,
+// weighted index_add back to the token rows).
+//
+// Dispatch order: experts ascending, tokens ascending within an expert.  It is built
+// without atomics (counting sort over fixed token chunks), so it is bit-reproducible:
+//   hist    per chunk, thread e counts the chunk's choices of expert e
+//   scan    per expert: chunk bases, totals, offsets, and the m-tile table the grouped
+//           GEMM walks (tile -> expert, first row)
+//   scatter per chunk, thread e walks the chunk in token order and assigns rows
+#include <algorithm>
+
+#include "launch.h"
+
+namespace q3 {
+namespace {
+
+constexpr int kChunk = 256;  // tokens per routing chunk
+constexpr int kMaxK = 8;
+constexpr int kMaxE = 256;
+
+// One wave per token: k rounds of a wave-wide (value desc, index asc) argmax.
+__global__ void __launch_bounds__(256) topk_kernel(MoeRouteArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const float* r = a.logits + (int64_t)t * a.E;
+  float v[4];
+  int e_of[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int e = lane + 64 * i;
+    e_of[i] = e;
+    v[i] = e < a.E ? r[e] : -INFINITY;
+  }
+  bool taken[4] = {false, false, false, false};
+  float sel_v[kMaxK];
+  int sel_e[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j >= a.k) break;
+    float bv = -INFINITY;
+    int be = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (!taken[i] && e_of[i] < a.E && (v[i] > bv || (v[i] == bv && e_of[i] < be))) {
+        bv = v[i];
+        be = e_of[i];
+      }
+    for (int o = 32; o > 0; o >>= 1) {
+      float ov = __shfl_xor(bv, o, 64);
+      int oe = __shfl_xor(be, o, 64);
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (e_of[i] == be) taken[i] = true;
+    sel_v[j] = bv;
+    sel_e[j] = be;
+  }
+  // probabilities: softmax over all experts (max = sel_v[0]); renormalised over the k
+  float denom = 0.f;
+  if (a.norm_topk) {
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < a.k) denom += __expf(sel_v[j] - sel_v[0]);
+  } else {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (e_of[i] < a.E) s += __expf(v[i] - sel_v[0]);
+    denom = warp_sum(s);
+  }
+  if (lane < a.k) {
+    float sv = sel_v[0];
+    int se = sel_e[0];
+#pragma unroll
+    for (int j = 1; j < kMaxK; ++j)
+      if (j == lane && j < a.k) { sv = sel_v[j]; se = sel_e[j]; }
+    a.idx[(int64_t)t * a.k + lane] = se;
+    a.w[(int64_t)t * a.k + lane] = __expf(sv - sel_v[0]) / denom;
+  }
+}
+
+__global__ void __launch_bounds__(256) hist_kernel(MoeRouteArgs a) {
+  __shared__ int sidx[kChunk * kMaxK];
+  const int c = blockIdx.x;
+  const int t0 = c * kChunk, nt = min(kChunk, a.T - t0);
+  for (int i = threadIdx.x; i < nt * a.k; i += 256) sidx[i] = a.idx[(int64_t)t0 * a.k + i];
+  __syncthreads();
+  const int e = threadIdx.x;
+  if (e >= a.E) return;
+  int cnt = 0;
+  for (int i = 0; i < nt * a.k; ++i) cnt += sidx[i] == e;
+  a.chunk_counts[(int64_t)c * a.E + e] = cnt;
+}
+
+__global__ void __launch_bounds__(256) scan_kernel(MoeRouteArgs a, int nchunks) {
+  __shared__ int s_tot[kMaxE], s_tiles[kMaxE];
+  const int e = threadIdx.x;
+  int tot = 0;
+  if (e < a.E) {
+    for (int c = 0; c < nchunks; ++c) {
+      int v = a.chunk_counts[(int64_t)c * a.E + e];
+      a.chunk_counts[(int64_t)c * a.E + e] = tot;  // exclusive base within the expert
+      tot += v;
+    }
+  }
+  s_tot[e] = e < a.E ? tot : 0;
+  s_tiles[e] = e < a.E ? (tot + a.tile_m - 1) / a.tile_m : 0;
+  __syncthreads();
+  if (e == 0) {
+    int off = 0, toff = 0;
+    for (int i = 0; i < a.E; ++i) {
+      int n = s_tot[i], tl = s_tiles[i];
+      a.counts[i] = n;
+      a.offsets[i] = off;
+      s_tot[i] = off;
+      s_tiles[i] = toff;
+      off += n;
+      toff += tl;
+    }
+    a.offsets[a.E] = off;
+  }
+  __syncthreads();
+  // tile table: idle entries first, then each expert's tiles
+  for (int i = e; i < a.max_tiles; i += 256) {
+    a.tile_expert[i] = -1;
+    a.tile_row0[i] = 0;
+  }
+  __syncthreads();
+  if (e < a.E) {
+    int first = s_tiles[e];
+    int ntl = (tot + a.tile_m - 1) / a.tile_m;
+    for (int i = 0; i < ntl; ++i) {
+      a.tile_expert[first + i] = e;
+      a.tile_row0[first + i] = i * a.tile_m;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) scatter_kernel(MoeRouteArgs a) {
+  __shared__ int sidx[kChunk * kMaxK];
+  const int c = blockIdx.x;
+  const int t0 = c * kChunk, nt = min(kChunk, a.T - t0);
+  for (int i = threadIdx.x; i < nt * a.k; i += 256) sidx[i] = a.idx[(int64_t)t0 * a.k + i];
+  __syncthreads();
+  const int e = threadIdx.x;
+  if (e >= a.E) return;
+  int row = a.offsets[e] + a.chunk_counts[(int64_t)c * a.E + e];
+  for (int i = 0; i < nt * a.k; ++i) {
+    if (sidx[i] == e) {
+      int t = t0 + i / a.k;
+      a.perm_token[row] = t;
+      a.inv_row[(int64_t)t0 * a.k + i] = row;
+      ++row;
+    }
+  }
+}
+
+// y[t] = sum_j w[t][j] * y_rows[inv_row[t][j]], in slot order, rounded once to bf16.
+__global__ void __launch_bounds__(256)
+combine_kernel(const float* __restrict__ y_rows, const int32_t* __restrict__ inv_row,
+               const float* __restrict__ w, bf16_t* __restrict__ y, int T, int k, int H) {
+  const int nchunk = H / 8;
+  const int64_t total = (int64_t)T * nchunk;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int t = (int)(i / nchunk), c = (int)(i % nchunk);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      float wj = w[(int64_t)t * k + j];
+      const float* src = y_rows + (int64_t)inv_row[(int64_t)t * k + j] * H + c * 8;
+      f32x4_t a0 = *(const f32x4_t*)src, a1 = *(const f32x4_t*)(src + 4);
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += wj * a0[e];
+        acc[4 + e] += wj * a1[e];
+      }
+    }
+    u32x4_t o;
+    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+    st16(y + (int64_t)t * H + c * 8, o);
+  }
+}
+
+}  // namespace
+
+int moe_route_chunks(int T) { return (T + kChunk - 1) / kChunk; }
+
+hipError_t moe_route(const MoeRouteArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+  const int nchunks = moe_route_chunks(a.T);
+  hipLaunchKernelGGL(hist_kernel, dim3(nchunks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, s, a, nchunks);
+  hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t moe_combine(const float* y_rows, const int32_t* inv_row, const float* w, bf16_t* y,
+                       int T, int k, int H, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  int64_t work = (int64_t)T * H / 8;
+  int blocks = (int)std::min<int64_t>(65536, (work + 255) / 256);
+  hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, s, y_rows, inv_row, w, y, T,
+                     k, H);
+  return hipGetLastError();
+}
+
+}  // namespace q3

@@ -1,0 +1,621 @@
+// libqwen3 C ABI: argument validation, workspace layout and launch sequencing.
+// Nothing here allocates or synchronises; every kernel goes on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+
+#include "../../include/qwen3.h"
+#include "launch.h"
+
+using namespace q3;
+using gemm::Args;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define CHECK_HIP(expr)                                                                  \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess) return fail(QWEN3_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+bool aligned16(const void* p) { return p && ((uintptr_t)p & 15u) == 0; }
+
+#define REQ_PTR(p, name)                                                                  \
+  do {                                                                                    \
+    if (!aligned16(p)) return fail(QWEN3_EINVAL, "%s is NULL or not 16-byte aligned", name); \
+  } while (0)
+
+// ---------------------------------------------------------------- workspace layout
+struct Bump {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  }
+};
+
+struct DenseLayout {
+  size_t xn, qkv, q, attn, h1, act, res, hf, part_attn, part_gemm, am_val, am_idx, lg_scratch;
+  size_t total;
+  int T, rows_out, attn_splits, attn_chunk, am_chunks;
+};
+
+constexpr int kArgmaxChunks = 64;
+
+size_t max_gemm_partial(const qwen3_config* c, int T) {
+  const int H = c->hidden_size, nq = c->num_attention_heads, nkv = c->num_key_value_heads,
+            hd = c->head_dim, I = c->intermediate_size;
+  size_t m = 0;
+  m = std::max(m, gemm_plan(T, (nq + 2 * nkv) * hd, H, gemm::B_QKV, gemm::E_F32, false).partial_bytes);
+  m = std::max(m, gemm_plan(T, H, nq * hd, gemm::B_DENSE, gemm::E_RES_F32, false).partial_bytes);
+  m = std::max(m, gemm_plan(T, 2 * I, H, gemm::B_SWIGLU, gemm::E_SWIGLU, false).partial_bytes);
+  m = std::max(m, gemm_plan(T, H, I, gemm::B_DENSE, gemm::E_RES_F32, false).partial_bytes);
+  return m;
+}
+
+// op: block prefill / decode (bf16 block I/O) or stack prefill / decode
+DenseLayout dense_layout(const qwen3_config* c, int op, int B, int S, int cap_hint) {
+  DenseLayout L{};
+  const bool decode = op == QWEN3_OP_BLOCK_DECODE || op == QWEN3_OP_STACK_DECODE;
+  const bool stack = op == QWEN3_OP_STACK_PREFILL || op == QWEN3_OP_STACK_DECODE;
+  const int T = decode ? B : B * S;
+  const int H = c->hidden_size, nq = c->num_attention_heads, nkv = c->num_key_value_heads,
+            hd = c->head_dim, I = c->intermediate_size;
+  L.T = T;
+  Bump b;
+  L.xn = b.take((size_t)T * H * 2);
+  L.qkv = b.take((size_t)T * (nq + 2 * nkv) * hd * 4);
+  L.q = b.take((size_t)T * nq * hd * 2);
+  L.attn = b.take((size_t)T * nq * hd * 2);
+  L.act = b.take((size_t)T * I * 2);
+  L.h1 = stack ? 0 : b.take((size_t)T * H * 4);
+  L.res = stack ? b.take((size_t)T * H * 4) : 0;
+  L.part_gemm = b.take(max_gemm_partial(c, T));
+  if (decode) {
+    attn_decode_plan(cap_hint, L.attn_splits, L.attn_chunk);
+    L.part_attn = b.take((size_t)B * nq * L.attn_splits * (hd + 2) * 4);
+  }
+  if (stack) {
+    L.rows_out = T;  // upper bound: ALL mode needs every row normalised
+    L.hf = b.take((size_t)T * H * 2);
+    L.am_chunks = kArgmaxChunks;
+    L.am_val = b.take((size_t)B * kArgmaxChunks * 4);
+    L.am_idx = b.take((size_t)B * kArgmaxChunks * 4);
+    L.lg_scratch = b.take((size_t)B * c->vocab_size * 4);
+  }
+  L.total = b.off;
+  return L;
+}
+
+struct MoeLayout {
+  size_t logits, idx, w, chunk_counts, counts, offsets, perm, inv, tile_e, tile_r, act, yrows;
+  size_t total;
+  int max_tiles, tile_m;
+};
+
+MoeLayout moe_layout(const qwen3_config* c, int T) {
+  MoeLayout L{};
+  const int E = c->num_experts, k = c->num_experts_per_tok, H = c->hidden_size,
+            I = c->moe_intermediate_size;
+  L.tile_m = 128;
+  L.max_tiles = (int)(((int64_t)T * k + L.tile_m - 1) / L.tile_m) + E;
+  Bump b;
+  L.logits = b.take((size_t)T * E * 4);
+  L.idx = b.take((size_t)T * k * 4);
+  L.w = b.take((size_t)T * k * 4);
+  L.chunk_counts = b.take((size_t)moe_route_chunks(T) * E * 4);
+  L.counts = b.take((size_t)E * 4);
+  L.offsets = b.take((size_t)(E + 1) * 4);
+  L.perm = b.take((size_t)T * k * 4);
+  L.inv = b.take((size_t)T * k * 4);
+  L.tile_e = b.take((size_t)L.max_tiles * 4);
+  L.tile_r = b.take((size_t)L.max_tiles * 4);
+  L.act = b.take((size_t)T * k * I * 2);
+  L.yrows = b.take((size_t)T * k * H * 4);
+  L.total = b.off;
+  return L;
+}
+
+// ---------------------------------------------------------------- validation
+int check_dense_cfg(const qwen3_config* c) {
+  if (!c) return fail(QWEN3_EINVAL, "cfg is NULL");
+  if (c->head_dim != 128)
+    return fail(QWEN3_EUNSUPPORTED, "head_dim=%d: only 128 is supported", c->head_dim);
+  if (c->hidden_size <= 0 || c->hidden_size % 64)
+    return fail(QWEN3_EUNSUPPORTED, "hidden_size=%d must be a positive multiple of 64",
+                c->hidden_size);
+  if (c->intermediate_size <= 0 || c->intermediate_size % 64)
+    return fail(QWEN3_EUNSUPPORTED, "intermediate_size=%d must be a positive multiple of 64",
+                c->intermediate_size);
+  if (c->num_attention_heads <= 0 || c->num_key_value_heads <= 0)
+    return fail(QWEN3_EINVAL, "num_attention_heads and num_key_value_heads must be positive");
+  if (c->num_attention_heads % c->num_key_value_heads)
+    return fail(QWEN3_EINVAL, "num_attention_heads=%d is not a multiple of num_key_value_heads=%d",
+                c->num_attention_heads, c->num_key_value_heads);
+  if (c->num_attention_heads / c->num_key_value_heads > 8)
+    return fail(QWEN3_EUNSUPPORTED, "group size %d > 8",
+                c->num_attention_heads / c->num_key_value_heads);
+  if (c->max_position_embeddings <= 0)
+    return fail(QWEN3_EINVAL, "max_position_embeddings=%d", c->max_position_embeddings);
+  if (!(c->rms_norm_eps >= 0.f)) return fail(QWEN3_EINVAL, "rms_norm_eps must be >= 0");
+  if (!(c->rope_theta > 0.f)) return fail(QWEN3_EINVAL, "rope_theta must be > 0");
+  return QWEN3_OK;
+}
+
+int check_layer(const qwen3_config* c, const qwen3_layer_weights* w) {
+  if (!w) return fail(QWEN3_EINVAL, "layer weights are NULL");
+  REQ_PTR(w->input_layernorm, "input_layernorm");
+  REQ_PTR(w->q_proj, "q_proj");
+  REQ_PTR(w->k_proj, "k_proj");
+  REQ_PTR(w->v_proj, "v_proj");
+  if (c->qk_norm) {
+    REQ_PTR(w->q_norm, "q_norm");
+    REQ_PTR(w->k_norm, "k_norm");
+  }
+  REQ_PTR(w->o_proj, "o_proj");
+  REQ_PTR(w->post_attention_layernorm, "post_attention_layernorm");
+  REQ_PTR(w->gate_proj, "gate_proj");
+  REQ_PTR(w->up_proj, "up_proj");
+  REQ_PTR(w->down_proj, "down_proj");
+  return QWEN3_OK;
+}
+
+int check_cache(const qwen3_config* c, const qwen3_kv_layer* kv, const char* what) {
+  if (!kv) return fail(QWEN3_EINVAL, "%s: cache is NULL", what);
+  if (!aligned16(kv->k) || !aligned16(kv->vt))
+    return fail(QWEN3_EINVAL, "%s: cache k/vt NULL or not 16-byte aligned", what);
+  if (kv->capacity <= 0 || kv->capacity % 64)
+    return fail(QWEN3_EINVAL, "%s: capacity=%d must be a positive multiple of 64", what,
+                kv->capacity);
+  if (kv->capacity > ((c->max_position_embeddings + 63) / 64) * 64)
+    return fail(QWEN3_EINVAL, "%s: capacity=%d exceeds max_position_embeddings rounded up to 64",
+                what, kv->capacity);
+  return QWEN3_OK;
+}
+
+int check_range(const qwen3_config* c, const qwen3_kv_layer* kv, int pos0, int S) {
+  if (pos0 < 0) return fail(QWEN3_ERANGE, "pos0=%d is negative", pos0);
+  if ((int64_t)pos0 + S > kv->capacity)
+    return fail(QWEN3_ERANGE, "pos0 + seq_len = %lld exceeds cache capacity %d",
+                (long long)pos0 + S, kv->capacity);
+  if ((int64_t)pos0 + S > c->max_position_embeddings)
+    return fail(QWEN3_ERANGE, "pos0 + seq_len = %lld exceeds max_position_embeddings %d",
+                (long long)pos0 + S, c->max_position_embeddings);
+  return QWEN3_OK;
+}
+
+#define TRY(x)                  \
+  do {                          \
+    int rc_ = (x);              \
+    if (rc_ != QWEN3_OK) return rc_; \
+  } while (0)
+
+// ---------------------------------------------------------------- one layer
+struct LayerIO {
+  int T, B, S, pos0;
+  const int32_t* pos;  // decode positions (device) or nullptr
+  const bf16_t* x_bf16;  // block API input (nullptr in the stack)
+  float* res;            // stack residual (in/out) (nullptr in the block API)
+  bf16_t* x_out;         // block API output
+};
+
+int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* rope,
+              const qwen3_kv_layer* kv, const LayerIO& io, char* ws, const DenseLayout& L,
+              hipStream_t s) {
+  const int H = c->hidden_size, nq = c->num_attention_heads, nkv = c->num_key_value_heads,
+            hd = c->head_dim, I = c->intermediate_size, T = io.T;
+  // transient activations feeding the matrix cores are fp16
+  f16_t* xn = (f16_t*)(ws + L.xn);
+  float* qkv = (float*)(ws + L.qkv);
+  f16_t* q = (f16_t*)(ws + L.q);
+  f16_t* attn = (f16_t*)(ws + L.attn);
+  f16_t* act = (f16_t*)(ws + L.act);
+  float* part = (float*)(ws + L.part_gemm);
+  float* h1 = io.res ? io.res : (float*)(ws + L.h1);
+  const float eps = c->rms_norm_eps;
+
+  // input RMSNorm
+  if (io.res)
+    CHECK_HIP(rmsnorm_f32(io.res, 1, 0, (const bf16_t*)w->input_layernorm, xn, T, H, eps, s));
+  else
+    CHECK_HIP(rmsnorm_bf16(io.x_bf16, 1, 0, (const bf16_t*)w->input_layernorm, xn, T, H, eps, s));
+
+  // QKV projection (q, k, v weights stacked along N without a copy), fp32 out so the
+  // q/k RMSNorm sees unrounded projections
+  {
+    Args a{};
+    a.M = T; a.N = (nq + 2 * nkv) * hd; a.K = H;
+    a.A = xn; a.lda = H;
+    a.B0 = (const bf16_t*)w->q_proj; a.B1 = (const bf16_t*)w->k_proj;
+    a.B2 = (const bf16_t*)w->v_proj; a.ldb = H;
+    a.seg1 = nq * hd; a.seg2 = (nq + nkv) * hd;
+    a.C = qkv; a.ldc = a.N;
+    GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_QKV, gemm::E_F32, false);
+    CHECK_HIP(gemm_run(a, true, gemm::B_QKV, gemm::E_F32, false, p, part, s));
+  }
+  // q/k RMSNorm + RoPE, K/V into the cache
+  {
+    RopeCacheArgs r{};
+    r.qkv = qkv; r.rope = rope;
+    r.q_norm = (const bf16_t*)w->q_norm; r.k_norm = (const bf16_t*)w->k_norm;
+    r.q_out = q; r.k_cache = (bf16_t*)kv->k; r.vt_cache = (bf16_t*)kv->vt;
+    r.pos = io.pos; r.pos0 = io.pos0; r.B = io.B; r.S = io.pos ? 1 : io.S;
+    r.nq = nq; r.nkv = nkv; r.cap = kv->capacity; r.max_pos = c->max_position_embeddings;
+    r.qk_norm = c->qk_norm; r.eps = eps;
+    CHECK_HIP(qkv_rope_cache(r, s));
+  }
+  // attention
+  if (io.pos) {
+    AttnDecodeArgs d{};
+    d.q = q; d.k_cache = (const bf16_t*)kv->k; d.vt_cache = (const bf16_t*)kv->vt;
+    d.pos = io.pos; d.out = attn; d.part = (float*)(ws + L.part_attn);
+    d.B = io.B; d.nq = nq; d.nkv = nkv; d.cap = kv->capacity;
+    d.max_pos = c->max_position_embeddings;
+    attn_decode_plan(kv->capacity, d.splits, d.chunk);
+    CHECK_HIP(attn_decode(d, s));
+  } else {
+    AttnPrefillArgs p{};
+    p.q = q; p.k_cache = (const bf16_t*)kv->k; p.vt_cache = (const bf16_t*)kv->vt;
+    p.out = attn; p.B = io.B; p.S = io.S; p.pos0 = io.pos0; p.nq = nq; p.nkv = nkv;
+    p.cap = kv->capacity;
+    CHECK_HIP(attn_prefill(p, s));
+  }
+  // o_proj + residual -> h1 (fp32)
+  {
+    Args a{};
+    a.M = T; a.N = H; a.K = nq * hd;
+    a.A = attn; a.lda = nq * hd;
+    a.B0 = (const bf16_t*)w->o_proj; a.ldb = nq * hd;
+    a.C = h1; a.ldc = H;
+    int epi = io.res ? gemm::E_RES_F32 : gemm::E_RESB_F32;
+    a.R = io.res ? (const void*)io.res : (const void*)io.x_bf16; a.ldr = H;
+    GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_DENSE, epi, false);
+    CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, epi, false, p, part, s));
+  }
+  // post-attention RMSNorm
+  CHECK_HIP(rmsnorm_f32(h1, 1, 0, (const bf16_t*)w->post_attention_layernorm, xn, T, H, eps, s));
+  // gate | up with SwiGLU
+  {
+    Args a{};
+    a.M = T; a.N = 2 * I; a.K = H;
+    a.A = xn; a.lda = H;
+    a.B0 = (const bf16_t*)w->gate_proj; a.B1 = (const bf16_t*)w->up_proj; a.ldb = H;
+    a.C = act; a.ldc = I;
+    GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_SWIGLU, gemm::E_SWIGLU, false);
+    CHECK_HIP(gemm_run(a, true, gemm::B_SWIGLU, gemm::E_SWIGLU, false, p, part, s));
+  }
+  // down + residual
+  {
+    Args a{};
+    a.M = T; a.N = H; a.K = I;
+    a.A = act; a.lda = I;
+    a.B0 = (const bf16_t*)w->down_proj; a.ldb = I;
+    a.R = h1; a.ldr = H;
+    int epi;
+    if (io.res) {
+      epi = gemm::E_RES_F32;
+      a.C = io.res;
+    } else {
+      epi = gemm::E_RESF_B16;
+      a.C = io.x_out;
+    }
+    a.ldc = H;
+    GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_DENSE, epi, false);
+    CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, epi, false, p, part, s));
+  }
+  return QWEN3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qwen3_status_string(int status) {
+  switch (status) {
+    case QWEN3_OK: return "ok";
+    case QWEN3_EINVAL: return "invalid argument";
+    case QWEN3_EUNSUPPORTED: return "unsupported configuration";
+    case QWEN3_ERANGE: return "position out of range";
+    case QWEN3_EWORKSPACE: return "workspace too small";
+    case QWEN3_EHIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+const char* qwen3_last_error(void) { return g_err.c_str(); }
+
+size_t qwen3_workspace_bytes(const qwen3_config* c, int32_t op, int32_t batch, int32_t seq_len) {
+  g_err.clear();
+  if (batch <= 0) { fail(QWEN3_EINVAL, "batch=%d", batch); return 0; }
+  if (op == QWEN3_OP_MOE_FFN) {
+    if (!c || c->num_experts <= 0 || c->num_experts_per_tok <= 0) {
+      fail(QWEN3_EINVAL, "MoE configuration missing");
+      return 0;
+    }
+    return moe_layout(c, batch).total;
+  }
+  if (check_dense_cfg(c) != QWEN3_OK) return 0;
+  if (op == QWEN3_OP_BLOCK_DECODE || op == QWEN3_OP_STACK_DECODE) {
+    // decode partials scale with the cache capacity; size for max_position_embeddings
+    int cap = ((c->max_position_embeddings + 63) / 64) * 64;
+    return dense_layout(c, op, batch, 1, cap).total;
+  }
+  if (op != QWEN3_OP_BLOCK_PREFILL && op != QWEN3_OP_STACK_PREFILL) {
+    fail(QWEN3_EINVAL, "unknown op %d", op);
+    return 0;
+  }
+  if (seq_len <= 0) { fail(QWEN3_EINVAL, "seq_len=%d", seq_len); return 0; }
+  if (op == QWEN3_OP_STACK_PREFILL && c->vocab_size <= 0) {
+    fail(QWEN3_EINVAL, "vocab_size=%d", c->vocab_size);
+    return 0;
+  }
+  return dense_layout(c, op, batch, seq_len, 64).total;
+}
+
+int qwen3_rope_table_init(const qwen3_config* c, float* rope, void* stream) {
+  g_err.clear();
+  if (!c) return fail(QWEN3_EINVAL, "cfg is NULL");
+  if (c->head_dim <= 0 || c->head_dim % 2)
+    return fail(QWEN3_EINVAL, "head_dim=%d must be positive and even", c->head_dim);
+  if (c->max_position_embeddings <= 0)
+    return fail(QWEN3_EINVAL, "max_position_embeddings=%d", c->max_position_embeddings);
+  if (!(c->rope_theta > 0.f)) return fail(QWEN3_EINVAL, "rope_theta must be > 0");
+  REQ_PTR(rope, "rope");
+  CHECK_HIP(q3::rope_table(rope, c->max_position_embeddings, c->head_dim, (double)c->rope_theta,
+                           (hipStream_t)stream));
+  return QWEN3_OK;
+}
+
+int qwen3_block_prefill(const qwen3_config* c, const qwen3_layer_weights* w, const float* rope,
+                        const void* x_in, void* x_out, int32_t batch, int32_t seq_len,
+                        int32_t pos0, const qwen3_kv_layer* cache, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  TRY(check_dense_cfg(c));
+  TRY(check_layer(c, w));
+  if (batch <= 0 || seq_len <= 0)
+    return fail(QWEN3_EINVAL, "batch=%d seq_len=%d must be positive", batch, seq_len);
+  REQ_PTR(rope, "rope");
+  REQ_PTR(x_in, "x_in");
+  REQ_PTR(x_out, "x_out");
+  if (x_in == x_out) return fail(QWEN3_EINVAL, "x_in and x_out may not alias");
+  TRY(check_cache(c, cache, "cache"));
+  TRY(check_range(c, cache, pos0, seq_len));
+  if ((int64_t)batch * seq_len > (1 << 30)) return fail(QWEN3_EINVAL, "too many tokens");
+  DenseLayout L = dense_layout(c, QWEN3_OP_BLOCK_PREFILL, batch, seq_len, cache->capacity);
+  if (!aligned16(workspace) || workspace_bytes < L.total)
+    return fail(QWEN3_EWORKSPACE, "workspace needs %zu bytes (got %zu)", L.total,
+                workspace_bytes);
+  LayerIO io{};
+  io.T = batch * seq_len; io.B = batch; io.S = seq_len; io.pos0 = pos0;
+  io.x_bf16 = (const bf16_t*)x_in; io.x_out = (bf16_t*)x_out;
+  return run_layer(c, w, rope, cache, io, (char*)workspace, L, (hipStream_t)stream);
+}
+
+int qwen3_block_decode(const qwen3_config* c, const qwen3_layer_weights* w, const float* rope,
+                       const void* x_in, void* x_out, int32_t batch, const int32_t* pos,
+                       const qwen3_kv_layer* cache, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  g_err.clear();
+  TRY(check_dense_cfg(c));
+  TRY(check_layer(c, w));
+  if (batch <= 0) return fail(QWEN3_EINVAL, "batch=%d must be positive", batch);
+  REQ_PTR(rope, "rope");
+  REQ_PTR(x_in, "x_in");
+  REQ_PTR(x_out, "x_out");
+  if (!pos) return fail(QWEN3_EINVAL, "pos is NULL");
+  if (x_in == x_out) return fail(QWEN3_EINVAL, "x_in and x_out may not alias");
+  TRY(check_cache(c, cache, "cache"));
+  DenseLayout L = dense_layout(c, QWEN3_OP_BLOCK_DECODE, batch, 1, cache->capacity);
+  if (!aligned16(workspace) || workspace_bytes < L.total)
+    return fail(QWEN3_EWORKSPACE, "workspace needs %zu bytes (got %zu)", L.total,
+                workspace_bytes);
+  LayerIO io{};
+  io.T = batch; io.B = batch; io.S = 1; io.pos = pos;
+  io.x_bf16 = (const bf16_t*)x_in; io.x_out = (bf16_t*)x_out;
+  return run_layer(c, w, rope, cache, io, (char*)workspace, L, (hipStream_t)stream);
+}
+
+int qwen3_stack_forward(const qwen3_config* c, const qwen3_model_weights* w, const float* rope,
+                        const int32_t* ids, int32_t batch, int32_t seq_len, int32_t pos0,
+                        const int32_t* pos, const qwen3_kv_layer* caches, float* logits,
+                        int32_t logits_mode, int32_t* next_ids, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  TRY(check_dense_cfg(c));
+  if (!w) return fail(QWEN3_EINVAL, "model weights are NULL");
+  if (c->num_hidden_layers <= 0 || !w->layers)
+    return fail(QWEN3_EINVAL, "num_hidden_layers=%d / layers array missing",
+                c->num_hidden_layers);
+  if (c->vocab_size <= 0) return fail(QWEN3_EINVAL, "vocab_size=%d", c->vocab_size);
+  REQ_PTR(w->embed_tokens, "embed_tokens");
+  REQ_PTR(w->norm, "norm");
+  if (!c->tie_word_embeddings) REQ_PTR(w->lm_head, "lm_head");
+  for (int l = 0; l < c->num_hidden_layers; ++l) {
+    int rc = check_layer(c, &w->layers[l]);
+    if (rc) return fail(rc, "layer %d: %s", l, g_err.c_str());
+  }
+  REQ_PTR(rope, "rope");
+  if (!ids) return fail(QWEN3_EINVAL, "ids is NULL");
+  if (batch <= 0 || seq_len <= 0)
+    return fail(QWEN3_EINVAL, "batch=%d seq_len=%d must be positive", batch, seq_len);
+  if (logits_mode != QWEN3_LOGITS_NONE && logits_mode != QWEN3_LOGITS_ALL &&
+      logits_mode != QWEN3_LOGITS_LAST)
+    return fail(QWEN3_EINVAL, "logits_mode=%d", logits_mode);
+  if (logits_mode != QWEN3_LOGITS_NONE) REQ_PTR(logits, "logits");
+  if (!caches) return fail(QWEN3_EINVAL, "caches is NULL");
+  const bool decode = seq_len == 1 && pos != nullptr;
+  for (int l = 0; l < c->num_hidden_layers; ++l) {
+    TRY(check_cache(c, &caches[l], "caches[l]"));
+    if (!decode) TRY(check_range(c, &caches[l], pos0, seq_len));
+  }
+  const int op = decode ? QWEN3_OP_STACK_DECODE : QWEN3_OP_STACK_PREFILL;
+  DenseLayout L = dense_layout(c, op, batch, seq_len, caches[0].capacity);
+  for (int l = 1; l < c->num_hidden_layers; ++l)
+    if (caches[l].capacity != caches[0].capacity)
+      return fail(QWEN3_EINVAL, "all layers' caches must share one capacity");
+  if (!aligned16(workspace) || workspace_bytes < L.total)
+    return fail(QWEN3_EWORKSPACE, "workspace needs %zu bytes (got %zu)", L.total,
+                workspace_bytes);
+
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int H = c->hidden_size, V = c->vocab_size, T = L.T;
+  float* res = (float*)(ws + L.res);
+  CHECK_HIP(embed_gather(ids, (const bf16_t*)w->embed_tokens, res, T, H, V, s));
+  LayerIO io{};
+  io.T = T; io.B = batch; io.S = decode ? 1 : seq_len; io.pos0 = pos0;
+  io.pos = decode ? pos : nullptr; io.res = res;
+  for (int l = 0; l < c->num_hidden_layers; ++l)
+    TRY(run_layer(c, &w->layers[l], rope, &caches[l], io, ws, L, s));
+
+  // final RMSNorm on the rows that need logits, LM head (tied: embed_tokens)
+  const bf16_t* head = (const bf16_t*)(c->tie_word_embeddings ? w->embed_tokens : w->lm_head);
+  f16_t* hf = (f16_t*)(ws + L.hf);
+  const int S = io.S;
+  int rows;
+  float* out;
+  if (logits_mode == QWEN3_LOGITS_ALL) {
+    rows = T;
+    out = logits;
+    CHECK_HIP(rmsnorm_f32(res, 1, 0, (const bf16_t*)w->norm, hf, rows, H, c->rms_norm_eps, s));
+  } else {
+    if (logits_mode == QWEN3_LOGITS_NONE && !next_ids) return QWEN3_OK;
+    rows = batch;
+    out = logits_mode == QWEN3_LOGITS_LAST ? logits : (float*)(ws + L.lg_scratch);
+    CHECK_HIP(rmsnorm_f32(res, S, S - 1, (const bf16_t*)w->norm, hf, rows, H, c->rms_norm_eps, s));
+  }
+  {
+    Args a{};
+    a.M = rows; a.N = V; a.K = H;
+    a.A = hf; a.lda = H;
+    a.B0 = head; a.ldb = H;
+    a.C = out; a.ldc = V;
+    GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_DENSE, gemm::E_F32, false);
+    if (p.partial_bytes > 0) p = GemmPlan{kSkinny, 1, 0};
+    CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, gemm::E_F32, false, p, nullptr, s));
+  }
+  if (next_ids) {
+    const float* last = out;
+    int64_t stride = V;
+    if (logits_mode == QWEN3_LOGITS_ALL) {
+      last = out + (int64_t)(S - 1) * V;
+      stride = (int64_t)S * V;
+    }
+    CHECK_HIP(argmax_rows(last, stride, batch, V, next_ids, (float*)(ws + L.am_val),
+                          (int32_t*)(ws + L.am_idx), L.am_chunks, s));
+  }
+  return QWEN3_OK;
+}
+
+int qwen3_moe_ffn(const qwen3_config* c, const qwen3_moe_weights* w, const void* x, void* y,
+                  int32_t n_tokens, float* router_logits, int32_t* topk_idx, float* topk_w,
+                  int32_t* expert_offsets, int32_t* perm_token, int32_t* inv_row,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!c) return fail(QWEN3_EINVAL, "cfg is NULL");
+  const int E = c->num_experts, k = c->num_experts_per_tok, H = c->hidden_size,
+            I = c->moe_intermediate_size;
+  if (E <= 0 || E > 256) return fail(QWEN3_EUNSUPPORTED, "num_experts=%d must be in [1, 256]", E);
+  if (k <= 0 || k > 8 || k > E)
+    return fail(QWEN3_EUNSUPPORTED, "num_experts_per_tok=%d must be in [1, min(E, 8)]", k);
+  if (H <= 0 || H % 64) return fail(QWEN3_EUNSUPPORTED, "hidden_size=%d must be a multiple of 64", H);
+  if (I <= 0 || I % 64)
+    return fail(QWEN3_EUNSUPPORTED, "moe_intermediate_size=%d must be a multiple of 64", I);
+  if (n_tokens <= 0) return fail(QWEN3_EINVAL, "n_tokens=%d must be positive", n_tokens);
+  if ((int64_t)n_tokens * k > (1 << 30)) return fail(QWEN3_EINVAL, "too many tokens");
+  if (!w) return fail(QWEN3_EINVAL, "MoE weights are NULL");
+  REQ_PTR(w->router, "router");
+  REQ_PTR(w->gate_up_proj, "gate_up_proj");
+  REQ_PTR(w->down_proj, "down_proj");
+  REQ_PTR(x, "x");
+  REQ_PTR(y, "y");
+  MoeLayout L = moe_layout(c, n_tokens);
+  if (!aligned16(workspace) || workspace_bytes < L.total)
+    return fail(QWEN3_EWORKSPACE, "workspace needs %zu bytes (got %zu)", L.total,
+                workspace_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int T = n_tokens;
+  float* lg = router_logits ? router_logits : (float*)(ws + L.logits);
+  int32_t* idx = topk_idx ? topk_idx : (int32_t*)(ws + L.idx);
+  float* wt = topk_w ? topk_w : (float*)(ws + L.w);
+  int32_t* offs = expert_offsets ? expert_offsets : (int32_t*)(ws + L.offsets);
+  int32_t* perm = perm_token ? perm_token : (int32_t*)(ws + L.perm);
+  int32_t* inv = inv_row ? inv_row : (int32_t*)(ws + L.inv);
+  int32_t* tile_e = (int32_t*)(ws + L.tile_e);
+  int32_t* tile_r = (int32_t*)(ws + L.tile_r);
+  f16_t* act = (f16_t*)(ws + L.act);
+  float* yrows = (float*)(ws + L.yrows);
+
+  // router logits (fp32)
+  {
+    Args a{};
+    a.M = T; a.N = E; a.K = H;
+    a.A = (const bf16_t*)x; a.lda = H;
+    a.B0 = (const bf16_t*)w->router; a.ldb = H;
+    a.C = lg; a.ldc = E;
+    GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_DENSE, gemm::E_F32, false);
+    if (p.partial_bytes > 0) p = GemmPlan{kSkinny, 1, 0};
+    CHECK_HIP(gemm_run(a, false, gemm::B_DENSE, gemm::E_F32, false, p, nullptr, s));
+  }
+  // top-k, weights, dispatch order, tile table
+  {
+    MoeRouteArgs r{};
+    r.logits = lg; r.T = T; r.E = E; r.k = k; r.norm_topk = c->norm_topk_prob;
+    r.idx = idx; r.w = wt;
+    r.chunk_counts = (int32_t*)(ws + L.chunk_counts);
+    r.counts = (int32_t*)(ws + L.counts);
+    r.offsets = offs; r.perm_token = perm; r.inv_row = inv;
+    r.tile_expert = tile_e; r.tile_row0 = tile_r;
+    r.max_tiles = L.max_tiles; r.tile_m = L.tile_m;
+    CHECK_HIP(moe_route(r, s));
+  }
+  // grouped gate|up + SwiGLU over gathered token rows
+  {
+    Args a{};
+    a.M = T * k; a.N = 2 * I; a.K = H;
+    a.A = (const uint16_t*)x; a.lda = H; a.a_rows = perm;
+    a.B0 = (const bf16_t*)w->gate_up_proj;
+    a.B1 = (const bf16_t*)w->gate_up_proj + (int64_t)I * H;
+    a.ldb = H;
+    a.g_offsets = offs; a.g_tile_expert = tile_e; a.g_tile_row0 = tile_r;
+    a.g_b_stride = (int64_t)2 * I * H;
+    a.m_tiles = L.max_tiles;
+    a.C = act; a.ldc = I;
+    GemmPlan p{kMid, 1, 0};
+    CHECK_HIP(gemm_run(a, false, gemm::B_SWIGLU, gemm::E_SWIGLU, true, p, nullptr, s));
+  }
+  // grouped down -> per-row fp32 outputs in dispatch order
+  {
+    Args a{};
+    a.M = T * k; a.N = H; a.K = I;
+    a.A = act; a.lda = I;
+    a.B0 = (const bf16_t*)w->down_proj; a.B1 = a.B0; a.ldb = I;
+    a.g_offsets = offs; a.g_tile_expert = tile_e; a.g_tile_row0 = tile_r;
+    a.g_b_stride = (int64_t)H * I;
+    a.m_tiles = L.max_tiles;
+    a.C = yrows; a.ldc = H;
+    GemmPlan p{kMid, 1, 0};
+    CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, gemm::E_F32, true, p, nullptr, s));
+  }
+  CHECK_HIP(moe_combine(yrows, inv, wt, (bf16_t*)y, T, k, H, s));
+  return QWEN3_OK;
+}
+
+}  // extern "C"

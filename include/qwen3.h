@@ -1,0 +1,207 @@
+/*
+ * qwen3.h -- C ABI of the MI355X (gfx950) Qwen3 decoder-forward library (libqwen3.so).
+ *
+ * The operations follow the hand-built Qwen3 described on these web pages
+ * (sections named as on the pages):
+ *   [P1] "Building Qwen-3 MoE from scratch" (adg.csdn.net), sections 5-13.
+ *   [P3] "从零实现 Qwen3：拆解 mini-qwen3 的 0.6B Dense 架构" (quarkcode.cn):
+ *        config table, "骨架", "prefill 与 decode", "RMSNorm", "GQA 注意力",
+ *        "RoPE", "SwiGLU FFN", "TransformerBlock", "MoE".
+ *   [P4] "从0实现SGLang" part 3 (wmrh.cn), sections 3.1-3.8 and 六.
+ *
+ * General conventions
+ *   - Every tensor pointer is a DEVICE pointer unless stated otherwise; tensors are
+ *     dense row-major.  "bf16" means IEEE bfloat16 bits (uint16).
+ *   - Weights use the Hugging Face [out_features, in_features] layout: a projection
+ *     computes y = x W^T without bias ([P1] section 7; [P3] "GQA 注意力").
+ *   - Ownership: the caller owns all memory.  The library never allocates, frees or
+ *     synchronises; it enqueues kernels on `stream` (a hipStream_t; NULL = default
+ *     stream) and returns while they run.  Scratch space is the caller's `workspace`,
+ *     sized by qwen3_workspace_bytes().
+ *   - Errors: arguments are validated on the host before anything is enqueued; on a
+ *     failure nothing is enqueued, a negative QWEN3_E* code is returned and
+ *     qwen3_last_error() names the offending field.  A failed kernel launch returns
+ *     QWEN3_EHIP.  Device faults surface at the caller's next synchronisation.
+ *   - Alignment: every pointer must be 16-byte aligned.
+ *   - Supported shapes: head_dim == 128; hidden_size and the intermediate sizes
+ *     multiples of 64; num_attention_heads a multiple of num_key_value_heads with a
+ *     group size of at most 8; MoE: at most 256 experts and 8 experts per token.
+ *
+ * KV cache (per layer, caller-owned, bf16):
+ *   k  [batch][num_key_value_heads][capacity][head_dim]   key rows by position
+ *   vt [batch][num_key_value_heads][head_dim][capacity]   values, position-minor
+ *   Keys are stored after q/k-norm and RoPE, values as projected ([P3] "GQA 注意力":
+ *   the cache keeps normalised, rotated K).  The value half is kept transposed so the
+ *   attention kernels read it in the operand order of the matrix cores.
+ *   capacity must be a multiple of 64 and at most max_position_embeddings rounded
+ *   up to 64.
+ */
+#ifndef QWEN3_H
+#define QWEN3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define QWEN3_OK 0
+#define QWEN3_EINVAL (-1)       /* bad pointer, shape or size */
+#define QWEN3_EUNSUPPORTED (-2) /* valid but not implemented (e.g. head_dim != 128) */
+#define QWEN3_ERANGE (-3)       /* positions beyond the cache or max_position_embeddings */
+#define QWEN3_EWORKSPACE (-4)   /* workspace missing or too small */
+#define QWEN3_EHIP (-5)         /* a HIP launch failed */
+
+/* Model configuration; field names follow the Hugging Face config.json
+ * ([P3] config table; [P1] section 2 config; [P4] Qwen3Config). */
+typedef struct qwen3_config {
+  int32_t hidden_size;             /* H, e.g. 1024 */
+  int32_t num_attention_heads;     /* nq, e.g. 16 */
+  int32_t num_key_value_heads;     /* nkv, e.g. 8; nq % nkv == 0 */
+  int32_t head_dim;                /* hd, independent of H; must be 128 */
+  int32_t intermediate_size;       /* dense SwiGLU width I, e.g. 3072 */
+  int32_t num_hidden_layers;       /* L (stack only) */
+  int32_t vocab_size;              /* V (stack only) */
+  int32_t max_position_embeddings; /* largest position + 1, e.g. 40960 */
+  float rms_norm_eps;              /* 1e-6 */
+  float rope_theta;                /* RoPE base, 1e6 */
+  int32_t qk_norm;                 /* 1: per-head RMSNorm of q and k before RoPE */
+  int32_t tie_word_embeddings;     /* 1: LM head reuses embed_tokens */
+  int32_t num_experts;             /* E (MoE only) */
+  int32_t num_experts_per_tok;     /* k (MoE only), 1 <= k <= min(E, 8) */
+  int32_t moe_intermediate_size;   /* I_moe (MoE only) */
+  int32_t norm_topk_prob;          /* 1: renormalise the k selected probabilities */
+} qwen3_config;
+
+/* One decoder layer's weights (device, bf16). */
+typedef struct qwen3_layer_weights {
+  const void *input_layernorm;          /* [H] */
+  const void *q_proj;                   /* [nq*hd, H] */
+  const void *k_proj;                   /* [nkv*hd, H] */
+  const void *v_proj;                   /* [nkv*hd, H] */
+  const void *q_norm;                   /* [hd]  (read only when qk_norm) */
+  const void *k_norm;                   /* [hd] */
+  const void *o_proj;                   /* [H, nq*hd] */
+  const void *post_attention_layernorm; /* [H] */
+  const void *gate_proj;                /* [I, H] */
+  const void *up_proj;                  /* [I, H] */
+  const void *down_proj;                /* [H, I] */
+} qwen3_layer_weights;
+
+/* Whole-model weights. `layers` is a HOST array of num_hidden_layers entries. */
+typedef struct qwen3_model_weights {
+  const void *embed_tokens;              /* [V, H] bf16 */
+  const void *norm;                      /* [H] final RMSNorm weight */
+  const void *lm_head;                   /* [V, H]; ignored when tie_word_embeddings */
+  const qwen3_layer_weights *layers;     /* host array [L] */
+} qwen3_model_weights;
+
+/* Routed-MoE FFN weights ([P3] "MoE": fused gate_up_proj, experts along dim 0). */
+typedef struct qwen3_moe_weights {
+  const void *router;       /* [E, H] bf16 (the MoE "gate" linear) */
+  const void *gate_up_proj; /* [E, 2*I_moe, H] bf16; rows [0, I_moe) gate, [I_moe, 2 I_moe) up */
+  const void *down_proj;    /* [E, H, I_moe] bf16 */
+} qwen3_moe_weights;
+
+/* One layer's KV cache (see layout above). */
+typedef struct qwen3_kv_layer {
+  void *k;          /* [B][nkv][capacity][hd] bf16 */
+  void *vt;         /* [B][nkv][hd][capacity] bf16 */
+  int32_t capacity; /* positions per sequence, multiple of 64 */
+} qwen3_kv_layer;
+
+/* Operation selector for qwen3_workspace_bytes. */
+#define QWEN3_OP_BLOCK_PREFILL 1
+#define QWEN3_OP_BLOCK_DECODE 2
+#define QWEN3_OP_MOE_FFN 3
+#define QWEN3_OP_STACK_PREFILL 4
+#define QWEN3_OP_STACK_DECODE 5
+
+/* Logits selection for qwen3_stack_forward. */
+#define QWEN3_LOGITS_NONE 0 /* no logits (next_ids still allowed) */
+#define QWEN3_LOGITS_ALL 1  /* [B][S][V]: every position */
+#define QWEN3_LOGITS_LAST 2 /* [B][V]: last position of each sequence */
+
+/* Bytes of workspace needed by `op` for `batch` sequences of `seq_len` new tokens
+ * (for QWEN3_OP_MOE_FFN: batch = number of tokens, seq_len ignored).  Returns 0 for an
+ * invalid configuration (qwen3_last_error() says why). */
+size_t qwen3_workspace_bytes(const qwen3_config *cfg, int32_t op, int32_t batch,
+                             int32_t seq_len);
+
+/* Fill the RoPE table ([P3] "RoPE": per-position cos/sin of pos * theta_i with
+ * theta_i = rope_theta^(-2i/hd), i < hd/2, precomputed up to max_position_embeddings).
+ * rope: device fp32 [2][max_position_embeddings][hd/2]; cos block first, then sin.
+ * Values are computed in fp64 on the device and rounded once to fp32. */
+int qwen3_rope_table_init(const qwen3_config *cfg, float *rope, void *stream);
+
+/* One pre-norm decoder block, prefill of `seq_len` new tokens for each of `batch`
+ * sequences that all start at absolute position pos0 ([P3] "TransformerBlock",
+ * "GQA 注意力", "prefill 与 decode"; [P4] decoder layer):
+ *   h1 = x + o_proj(attn(rope(qk_norm(split_heads(rmsnorm(x) W_qkv^T)))))
+ *   x_out = h1 + down(silu(gate(rmsnorm(h1))) * up(rmsnorm(h1)))
+ * Query row s (absolute position pos0+s) attends to keys 0..pos0+s: positions < pos0 are
+ * read from `cache`, the new keys/values are written into it at [pos0, pos0+seq_len).
+ *   x_in, x_out: bf16 [batch][seq_len][H] (may not alias)
+ *   rope: table from qwen3_rope_table_init
+ *   cache: required (holds the new K/V); pos0 + seq_len <= capacity and
+ *          <= max_position_embeddings, else QWEN3_ERANGE. */
+int qwen3_block_prefill(const qwen3_config *cfg, const qwen3_layer_weights *w,
+                        const float *rope, const void *x_in, void *x_out, int32_t batch,
+                        int32_t seq_len, int32_t pos0, const qwen3_kv_layer *cache,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* One decoder block, decode step: one new token per sequence at its own position
+ * ([P3] "prefill 与 decode": the new token sees all cached positions and itself).
+ *   x_in, x_out: bf16 [batch][H]
+ *   pos: DEVICE int32 [batch]; the token of sequence b is written to cache slot pos[b]
+ *        and attends to slots 0..pos[b].  A position outside [0, min(capacity,
+ *        max_position_embeddings)) is not written and yields a NaN output row. */
+int qwen3_block_decode(const qwen3_config *cfg, const qwen3_layer_weights *w,
+                       const float *rope, const void *x_in, void *x_out, int32_t batch,
+                       const int32_t *pos, const qwen3_kv_layer *cache, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* Routed MoE FFN sub-layer on already-normalised inputs ([P3] "MoE"):
+ *   r = x Wr^T (fp32); the k experts with the largest r are chosen (descending, ties to
+ *   the lower index); w = their softmax probabilities, renormalised over the k when
+ *   norm_topk_prob; y = sum_j w_j down_e(silu(gate_e x) * up_e x).  No residual.
+ *   x: bf16 [n_tokens][H]; y: bf16 [n_tokens][H]
+ * Optional outputs (device, may be NULL):
+ *   router_logits fp32 [T][E]; topk_idx int32 [T][k]; topk_w fp32 [T][k];
+ *   expert_offsets int32 [E+1] (rows of expert e are [off[e], off[e+1]) of the
+ *   dispatch order); perm_token int32 [T*k] (token of each dispatch row; experts
+ *   ascending, tokens ascending within an expert); inv_row int32 [T][k]. */
+int qwen3_moe_ffn(const qwen3_config *cfg, const qwen3_moe_weights *w, const void *x, void *y,
+                  int32_t n_tokens, float *router_logits, int32_t *topk_idx, float *topk_w,
+                  int32_t *expert_offsets, int32_t *perm_token, int32_t *inv_row,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* Whole model ([P3] "骨架"; [P1] sections 12-13): embedding gather, num_hidden_layers
+ * blocks with an fp32 residual stream, final RMSNorm, LM head (tied unless
+ * tie_word_embeddings == 0), optional greedy argmax.
+ *   ids: device int32 [batch][seq_len], each in [0, V) (an out-of-range id gives a NaN row)
+ *   seq_len > 1 or pos == NULL: prefill of every sequence from position pos0
+ *     (pos0 + seq_len <= capacity, <= max_position_embeddings).
+ *   seq_len == 1 and pos != NULL: decode step, sequence b at device position pos[b].
+ *   caches: HOST array [L] of per-layer caches (required).
+ *   logits: fp32, layout by logits_mode (NULL only with QWEN3_LOGITS_NONE).
+ *   next_ids: device int32 [batch] (nullable): argmax of each sequence's last-position
+ *             logits, lowest index on ties ([P1] section 13; [P4] greedy generation). */
+int qwen3_stack_forward(const qwen3_config *cfg, const qwen3_model_weights *w,
+                        const float *rope, const int32_t *ids, int32_t batch, int32_t seq_len,
+                        int32_t pos0, const int32_t *pos, const qwen3_kv_layer *caches,
+                        float *logits, int32_t logits_mode, int32_t *next_ids, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* Text for a status code. */
+const char *qwen3_status_string(int status);
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char *qwen3_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,100 @@
+"""Shared helpers for the GPU parity tests: upload synthetic inputs, build caches, compare
+against the oracle with the parity bar.
+
+Parity bar (floating point): max |gpu - oracle| <= 2e-2 * rms(oracle) and
+sum |gpu - oracle| / sum |oracle| <= 5e-3 (bf16 storage, fp32 accumulation).
+Integer outputs are compared exactly.
+"""
+import sys
+
+import numpy as np
+
+import synth
+from synth import recipes
+
+MAX_ABS_REL_RMS = 2e-2
+MEAN_REL = 5e-3
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def parity(got, ref, what="", max_abs_rel=MAX_ABS_REL_RMS, mean_rel=MEAN_REL):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite GPU output"
+    err = np.abs(got - ref)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    max_abs = float(err.max()) if err.size else 0.0
+    l1 = float(err.sum() / max(np.abs(ref).sum(), 1e-300))
+    log(f"  parity {what}: max_abs={max_abs:.3e} (bar {max_abs_rel * rms:.3e}) "
+        f"mean_rel={l1:.3e} (bar {mean_rel:.1e})")
+    assert max_abs <= max_abs_rel * rms, f"{what}: max_abs {max_abs} > {max_abs_rel} * rms {rms}"
+    assert l1 <= mean_rel, f"{what}: mean relative error {l1} > {mean_rel}"
+    return max_abs, l1
+
+
+def f64(u16):
+    return synth.bf16_to_f32(u16).astype(np.float64)
+
+
+def to_dev_bf16(u16, device):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(u16)).view(torch.bfloat16).to(device)
+
+
+def bf16_host(t):
+    import torch
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def layer_to_dev(layer_host, device):
+    """Oracle-side field names -> library field names, on the device."""
+    m = {"in_norm": "input_layernorm", "q": "q_proj", "k": "k_proj", "v": "v_proj",
+         "q_norm": "q_norm", "k_norm": "k_norm", "o": "o_proj",
+         "post_norm": "post_attention_layernorm", "gate": "gate_proj", "up": "up_proj",
+         "down": "down_proj"}
+    return {m[k]: to_dev_bf16(v, device) for k, v in layer_host.items()}
+
+
+def new_cache(B, nkv, cap, device, hd=128, fill=None):
+    import torch
+    k = torch.empty((B, nkv, cap, hd), dtype=torch.bfloat16, device=device)
+    vt = torch.empty((B, nkv, hd, cap), dtype=torch.bfloat16, device=device)
+    if fill is None:
+        k.fill_(float("nan"))  # untouched slots must never be read
+        vt.fill_(float("nan"))
+    return k, vt
+
+
+def fill_cache_synthetic(k, vt, seed, l, n_pos, ctx):
+    """Positions [0, n_pos) of every (sequence, kv head) from the generator, logical tensor
+    [B, nkv, ctx, hd] named kv.{l}.k / kv.{l}.v."""
+    B, nkv, cap, hd = k.shape
+    kn, vn = recipes.kv_names(l)
+    for b in range(B):
+        for h in range(nkv):
+            off = ((b * nkv + h) * ctx) * hd
+            synth.normal_bf16_device(k[b, h], seed, kn, 0.0, 1.0, offset=off,
+                                     logical=(1, n_pos, hd), strides=(0, hd, 1))
+            synth.normal_bf16_device(vt[b, h], seed, vn, 0.0, 1.0, offset=off,
+                                     logical=(1, n_pos, hd), strides=(0, 1, cap))
+
+
+def cache_k_logical(k, b, n_pos):
+    """[nkv, n_pos, hd] float64 from the device K cache."""
+    return f64(bf16_host(k[b, :, :n_pos, :]))
+
+
+def cache_v_logical(vt, b, n_pos):
+    return f64(bf16_host(vt[b, :, :, :n_pos])).transpose(0, 2, 1)
+
+
+def small_cfg(H=256, nq=4, nkv=2, I=512, L=2, V=512, qk_norm=1, max_pos=4096):
+    return dict(hidden_size=H, num_attention_heads=nq, num_key_value_heads=nkv, head_dim=128,
+                intermediate_size=I, num_hidden_layers=L, vocab_size=V,
+                max_position_embeddings=max_pos, rms_norm_eps=1e-6, rope_theta=1e6,
+                qk_norm=qk_norm, tie_word_embeddings=1)

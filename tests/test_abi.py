@@ -1,0 +1,126 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry point, and
+rejects bad arguments on the host (nothing reaches the GPU on these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decoder_only_forward_amd as q3
+from synth import recipes
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "qwen3.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qwen3_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    decl = declared_functions()
+    assert set(decl) == set(q3.EXPORTS), decl
+
+
+def test_library_exports_every_declared_symbol():
+    lib = q3.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    lib = q3.lib()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.qwen3_status_string(code)
+
+
+def _fake_layer():
+    return {k: 0x1000 * (i + 1) for i, k in enumerate(q3.LAYER_FIELDS)}
+
+
+def _expect(rc_fn, code, text):
+    with pytest.raises(RuntimeError) as ei:
+        rc_fn()
+    msg = str(ei.value)
+    assert q3.lib().qwen3_status_string(code).decode() in msg, msg
+    assert text in msg, msg
+
+
+def test_workspace_bytes_scale_with_tokens():
+    cfg = recipes.QWEN3_0P6B
+    a = q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_BLOCK_PREFILL, 1, 128)
+    b = q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_BLOCK_PREFILL, 4, 2048)
+    assert 0 < a < b
+    assert q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_STACK_DECODE, 64) > 0
+    assert q3.qwen3_workspace_bytes(recipes.MOE_2048, q3.QWEN3_OP_MOE_FFN, 8192) > 0
+    bad = dict(cfg, head_dim=64)
+    assert q3.qwen3_workspace_bytes(bad, q3.QWEN3_OP_BLOCK_PREFILL, 1, 8) == 0
+    assert b"head_dim" in q3.lib().qwen3_last_error()
+
+
+def test_block_prefill_rejects_bad_arguments():
+    cfg = dict(recipes.QWEN3_0P6B)
+    lw = _fake_layer()
+    cache = q3.make_kv_layer(0x10000, 0x20000, 128)
+    args = dict(rope=0x3000, x_in=0x4000, x_out=0x5000, batch=1, seq_len=64, pos0=0,
+                cache=cache, workspace=None)
+
+    def call(c=cfg, w=lw, **kw):
+        a = dict(args, **kw)
+        return q3.qwen3_block_prefill(c, w, a["rope"], a["x_in"], a["x_out"], a["batch"],
+                                      a["seq_len"], a["pos0"], a["cache"], a["workspace"],
+                                      stream=0)
+
+    _expect(lambda: call(c=dict(cfg, head_dim=64)), q3.QWEN3_EUNSUPPORTED, "head_dim")
+    _expect(lambda: call(c=dict(cfg, num_key_value_heads=3)), q3.QWEN3_EINVAL,
+            "num_key_value_heads")
+    _expect(lambda: call(c=dict(cfg, num_attention_heads=32, num_key_value_heads=2)),
+            q3.QWEN3_EUNSUPPORTED, "group size")
+    _expect(lambda: call(w=dict(lw, o_proj=0)), q3.QWEN3_EINVAL, "o_proj")
+    _expect(lambda: call(w=dict(lw, q_proj=0x1001)), q3.QWEN3_EINVAL, "q_proj")
+    _expect(lambda: call(x_out=0x4000), q3.QWEN3_EINVAL, "alias")
+    _expect(lambda: call(seq_len=129), q3.QWEN3_ERANGE, "capacity")
+    _expect(lambda: call(pos0=-1), q3.QWEN3_ERANGE, "pos0")
+    _expect(lambda: call(cache=q3.make_kv_layer(0x10000, 0x20000, 100)), q3.QWEN3_EINVAL,
+            "capacity")
+    big = dict(cfg, max_position_embeddings=100)
+    _expect(lambda: call(c=big, seq_len=101, cache=q3.make_kv_layer(0x10000, 0x20000, 128)),
+            q3.QWEN3_ERANGE, "max_position_embeddings")
+    _expect(lambda: call(), q3.QWEN3_EWORKSPACE, "workspace")
+
+
+def test_moe_rejects_bad_arguments():
+    w = q3.make_moe_weights(0x1000, 0x2000, 0x3000)
+    base = dict(recipes.MOE_2048)
+
+    def call(c=base, n=16):
+        q3.qwen3_moe_ffn(c, w, 0x4000, 0x5000, n, stream=0)
+
+    _expect(lambda: call(c=dict(base, num_experts_per_tok=9)), q3.QWEN3_EUNSUPPORTED,
+            "num_experts_per_tok")
+    _expect(lambda: call(c=dict(base, num_experts=300)), q3.QWEN3_EUNSUPPORTED, "num_experts")
+    _expect(lambda: call(c=dict(base, moe_intermediate_size=100)), q3.QWEN3_EUNSUPPORTED,
+            "moe_intermediate_size")
+    _expect(lambda: call(n=0), q3.QWEN3_EINVAL, "n_tokens")
+    _expect(lambda: call(), q3.QWEN3_EWORKSPACE, "workspace")
+
+
+def test_stack_rejects_bad_arguments():
+    cfg = dict(recipes.QWEN3_0P6B, num_hidden_layers=2)
+    layers = [_fake_layer(), _fake_layer()]
+    mw, keep = q3.make_model_weights(0x7000, 0x8000, layers)
+    caches = [q3.make_kv_layer(0x10000, 0x20000, 128)] * 2
+
+    def call(c=cfg, mode=q3.QWEN3_LOGITS_ALL, logits=0x9000, seq_len=16, cs=caches):
+        q3.qwen3_stack_forward(c, mw, 0x3000, 0x6000, 1, seq_len, 0, None, cs, logits, mode,
+                               None, None, stream=0)
+
+    _expect(lambda: call(mode=7), q3.QWEN3_EINVAL, "logits_mode")
+    _expect(lambda: call(logits=0), q3.QWEN3_EINVAL, "logits")
+    _expect(lambda: call(seq_len=200), q3.QWEN3_ERANGE, "capacity")
+    _expect(lambda: call(cs=[caches[0], q3.make_kv_layer(0x10000, 0x20000, 192)]),
+            q3.QWEN3_EINVAL, "capacity")
+    _expect(lambda: call(), q3.QWEN3_EWORKSPACE, "workspace")

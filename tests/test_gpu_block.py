@@ -1,0 +1,145 @@
+"""GPU parity: one decoder block (prefill, chunked prefill, decode) against the oracle."""
+import numpy as np
+import pytest
+
+import decoder_only_forward_amd as q3
+import oracle
+import synth
+from synth import recipes
+from q3_testutil import (bf16_host, cache_k_logical, cache_v_logical, f64, fill_cache_synthetic,
+                         layer_to_dev, log, new_cache, parity, small_cfg, to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+def _rope(cfg, dev):
+    import torch
+    rope = torch.empty(2 * cfg["max_position_embeddings"] * 64, dtype=torch.float32, device=dev)
+    q3.qwen3_rope_table_init(cfg, rope)
+    return rope
+
+
+PREFILL_CASES = {
+    # name: (cfg kwargs, B, S, pos0)
+    "small_ragged": (dict(), 2, 200, 0),
+    "small_chunked": (dict(), 2, 93, 70),
+    "group7": (dict(nq=7, nkv=1), 1, 130, 0),
+    "no_qk_norm": (dict(qk_norm=0), 1, 64, 0),
+    "one_token": (dict(), 3, 1, 0),
+    "cfg1_0p6b": (None, 1, 128, 0),
+}
+
+
+@pytest.mark.parametrize("name", list(PREFILL_CASES))
+def test_block_prefill_parity(gpu, name):
+    import torch
+    kw, B, S, pos0 = PREFILL_CASES[name]
+    cfg = dict(recipes.QWEN3_0P6B) if kw is None else small_cfg(**kw)
+    log(f"case block_prefill/{name}: B={B} S={S} pos0={pos0}")
+    seed = 11
+    H, nkv = cfg["hidden_size"], cfg["num_key_value_heads"]
+    layer = recipes.layer_host(seed, cfg, 0)
+    x = synth.normal_bf16(seed, recipes.activations_name(), (B, S, H))
+    lw = layer_to_dev(layer, gpu)
+    rope = _rope(cfg, gpu)
+    cap = ((pos0 + S + 63) // 64) * 64
+    k, vt = new_cache(B, nkv, cap, gpu)
+    if pos0:
+        fill_cache_synthetic(k, vt, seed, 0, pos0, pos0)
+    xd = to_dev_bf16(x, gpu)
+    out = torch.empty_like(xd)
+    ws = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_BLOCK_PREFILL, B, S),
+                     dtype=torch.uint8, device=gpu)
+    kv = q3.make_kv_layer(k, vt, cap)
+    q3.qwen3_block_prefill(cfg, lw, rope, xd, out, B, S, pos0, kv, ws)
+    torch.cuda.synchronize()
+    got = f64(bf16_host(out))
+    for b in range(B):
+        pk = pv = None
+        if pos0:
+            pk, pv = recipes.kv_host(seed, cfg, 0, b, pos0, (nkv, pos0))
+            pk, pv = f64(pk), f64(pv)
+        ref, nk, nv = oracle.block(cfg, layer, f64(x[b]), pos0, pk, pv)
+        parity(got[b], ref, f"x_out[b={b}]")
+        parity(cache_k_logical(k, b, pos0 + S)[:, pos0:], nk, f"cache_k[b={b}]")
+        parity(cache_v_logical(vt, b, pos0 + S)[:, pos0:], nv, f"cache_v[b={b}]")
+        if pos0:  # the past must be left untouched
+            np.testing.assert_array_equal(cache_k_logical(k, b, pos0), pk)
+
+
+def test_block_prefill_deterministic(gpu):
+    import torch
+    cfg = small_cfg()
+    B, S = 2, 150
+    layer = layer_to_dev(recipes.layer_host(3, cfg, 0), gpu)
+    x = to_dev_bf16(synth.normal_bf16(3, recipes.activations_name(), (B, S, 256)), gpu)
+    rope = _rope(cfg, gpu)
+    outs = []
+    for _ in range(2):
+        k, vt = new_cache(B, 2, 192, gpu)
+        out = torch.empty_like(x)
+        ws = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_BLOCK_PREFILL, B, S),
+                         dtype=torch.uint8, device=gpu)
+        q3.qwen3_block_prefill(cfg, layer, rope, x, out, B, S, 0, q3.make_kv_layer(k, vt, 192),
+                               ws)
+        torch.cuda.synchronize()
+        outs.append(bf16_host(out))
+    np.testing.assert_array_equal(outs[0], outs[1])
+
+
+DECODE_CASES = {
+    "small": (dict(), [0, 100, 255, 37], 256),
+    "group7": (dict(nq=7, nkv=1), [300, 5], 320),
+    "cfg_0p6b": (None, [4096, 1000], 4160),
+}
+
+
+@pytest.mark.parametrize("name", list(DECODE_CASES))
+def test_block_decode_parity(gpu, name):
+    import torch
+    kw, positions, cap = DECODE_CASES[name]
+    cfg = dict(recipes.QWEN3_0P6B) if kw is None else small_cfg(**kw)
+    log(f"case block_decode/{name}: pos={positions} cap={cap}")
+    seed = 12
+    B = len(positions)
+    H, nkv = cfg["hidden_size"], cfg["num_key_value_heads"]
+    layer = recipes.layer_host(seed, cfg, 0)
+    x = synth.normal_bf16(seed, recipes.activations_name(), (B, H))
+    ctx = max(positions)
+    k, vt = new_cache(B, nkv, cap, gpu)
+    fill_cache_synthetic(k, vt, seed, 0, ctx, ctx)  # every sequence: positions < ctx
+    pos = torch.tensor(positions, dtype=torch.int32, device=gpu)
+    xd = to_dev_bf16(x, gpu)
+    out = torch.empty_like(xd)
+    ws = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_BLOCK_DECODE, B),
+                     dtype=torch.uint8, device=gpu)
+    q3.qwen3_block_decode(cfg, layer_to_dev(layer, gpu), _rope(cfg, gpu), xd, out, B, pos,
+                          q3.make_kv_layer(k, vt, cap), ws)
+    torch.cuda.synchronize()
+    got = f64(bf16_host(out))
+    for b, p in enumerate(positions):
+        pk, pv = recipes.kv_host(seed, cfg, 0, b, p, (nkv, ctx))
+        ref, nk, nv = oracle.block(cfg, layer, f64(x[b:b + 1]), p, f64(pk), f64(pv))
+        parity(got[b:b + 1], ref, f"x_out[b={b}]")
+        parity(cache_k_logical(k, b, p + 1)[:, p:], nk, f"cache_k[b={b}]")
+        parity(cache_v_logical(vt, b, p + 1)[:, p:], nv, f"cache_v[b={b}]")
+
+
+def test_block_decode_out_of_range_position_gives_nan_row(gpu):
+    import torch
+    cfg = small_cfg()
+    B, cap = 2, 128
+    layer = layer_to_dev(recipes.layer_host(5, cfg, 0), gpu)
+    x = to_dev_bf16(synth.normal_bf16(5, recipes.activations_name(), (B, 256)), gpu)
+    k, vt = new_cache(B, 2, cap, gpu)
+    k.zero_()
+    vt.zero_()
+    pos = torch.tensor([10, cap], dtype=torch.int32, device=gpu)
+    out = torch.empty_like(x)
+    ws = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_BLOCK_DECODE, B),
+                     dtype=torch.uint8, device=gpu)
+    q3.qwen3_block_decode(cfg, layer, _rope(cfg, gpu), x, out, B, pos,
+                          q3.make_kv_layer(k, vt, cap), ws)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    assert np.all(np.isfinite(o[0])) and np.all(np.isnan(o[1]))

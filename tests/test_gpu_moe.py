@@ -1,0 +1,87 @@
+"""GPU parity: routed MoE FFN (router, top-k, dispatch order, grouped SwiGLU experts,
+weighted combine) against the oracle.  Integer results (top-k indices, dispatch order)
+must be bit-exact when computed from the same router logits."""
+import numpy as np
+import pytest
+
+import decoder_only_forward_amd as q3
+import oracle
+import synth
+from synth import recipes
+from q3_testutil import bf16_host, f64, log, parity, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def run_moe(cfg, router, gu, dn, x, dev):
+    import torch
+    T = x.shape[0]
+    E, k, H = cfg["num_experts"], cfg["num_experts_per_tok"], cfg["hidden_size"]
+    w = q3.make_moe_weights(to_dev_bf16(router, dev), to_dev_bf16(gu, dev), to_dev_bf16(dn, dev))
+    keep = [to_dev_bf16(a, dev) for a in (router, gu, dn)]
+    w = q3.make_moe_weights(*keep)
+    xd = to_dev_bf16(x, dev)
+    y = torch.empty_like(xd)
+    out = dict(
+        logits=torch.empty((T, E), dtype=torch.float32, device=dev),
+        idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+        w=torch.empty((T, k), dtype=torch.float32, device=dev),
+        offsets=torch.empty((E + 1,), dtype=torch.int32, device=dev),
+        perm=torch.empty((T * k,), dtype=torch.int32, device=dev),
+        inv=torch.empty((T, k), dtype=torch.int32, device=dev))
+    ws = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_MOE_FFN, T), dtype=torch.uint8,
+                     device=dev)
+    q3.qwen3_moe_ffn(cfg, w, xd, y, T, out["logits"], out["idx"], out["w"], out["offsets"],
+                     out["perm"], out["inv"], ws)
+    torch.cuda.synchronize()
+    res = {k_: v.cpu().numpy() for k_, v in out.items()}
+    res["y"] = f64(bf16_host(y))
+    return res
+
+
+MOE_CASES = {
+    "e16_k4_ragged": (dict(num_experts=16, num_experts_per_tok=4, moe_intermediate_size=128,
+                           hidden_size=256), 300, False),
+    "e128_k8_sparse": (dict(num_experts=128, num_experts_per_tok=8, moe_intermediate_size=256,
+                            hidden_size=512), 200, True),
+    "e8_k2_unnormalised": (dict(num_experts=8, num_experts_per_tok=2, moe_intermediate_size=128,
+                                hidden_size=256, norm_topk_prob=0), 130, False),
+}
+
+
+@pytest.mark.parametrize("name", list(MOE_CASES))
+def test_moe_parity(gpu, name):
+    kw, T, skew = MOE_CASES[name]
+    cfg = dict(norm_topk_prob=1, rms_norm_eps=1e-6)
+    cfg.update(kw)
+    log(f"case moe/{name}: T={T} {kw}")
+    router, gu, dn = recipes.moe_host(31, cfg, skew=skew)
+    x = synth.normal_bf16(31, recipes.activations_name(), (T, cfg["hidden_size"]))
+    g = run_moe(cfg, router, gu, dn, x, gpu)
+    y_ref, idx_ref, w_ref, lg_ref = oracle.moe_ffn(cfg, router, gu, dn, f64(x))
+    parity(g["logits"], lg_ref, "router_logits")
+    k, E = cfg["num_experts_per_tok"], cfg["num_experts"]
+    # integer work on the GPU's own logits: bit-exact
+    np.testing.assert_array_equal(g["idx"], oracle.topk(g["logits"], k))
+    counts, offsets, perm, inv = oracle.permute(g["idx"], E)
+    np.testing.assert_array_equal(g["offsets"], offsets)
+    np.testing.assert_array_equal(g["perm"], perm)
+    np.testing.assert_array_equal(g["inv"], inv)
+    w_same = oracle.route_weights(g["logits"].astype(np.float64), g["idx"], cfg["norm_topk_prob"])
+    np.testing.assert_allclose(g["w"], w_same, rtol=2e-6, atol=1e-7)
+    # outputs: tokens whose routing agrees with the oracle's own routing
+    agree = np.all(np.sort(g["idx"], axis=1) == np.sort(idx_ref, axis=1), axis=1)
+    log(f"  routing agreement {agree.sum()}/{T}")
+    assert agree.mean() > 0.97
+    parity(g["y"][agree], y_ref[agree], "y")
+
+
+def test_moe_deterministic(gpu):
+    kw, T, _ = MOE_CASES["e16_k4_ragged"]
+    cfg = dict(norm_topk_prob=1, rms_norm_eps=1e-6, **kw)
+    router, gu, dn = recipes.moe_host(32, cfg, skew=False)
+    x = synth.normal_bf16(32, recipes.activations_name(), (T, cfg["hidden_size"]))
+    a = run_moe(cfg, router, gu, dn, x, gpu)
+    b = run_moe(cfg, router, gu, dn, x, gpu)
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key])
