@@ -1,0 +1,401 @@
+#!/usr/bin/env python3
+"""Throughput benchmark of the Qwen3 decoder forward on one MI355X.
+
+Default workload (the one the JSON line's value is quoted on): the 28-layer
+Qwen3-0.6B-shaped stack, prefill of 4 sequences x 2048 tokens with the tied LM head on
+every position (fp32 logits) and the greedy next token; one step = one forward pass.
+Also measured, reported under "workloads": one decode step of the same stack at batch
+64 against a 4096-token KV cache, the routed MoE FFN layer (8192 tokens, 128 experts,
+top-8, skewed load), the 7B-shaped block at 32768 tokens and the 0.6B block at 128.
+
+All inputs are seeded synthetic data generated directly in HBM; the timed region
+contains only library calls.  Per-kernel durations come from HIP events the library
+records around the launches of one kernel class (qwen3_profile_begin/end) during the
+timed region; rooflines use algorithmic flops or bytes per launch.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads a,b,...]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill & decode tokens/s, Qwen3-0.6B-shape stack; % of bf16 MFMA / HBM peak"
+PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E peak
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def roofline_mfma(flops_per_launch, avg_ms, traffic=None):
+    ach = flops_per_launch / (avg_ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_MFMA_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ach / PEAK_MFMA_TFLOPS, 4), "traffic": traffic}
+
+
+def roofline_hbm(bytes_per_launch, avg_ms, traffic=None):
+    ach = bytes_per_launch / (avg_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic}
+
+
+class Timer:
+    """Times K calls of fn on torch's current stream with HIP events; optionally has the
+    library time one kernel class over the same region."""
+
+    def __init__(self, torch, q3):
+        self.torch, self.q3 = torch, q3
+
+    def run(self, fn, steps, warmup, tag=None, launches_per_step=1):
+        torch, q3 = self.torch, self.q3
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        if tag:
+            q3.qwen3_profile_begin(tag, steps * launches_per_step)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        total = t0.elapsed_time(t1)
+        kernel = None
+        if tag:
+            kms, n = q3.qwen3_profile_end()
+            kernel = {"tag": tag, "launches": n, "avg_ms": kms / max(n, 1)}
+        return total / steps, kernel
+
+
+# ------------------------------------------------------------------------- workloads
+
+def setup_stack(torch, q3, recipes, dev, cfg, B, S, cap, seed_model, seed_in):
+    model = recipes.model_device(seed_model, cfg, dev)
+    mw, keep = q3.make_model_weights(model["embed"], model["norm"], model["layers"],
+                                     model["lm_head"])
+    rope = torch.empty(2 * cfg["max_position_embeddings"] * 64, dtype=torch.float32, device=dev)
+    q3.qwen3_rope_table_init(cfg, rope)
+    L, nkv = cfg["num_hidden_layers"], cfg["num_key_value_heads"]
+    caches = []
+    for _ in range(L):
+        k = torch.empty((B, nkv, cap, 128), dtype=torch.bfloat16, device=dev)
+        vt = torch.empty((B, nkv, 128, cap), dtype=torch.bfloat16, device=dev)
+        caches.append((k, vt))
+    return model, mw, keep, rope, caches
+
+
+def wl_prefill(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown):
+    cfg = dict(recipes.QWEN3_0P6B)
+    B, S = 4, 2048
+    model, mw, keep, rope, caches = setup_stack(torch, q3, recipes, dev, cfg, B, S, S,
+                                                recipes.MODEL_SEED_0P6B, 2)
+    kvs = [q3.make_kv_layer(k, vt, S) for k, vt in caches]
+    ids = torch.empty((B, S), dtype=torch.int32, device=dev)
+    synth.uniform_i32_device(ids, 2, "input.ids", 0, cfg["vocab_size"])
+    V = cfg["vocab_size"]
+    logits = torch.empty((B, S, V), dtype=torch.float32, device=dev)
+    nxt = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_STACK_PREFILL, B, S),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        q3.qwen3_stack_forward(cfg, mw, rope, ids, B, S, 0, None, kvs, logits,
+                               q3.QWEN3_LOGITS_ALL, nxt, ws)
+
+    L, H, I = cfg["num_hidden_layers"], cfg["hidden_size"], cfg["intermediate_size"]
+    T = B * S
+    ms, kern = timer.run(step, steps, warmup, tag="gate_up_gemm", launches_per_step=L)
+    flops_gu = 2.0 * T * 2 * I * H
+    out = {"name": "stack_0p6b_prefill", "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms,
+           "config": {"workload": "stack_0p6b_prefill", "batch": B, "seq_len": S, "layers": L,
+                      "hidden": H, "heads": "16q/8kv x128", "intermediate": I, "vocab": V,
+                      "lm_head": "tied, fp32 logits for all positions",
+                      "greedy_next_token": True},
+           "dominant_kernel": dict(kern, flops_per_launch=flops_gu),
+           "roofline": roofline_mfma(flops_gu, kern["avg_ms"])}
+    total_flops = stack_prefill_flops(cfg, B, S)
+    out["whole_step_mfma_frac"] = round(total_flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)
+    out["algorithmic_tflop_per_step"] = round(total_flops / 1e12, 3)
+    if breakdown:
+        out["kernels"] = kernel_breakdown(timer, step, {
+            "qkv_gemm": L, "qk_norm_rope_cache": L, "attn_prefill": L, "o_proj_gemm": L,
+            "gate_up_gemm": L, "down_gemm": L, "lm_head_gemm": 1, "argmax": 1},
+            steps=min(steps, 3))
+    del logits, caches, kvs, model, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def stack_prefill_flops(cfg, B, S):
+    H, nq, nkv, hd, I, L, V = (cfg["hidden_size"], cfg["num_attention_heads"],
+                               cfg["num_key_value_heads"], cfg["head_dim"],
+                               cfg["intermediate_size"], cfg["num_hidden_layers"],
+                               cfg["vocab_size"])
+    T = B * S
+    gemm = 2.0 * T * H * ((nq + 2 * nkv) * hd + nq * hd + 3 * I)
+    attn = 4.0 * hd * nq * B * S * (S + 1) / 2
+    return L * (gemm + attn) + 2.0 * T * H * V
+
+
+def kernel_breakdown(timer, step, tags, steps):
+    res = {}
+    for tag, per_step in tags.items():
+        _, k = timer.run(step, steps, 1, tag=tag, launches_per_step=per_step)
+        res[tag] = {"avg_ms": round(k["avg_ms"], 4), "launches_per_step": per_step,
+                    "ms_per_step": round(k["avg_ms"] * per_step, 4)}
+    return res
+
+
+def wl_decode(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown):
+    cfg = dict(recipes.QWEN3_0P6B)
+    B, ctx = 64, 4096
+    cap = 4160
+    model, mw, keep, rope, caches = setup_stack(torch, q3, recipes, dev, cfg, B, 1, cap,
+                                                recipes.MODEL_SEED_0P6B, 3)
+    t0 = time.time()
+    for l, (k, vt) in enumerate(caches):
+        recipes.kv_fill_device(k, vt, 3, l, ctx, ctx)
+    torch.cuda.synchronize()
+    log(f"  decode: KV cache {len(caches)} x 2 x {tuple(caches[0][0].shape)} filled in "
+        f"{time.time() - t0:.1f}s")
+    kvs = [q3.make_kv_layer(k, vt, cap) for k, vt in caches]
+    ids = torch.empty((B,), dtype=torch.int32, device=dev)
+    synth.uniform_i32_device(ids, 3, "input.ids", 0, cfg["vocab_size"])
+    pos = torch.full((B,), ctx, dtype=torch.int32, device=dev)
+    V = cfg["vocab_size"]
+    logits = torch.empty((B, V), dtype=torch.float32, device=dev)
+    nxt = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_STACK_DECODE, B),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        q3.qwen3_stack_forward(cfg, mw, rope, ids, B, 1, 0, pos, kvs, logits,
+                               q3.QWEN3_LOGITS_LAST, nxt, ws)
+
+    L, nkv, nq = cfg["num_hidden_layers"], cfg["num_key_value_heads"], cfg["num_attention_heads"]
+    ms, kern = timer.run(step, steps, warmup, tag="attn_decode", launches_per_step=L)
+    kv_bytes = 2.0 * B * nkv * (ctx + 1) * 128 * 2
+    attn_bytes = kv_bytes + 2.0 * B * nq * 128 * 2  # + q in, o out
+    step_bytes = decode_step_bytes(cfg, B, ctx)
+    out = {"name": "stack_0p6b_decode", "tokens_per_s": B / (ms * 1e-3), "ms_per_step": ms,
+           "config": {"workload": "stack_0p6b_decode", "batch": B, "context": ctx,
+                      "new_tokens_per_seq": 1, "layers": L, "greedy_next_token": True},
+           "dominant_kernel": dict(kern, bytes_per_launch=attn_bytes),
+           "roofline": roofline_hbm(attn_bytes, kern["avg_ms"]),
+           "whole_step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "algorithmic_gb_per_step": round(step_bytes / 1e9, 3)}
+    if breakdown:
+        out["kernels"] = kernel_breakdown(timer, step, {
+            "qkv_gemm": L, "qk_norm_rope_cache": L, "attn_decode": L, "o_proj_gemm": L,
+            "gate_up_gemm": L, "down_gemm": L, "lm_head_gemm": 1, "argmax": 1},
+            steps=min(steps, 3))
+    del caches, kvs, model, ws, logits
+    torch.cuda.empty_cache()
+    return out
+
+
+def decode_step_bytes(cfg, B, ctx):
+    H, nq, nkv, hd, I, L, V = (cfg["hidden_size"], cfg["num_attention_heads"],
+                               cfg["num_key_value_heads"], cfg["head_dim"],
+                               cfg["intermediate_size"], cfg["num_hidden_layers"],
+                               cfg["vocab_size"])
+    layer_w = 2.0 * (H * (nq + 2 * nkv) * hd + nq * hd * H + 3 * I * H + 2 * H + 2 * hd)
+    kv_read = 2.0 * B * nkv * (ctx + 1) * hd * 2
+    kv_write = 2.0 * B * nkv * hd * 2
+    return L * (layer_w + kv_read + kv_write) + 2.0 * V * H + 4.0 * B * V
+
+
+def wl_moe(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown):
+    cfg = dict(recipes.MOE_2048)
+    T = 8192
+    router, gu, dn = recipes.moe_device(4, cfg, dev)
+    w = q3.make_moe_weights(router, gu, dn)
+    x = torch.empty((T, cfg["hidden_size"]), dtype=torch.bfloat16, device=dev)
+    synth.normal_bf16_device(x, 4, recipes.activations_name(), 0.0, 1.0)
+    y = torch.empty_like(x)
+    E, k = cfg["num_experts"], cfg["num_experts_per_tok"]
+    offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    ws = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_MOE_FFN, T), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        q3.qwen3_moe_ffn(cfg, w, x, y, T, None, None, None, offsets, None, None, ws)
+
+    ms, kern = timer.run(step, steps, warmup, tag="moe_gate_up_gemm", launches_per_step=1)
+    H, I = cfg["hidden_size"], cfg["moe_intermediate_size"]
+    flops_gu = 2.0 * T * k * 2 * I * H
+    counts = (offsets[1:] - offsets[:-1]).cpu().numpy()
+    total = 2.0 * T * E * H + flops_gu + 2.0 * T * k * I * H
+    out = {"name": "moe_ffn", "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms,
+           "config": {"workload": "moe_ffn_2048x128e_top8", "tokens": T, "hidden": H,
+                      "experts": E, "top_k": k, "expert_intermediate": I,
+                      "load_max_over_mean": round(float(counts.max() / counts.mean()), 2),
+                      "load_min": int(counts.min()), "load_max": int(counts.max())},
+           "dominant_kernel": dict(kern, flops_per_launch=flops_gu),
+           "roofline": roofline_mfma(flops_gu, kern["avg_ms"]),
+           "whole_step_mfma_frac": round(total / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)}
+    if breakdown:
+        out["kernels"] = kernel_breakdown(timer, step, {
+            "moe_router_gemm": 1, "moe_route": 1, "moe_gate_up_gemm": 1, "moe_down_gemm": 1,
+            "moe_combine": 1}, steps=min(steps, 3))
+    del router, gu, dn, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def wl_block(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, big):
+    cfg = dict(recipes.QWEN_7B_BLOCK if big else recipes.QWEN3_0P6B)
+    B, S = (1, 32768) if big else (1, 128)
+    seed = 5 if big else 1
+    w = recipes.layer_device(seed, cfg, 0, dev)
+    rope = torch.empty(2 * cfg["max_position_embeddings"] * 64, dtype=torch.float32, device=dev)
+    q3.qwen3_rope_table_init(cfg, rope)
+    nkv = cfg["num_key_value_heads"]
+    cap = ((S + 63) // 64) * 64
+    k = torch.empty((B, nkv, cap, 128), dtype=torch.bfloat16, device=dev)
+    vt = torch.empty((B, nkv, 128, cap), dtype=torch.bfloat16, device=dev)
+    kv = q3.make_kv_layer(k, vt, cap)
+    H = cfg["hidden_size"]
+    x = torch.empty((B, S, H), dtype=torch.bfloat16, device=dev)
+    synth.normal_bf16_device(x, seed, recipes.activations_name(), 0.0, 1.0)
+    xo = torch.empty_like(x)
+    ws = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_BLOCK_PREFILL, B, S),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        q3.qwen3_block_prefill(cfg, w, rope, x, xo, B, S, 0, kv, ws)
+
+    c1 = dict(cfg, num_hidden_layers=1, vocab_size=0)
+    flops = stack_prefill_flops(c1, B, S)
+    nq, hd, I = cfg["num_attention_heads"], 128, cfg["intermediate_size"]
+    attn_flops = 4.0 * hd * nq * B * S * (S + 1) / 2
+    ms, kern = timer.run(step, steps, warmup, tag="attn_prefill")
+    out = {"name": "block_7b" if big else "block_0p6b", "tokens_per_s": B * S / (ms * 1e-3),
+           "ms_per_step": ms,
+           "config": {"workload": "block_7b" if big else "block_0p6b", "batch": B,
+                      "seq_len": S, "hidden": H, "heads": f"{nq}q/{nkv}kv x128",
+                      "intermediate": I},
+           "dominant_kernel": dict(kern, flops_per_launch=attn_flops),
+           "roofline": roofline_mfma(attn_flops, kern["avg_ms"]),
+           "whole_step_mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+           "algorithmic_tflop_per_step": round(flops / 1e12, 3)}
+    if breakdown:
+        kb = kernel_breakdown(timer, step, {
+            "qkv_gemm": 1, "qk_norm_rope_cache": 1, "attn_prefill": 1, "o_proj_gemm": 1,
+            "gate_up_gemm": 1, "down_gemm": 1}, steps=min(steps, 3))
+        T = B * S
+        gf = {"qkv_gemm": 2.0 * T * H * (nq + 2 * nkv) * hd, "o_proj_gemm": 2.0 * T * H * nq * hd,
+              "gate_up_gemm": 2.0 * T * H * 2 * I, "down_gemm": 2.0 * T * H * I,
+              "attn_prefill": attn_flops}
+        for t, f in gf.items():
+            kb[t]["mfma_frac"] = round(f / (kb[t]["avg_ms"] * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)
+        out["kernels"] = kb
+    del w, k, vt, x, xo, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+# ------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(n_tokens):
+    """The oracle (as it stands) on a bounded sample of the prefill workload: the first
+    n_tokens of sequence 0, all 28 layers, final norm and tied LM head on every row."""
+    import numpy as np
+    import oracle
+    import synth
+    from synth import recipes
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
+    oracle.set_threads(threads)
+    cfg = dict(recipes.QWEN3_0P6B)
+    model = recipes.model_host(recipes.MODEL_SEED_0P6B, cfg)
+    ids = synth.uniform_i32(2, "input.ids", (4, 2048), 0, cfg["vocab_size"])[0, :n_tokens]
+    t0 = time.time()
+    oracle.stack_prefill(cfg, model, np.ascontiguousarray(ids))
+    dt = time.time() - t0
+    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": oracle.get_threads(),
+            "kind": "oracle",
+            "sample": f"sequence 0, first {n_tokens} tokens of the 4x2048 prefill workload; 28 "
+                      f"layers + final norm + tied LM head on all {n_tokens} rows; fp64 C++ "
+                      f"oracle, {dt:.1f}s wall"}
+
+
+# ------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workloads", default="prefill,decode,moe,block7b,block")
+    ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=192,
+                    help="prefix length for the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--copy-gib", type=float, default=0.0,
+                    help="run a plain device copy of this size first (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU design is described in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import decoder_only_forward_amd as q3
+    import synth
+    from synth import recipes
+    dev = torch.device("cuda:0")
+    q3.lib()
+    timer = Timer(torch, q3)
+    if args.copy_gib > 0:
+        n = int(args.copy_gib * (1 << 30)) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+    wls = [w.strip() for w in args.workloads.split(",") if w.strip()]
+    bd = not args.no_breakdown
+    results = {}
+    fns = {"prefill": lambda: wl_prefill(torch, q3, recipes, synth, dev, args.steps, args.warmup,
+                                         timer, bd),
+           "decode": lambda: wl_decode(torch, q3, recipes, synth, dev, 2 * args.steps,
+                                       args.warmup, timer, bd),
+           "moe": lambda: wl_moe(torch, q3, recipes, synth, dev, 2 * args.steps, args.warmup,
+                                 timer, bd),
+           "block7b": lambda: wl_block(torch, q3, recipes, synth, dev, max(2, args.steps // 3),
+                                       1, timer, bd, True),
+           "block": lambda: wl_block(torch, q3, recipes, synth, dev, 10 * args.steps,
+                                     args.warmup, timer, bd, False)}
+    for w in wls:
+        log(f"workload {w} ...")
+        t0 = time.time()
+        results[w] = fns[w]()
+        log(f"  {w}: {results[w]['tokens_per_s']:.1f} tokens/s, "
+            f"{results[w]['ms_per_step']:.3f} ms/step ({time.time() - t0:.1f}s)")
+
+    main_wl = "prefill" if "prefill" in results else wls[0]
+    m = results[main_wl]
+    line = {"metric": METRIC, "value": round(m["tokens_per_s"], 1), "unit": "tokens/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(m["ms_per_step"], 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+            "data": "synthetic (seeded counter-based generator, random-init weights)",
+            "config": m["config"], "roofline": m["roofline"]}
+    if "decode" in results:
+        line["decode_tokens_per_s"] = round(results["decode"]["tokens_per_s"], 1)
+    if args.cpu_tokens > 0 and main_wl == "prefill":
+        log("cpu baseline (oracle) ...")
+        line["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
+    line["workloads"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                             for kk, vv in v.items()} for k, v in results.items()}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

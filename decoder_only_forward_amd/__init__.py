@@ -33,7 +33,8 @@ QWEN3_LOGITS_LAST = 2
 
 EXPORTS = ("qwen3_workspace_bytes", "qwen3_rope_table_init", "qwen3_block_prefill",
            "qwen3_block_decode", "qwen3_moe_ffn", "qwen3_stack_forward",
-           "qwen3_status_string", "qwen3_last_error")
+           "qwen3_status_string", "qwen3_last_error", "qwen3_profile_begin",
+           "qwen3_profile_end")
 
 
 class Config(ctypes.Structure):
@@ -97,6 +98,10 @@ def lib():
         L.qwen3_status_string.argtypes = [ctypes.c_int]
         L.qwen3_last_error.restype = ctypes.c_char_p
         L.qwen3_last_error.argtypes = []
+        L.qwen3_profile_begin.restype = ctypes.c_int
+        L.qwen3_profile_begin.argtypes = [ctypes.c_char_p, i32]
+        L.qwen3_profile_end.restype = ctypes.c_int
+        L.qwen3_profile_end.argtypes = [vp, vp]
         _lib = L
     return _lib
 
@@ -222,3 +227,15 @@ def qwen3_stack_forward(cfg, w, rope, ids, batch, seq_len, pos0, pos, caches, lo
                                      _ptr(ids), batch, seq_len, pos0, _ptr(pos), arr,
                                      _ptr(logits), logits_mode, _ptr(next_ids), wp, wb,
                                      _stream(stream)))
+
+
+def qwen3_profile_begin(tag, max_launches):
+    _check(lib().qwen3_profile_begin(tag.encode(), max_launches))
+
+
+def qwen3_profile_end():
+    """Returns (total_ms, launches); synchronise the stream first."""
+    ms = ctypes.c_float()
+    n = ctypes.c_int32()
+    _check(lib().qwen3_profile_end(ctypes.byref(ms), ctypes.byref(n)))
+    return float(ms.value), int(n.value)

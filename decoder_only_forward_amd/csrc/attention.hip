@@ -4,9 +4,10 @@
 // sequence, query row at absolute position p, kv head h / (nq / nkv):
 //     o = sum_{j <= p} softmax_j(q . k_j / sqrt(hd)) v_j
 //
-// Operands: q arrives in fp16; the bf16 K/V cache tiles are converted to fp16 (exact in
-// fp16's normal range) as they are staged, and P is rounded to fp16, so both products run
-// on v_mfma_f32_16x16x32_f16 with 8x finer operand rounding than bf16 for q and P.
+// Operands: q arrives in fp16; keys/values produced by this call come from unrounded fp16
+// copies, older ones from the bf16 cache (converted to fp16, exact in fp16's normal range,
+// as they are staged); P is rounded to fp16.  Both products run on
+// v_mfma_f32_16x16x32_f16.
 // Prefill (flash-style, matrix cores):
 //   one block = 128 query rows of one q head, 4 waves x 32 rows; K tiles of 64 keys
 //   [64][128] and the matching V^T tile [128][64] are staged in LDS (double buffered).
@@ -87,6 +88,11 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnPrefillArgs a) {
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
   const float sl2 = 0.08838834764831845f * kLog2e;  // log2(e) / sqrt(128)
 
+  // Tile staging.  Keys / values at positions < pos0 come from the bf16 cache (converted
+  // to fp16 here); positions >= pos0 were produced by this call and are read from the
+  // unrounded fp16 copies.  Rows / columns at or beyond kv_len are zero.
+  const f16_t* kfbase = a.k_fresh + ((int64_t)b * a.nkv + kvh) * a.fresh_w * HD;
+  const f16_t* vfbase = a.vt_fresh + ((int64_t)b * a.nkv + kvh) * HD * a.fresh_w;
   u32x4_t rk[4], rv[4];
   const u32x4_t zero4 = {0u, 0u, 0u, 0u};
   auto gload = [&](int t) {
@@ -95,22 +101,40 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnPrefillArgs a) {
     for (int i = 0; i < 4; ++i) {
       int c = tid & 15, r = (tid >> 4) + 16 * i;
       int key = j0 + r;
-      rk[i] = key < kv_len ? ld16(kbase + (int64_t)key * HD + c * 8) : zero4;
+      u32x4_t v = zero4;
+      if (key < a.pos0)
+        v = bf16x8_to_f16x8(ld16(kbase + (int64_t)key * HD + c * 8));
+      else if (key < kv_len)
+        v = ld16(kfbase + (int64_t)(key - a.fresh_base) * HD + c * 8);
+      rk[i] = v;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int c = tid & 7, d = (tid >> 3) + 32 * i;
       int key = j0 + c * 8;
       u32x4_t v = zero4;
-      if (key + 8 <= kv_len) {
-        v = ld16(vbase + (int64_t)d * a.cap + key);
-      } else if (key < kv_len) {
-        v = ld16(vbase + (int64_t)d * a.cap + key);
-        int nvalid = kv_len - key;  // 1..7 keys valid in this chunk
+      if (key < kv_len) {
+        if (key + 8 <= a.pos0) {
+          v = bf16x8_to_f16x8(ld16(vbase + (int64_t)d * a.cap + key));
+        } else if (key >= a.pos0) {
+          v = ld16(vfbase + (int64_t)d * a.fresh_w + (key - a.fresh_base));
+        } else {  // chunk straddles pos0: element-wise choice
+          u32x4_t vc = bf16x8_to_f16x8(ld16(vbase + (int64_t)d * a.cap + key));
+          u32x4_t vf = ld16(vfbase + (int64_t)d * a.fresh_w + (key - a.fresh_base));
+          int ncache = a.pos0 - key;  // 1..7 elements from the cache
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          uint32_t keep = (2 * e + 1 < nvalid) ? 0xFFFFFFFFu : (2 * e < nvalid ? 0xFFFFu : 0u);
-          v[e] &= keep;
+          for (int e = 0; e < 4; ++e) {
+            uint32_t mc = (2 * e + 1 < ncache) ? 0xFFFFFFFFu : (2 * e < ncache ? 0xFFFFu : 0u);
+            v[e] = (vc[e] & mc) | (vf[e] & ~mc);
+          }
+        }
+        if (key + 8 > kv_len) {
+          int nvalid = kv_len - key;  // 1..7 keys valid in this chunk
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            uint32_t keep = (2 * e + 1 < nvalid) ? 0xFFFFFFFFu : (2 * e < nvalid ? 0xFFFFu : 0u);
+            v[e] &= keep;
+          }
         }
       }
       rv[i] = v;
@@ -120,14 +144,14 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnPrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int c = tid & 15, r = (tid >> 4) + 16 * i;
-      st16(&sK[st][k_off(r, c)], bf16x8_to_f16x8(rk[i]));
+      st16(&sK[st][k_off(r, c)], rk[i]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int c = tid & 7, d = (tid >> 3) + 32 * i;
       int x = d & 15;
       int base8 = (2 * c) ^ (x & ~1);
-      u32x4_t v = bf16x8_to_f16x8(rv[i]);
+      u32x4_t v = rv[i];
       if (x & 1) v = u32x4_t{v[2], v[3], v[0], v[1]};
       st16(&sV[st][d * BKV + (base8 << 2)], v);
     }

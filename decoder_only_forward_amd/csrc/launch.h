@@ -49,6 +49,12 @@ struct RopeCacheArgs {
   bf16_t* k_cache;  // [B][nkv][cap][hd]
   bf16_t* vt_cache; // [B][nkv][hd][cap]
   const int32_t* pos;  // decode: device [B] (S == 1); prefill: nullptr
+  // prefill only: unrounded fp16 copies of the new keys / values for the attention,
+  // indexed by absolute position - fresh_base; k_fresh [B][nkv][fresh_w][hd],
+  // vt_fresh [B][nkv][hd][fresh_w] (nullptr: not written)
+  f16_t* k_fresh;
+  f16_t* vt_fresh;
+  int fresh_base, fresh_w;
   int pos0, B, S, nq, nkv, cap, max_pos, qk_norm;
   float eps;
 };
@@ -60,6 +66,10 @@ struct AttnPrefillArgs {
   const bf16_t* k_cache; // [B][nkv][cap][hd]
   const bf16_t* vt_cache;// [B][nkv][hd][cap]
   f16_t* out;            // [B][S][nq][hd] fp16
+  // keys / values at positions >= pos0 come from these fp16 copies (see RopeCacheArgs)
+  const f16_t* k_fresh;
+  const f16_t* vt_fresh;
+  int fresh_base, fresh_w;
   int B, S, pos0, nq, nkv, cap;
 };
 hipError_t attn_prefill(const AttnPrefillArgs& a, hipStream_t s);

@@ -136,13 +136,19 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
         bf16_t* dst = a.k_cache + (((int64_t)b * a.nkv + h) * a.cap + pos) * HD;
         dst[lane] = f2bf(y0);
         dst[lane + half] = f2bf(y1);
+        if (a.k_fresh) {
+          f16_t* kf = a.k_fresh +
+                      (((int64_t)b * a.nkv + h) * a.fresh_w + (pos - a.fresh_base)) * HD;
+          kf[lane] = f2h(y0);
+          kf[lane + half] = f2h(y1);
+        }
       }
     }
     return;
   }
 
   // value head: stage [64 tokens][128] in LDS, write 64 consecutive positions per d row
-  __shared__ bf16_t sv[kRopeTile][HD + 2];
+  __shared__ float sv[kRopeTile][HD + 1];
   const int h = slot - a.nq - a.nkv;
   for (int i = threadIdx.x; i < kRopeTile * (HD / 2); i += 256) {
     int j = i / (HD / 2), d2 = (i % (HD / 2)) * 2;
@@ -154,8 +160,8 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
       v0 = src[0];
       v1 = src[1];
     }
-    sv[j][d2] = f2bf(v0);
-    sv[j][d2 + 1] = f2bf(v1);
+    sv[j][d2] = v0;
+    sv[j][d2 + 1] = v1;
   }
   __syncthreads();
   const int s = s0 + lane;
@@ -163,7 +169,11 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
     const int pos = a.pos ? a.pos[b] : a.pos0 + s;
     if (pos >= 0 && pos < a.cap && pos < a.max_pos) {
       bf16_t* base = a.vt_cache + ((int64_t)b * a.nkv + h) * HD * a.cap + pos;
-      for (int d = wave; d < HD; d += 4) base[(int64_t)d * a.cap] = sv[lane][d];
+      for (int d = wave; d < HD; d += 4) base[(int64_t)d * a.cap] = f2bf(sv[lane][d]);
+      if (a.vt_fresh) {
+        f16_t* fb = a.vt_fresh + ((int64_t)b * a.nkv + h) * HD * a.fresh_w + (pos - a.fresh_base);
+        for (int d = wave; d < HD; d += 4) fb[(int64_t)d * a.fresh_w] = f2h(sv[lane][d]);
+      }
     }
   }
 }

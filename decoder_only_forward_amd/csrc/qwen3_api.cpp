@@ -16,6 +16,34 @@ namespace {
 
 thread_local std::string g_err;
 
+// ---------------------------------------------------------------- opt-in kernel timing
+// When enabled for a tag, every launch carrying that tag is bracketed by a pair of HIP
+// events recorded on the launch stream.  Events are created once, when enabled.
+struct Profiler {
+  std::string tag;
+  int cap = 0, used = 0;
+  bool on = false;
+  hipEvent_t* ev = nullptr;  // 2 * cap events
+};
+Profiler g_prof;
+
+struct ProfScope {
+  hipStream_t s;
+  bool active;
+  ProfScope(const char* tag, hipStream_t st) : s(st), active(false) {
+    if (g_prof.on && g_prof.used < g_prof.cap && g_prof.tag == tag) {
+      hipEventRecord(g_prof.ev[2 * g_prof.used], s);
+      active = true;
+    }
+  }
+  ~ProfScope() {
+    if (active) {
+      hipEventRecord(g_prof.ev[2 * g_prof.used + 1], s);
+      ++g_prof.used;
+    }
+  }
+};
+
 int fail(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -51,8 +79,9 @@ struct Bump {
 
 struct DenseLayout {
   size_t xn, qkv, q, attn, h1, act, res, hf, part_attn, part_gemm, am_val, am_idx, lg_scratch;
+  size_t kf, vtf;  // prefill: fp16 copies of the new keys / values
   size_t total;
-  int T, rows_out, attn_splits, attn_chunk, am_chunks;
+  int T, rows_out, attn_splits, attn_chunk, am_chunks, fresh_w_max;
 };
 
 constexpr int kArgmaxChunks = 64;
@@ -86,6 +115,11 @@ DenseLayout dense_layout(const qwen3_config* c, int op, int B, int S, int cap_hi
   L.h1 = stack ? 0 : b.take((size_t)T * H * 4);
   L.res = stack ? b.take((size_t)T * H * 4) : 0;
   L.part_gemm = b.take(max_gemm_partial(c, T));
+  if (!decode) {
+    L.fresh_w_max = ((S + 63 + 63) / 64) * 64;
+    L.kf = b.take((size_t)B * nkv * L.fresh_w_max * hd * 2);
+    L.vtf = b.take((size_t)B * nkv * L.fresh_w_max * hd * 2);
+  }
   if (decode) {
     attn_decode_plan(cap_hint, L.attn_splits, L.attn_chunk);
     L.part_attn = b.take((size_t)B * nq * L.attn_splits * (hd + 2) * 4);
@@ -246,6 +280,7 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
     a.seg1 = nq * hd; a.seg2 = (nq + nkv) * hd;
     a.C = qkv; a.ldc = a.N;
     GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_QKV, gemm::E_F32, false);
+    ProfScope ps("qkv_gemm", s);
     CHECK_HIP(gemm_run(a, true, gemm::B_QKV, gemm::E_F32, false, p, part, s));
   }
   // q/k RMSNorm + RoPE, K/V into the cache
@@ -257,6 +292,13 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
     r.pos = io.pos; r.pos0 = io.pos0; r.B = io.B; r.S = io.pos ? 1 : io.S;
     r.nq = nq; r.nkv = nkv; r.cap = kv->capacity; r.max_pos = c->max_position_embeddings;
     r.qk_norm = c->qk_norm; r.eps = eps;
+    if (!io.pos) {
+      r.k_fresh = (f16_t*)(ws + L.kf);
+      r.vt_fresh = (f16_t*)(ws + L.vtf);
+      r.fresh_base = io.pos0 & ~63;
+      r.fresh_w = ((io.pos0 + io.S - r.fresh_base + 63) / 64) * 64;
+    }
+    ProfScope ps("qk_norm_rope_cache", s);
     CHECK_HIP(qkv_rope_cache(r, s));
   }
   // attention
@@ -267,12 +309,18 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
     d.B = io.B; d.nq = nq; d.nkv = nkv; d.cap = kv->capacity;
     d.max_pos = c->max_position_embeddings;
     attn_decode_plan(kv->capacity, d.splits, d.chunk);
+    ProfScope ps("attn_decode", s);
     CHECK_HIP(attn_decode(d, s));
   } else {
     AttnPrefillArgs p{};
     p.q = q; p.k_cache = (const bf16_t*)kv->k; p.vt_cache = (const bf16_t*)kv->vt;
     p.out = attn; p.B = io.B; p.S = io.S; p.pos0 = io.pos0; p.nq = nq; p.nkv = nkv;
     p.cap = kv->capacity;
+    p.k_fresh = (const f16_t*)(ws + L.kf);
+    p.vt_fresh = (const f16_t*)(ws + L.vtf);
+    p.fresh_base = io.pos0 & ~63;
+    p.fresh_w = ((io.pos0 + io.S - p.fresh_base + 63) / 64) * 64;
+    ProfScope ps("attn_prefill", s);
     CHECK_HIP(attn_prefill(p, s));
   }
   // o_proj + residual -> h1 (fp32)
@@ -285,6 +333,7 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
     int epi = io.res ? gemm::E_RES_F32 : gemm::E_RESB_F32;
     a.R = io.res ? (const void*)io.res : (const void*)io.x_bf16; a.ldr = H;
     GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_DENSE, epi, false);
+    ProfScope ps("o_proj_gemm", s);
     CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, epi, false, p, part, s));
   }
   // post-attention RMSNorm
@@ -297,6 +346,7 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
     a.B0 = (const bf16_t*)w->gate_proj; a.B1 = (const bf16_t*)w->up_proj; a.ldb = H;
     a.C = act; a.ldc = I;
     GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_SWIGLU, gemm::E_SWIGLU, false);
+    ProfScope ps("gate_up_gemm", s);
     CHECK_HIP(gemm_run(a, true, gemm::B_SWIGLU, gemm::E_SWIGLU, false, p, part, s));
   }
   // down + residual
@@ -316,6 +366,7 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
     }
     a.ldc = H;
     GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_DENSE, epi, false);
+    ProfScope ps("down_gemm", s);
     CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, epi, false, p, part, s));
   }
   return QWEN3_OK;
@@ -338,6 +389,36 @@ const char* qwen3_status_string(int status) {
 }
 
 const char* qwen3_last_error(void) { return g_err.c_str(); }
+
+int qwen3_profile_begin(const char* tag, int32_t max_launches) {
+  g_err.clear();
+  if (!tag || max_launches <= 0) return fail(QWEN3_EINVAL, "tag / max_launches");
+  if (g_prof.cap < max_launches) {
+    for (int i = 0; i < 2 * g_prof.cap; ++i) hipEventDestroy(g_prof.ev[i]);
+    delete[] g_prof.ev;
+    g_prof.ev = new hipEvent_t[2 * max_launches];
+    for (int i = 0; i < 2 * max_launches; ++i) CHECK_HIP(hipEventCreate(&g_prof.ev[i]));
+    g_prof.cap = max_launches;
+  }
+  g_prof.tag = tag;
+  g_prof.used = 0;
+  g_prof.on = true;
+  return QWEN3_OK;
+}
+
+int qwen3_profile_end(float* total_ms, int32_t* launches) {
+  g_err.clear();
+  g_prof.on = false;
+  float total = 0.f;
+  for (int i = 0; i < g_prof.used; ++i) {
+    float ms = 0.f;
+    CHECK_HIP(hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]));
+    total += ms;
+  }
+  if (total_ms) *total_ms = total;
+  if (launches) *launches = g_prof.used;
+  return QWEN3_OK;
+}
 
 size_t qwen3_workspace_bytes(const qwen3_config* c, int32_t op, int32_t batch, int32_t seq_len) {
   g_err.clear();
@@ -508,6 +589,7 @@ int qwen3_stack_forward(const qwen3_config* c, const qwen3_model_weights* w, con
     a.C = out; a.ldc = V;
     GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_DENSE, gemm::E_F32, false);
     if (p.partial_bytes > 0) p = GemmPlan{kSkinny, 1, 0};
+    ProfScope ps("lm_head_gemm", s);
     CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, gemm::E_F32, false, p, nullptr, s));
   }
   if (next_ids) {
@@ -517,6 +599,7 @@ int qwen3_stack_forward(const qwen3_config* c, const qwen3_model_weights* w, con
       last = out + (int64_t)(S - 1) * V;
       stride = (int64_t)S * V;
     }
+    ProfScope ps("argmax", s);
     CHECK_HIP(argmax_rows(last, stride, batch, V, next_ids, (float*)(ws + L.am_val),
                           (int32_t*)(ws + L.am_idx), L.am_chunks, s));
   }
@@ -572,6 +655,7 @@ int qwen3_moe_ffn(const qwen3_config* c, const qwen3_moe_weights* w, const void*
     a.C = lg; a.ldc = E;
     GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_DENSE, gemm::E_F32, false);
     if (p.partial_bytes > 0) p = GemmPlan{kSkinny, 1, 0};
+    ProfScope ps("moe_router_gemm", s);
     CHECK_HIP(gemm_run(a, false, gemm::B_DENSE, gemm::E_F32, false, p, nullptr, s));
   }
   // top-k, weights, dispatch order, tile table
@@ -584,6 +668,7 @@ int qwen3_moe_ffn(const qwen3_config* c, const qwen3_moe_weights* w, const void*
     r.offsets = offs; r.perm_token = perm; r.inv_row = inv;
     r.tile_expert = tile_e; r.tile_row0 = tile_r;
     r.max_tiles = L.max_tiles; r.tile_m = L.tile_m;
+    ProfScope ps("moe_route", s);
     CHECK_HIP(moe_route(r, s));
   }
   // grouped gate|up + SwiGLU over gathered token rows
@@ -599,6 +684,7 @@ int qwen3_moe_ffn(const qwen3_config* c, const qwen3_moe_weights* w, const void*
     a.m_tiles = L.max_tiles;
     a.C = act; a.ldc = I;
     GemmPlan p{kMid, 1, 0};
+    ProfScope ps("moe_gate_up_gemm", s);
     CHECK_HIP(gemm_run(a, false, gemm::B_SWIGLU, gemm::E_SWIGLU, true, p, nullptr, s));
   }
   // grouped down -> per-row fp32 outputs in dispatch order
@@ -612,9 +698,13 @@ int qwen3_moe_ffn(const qwen3_config* c, const qwen3_moe_weights* w, const void*
     a.m_tiles = L.max_tiles;
     a.C = yrows; a.ldc = H;
     GemmPlan p{kMid, 1, 0};
+    ProfScope ps("moe_down_gemm", s);
     CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, gemm::E_F32, true, p, nullptr, s));
   }
-  CHECK_HIP(moe_combine(yrows, inv, wt, (bf16_t*)y, T, k, H, s));
+  {
+    ProfScope ps("moe_combine", s);
+    CHECK_HIP(moe_combine(yrows, inv, wt, (bf16_t*)y, T, k, H, s));
+  }
   return QWEN3_OK;
 }
 

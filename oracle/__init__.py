@@ -118,6 +118,18 @@ def attention(q, k, v, qpos):
     return o
 
 
+def linear_rows(x, W):
+    """y = x W^T for x [T, K] (float) and bf16 weights W [N, K]."""
+    x = _f64(x)
+    T, K = x.shape
+    W = _u16(W)
+    N = W.shape[0]
+    y = np.empty((T, N), dtype=np.float64)
+    lib().oracle_linear_rows(_p(x), ctypes.c_int64(T), ctypes.c_int64(K), _p(W),
+                             ctypes.c_int64(N), _p(y))
+    return y
+
+
 def swiglu_ffn(x, gate, up, down):
     x = _f64(x)
     T, H = x.shape

@@ -150,6 +150,13 @@ void oracle_attention(const double *q, const double *k, const double *v, const i
   });
 }
 
+// Bias-free linear layer over rows: y[t] = x[t] W^T ([P1] section 7; [P3] "MoE": the
+// router is such a linear map from hidden to experts).
+void oracle_linear_rows(const double *x, int64_t T, int64_t K, const uint16_t *W, int64_t N,
+                        double *y) {
+  parallel_for(T, [&](int64_t t) { linear_row(x + t * K, W, N, K, y + t * N); });
+}
+
 // SwiGLU FFN: down(silu(gate x) * up x) ([P3] "SwiGLU FFN" formula; [P4] 3.8).
 void oracle_swiglu_ffn(const double *x, int64_t T, int H, int I, const uint16_t *gate,
                        const uint16_t *up, const uint16_t *down, double *y) {

@@ -50,6 +50,8 @@ void oracle_rope(const double *x, int64_t nvec, int hd, const int64_t *pos, doub
                  double *y);
 void oracle_attention(const double *q, const double *k, const double *v, const int64_t *qpos,
                       int64_t S, int64_t L, int nq, int nkv, int hd, double *o);
+void oracle_linear_rows(const double *x, int64_t T, int64_t K, const uint16_t *W, int64_t N,
+                        double *y);
 void oracle_swiglu_ffn(const double *x, int64_t T, int H, int I, const uint16_t *gate,
                        const uint16_t *up, const uint16_t *down, double *y);
 void oracle_block(const oracle_cfg *c, const oracle_layer *w, const double *x, int64_t S,

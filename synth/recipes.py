@@ -183,3 +183,70 @@ def param_count(cfg, tied=True):
     if not tied:
         total += V * H
     return total
+
+
+# ---- device-side generation (same values as the host recipes, written in HBM) ----------
+
+LIB_LAYER_NAMES = {"in_norm": "input_layernorm", "q": "q_proj", "k": "k_proj", "v": "v_proj",
+                   "q_norm": "q_norm", "k_norm": "k_norm", "o": "o_proj",
+                   "post_norm": "post_attention_layernorm", "gate": "gate_proj",
+                   "up": "up_proj", "down": "down_proj"}
+
+
+def _dev_normal(shape, seed, name, mean, std, device):
+    import torch
+    from . import normal_bf16_device
+    t = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    normal_bf16_device(t, seed, name, mean, std)
+    return t
+
+
+def layer_device(seed, cfg, l, device):
+    """One layer's weights on the device, keyed by the library's field names."""
+    return {LIB_LAYER_NAMES[f]: _dev_normal(s, seed, n, m, sd, device)
+            for f, n, s, m, sd in layer_specs(cfg, l)}
+
+
+def model_device(seed, cfg, device, n_layers=None):
+    n_layers = cfg["num_hidden_layers"] if n_layers is None else n_layers
+    d = {f: _dev_normal(s, seed, n, m, sd, device) for f, n, s, m, sd in model_specs(cfg)}
+    d.setdefault("lm_head", None)
+    d["layers"] = [layer_device(seed, cfg, l, device) for l in range(n_layers)]
+    return d
+
+
+def kv_fill_device(k, vt, seed, l, n_pos, ctx):
+    """Fill cache slots [0, n_pos) of every (sequence, kv head) of one layer with the
+    logical tensor [B, nkv, ctx, hd] named kv.{l}.k / kv.{l}.v.
+    k: [B, nkv, cap, hd]; vt: [B, nkv, hd, cap]."""
+    from . import normal_bf16_device
+    B, nkv, cap, hd = k.shape
+    kn, vn = kv_names(l)
+    if n_pos == ctx:
+        normal_bf16_device(k, seed, kn, 0.0, 1.0, logical=(B * nkv, n_pos, hd),
+                           strides=(cap * hd, hd, 1))
+        normal_bf16_device(vt, seed, vn, 0.0, 1.0, logical=(B * nkv, n_pos, hd),
+                           strides=(hd * cap, 1, cap))
+        return
+    for i in range(B * nkv):
+        b, h = divmod(i, nkv)
+        normal_bf16_device(k[b, h], seed, kn, 0.0, 1.0, offset=i * ctx * hd,
+                           logical=(1, n_pos, hd), strides=(0, hd, 1))
+        normal_bf16_device(vt[b, h], seed, vn, 0.0, 1.0, offset=i * ctx * hd,
+                           logical=(1, n_pos, hd), strides=(0, 1, cap))
+
+
+def moe_device(seed, cfg, device, skew=True):
+    import torch
+    from . import normal_bf16_device
+    H, E = cfg["hidden_size"], cfg["num_experts"]
+    specs = dict((f, (n, s)) for f, n, s in moe_specs(cfg))
+    g = router_row_scales(E) if skew else np.ones(E)
+    n, _ = specs["router"]
+    router = torch.empty((E, H), dtype=torch.bfloat16, device=device)
+    for e in range(E):
+        normal_bf16_device(router[e], seed, n, 0.0, float(np.float32(W_STD * g[e])),
+                           offset=e * H, logical=(1, 1, H), strides=(0, 0, 1))
+    gu = _dev_normal(specs["gate_up"][1], seed, specs["gate_up"][0], 0.0, W_STD, device)
+    dn = _dev_normal(specs["down"][1], seed, specs["down"][0], 0.0, W_STD, device)
+    return router, gu, dn

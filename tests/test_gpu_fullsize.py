@@ -1,0 +1,204 @@
+"""GPU parity at the benchmark's full sizes, in the launch configuration bench.py times.
+
+The oracle cannot recompute every output at these sizes, so each test checks outputs the
+oracle can compute one by one:
+  * prefill stack 4 x 2048: a causal model's first P rows depend only on the first P
+    tokens, so logits rows [0, P) of the full run equal an oracle prefill of the prefix;
+    layer-0 keys/values at any position depend only on that position's token;
+  * decode batch 64 at a 4096-token cache: sampled sequences, each recomputed by the
+    oracle from its own regenerated cache;
+  * MoE 8192 tokens: router logits, top-k and dispatch order for every token, expert
+    outputs for a sampled token subset;
+  * 7B block at 32768 tokens: a prefix of rows plus late rows (keys/values for every
+    position are recomputed), and sampled cache rows.
+"""
+import numpy as np
+import pytest
+
+import decoder_only_forward_amd as q3
+import oracle
+import synth
+from synth import recipes
+from q3_testutil import bf16_host, f64, log, parity
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+
+def _rope(cfg, dev):
+    import torch
+    rope = torch.empty(2 * cfg["max_position_embeddings"] * 64, dtype=torch.float32, device=dev)
+    q3.qwen3_rope_table_init(cfg, rope)
+    return rope
+
+
+def _threads():
+    import os
+    oracle.set_threads(int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count()))
+
+
+def test_stack_prefill_4x2048(gpu):
+    import torch
+    _threads()
+    cfg = dict(recipes.QWEN3_0P6B)
+    B, S, V, L = 4, 2048, cfg["vocab_size"], cfg["num_hidden_layers"]
+    log("case full/stack_prefill 4x2048, 28 layers, all-position logits")
+    model = recipes.model_device(recipes.MODEL_SEED_0P6B, cfg, gpu)
+    mw, keep = q3.make_model_weights(model["embed"], model["norm"], model["layers"], None)
+    caches = [(torch.empty((B, 8, S, 128), dtype=torch.bfloat16, device=gpu),
+               torch.empty((B, 8, 128, S), dtype=torch.bfloat16, device=gpu)) for _ in range(L)]
+    kvs = [q3.make_kv_layer(k, vt, S) for k, vt in caches]
+    ids = torch.empty((B, S), dtype=torch.int32, device=gpu)
+    synth.uniform_i32_device(ids, 2, "input.ids", 0, V)
+    logits = torch.empty((B, S, V), dtype=torch.float32, device=gpu)
+    nxt = torch.empty((B,), dtype=torch.int32, device=gpu)
+    ws = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_STACK_PREFILL, B, S),
+                     dtype=torch.uint8, device=gpu)
+    q3.qwen3_stack_forward(cfg, mw, _rope(cfg, gpu), ids, B, S, 0, None, kvs, logits,
+                           q3.QWEN3_LOGITS_ALL, nxt, ws)
+    torch.cuda.synchronize()
+    ids_h = ids.cpu().numpy()
+    np.testing.assert_array_equal(ids_h, synth.uniform_i32(2, "input.ids", (B, S), 0, V))
+    last = logits[:, -1, :].cpu().numpy()
+    assert np.all(np.isfinite(last))
+    np.testing.assert_array_equal(nxt.cpu().numpy(), oracle.argmax(last))
+    del model, mw
+    host = recipes.model_host(recipes.MODEL_SEED_0P6B, cfg)
+    P = 40
+    for b in (0, 3):
+        ref = oracle.stack_prefill(cfg, host, ids_h[b, :P])
+        parity(logits[b, :P].cpu().numpy(), ref, f"logits[b={b}, rows 0..{P - 1}]")
+    # layer-0 keys / values at late positions depend only on that position's token
+    lay0 = host["layers"][0]
+    emb = f64(host["embed"])
+    k0, vt0 = caches[0]
+    for b, p in ((1, 2047), (2, 1500), (0, 777)):
+        x = emb[ids_h[b, p]][None]
+        z = np.zeros((8, p, 128))
+        _, nk, nv = oracle.block(cfg, lay0, x, p, z, z)
+        gk = f64(bf16_host(k0[b, :, p, :]))
+        gv = f64(bf16_host(vt0[b, :, :, p]))
+        parity(gk, nk[:, 0, :], f"layer0 k[b={b}, pos={p}]")
+        parity(gv, nv[:, 0, :], f"layer0 v[b={b}, pos={p}]")
+
+
+def test_stack_decode_64_ctx4096(gpu):
+    import torch
+    _threads()
+    cfg = dict(recipes.QWEN3_0P6B)
+    B, ctx, cap, V, L = 64, 4096, 4160, cfg["vocab_size"], cfg["num_hidden_layers"]
+    log("case full/stack_decode batch 64, cache 4096, 28 layers")
+    model = recipes.model_device(recipes.MODEL_SEED_0P6B, cfg, gpu)
+    mw, keep = q3.make_model_weights(model["embed"], model["norm"], model["layers"], None)
+    caches = []
+    for l in range(L):
+        k = torch.empty((B, 8, cap, 128), dtype=torch.bfloat16, device=gpu)
+        vt = torch.empty((B, 8, 128, cap), dtype=torch.bfloat16, device=gpu)
+        recipes.kv_fill_device(k, vt, 3, l, ctx, ctx)
+        caches.append((k, vt))
+    kvs = [q3.make_kv_layer(k, vt, cap) for k, vt in caches]
+    ids = torch.empty((B,), dtype=torch.int32, device=gpu)
+    synth.uniform_i32_device(ids, 3, "input.ids", 0, V)
+    pos = torch.full((B,), ctx, dtype=torch.int32, device=gpu)
+    logits = torch.empty((B, V), dtype=torch.float32, device=gpu)
+    nxt = torch.empty((B,), dtype=torch.int32, device=gpu)
+    ws = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_STACK_DECODE, B),
+                     dtype=torch.uint8, device=gpu)
+    q3.qwen3_stack_forward(cfg, mw, _rope(cfg, gpu), ids, B, 1, 0, pos, kvs, logits,
+                           q3.QWEN3_LOGITS_LAST, nxt, ws)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    assert np.all(np.isfinite(lg))
+    ids_gpu = nxt.cpu().numpy()
+    np.testing.assert_array_equal(ids_gpu, oracle.argmax(lg))  # same-input rule
+    ids_h = ids.cpu().numpy()
+    del model, mw
+    host = recipes.model_host(recipes.MODEL_SEED_0P6B, cfg)
+    near_ties = 0
+    for b in (0, 37, 63):
+        ck, cv = zip(*[recipes.kv_host(3, cfg, l, b, ctx, (8, ctx)) for l in range(L)])
+        ref = oracle.stack_decode(cfg, host, ids_h[b], ctx, list(ck), list(cv))
+        _, err = parity(lg[b], ref, f"decode logits[b={b}]")
+        max_err = float(np.abs(lg[b] - ref).max())
+        top2 = np.sort(ref)[-2:]
+        if top2[1] - top2[0] > 2 * max_err:
+            assert ids_gpu[b] == int(np.argmax(ref)), b
+        else:
+            near_ties += 1
+            assert ref[ids_gpu[b]] >= ref.max() - 2 * max_err
+    log(f"  near-tie rows: {near_ties}")
+
+
+def test_moe_8192_tokens_128_experts(gpu):
+    import torch
+    _threads()
+    cfg = dict(recipes.MOE_2048)
+    T, E, k, H = 8192, cfg["num_experts"], cfg["num_experts_per_tok"], cfg["hidden_size"]
+    log("case full/moe 8192 tokens, 128 experts, top-8, skewed router")
+    router, gu, dn = recipes.moe_device(4, cfg, gpu)
+    w = q3.make_moe_weights(router, gu, dn)
+    x = torch.empty((T, H), dtype=torch.bfloat16, device=gpu)
+    synth.normal_bf16_device(x, 4, recipes.activations_name(), 0.0, 1.0)
+    y = torch.empty_like(x)
+    out = dict(logits=torch.empty((T, E), dtype=torch.float32, device=gpu),
+               idx=torch.empty((T, k), dtype=torch.int32, device=gpu),
+               w=torch.empty((T, k), dtype=torch.float32, device=gpu),
+               offsets=torch.empty((E + 1,), dtype=torch.int32, device=gpu),
+               perm=torch.empty((T * k,), dtype=torch.int32, device=gpu),
+               inv=torch.empty((T, k), dtype=torch.int32, device=gpu))
+    ws = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_MOE_FFN, T), dtype=torch.uint8,
+                     device=gpu)
+    q3.qwen3_moe_ffn(cfg, w, x, y, T, out["logits"], out["idx"], out["w"], out["offsets"],
+                     out["perm"], out["inv"], ws)
+    torch.cuda.synchronize()
+    g = {kk: v.cpu().numpy() for kk, v in out.items()}
+    gy = f64(bf16_host(y))
+    rh, guh, dnh = recipes.moe_host(4, cfg)
+    xh = f64(synth.normal_bf16(4, recipes.activations_name(), (T, H)))
+    np.testing.assert_array_equal(bf16_host(x), synth.normal_bf16(4, recipes.activations_name(),
+                                                                  (T, H)))
+    lg_ref = oracle.linear_rows(xh, rh)
+    parity(g["logits"], lg_ref, "router_logits[all tokens]")
+    np.testing.assert_array_equal(g["idx"], oracle.topk(g["logits"], k))
+    counts, offsets, perm, inv = oracle.permute(g["idx"], E)
+    np.testing.assert_array_equal(g["offsets"], offsets)
+    np.testing.assert_array_equal(g["perm"], perm)
+    np.testing.assert_array_equal(g["inv"], inv)
+    np.testing.assert_allclose(g["w"], oracle.route_weights(g["logits"].astype(np.float64),
+                                                            g["idx"]), rtol=2e-6, atol=1e-7)
+    log(f"  expert load: max {counts.max()}, min {counts.min()}, "
+        f"max/mean {counts.max() / counts.mean():.2f}")
+    sample = np.random.default_rng(0).choice(T, 192, replace=False)
+    sample.sort()
+    y_ref, idx_ref, _, _ = oracle.moe_ffn(cfg, rh, guh, dnh, xh[sample])
+    agree = np.all(np.sort(g["idx"][sample], 1) == np.sort(idx_ref, 1), axis=1)
+    log(f"  routing agreement on the sample {agree.sum()}/{len(sample)}")
+    assert agree.mean() > 0.95
+    parity(gy[sample][agree], y_ref[agree], "y[sampled tokens]")
+
+
+def test_block_7b_32768(gpu):
+    import torch
+    _threads()
+    cfg = dict(recipes.QWEN_7B_BLOCK)
+    B, S, H, nkv = 1, 32768, cfg["hidden_size"], cfg["num_key_value_heads"]
+    log("case full/block_7b 1 x 32768")
+    w = recipes.layer_device(5, cfg, 0, gpu)
+    k = torch.empty((B, nkv, S, 128), dtype=torch.bfloat16, device=gpu)
+    vt = torch.empty((B, nkv, 128, S), dtype=torch.bfloat16, device=gpu)
+    x = torch.empty((B, S, H), dtype=torch.bfloat16, device=gpu)
+    synth.normal_bf16_device(x, 5, recipes.activations_name(), 0.0, 1.0)
+    xo = torch.empty_like(x)
+    ws = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_BLOCK_PREFILL, B, S),
+                     dtype=torch.uint8, device=gpu)
+    q3.qwen3_block_prefill(cfg, w, _rope(cfg, gpu), x, xo, B, S, 0, q3.make_kv_layer(k, vt, S),
+                           ws)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 63, 64, 127, 128, 4095, 16383, 20000, 32767])
+    got = f64(bf16_host(xo[0]))[rows]
+    layer = recipes.layer_host(5, cfg, 0)
+    xh = f64(synth.normal_bf16(5, recipes.activations_name(), (S, H)))
+    ref, nk, nv = oracle.block(cfg, layer, xh, 0, None, None, rows=rows)
+    parity(got, ref, f"x_out rows {rows.tolist()}")
+    kp = [0, 777, 32767]
+    parity(f64(bf16_host(k[0, :, kp, :])), nk[:, kp, :], "cache k rows")
+    parity(f64(bf16_host(vt[0, :, :, kp])).transpose(0, 2, 1), nv[:, kp, :], "cache v rows")

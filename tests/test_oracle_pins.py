@@ -372,6 +372,7 @@ def test_moe_weights_sum_to_one_and_topk_is_sorted_prefix():
     order = np.argsort(-lg, axis=1, kind="stable")[:, :4]
     np.testing.assert_array_equal(idx, order)
     np.testing.assert_allclose(lg, x @ _f(r).T, rtol=1e-12)
+    np.testing.assert_allclose(oracle.linear_rows(x, r), lg, rtol=1e-13)
     # the weights equal a softmax restricted to the selected logits
     sel = np.take_along_axis(lg, idx, axis=1)
     e = np.exp(sel - sel.max(axis=1, keepdims=True))
