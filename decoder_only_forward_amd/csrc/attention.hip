@@ -26,23 +26,42 @@ namespace q3 {
 namespace {
 
 constexpr int HD = 128;
-constexpr int BQ = 128;  // query rows per block
-constexpr int BKV = 64;  // keys per tile
+constexpr int WROWS = 64;   // query rows per wave (two 32-column MFMA tiles)
+constexpr int PF_WAVES = 4;
+constexpr int BQ = WROWS * PF_WAVES;  // query rows per block
+constexpr int BKV = 64;     // keys per tile
 
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-
-DEV int k_off(int row, int chunk) { return row * HD + ((chunk ^ (row & 7)) << 3); }
-// V^T tile row = 64 keys = 16 chunks of 8 bytes, chunk index XOR (row & 15)
-DEV int vt_off8(int row, int chunk8) { return row * BKV + ((chunk8 ^ (row & 15)) << 2); }
+// LDS layouts (16-byte chunks, XOR-swizzled so that the fragment reads of 16 consecutive
+// rows at one logical chunk hit distinct banks):
+//   K tile   [64 keys][128 dims]  = 16 chunks per row, chunk ^ (row & 15)
+//   V^T tile [128 dims][64 keys]  =  8 chunks per row, chunk ^ (row & 7) ^ (row >> 3 & 1)
+DEV int k_off(int row, int chunk) { return row * HD + ((chunk ^ (row & 15)) << 3); }
+DEV int v_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+DEV int v_off(int row, int chunk) { return row * BKV + ((chunk ^ v_swz(row)) << 3); }
 
 DEV float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+DEV f32x16_t mfma32(f16x8_t a, f16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Key order inside a 32-key MFMA tile: A-operand row rho reads key pi(rho), pi swapping
+// bits 2 and 3.  With the 32x32 accumulator layout (lane l, h = l / 32, register i ->
+// row 8(i/4) + 4h + i%4) this puts keys 16(i/8) + 8h + i%8 in register i of lane half h:
+// each 8-register group holds 8 consecutive keys, which is the B-operand k-slot order of
+// the P^T.V product, and the matching V^T fragment is one contiguous 16-byte read.
+DEV int key_perm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// 32x32x16 MFMA operand layouts (lane l, h = l / 32): A row l % 32 and B column l % 32,
+// k = 8h .. 8h + 7 for both.  S^T = K . Q^T puts one query in each lane's column, so the
+// row max needs one cross-lane step and the rescale is per lane.
+template <bool HAS_PAST>
 __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnPrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t sK[2][BKV * HD];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[2][HD * BKV];
+  __shared__ __attribute__((aligned(16))) f16_t sK[2][BKV * HD];
+  __shared__ __attribute__((aligned(16))) f16_t sV[2][HD * BKV];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q4 = lane >> 4, c16 = lane & 15;
+  const int l32 = lane & 31, hh = lane >> 5;
   const int nmb = (a.S + BQ - 1) / BQ;
   const int nblocks = nmb * a.B * a.nq;
   // contiguous work ranges per XCD; heavy (late) row blocks first
@@ -56,44 +75,67 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnPrefillArgs a) {
   const int b = rem / a.nq, h = rem % a.nq;
   const int g = a.nq / a.nkv, kvh = h / g;
 
-  const int row0 = mb * BQ;                       // first query row (token index)
-  const int kv_len = a.pos0 + min(a.S, row0 + BQ);  // keys this block may need
+  const int row0 = mb * BQ;                          // first query row (token index)
+  const int kv_len = a.pos0 + min(a.S, row0 + BQ);   // keys this block may need
   const int ntiles = (kv_len + BKV - 1) / BKV;
-  const int wrow0 = row0 + wave * 32;
-  const int wave_max_pos = a.pos0 + min(a.S - 1, wrow0 + 31);
+  const int wrow0 = row0 + wave * WROWS;
+  const int wave_max_pos = a.pos0 + min(a.S - 1, wrow0 + WROWS - 1);
   const int wave_min_pos = a.pos0 + wrow0;
 
-  const bf16_t* kbase = a.k_cache + ((int64_t)b * a.nkv + kvh) * a.cap * HD;
-  const bf16_t* vbase = a.vt_cache + ((int64_t)b * a.nkv + kvh) * HD * a.cap;
+  const f16_t* kfbase = a.k_fresh + ((int64_t)b * a.nkv + kvh) * a.fresh_w * HD;
+  const f16_t* vfbase = a.vt_fresh + ((int64_t)b * a.nkv + kvh) * HD * a.fresh_w;
 
   // Q^T fragments (B operand): column = query row, k = head dims
-  f16x8_t qf[2][4];
+  f16x8_t qf[2][8];
   int qpos[2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    int s = wrow0 + nt * 16 + c16;
+    int s = wrow0 + nt * 32 + l32;
     bool valid = s < a.S;
     int sc = valid ? s : a.S - 1;
     qpos[nt] = valid ? a.pos0 + s : kv_len - 1;
     const f16_t* qp = a.q + (((int64_t)b * a.S + sc) * a.nq + h) * HD;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[nt][ks] = as_f16x8(ld16(qp + ks * 32 + q4 * 8));
+    for (int ks = 0; ks < 8; ++ks) qf[nt][ks] = as_f16x8(ld16(qp + ks * 16 + hh * 8));
   }
 
-  f32x4_t acc_o[8][2];
+  f32x16_t oacc[4][2];
 #pragma unroll
-  for (int md = 0; md < 8; ++md)
+  for (int md = 0; md < 4; ++md)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) acc_o[md][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[md][nt][i] = 0.f;
+  // q arrives pre-scaled by log2(e) / sqrt(hd): scores are in log2 units
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-  const float sl2 = 0.08838834764831845f * kLog2e;  // log2(e) / sqrt(128)
 
-  // Tile staging.  Keys / values at positions < pos0 come from the bf16 cache (converted
-  // to fp16 here); positions >= pos0 were produced by this call and are read from the
-  // unrounded fp16 copies.  Rows / columns at or beyond kv_len are zero.
-  const f16_t* kfbase = a.k_fresh + ((int64_t)b * a.nkv + kvh) * a.fresh_w * HD;
-  const f16_t* vfbase = a.vt_fresh + ((int64_t)b * a.nkv + kvh) * HD * a.fresh_w;
-  u32x4_t rk[4], rv[4];
+  // ---- tile staging
+  // No past (pos0 == 0): every key/value of the block comes from the fp16 copies written
+  // by this call (zero beyond the last position), loaded straight into LDS with
+  // global_load_lds_dwordx4: lane L of a wave instruction lands at base + 16 L, so each
+  // lane fetches the logical chunk that the swizzle places at its physical slot.
+  // With a past: keys/values < pos0 come from the bf16 cache (converted to fp16 in
+  // registers), the rest from the fp16 copies; rows/columns >= kv_len are zero.
+  auto direct_load = [&](int t, int st) {
+    const int j0 = t * BKV;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int o = (wave * 4 + i) * 1024 + lane * 16;  // byte offset in the K tile
+      const int row = o >> 8, p = (o >> 4) & 15;
+      const f16_t* src = kfbase + (int64_t)(j0 + row - a.fresh_base) * HD + ((p ^ (row & 15)) << 3);
+      __builtin_amdgcn_global_load_lds(src, &sK[st][(wave * 4 + i) * 512], 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int o = (wave * 4 + i) * 1024 + lane * 16;  // byte offset in the V^T tile
+      const int d = o >> 7, p = (o >> 4) & 7;
+      const f16_t* src = vfbase + (int64_t)d * a.fresh_w + (j0 - a.fresh_base) + ((p ^ v_swz(d)) << 3);
+      __builtin_amdgcn_global_load_lds(src, &sV[st][(wave * 4 + i) * 512], 16, 0, 0);
+    }
+  };
+  const bf16_t* kbase = a.k_cache + ((int64_t)b * a.nkv + kvh) * a.cap * HD;
+  const bf16_t* vbase = a.vt_cache + ((int64_t)b * a.nkv + kvh) * HD * a.cap;
+  u32x4_t rk[HAS_PAST ? 4 : 1], rv[HAS_PAST ? 4 : 1];
   const u32x4_t zero4 = {0u, 0u, 0u, 0u};
   auto gload = [&](int t) {
     const int j0 = t * BKV;
@@ -149,124 +191,131 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnPrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int c = tid & 7, d = (tid >> 3) + 32 * i;
-      int x = d & 15;
-      int base8 = (2 * c) ^ (x & ~1);
-      u32x4_t v = rv[i];
-      if (x & 1) v = u32x4_t{v[2], v[3], v[0], v[1]};
-      st16(&sV[st][d * BKV + (base8 << 2)], v);
+      st16(&sV[st][v_off(d, c)], rv[i]);
     }
   };
 
-  gload(0);
-  sstore(0);
+  if (HAS_PAST) {
+    gload(0);
+    sstore(0);
+  } else {
+    direct_load(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   __syncthreads();
 
+  const int krow0 = key_perm(l32);
   for (int t = 0; t < ntiles; ++t) {
     const int st = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
+    if (t + 1 < ntiles) {
+      if (HAS_PAST) gload(t + 1);
+      else direct_load(t + 1, st ^ 1);
+    }
     const int j0 = t * BKV;
     if (j0 <= wave_max_pos) {
-      // S^T[key][qrow] for 64 keys x 32 query rows
-      f32x4_t sacc[4][2];
+      // S^T[key][qrow]: 64 keys (mt) x 64 query rows (nt)
+      f32x16_t sacc[2][2];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+          for (int i = 0; i < 16; ++i) sacc[mt][nt][i] = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          f16x8_t kf = as_f16x8(ld16(&sK[st][k_off(mt * 16 + c16, ks * 4 + q4)]));
+      for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-            sacc[mt][nt] =
-                __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[nt][ks], sacc[mt][nt], 0, 0, 0);
+        for (int mt = 0; mt < 2; ++mt) {
+          f16x8_t kf = as_f16x8(ld16(&sK[st][k_off(mt * 32 + krow0, ks * 2 + hh)]));
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = mfma32(kf, qf[nt][ks], sacc[mt][nt]);
         }
       }
       const bool need_mask = j0 + BKV - 1 > wave_min_pos;
-      f16x8_t pf[2][2];
+      f16x8_t pf[2][4];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         float tmax = -INFINITY;
+        if (need_mask) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+          for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float x = sacc[mt][nt][i] * sl2;
-            if (need_mask) {
-              int key = j0 + mt * 16 + q4 * 4 + i;
-              if (key > qpos[nt]) x = -INFINITY;
+            for (int i = 0; i < 16; ++i) {
+              int key = j0 + mt * 32 + (i >> 3) * 16 + hh * 8 + (i & 7);
+              if (key > qpos[nt]) sacc[mt][nt][i] = -INFINITY;
             }
-            sacc[mt][nt][i] = x;
-            tmax = fmaxf(tmax, x);
-          }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float m_new = fmaxf(m_run[nt], tmax);
-        const float alpha = exp2_fast(m_run[nt] - m_new);
-        m_run[nt] = m_new;
-        float psum = 0.f;
-        float p[4][4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[mt][i] = exp2_fast(sacc[mt][nt][i] - m_new);
-            psum += p[mt][i];
-          }
-        l_run[nt] = l_run[nt] * alpha + psum;
-#pragma unroll
-        for (int md = 0; md < 8; ++md)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc_o[md][nt][i] *= alpha;
-#pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2) {
-          u32x4_t u;
-          u[0] = pack_f16x2(p[2 * ks2][0], p[2 * ks2][1]);
-          u[1] = pack_f16x2(p[2 * ks2][2], p[2 * ks2][3]);
-          u[2] = pack_f16x2(p[2 * ks2 + 1][0], p[2 * ks2 + 1][1]);
-          u[3] = pack_f16x2(p[2 * ks2 + 1][2], p[2 * ks2 + 1][3]);
-          pf[nt][ks2] = as_f16x8(u);
         }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[mt][nt][i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        // Lazy rescaling: the running max is only raised when a score exceeds it by more
+        // than 8 (log2 units), so P <= 2^8 stays exact enough in fp16 and the output
+        // accumulators are rescaled only when some lane's max moved that far.
+        const bool raise = tmax > m_run[nt] + 8.0f;
+        if (__any(raise)) {
+          const float m_new = raise ? tmax : m_run[nt];
+          const float alpha = exp2_fast(m_run[nt] - m_new);
+          m_run[nt] = m_new;
+          l_run[nt] *= alpha;
+#pragma unroll
+          for (int md = 0; md < 4; ++md)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[md][nt][i] *= alpha;
+        }
+        const float m_use = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
+        float psum = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const int mt = s2 >> 1, i0 = (s2 & 1) * 8;
+          u32x4_t u;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float p0 = exp2_fast(sacc[mt][nt][i0 + 2 * e] - m_use);
+            float p1 = exp2_fast(sacc[mt][nt][i0 + 2 * e + 1] - m_use);
+            psum += p0 + p1;
+            u[e] = pack_f16x2(p0, p1);
+          }
+          pf[nt][s2] = as_f16x8(u);
+        }
+        l_run[nt] += psum;
       }
-      // O^T[d][qrow] += V^T[d][keys] . P^T[keys][qrow]
+      // O^T[d][qrow] += V^T[d][keys] . P^T[keys][qrow]; keys 16 s2 + 8h .. +8 per lane half
 #pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
+      for (int s2 = 0; s2 < 4; ++s2) {
 #pragma unroll
-        for (int md = 0; md < 8; ++md) {
-          const int d = md * 16 + c16;
-          const int c8a = ks2 * 8 + q4, c8b = ks2 * 8 + 4 + q4;
-          u32x2_t lo = *(const u32x2_t*)&sV[st][vt_off8(d, c8a)];
-          u32x2_t hi = *(const u32x2_t*)&sV[st][vt_off8(d, c8b)];
-          f16x8_t vf = as_f16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+        for (int md = 0; md < 4; ++md) {
+          f16x8_t vf = as_f16x8(ld16(&sV[st][v_off(md * 32 + l32, s2 * 2 + hh)]));
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-            acc_o[md][nt] =
-                __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[nt][ks2], acc_o[md][nt], 0, 0, 0);
+          for (int nt = 0; nt < 2; ++nt) oacc[md][nt] = mfma32(vf, pf[nt][s2], oacc[md][nt]);
         }
       }
     }
-    if (t + 1 < ntiles) sstore(st ^ 1);
+    if (t + 1 < ntiles) {
+      if (HAS_PAST) sstore(st ^ 1);
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __syncthreads();
   }
 
-  // normalise and store: lane owns query column c16 of n-tile nt, dims 16md + 4q4 + i
+  // normalise and store: lane owns query column l32 of n-tile nt, dims 32md + 8g + 4hh + i
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     float l = l_run[nt];
-    l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
     const float inv = 1.0f / l;
-    const int s = wrow0 + nt * 16 + c16;
+    const int s = wrow0 + nt * 32 + l32;
     if (s >= a.S) continue;
     f16_t* op = a.out + (((int64_t)b * a.S + s) * a.nq + h) * HD;
 #pragma unroll
-    for (int md = 0; md < 8; ++md) {
-      u32x2_t v;
-      v[0] = pack_f16x2(acc_o[md][nt][0] * inv, acc_o[md][nt][1] * inv);
-      v[1] = pack_f16x2(acc_o[md][nt][2] * inv, acc_o[md][nt][3] * inv);
-      *(u32x2_t*)(op + md * 16 + q4 * 4) = v;
-    }
+    for (int md = 0; md < 4; ++md)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        u32x2_t v;
+        v[0] = pack_f16x2(oacc[md][nt][4 * gq] * inv, oacc[md][nt][4 * gq + 1] * inv);
+        v[1] = pack_f16x2(oacc[md][nt][4 * gq + 2] * inv, oacc[md][nt][4 * gq + 3] * inv);
+        *(u32x2_t*)(op + md * 32 + gq * 8 + hh * 4) = v;
+      }
   }
 }
 
@@ -300,7 +349,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDecodeArgs a) {
 
   // phase 1: scores (log2 domain).  16 lanes per key row, 4 keys per wave step.
   const int kg = lane >> 4, dc = lane & 15;
-  const float sl2 = 0.08838834764831845f * kLog2e;
+  // q arrives pre-scaled by log2(e) / sqrt(hd): scores are in log2 units
   float qv[kMaxGroup][8];
 #pragma unroll
   for (int hh = 0; hh < kMaxGroup; ++hh) {
@@ -308,7 +357,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDecodeArgs a) {
       float f[8];
       unpack8_f16(ld16(a.q + ((int64_t)b * a.nq + kvh * g + hh) * HD + dc * 8), f);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qv[hh][e] = f[e] * sl2;
+      for (int e = 0; e < 8; ++e) qv[hh][e] = f[e];
     }
   }
   for (int j = wave * 4 + kg; j < n; j += 16) {
@@ -411,7 +460,10 @@ __global__ void __launch_bounds__(128) attn_decode_combine_kernel(AttnDecodeArgs
 hipError_t attn_prefill(const AttnPrefillArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.S <= 0) return hipSuccess;
   const int nmb = (a.S + BQ - 1) / BQ;
-  hipLaunchKernelGGL(attn_prefill_kernel, dim3(nmb * a.B * a.nq), dim3(256), 0, s, a);
+  if (a.pos0 > 0)
+    hipLaunchKernelGGL(attn_prefill_kernel<true>, dim3(nmb * a.B * a.nq), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3(nmb * a.B * a.nq), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

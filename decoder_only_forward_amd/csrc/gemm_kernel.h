@@ -9,8 +9,8 @@
 // fp16 MFMA runs at the same rate.
 // Block tile BM x BN x 64 staged through LDS, double buffered (one barrier per
 // k-step).  Each 128-byte tile row is stored with its eight 16-byte chunks XOR-swizzled
-// by (row & 7), so the 16-byte fragment reads of 8 consecutive lanes (8 rows, same
-// chunk) hit 8 distinct bank groups, and so do the row-contiguous tile stores.
+// (lds_off), so the 16-byte fragment reads of consecutive lanes (consecutive rows, same
+// chunk) hit distinct banks, and the row-contiguous tile stores stay contiguous.
 // Every wave owns a WM x WN sub-tile made of 32x32 MFMA tiles.
 //
 // Fused epilogues (one per projection of the decoder block):
@@ -93,7 +93,13 @@ DEV void tile_coords(int t, int m_tiles, int n_tiles, int& tm, int& tn) {
   tn = rem / gm;
 }
 
-DEV int lds_off(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
+// 16-byte chunk c of tile row `row` (128-byte rows).  The XOR spreads any 16 consecutive
+// rows' fragment reads (same logical chunk) over distinct banks whether the LDS serves 8
+// lanes (128 B) or 16 lanes (256 B) of a 16-byte read per cycle: rows r and r+8 differ in
+// bit 0 of the swizzle and rows of opposite parity sit in opposite 128-byte halves.
+DEV int lds_off(int row, int chunk) {
+  return row * 64 + ((chunk ^ (row & 7) ^ ((row >> 3) & 1)) << 3);
+}
 
 template <class T, bool F16, int BMODE, int EPI, bool GROUPED, bool SPLITK>
 __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
@@ -215,36 +221,48 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
   __syncthreads();
 
   const int frow = lane & 31, fhalf = lane >> 5;
-  for (int it = 0; it < nk; ++it) {
-    const int s = it & 1;
-    if (it + 1 < nk) gload(kt0 + it + 1);
+  // Software pipeline inside a stage: the fragments of k-step kk+1 are read from LDS
+  // while the MFMAs of k-step kk run; the next stage's global loads are issued at the
+  // start and its LDS stores sit between the MFMA groups of k-steps 2 and 3.
+  // sched_barrier fences keep the compiler from regrouping the phases.
+  u32x4_t fa[2][T::TM], fb[2][T::TN];
+  auto read = [&](int s, int kk, int slot) {
+    const int c = 2 * kk + fhalf;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int c = 2 * kk + fhalf;
-      u32x4_t fa[T::TM], fb[T::TN];
+    for (int i = 0; i < T::TM; ++i)
+      fa[slot][i] = ld16(&sA[s][lds_off(wm * T::WM + i * 32 + frow, c)]);
 #pragma unroll
-      for (int i = 0; i < T::TM; ++i) {
-        int r = wm * T::WM + i * 32 + frow;
-        fa[i] = ld16(&sA[s][lds_off(r, c)]);
-      }
+    for (int j = 0; j < T::TN; ++j)
+      fb[slot][j] = ld16(&sB[s][lds_off(wn * T::WN + j * 32 + frow, c)]);
+  };
+  auto mma = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
 #pragma unroll
       for (int j = 0; j < T::TN; ++j) {
-        int r = wn * T::WN + j * 32 + frow;
-        fb[j] = ld16(&sB[s][lds_off(r, c)]);
+        if (F16)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(fa[slot][i]),
+                                                             as_f16x8(fb[slot][j]), acc[i][j],
+                                                             0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[slot][i]),
+                                                              as_bf16x8(fb[slot][j]), acc[i][j],
+                                                              0, 0, 0);
       }
+  };
+  for (int it = 0; it < nk; ++it) {
+    const int s = it & 1;
+    const bool more = it + 1 < nk;
+    read(s, 0, 0);
+    if (more) gload(kt0 + it + 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < T::TN; ++j) {
-          if (F16)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(fa[i]), as_f16x8(fb[j]),
-                                                               acc[i][j], 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[i]), as_bf16x8(fb[j]),
-                                                                acc[i][j], 0, 0, 0);
-        }
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk < 3) read(s, kk + 1, (kk + 1) & 1);
+      mma(kk & 1);
+      if (kk == 2 && more) sstore(s ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (it + 1 < nk) sstore(s ^ 1);
     __syncthreads();
   }
 

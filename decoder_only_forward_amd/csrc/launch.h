@@ -45,7 +45,7 @@ struct RopeCacheArgs {
   const float* rope;  // [2][max_pos][hd/2]
   const bf16_t* q_norm;
   const bf16_t* k_norm;
-  f16_t* q_out;  // [T][nq][hd] fp16
+  f16_t* q_out;  // [T][nq][hd] fp16, pre-scaled by log2(e) / sqrt(hd)
   bf16_t* k_cache;  // [B][nkv][cap][hd]
   bf16_t* vt_cache; // [B][nkv][hd][cap]
   const int32_t* pos;  // decode: device [B] (S == 1); prefill: nullptr

@@ -84,7 +84,7 @@ rope_table_kernel(float* __restrict__ rope, int max_pos, int half, double theta,
 }
 
 // Per (64-token tile, sequence, head slot):
-//   q heads:  q = rope(rmsnorm_hd(q)) -> q_out [T][nq][hd] (fp16 attention operand)
+//   q heads:  q = rope(rmsnorm_hd(q)) * log2(e)/sqrt(hd) -> q_out [T][nq][hd] (fp16)
 //   k heads:  k = rope(rmsnorm_hd(k)) -> k_cache[b][h][pos][:]
 //   v heads:  v -> vt_cache[b][h][:][pos]  (transposed through LDS)
 // ([P3] "GQA 注意力": per-head q/k RMSNorm before RoPE, offset = cached length;
@@ -99,6 +99,21 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row_elems = (a.nq + 2 * a.nkv) * HD;
   const int half = HD / 2;
+
+  // The fp16 copies are read in whole 64-position tiles: the last token tile of each
+  // k / v head zeroes their tail, from the last new position to the padded width.
+  if (a.k_fresh && slot >= a.nq && tile == gridDim.x - 1) {
+    const bool is_k = slot < a.nq + a.nkv;
+    const int h = is_k ? slot - a.nq : slot - a.nq - a.nkv;
+    const int t0 = a.pos0 + a.S - a.fresh_base, nt = a.fresh_w - t0;
+    for (int i = threadIdx.x; i < nt * HD; i += 256) {
+      const int r = t0 + i / HD, d = i % HD;
+      if (is_k)
+        a.k_fresh[(((int64_t)b * a.nkv + h) * a.fresh_w + r) * HD + d] = 0;
+      else
+        a.vt_fresh[(((int64_t)b * a.nkv + h) * HD + d) * a.fresh_w + r] = 0;
+    }
+  }
 
   if (slot < a.nq + a.nkv) {
     const bool is_q = slot < a.nq;
@@ -128,6 +143,10 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
       float y0 = x0 * c - x1 * sn;
       float y1 = x0 * sn + x1 * c;
       if (is_q) {
+        // q carries the softmax scale log2(e) / sqrt(hd) for the attention kernels
+        const float qs = 0.08838834764831845f * kLog2e;
+        y0 *= qs;
+        y1 *= qs;
         if (!ok) y0 = y1 = __int_as_float(0x7FC00000);
         f16_t* dst = a.q_out + (t * a.nq + h) * HD;
         dst[lane] = f2h(y0);
