@@ -112,7 +112,7 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnPrefillArgs a) {
   // ---- tile staging
   // No past (pos0 == 0): every key/value of the block comes from the fp16 copies written
   // by this call (zero beyond the last position), loaded straight into LDS with
-  // global_load_lds_dwordx4: lane L of a wave instruction lands at base + 16 L, so each
+  // lds_dma16: lane L of a wave instruction lands at base + 16 L, so each
   // lane fetches the logical chunk that the swizzle places at its physical slot.
   // With a past: keys/values < pos0 come from the bf16 cache (converted to fp16 in
   // registers), the rest from the fp16 copies; rows/columns >= kv_len are zero.
@@ -123,14 +123,14 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnPrefillArgs a) {
       const int o = (wave * 4 + i) * 1024 + lane * 16;  // byte offset in the K tile
       const int row = o >> 8, p = (o >> 4) & 15;
       const f16_t* src = kfbase + (int64_t)(j0 + row - a.fresh_base) * HD + ((p ^ (row & 15)) << 3);
-      __builtin_amdgcn_global_load_lds(src, &sK[st][(wave * 4 + i) * 512], 16, 0, 0);
+      lds_dma16(src, &sK[st][(wave * 4 + i) * 512]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int o = (wave * 4 + i) * 1024 + lane * 16;  // byte offset in the V^T tile
       const int d = o >> 7, p = (o >> 4) & 7;
       const f16_t* src = vfbase + (int64_t)d * a.fresh_w + (j0 - a.fresh_base) + ((p ^ v_swz(d)) << 3);
-      __builtin_amdgcn_global_load_lds(src, &sV[st][(wave * 4 + i) * 512], 16, 0, 0);
+      lds_dma16(src, &sV[st][(wave * 4 + i) * 512]);
     }
   };
   const bf16_t* kbase = a.k_cache + ((int64_t)b * a.nkv + kvh) * a.cap * HD;
@@ -200,7 +200,7 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnPrefillArgs a) {
     sstore(0);
   } else {
     direct_load(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_dma();
   }
   __syncthreads();
 
@@ -293,7 +293,7 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnPrefillArgs a) {
     }
     if (t + 1 < ntiles) {
       if (HAS_PAST) sstore(st ^ 1);
-      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else wait_dma();
     }
     __syncthreads();
   }

@@ -85,3 +85,25 @@ DEV u32x4_t ld16(const void* p) { return *(const u32x4_t*)p; }
 DEV void st16(void* p, u32x4_t v) { *(u32x4_t*)p = v; }
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Asynchronous 16-byte global -> LDS copy (global_load_lds_dwordx4): the 64 lanes of the
+// wave write 1 KB at lds_base + 16 * lane (lds_base must be wave-uniform).  It is issued
+// from inline asm so that the compiler does not make every later LDS read wait for it
+// (it cannot tell that the copy targets the other half of a double buffer); the caller
+// publishes the data with wait_dma() before the barrier that precedes its use.  The copy
+// writes only LDS (no destination registers) and reads its address registers at issue;
+// M0 is saved and restored inside the block.
+DEV void lds_dma16(const void* gptr, void* lds_base) {
+  uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gptr), "s"(lds)
+      : "memory");
+}
+DEV void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

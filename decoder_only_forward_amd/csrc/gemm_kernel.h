@@ -66,11 +66,8 @@ struct Tile {
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr int THREADS = WAVES_M * WAVES_N * 64;
-  static constexpr int A_LOADS = BM * 8 / THREADS;  // 16-byte chunks per thread per stage
-  static constexpr int B_LOADS = BN * 8 / THREADS;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(A_LOADS >= 1 && B_LOADS >= 1, "tile too small for the thread count");
-  static_assert((BM * 8) % THREADS == 0 && (BN * 8) % THREADS == 0, "load split");
+  static_assert(THREADS == 256 && BM % 32 == 0 && BN % 32 == 0, "4 waves, 8 rows per load");
 };
 
 // Blocks are dispatched round-robin over the 8 XCDs; give each XCD a contiguous run of
@@ -144,43 +141,45 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
   }
   const int nk = kt1 - kt0;
 
-  // per-thread global row pointers (fixed across k)
-  const int lchunk = tid & 7;
-  const uint16_t* aptr[T::A_LOADS];
-  const bf16_t* bptr[T::B_LOADS];
+  // ---- operand tiles go global -> LDS directly (lds_dma16): lane L of a
+  // wave instruction lands at 16 L bytes past that instruction's 1 KB LDS slot, i.e. at
+  // row 8q + L/8, physical chunk L%8 of the tile, so each lane fetches the logical chunk
+  // the swizzle stores there.  Rows past the valid range are clamped to the last valid
+  // row: they only feed accumulator rows / columns the epilogue never stores.
+  constexpr int A_INSTS = T::BM / 32, B_INSTS = T::BN / 32;  // per wave, per stage
+  const int lrow = lane >> 3, pchunk = lane & 7;
+  const uint16_t* aptr[A_INSTS];
+  const bf16_t* bptr[B_INSTS];
 #pragma unroll
-  for (int i = 0; i < T::A_LOADS; ++i) {
-    int r = (tid >> 3) + i * (T::THREADS / 8);
-    const uint16_t* ptr = nullptr;
-    if (r < rows_valid) {
-      int orow = out_row0 + r;
-      int64_t arow = p.a_rows ? (int64_t)p.a_rows[orow] : (int64_t)orow;
-      ptr = p.A + arow * p.lda + lchunk * 8;
-    }
-    aptr[i] = ptr;
+  for (int i = 0; i < A_INSTS; ++i) {
+    int r = 8 * (wave * A_INSTS + i) + lrow;
+    int rc = min(r, rows_valid - 1);
+    int orow = out_row0 + rc;
+    int64_t arow = p.a_rows ? (int64_t)p.a_rows[orow] : (int64_t)orow;
+    int c = pchunk ^ (r & 7) ^ ((r >> 3) & 1);
+    aptr[i] = p.A + arow * p.lda + c * 8;
   }
 #pragma unroll
-  for (int i = 0; i < T::B_LOADS; ++i) {
-    int r = (tid >> 3) + i * (T::THREADS / 8);
-    const bf16_t* ptr = nullptr;
+  for (int i = 0; i < B_INSTS; ++i) {
+    int r = 8 * (wave * B_INSTS + i) + lrow;
+    int c = pchunk ^ (r & 7) ^ ((r >> 3) & 1);
+    const bf16_t* ptr;
     if (BMODE == B_SWIGLU) {
       const int half = T::WN / 2;
       int w = r / T::WN, j = r % T::WN;
-      int col = tn * (T::BN / 2) + w * half + (j % half);
-      if (col < p.N / 2) ptr = (j < half ? B0 : B1) + (int64_t)col * p.ldb;
+      int col = min(tn * (T::BN / 2) + w * half + (j % half), p.N / 2 - 1);
+      ptr = (j < half ? B0 : B1) + (int64_t)col * p.ldb;
     } else {
-      int n = n0 + r;
-      if (n < p.N) {
-        if (BMODE == B_QKV) {
-          if (n < p.seg1) ptr = B0 + (int64_t)n * p.ldb;
-          else if (n < p.seg2) ptr = B1 + (int64_t)(n - p.seg1) * p.ldb;
-          else ptr = p.B2 + (int64_t)(n - p.seg2) * p.ldb;
-        } else {
-          ptr = B0 + (int64_t)n * p.ldb;
-        }
+      int n = min(n0 + r, p.N - 1);
+      if (BMODE == B_QKV) {
+        if (n < p.seg1) ptr = B0 + (int64_t)n * p.ldb;
+        else if (n < p.seg2) ptr = B1 + (int64_t)(n - p.seg1) * p.ldb;
+        else ptr = p.B2 + (int64_t)(n - p.seg2) * p.ldb;
+      } else {
+        ptr = B0 + (int64_t)n * p.ldb;
       }
     }
-    bptr[i] = ptr ? ptr + lchunk * 8 : nullptr;
+    bptr[i] = ptr + c * 8;
   }
 
   f32x16_t acc[T::TM][T::TN];
@@ -191,40 +190,26 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  u32x4_t ra[T::A_LOADS], rb[T::B_LOADS];
-  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
-
-  auto gload = [&](int kt) {
+  auto load_stage = [&](int kt, int st) {
     const int koff = kt * 64;
 #pragma unroll
-    for (int i = 0; i < T::A_LOADS; ++i) ra[i] = aptr[i] ? ld16(aptr[i] + koff) : zero4;
+    for (int i = 0; i < A_INSTS; ++i)
+      lds_dma16(aptr[i] + koff, &sA[st][(wave * A_INSTS + i) * 512]);
 #pragma unroll
-    for (int i = 0; i < T::B_LOADS; ++i) rb[i] = bptr[i] ? ld16(bptr[i] + koff) : zero4;
-  };
-  auto sstore = [&](int s) {
-#pragma unroll
-    for (int i = 0; i < T::A_LOADS; ++i) {
-      int r = (tid >> 3) + i * (T::THREADS / 8);
-      st16(&sA[s][lds_off(r, lchunk)], ra[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < T::B_LOADS; ++i) {
-      int r = (tid >> 3) + i * (T::THREADS / 8);
-      st16(&sB[s][lds_off(r, lchunk)], F16 ? bf16x8_to_f16x8(rb[i]) : rb[i]);
-    }
+    for (int i = 0; i < B_INSTS; ++i)
+      lds_dma16(bptr[i] + koff, &sB[st][(wave * B_INSTS + i) * 512]);
   };
 
   if (nk > 0) {
-    gload(kt0);
-    sstore(0);
+    load_stage(kt0, 0);
+    wait_dma();
   }
   __syncthreads();
 
   const int frow = lane & 31, fhalf = lane >> 5;
-  // Software pipeline inside a stage: the fragments of k-step kk+1 are read from LDS
-  // while the MFMAs of k-step kk run; the next stage's global loads are issued at the
-  // start and its LDS stores sit between the MFMA groups of k-steps 2 and 3.
-  // sched_barrier fences keep the compiler from regrouping the phases.
+  // Inside a stage the fragments of k-step kk+1 are read from LDS while the MFMAs of
+  // k-step kk run; the next stage streams into the other buffer meanwhile.  bf16 weight
+  // fragments are converted to fp16 after the LDS read when the activations are fp16.
   u32x4_t fa[2][T::TM], fb[2][T::TN];
   auto read = [&](int s, int kk, int slot) {
     const int c = 2 * kk + fhalf;
@@ -232,8 +217,10 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
     for (int i = 0; i < T::TM; ++i)
       fa[slot][i] = ld16(&sA[s][lds_off(wm * T::WM + i * 32 + frow, c)]);
 #pragma unroll
-    for (int j = 0; j < T::TN; ++j)
-      fb[slot][j] = ld16(&sB[s][lds_off(wn * T::WN + j * 32 + frow, c)]);
+    for (int j = 0; j < T::TN; ++j) {
+      u32x4_t v = ld16(&sB[s][lds_off(wn * T::WN + j * 32 + frow, c)]);
+      fb[slot][j] = F16 ? bf16x8_to_f16x8(v) : v;
+    }
   };
   auto mma = [&](int slot) {
 #pragma unroll
@@ -253,16 +240,17 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
   for (int it = 0; it < nk; ++it) {
     const int s = it & 1;
     const bool more = it + 1 < nk;
+    // the other buffer was last read before the previous barrier
+    if (more) load_stage(kt0 + it + 1, s ^ 1);
     read(s, 0, 0);
-    if (more) gload(kt0 + it + 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       if (kk < 3) read(s, kk + 1, (kk + 1) & 1);
       mma(kk & 1);
-      if (kk == 2 && more) sstore(s ^ 1);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (more) wait_dma();
     __syncthreads();
   }
 
