@@ -10,8 +10,12 @@ top-8, skewed load), the 7B-shaped block at 32768 tokens and the 0.6B block at 1
 
 All inputs are seeded synthetic data generated directly in HBM; the timed region
 contains only library calls.  Per-kernel durations come from HIP events the library
-records around the launches of one kernel class (qwen3_profile_begin/end) during the
-timed region; rooflines use algorithmic flops or bytes per launch.
+records around the launches of one kernel class (qwen3_profile_begin/end).  A short
+breakdown run first times every kernel class; the timed region then records the events
+of the dominant one (largest time per step), whose roofline uses algorithmic flops or
+bytes per launch.  "traffic" is the HBM bytes per launch of that kernel from the
+committed rocprofv3 counter table (profiles/traffic.json), null once the kernel's sources
+differ from those the counters were taken with.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads a,b,...]
 """
@@ -111,26 +115,44 @@ def wl_prefill(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown):
 
     L, H, I = cfg["num_hidden_layers"], cfg["hidden_size"], cfg["intermediate_size"]
     T = B * S
-    ms, kern = timer.run(step, steps, warmup, tag="gate_up_gemm", launches_per_step=L)
-    flops_gu = 2.0 * T * 2 * I * H
+    units = dense_units(cfg, B, S, L)
+    units["lm_head_gemm"] = ("mfma", 2.0 * T * H * V, 1)
+    units["argmax"] = ("hbm", 4.0 * B * V, 1)
+    ms, dom, rf, kernels = measure(timer, step, steps, warmup, "stack_0p6b_prefill", units,
+                                   "attn_prefill", breakdown)
     out = {"name": "stack_0p6b_prefill", "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms,
            "config": {"workload": "stack_0p6b_prefill", "batch": B, "seq_len": S, "layers": L,
                       "hidden": H, "heads": "16q/8kv x128", "intermediate": I, "vocab": V,
                       "lm_head": "tied, fp32 logits for all positions",
                       "greedy_next_token": True},
-           "dominant_kernel": dict(kern, flops_per_launch=flops_gu),
-           "roofline": roofline_mfma(flops_gu, kern["avg_ms"])}
+           "dominant_kernel": dom, "roofline": rf}
     total_flops = stack_prefill_flops(cfg, B, S)
     out["whole_step_mfma_frac"] = round(total_flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)
     out["algorithmic_tflop_per_step"] = round(total_flops / 1e12, 3)
-    if breakdown:
-        out["kernels"] = kernel_breakdown(timer, step, {
-            "qkv_gemm": L, "qk_norm_rope_cache": L, "attn_prefill": L, "o_proj_gemm": L,
-            "gate_up_gemm": L, "down_gemm": L, "lm_head_gemm": 1, "argmax": 1},
-            steps=min(steps, 3))
+    if kernels:
+        out["kernels"] = kernels
     del logits, caches, kvs, model, ws
     torch.cuda.empty_cache()
     return out
+
+
+def dense_units(cfg, B, S, launches):
+    """Algorithmic work per launch of each dense-block kernel class for a prefill of B x S
+    tokens from position 0 (causal pairs only; the q/k-norm + RoPE + cache-write pass is
+    priced at the bytes this design moves: fp32 q/k/v in, fp16 q and bf16 cache plus fp16
+    fresh K/V out)."""
+    H, nq, nkv, hd, I = (cfg["hidden_size"], cfg["num_attention_heads"],
+                         cfg["num_key_value_heads"], cfg["head_dim"], cfg["intermediate_size"])
+    T = B * S
+    rope_bytes = T * (nq + 2 * nkv) * hd * 4 + T * nq * hd * 2 + 4.0 * T * nkv * hd * 2
+    return {
+        "qkv_gemm": ("mfma", 2.0 * T * H * (nq + 2 * nkv) * hd, launches),
+        "qk_norm_rope_cache": ("hbm", float(rope_bytes), launches),
+        "attn_prefill": ("mfma", 4.0 * hd * nq * B * S * (S + 1) / 2, launches),
+        "o_proj_gemm": ("mfma", 2.0 * T * nq * hd * H, launches),
+        "gate_up_gemm": ("mfma", 2.0 * T * H * 2 * I, launches),
+        "down_gemm": ("mfma", 2.0 * T * I * H, launches),
+    }
 
 
 def stack_prefill_flops(cfg, B, S):
@@ -144,13 +166,37 @@ def stack_prefill_flops(cfg, B, S):
     return L * (gemm + attn) + 2.0 * T * H * V
 
 
-def kernel_breakdown(timer, step, tags, steps):
+def kernel_breakdown(timer, step, units, steps):
+    """Per kernel class: average launch duration (HIP events around each launch) and its
+    roofline fraction from the algorithmic work per launch in `units`:
+    tag -> (bound "mfma" | "hbm", flops or bytes per launch, launches per step)."""
     res = {}
-    for tag, per_step in tags.items():
+    for tag, (bound, amount, per_step) in units.items():
         _, k = timer.run(step, steps, 1, tag=tag, launches_per_step=per_step)
-        res[tag] = {"avg_ms": round(k["avg_ms"], 4), "launches_per_step": per_step,
-                    "ms_per_step": round(k["avg_ms"] * per_step, 4)}
+        e = {"avg_ms": round(k["avg_ms"], 4), "launches_per_step": per_step,
+             "ms_per_step": round(k["avg_ms"] * per_step, 4), "bound": bound}
+        if amount:
+            rf = (roofline_mfma if bound == "mfma" else roofline_hbm)(amount, k["avg_ms"])
+            e["frac"] = rf["frac"]
+        res[tag] = e
     return res
+
+
+def measure(timer, step, steps, warmup, workload, units, default_tag, breakdown):
+    """Breakdown first (short runs), then the timed region with the dominant kernel class
+    (largest time per step) recording its launch events live."""
+    kernels = kernel_breakdown(timer, step, units, min(steps, 3)) if breakdown else None
+    tag = default_tag
+    if kernels:
+        tag = max(kernels, key=lambda t: kernels[t]["ms_per_step"])
+    bound, amount, per_step = units[tag]
+    ms, kern = timer.run(step, steps, warmup, tag=tag, launches_per_step=per_step)
+    from decoder_only_forward_amd import profiling
+    traffic = profiling.traffic_for(workload, tag)
+    rf = (roofline_mfma if bound == "mfma" else roofline_hbm)(amount, kern["avg_ms"], traffic)
+    dom = dict(kern, **({"flops_per_launch": amount} if bound == "mfma"
+                        else {"bytes_per_launch": amount}))
+    return ms, dom, rf, kernels
 
 
 def wl_decode(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown):
@@ -180,22 +226,35 @@ def wl_decode(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown):
                                q3.QWEN3_LOGITS_LAST, nxt, ws)
 
     L, nkv, nq = cfg["num_hidden_layers"], cfg["num_key_value_heads"], cfg["num_attention_heads"]
-    ms, kern = timer.run(step, steps, warmup, tag="attn_decode", launches_per_step=L)
-    kv_bytes = 2.0 * B * nkv * (ctx + 1) * 128 * 2
-    attn_bytes = kv_bytes + 2.0 * B * nq * 128 * 2  # + q in, o out
+    H, hd, I = cfg["hidden_size"], cfg["head_dim"], cfg["intermediate_size"]
+    kv_bytes = 2.0 * B * nkv * (ctx + 1) * hd * 2
+    nsplit = min(-(-cap // 256), max(-(-cap // 4096), -(-1024 // (B * nkv))))
+    part_bytes = 4.0 * B * nq * nsplit * (hd + 2)  # split partials: design bytes, not algorithmic
+    units = {
+        # weights dominate the skinny GEMMs; activations in/out are counted too
+        "qkv_gemm": ("hbm", 2.0 * H * (nq + 2 * nkv) * hd + 2.0 * B * H
+                     + 4.0 * B * (nq + 2 * nkv) * hd, L),
+        "qk_norm_rope_cache": ("hbm", 4.0 * B * (nq + 2 * nkv) * hd + 2.0 * B * nq * hd
+                               + 2.0 * B * 2 * nkv * hd, L),
+        "attn_decode": ("hbm", kv_bytes + 2.0 * B * nq * hd, L),
+        "attn_decode_combine": ("hbm", part_bytes + 2.0 * B * nq * hd, L),
+        "o_proj_gemm": ("hbm", 2.0 * nq * hd * H + 2.0 * B * nq * hd + 8.0 * B * H, L),
+        "gate_up_gemm": ("hbm", 2.0 * 2 * I * H + 2.0 * B * H + 2.0 * B * I, L),
+        "down_gemm": ("hbm", 2.0 * I * H + 2.0 * B * I + 8.0 * B * H, L),
+        "lm_head_gemm": ("hbm", 2.0 * V * H + 4.0 * B * V, 1),
+        "argmax": ("hbm", 4.0 * B * V, 1),
+    }
+    ms, dom, rf, kernels = measure(timer, step, steps, warmup, "stack_0p6b_decode", units,
+                                   "attn_decode", breakdown)
     step_bytes = decode_step_bytes(cfg, B, ctx)
     out = {"name": "stack_0p6b_decode", "tokens_per_s": B / (ms * 1e-3), "ms_per_step": ms,
            "config": {"workload": "stack_0p6b_decode", "batch": B, "context": ctx,
                       "new_tokens_per_seq": 1, "layers": L, "greedy_next_token": True},
-           "dominant_kernel": dict(kern, bytes_per_launch=attn_bytes),
-           "roofline": roofline_hbm(attn_bytes, kern["avg_ms"]),
+           "dominant_kernel": dom, "roofline": rf,
            "whole_step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
            "algorithmic_gb_per_step": round(step_bytes / 1e9, 3)}
-    if breakdown:
-        out["kernels"] = kernel_breakdown(timer, step, {
-            "qkv_gemm": L, "qk_norm_rope_cache": L, "attn_decode": L, "o_proj_gemm": L,
-            "gate_up_gemm": L, "down_gemm": L, "lm_head_gemm": 1, "argmax": 1},
-            steps=min(steps, 3))
+    if kernels:
+        out["kernels"] = kernels
     del caches, kvs, model, ws, logits
     torch.cuda.empty_cache()
     return out
@@ -228,23 +287,27 @@ def wl_moe(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown):
     def step():
         q3.qwen3_moe_ffn(cfg, w, x, y, T, None, None, None, offsets, None, None, ws)
 
-    ms, kern = timer.run(step, steps, warmup, tag="moe_gate_up_gemm", launches_per_step=1)
     H, I = cfg["hidden_size"], cfg["moe_intermediate_size"]
-    flops_gu = 2.0 * T * k * 2 * I * H
+    units = {
+        "moe_router_gemm": ("mfma", 2.0 * T * E * H, 1),
+        "moe_route": ("hbm", 4.0 * T * E + 8.0 * T * k * 3, 1),
+        "moe_gate_up_gemm": ("mfma", 2.0 * T * k * 2 * I * H, 1),
+        "moe_down_gemm": ("mfma", 2.0 * T * k * I * H, 1),
+        "moe_combine": ("hbm", 4.0 * T * k * H + 2.0 * T * H, 1),
+    }
+    ms, dom, rf, kernels = measure(timer, step, steps, warmup, "moe_ffn", units,
+                                   "moe_gate_up_gemm", breakdown)
     counts = (offsets[1:] - offsets[:-1]).cpu().numpy()
-    total = 2.0 * T * E * H + flops_gu + 2.0 * T * k * I * H
+    total = 2.0 * T * E * H + 2.0 * T * k * 2 * I * H + 2.0 * T * k * I * H
     out = {"name": "moe_ffn", "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms,
            "config": {"workload": "moe_ffn_2048x128e_top8", "tokens": T, "hidden": H,
                       "experts": E, "top_k": k, "expert_intermediate": I,
                       "load_max_over_mean": round(float(counts.max() / counts.mean()), 2),
                       "load_min": int(counts.min()), "load_max": int(counts.max())},
-           "dominant_kernel": dict(kern, flops_per_launch=flops_gu),
-           "roofline": roofline_mfma(flops_gu, kern["avg_ms"]),
+           "dominant_kernel": dom, "roofline": rf,
            "whole_step_mfma_frac": round(total / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)}
-    if breakdown:
-        out["kernels"] = kernel_breakdown(timer, step, {
-            "moe_router_gemm": 1, "moe_route": 1, "moe_gate_up_gemm": 1, "moe_down_gemm": 1,
-            "moe_combine": 1}, steps=min(steps, 3))
+    if kernels:
+        out["kernels"] = kernels
     del router, gu, dn, ws
     torch.cuda.empty_cache()
     return out
@@ -274,29 +337,19 @@ def wl_block(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, bi
 
     c1 = dict(cfg, num_hidden_layers=1, vocab_size=0)
     flops = stack_prefill_flops(c1, B, S)
-    nq, hd, I = cfg["num_attention_heads"], 128, cfg["intermediate_size"]
-    attn_flops = 4.0 * hd * nq * B * S * (S + 1) / 2
-    ms, kern = timer.run(step, steps, warmup, tag="attn_prefill")
-    out = {"name": "block_7b" if big else "block_0p6b", "tokens_per_s": B * S / (ms * 1e-3),
-           "ms_per_step": ms,
-           "config": {"workload": "block_7b" if big else "block_0p6b", "batch": B,
-                      "seq_len": S, "hidden": H, "heads": f"{nq}q/{nkv}kv x128",
-                      "intermediate": I},
-           "dominant_kernel": dict(kern, flops_per_launch=attn_flops),
-           "roofline": roofline_mfma(attn_flops, kern["avg_ms"]),
+    nq = cfg["num_attention_heads"]
+    name = "block_7b" if big else "block_0p6b"
+    units = dense_units(cfg, B, S, 1)
+    ms, dom, rf, kernels = measure(timer, step, steps, warmup, name, units, "attn_prefill",
+                                   breakdown)
+    out = {"name": name, "tokens_per_s": B * S / (ms * 1e-3), "ms_per_step": ms,
+           "config": {"workload": name, "batch": B, "seq_len": S, "hidden": H,
+                      "heads": f"{nq}q/{nkv}kv x128", "intermediate": cfg["intermediate_size"]},
+           "dominant_kernel": dom, "roofline": rf,
            "whole_step_mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
            "algorithmic_tflop_per_step": round(flops / 1e12, 3)}
-    if breakdown:
-        kb = kernel_breakdown(timer, step, {
-            "qkv_gemm": 1, "qk_norm_rope_cache": 1, "attn_prefill": 1, "o_proj_gemm": 1,
-            "gate_up_gemm": 1, "down_gemm": 1}, steps=min(steps, 3))
-        T = B * S
-        gf = {"qkv_gemm": 2.0 * T * H * (nq + 2 * nkv) * hd, "o_proj_gemm": 2.0 * T * H * nq * hd,
-              "gate_up_gemm": 2.0 * T * H * 2 * I, "down_gemm": 2.0 * T * H * I,
-              "attn_prefill": attn_flops}
-        for t, f in gf.items():
-            kb[t]["mfma_frac"] = round(f / (kb[t]["avg_ms"] * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)
-        out["kernels"] = kb
+    if kernels:
+        out["kernels"] = kernels
     del w, k, vt, x, xo, ws
     torch.cuda.empty_cache()
     return out
@@ -335,10 +388,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads", default="prefill,decode,moe,block7b,block")
     ap.add_argument("--no-breakdown", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=192,
+    ap.add_argument("--cpu-tokens", type=int, default=512,
                     help="prefix length for the oracle CPU baseline (0 = skip)")
     ap.add_argument("--copy-gib", type=float, default=0.0,
-                    help="run a plain device copy of this size first (counter calibration)")
+                    help="run a plain elementwise copy of this size first (calibrates the "
+                         "HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -356,7 +410,7 @@ def main():
         n = int(args.copy_gib * (1 << 30)) // 4
         a = torch.ones(n, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
-        b.copy_(a)
+        torch.neg(a, out=b)  # elementwise: reads and writes copy_gib each
         torch.cuda.synchronize()
         del a, b
     wls = [w.strip() for w in args.workloads.split(",") if w.strip()]

@@ -4,22 +4,26 @@
 // sequence, query row at absolute position p, kv head h / (nq / nkv):
 //     o = sum_{j <= p} softmax_j(q . k_j / sqrt(hd)) v_j
 //
-// Operands: q arrives in fp16; keys/values produced by this call come from unrounded fp16
-// copies, older ones from the bf16 cache (converted to fp16, exact in fp16's normal range,
-// as they are staged); P is rounded to fp16.  Both products run on
-// v_mfma_f32_16x16x32_f16.
+// Prefill operands: q arrives in fp16; keys/values produced by this call come from
+// unrounded fp16 copies, older ones from the bf16 cache (converted to fp16, exact in fp16's
+// normal range, as they are staged); P is rounded to fp16.  Both products run on
+// v_mfma_f32_32x32x16_f16.
 // Prefill (flash-style, matrix cores):
-//   one block = 128 query rows of one q head, 4 waves x 32 rows; K tiles of 64 keys
+//   one block = 256 query rows of one q head, 4 waves x 64 rows; K tiles of 64 keys
 //   [64][128] and the matching V^T tile [128][64] are staged in LDS (double buffered).
 //   Scores are formed transposed, S^T = K . Q^T, so each lane owns one query column:
-//   the row max needs only two cross-lane steps and the rescale is per lane.  The
+//   the row max needs one cross-lane step and the rescale is per lane.  The
 //   probabilities P^T then sit in registers exactly in the B-operand order of
 //   O^T = V^T . P^T (k-slots permuted consistently with the V^T reads), so P never
 //   leaves registers; this is why the cache keeps V transposed.  Tiles entirely above
 //   a wave's rows are skipped; heavy row blocks are dispatched first.
-// Decode (bandwidth bound): split-K over the cache positions, one block per
-// (sequence, kv head, 256-position chunk) serving all q heads of the group from one
-// read of K and V; a second kernel merges the partial (max, sum, output) triples.
+// Decode (bandwidth bound): the positions of each (sequence, kv head) are split evenly
+// over the waves of several blocks; each wave streams its run of 32-position tiles
+// straight from the bf16 cache into 16x16x32 bf16 MFMAs serving all q heads of the group,
+// with the next tile's loads in flight.  q and P enter as exact bf16 high + low pairs
+// (fp16 q is exactly representable that way), so no operand rounding is added.  The
+// block merges its waves in LDS; a second kernel merges the blocks' (max, sum, output)
+// partials.
 #include "launch.h"
 
 namespace q3 {
@@ -320,116 +324,255 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnPrefillArgs a) {
 }
 
 // ------------------------------------------------------------------ decode
-constexpr int kDecChunk = 256;
+// One wave streams a contiguous run of 32-key tiles of one (sequence, kv head) through
+// v_mfma_f32_16x16x32_bf16, reading the bf16 cache as-is.  Operand layouts (lane l,
+// r = l % 16, grp = l / 16): A row r, B column r, k = 8 grp .. 8 grp + 7 for both; the
+// accumulator holds column r, rows 4 grp .. 4 grp + 3.
+//   S^T = K . Q^T: columns 0..7 carry the bf16 high parts of the group's (pre-scaled)
+//   q heads, columns 8..15 the bf16 low parts (q - hi), so one MFMA per 32 dims gives
+//   both halves and a row_ror:8 DPP add forms the exact fp16 q . k in fp32.
+//   O^T = V^T . P^T: likewise P's high part in columns 0..7, its remainder in 8..15.
+// Key order: sub-tile s (16 keys) row rho holds key 8 (rho / 4) + 4 s + rho % 4, so the
+// two accumulators of a lane hold keys 8 grp .. 8 grp + 7 in B-operand k order and the
+// V^T fragment for them is one 16-byte read.
+constexpr int kDecWaves = 4;
+constexpr int kDecTile = 32;
 constexpr int kMaxGroup = 8;
 
+struct DecTile {
+  u32x4_t k[8];  // [sub-tile][32-dim chunk]
+  u32x4_t v[8];  // [16-dim row tile]
+};
+
+// The cache region of one (sequence, kv head) is addressed through buffer descriptors:
+// one 32-bit lane offset per operand, the tile position as a uniform add and the V^T
+// row-tile step as a scalar offset, so the loads need no 64-bit address registers.
+struct DecSrc {
+  __amdgpu_buffer_rsrc_t k, v;
+  uint32_t k_lane;  // bytes: K row 8 (r / 4) + r % 4 of the tile, dims 8 grp ..
+  uint32_t v_lane;  // bytes: V^T row r, positions 8 grp ..
+  uint32_t v_step;  // bytes between 16-row tiles of V^T
+};
+
+DEV void dec_load(DecTile& t, const DecSrc& src, int key0) {
+  const uint32_t ko = src.k_lane + (uint32_t)key0 * (HD * 2);
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      t.k[s * 4 + c] = __builtin_amdgcn_raw_buffer_load_b128(src.k, ko + s * 4 * HD * 2 + c * 64, 0, 0);
+  const uint32_t vo = src.v_lane + (uint32_t)key0 * 2;
+#pragma unroll
+  for (int rt = 0; rt < 8; ++rt)
+    t.v[rt] = __builtin_amdgcn_raw_buffer_load_b128(src.v, vo, rt * src.v_step, 0);
+}
+
+DEV f32x4_t mfma16_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// x + x from the lane 8 places round the same 16-lane row
+DEV float add_ror8(float x) {
+  int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false);
+  return x + __int_as_float(y);
+}
+
+DEV uint32_t cvt_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  f32x2v v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
+}
+
+// high part (columns 0..7) or remainder (columns 8..15) of x, rounded to bf16
+DEV float split_part(float x, bool low) {
+  float hi = __uint_as_float(__float_as_uint(x) & 0xffff0000u);
+  return low ? x - hi : hi;
+}
+
+struct DecState {
+  f32x4_t o[8];  // O^T row tiles: dims 16 rt + 4 grp + i, column r
+  float m, l;    // running max (log2 units) and sum for column r's head
+};
+
+DEV void dec_tile(DecState& st, const DecTile& t, const u32x4_t* qb, int key0, int kv_len,
+                  int lane) {
+  const int grp = lane >> 4;
+  const bool low = (lane & 15) >= 8;
+  f32x4_t sc[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc = mfma16_bf16(t.k[s * 4 + c], qb[c], acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = add_ror8(acc[i]);
+    sc[s] = acc;
+  }
+  const bool tail = key0 + kDecTile > kv_len;
+  if (tail) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (key0 + 8 * grp + 4 * s + i >= kv_len) sc[s][i] = -INFINITY;
+  }
+  float mx = sc[0][0];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[s][i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  // lazy rescale: move the reference max only when a score exceeds it by 2^8
+  if (__any(mx > st.m + 8.f)) {
+    const float mn = fmaxf(st.m, mx);
+    const float f = st.m == -INFINITY ? 0.f : exp2_fast(st.m - mn);
+    st.m = mn;
+    st.l *= f;
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.o[rt][i] *= f;
+  }
+  float p[8];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[4 * s + i] = exp2_fast(sc[s][i] - st.m);
+      st.l += p[4 * s + i];
+    }
+  u32x4_t pb;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    pb[e] = cvt_bf16x2(split_part(p[2 * e], low), split_part(p[2 * e + 1], low));
+  if (!tail) {
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt) st.o[rt] = mfma16_bf16(t.v[rt], pb, st.o[rt]);
+  } else {
+    // values past the sequence end may hold anything (NaN included): zero them
+    u32x4_t keep;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = key0 + 8 * grp + 2 * e;
+      keep[e] = (k < kv_len ? 0xffffu : 0u) | (k + 1 < kv_len ? 0xffff0000u : 0u);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt) st.o[rt] = mfma16_bf16(t.v[rt] & keep, pb, st.o[rt]);
+  }
+}
+
 __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDecodeArgs a) {
-  __shared__ float sp[kMaxGroup][kDecChunk];
-  __shared__ float sm[kMaxGroup], sl[kMaxGroup];
+  __shared__ float so[kDecWaves][kMaxGroup][HD];
+  __shared__ float sm[kDecWaves][kMaxGroup], sl[kDecWaves][kMaxGroup];
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = a.nq / a.nkv;
   const int pos = a.pos[b];
   const bool ok = pos >= 0 && pos < a.cap && pos < a.max_pos;
   const int kv_len = ok ? pos + 1 : 0;
-  const int j0 = split * kDecChunk;
-  const int n = max(0, min(kDecChunk, kv_len - j0));
+  // 64-key units spread evenly over all waves serving this (sequence, kv head)
+  const int n64 = (kv_len + 63) / 64;
+  const int nw = a.splits * kDecWaves, w = split * kDecWaves + wave;
+  const int kbeg = (int)((int64_t)w * n64 / nw) * 64;
+  const int kend = min((int)((int64_t)(w + 1) * n64 / nw) * 64, kv_len);
+
+  const int r = lane & 15, grp = lane >> 4;
+  const int hh = r & 7;
+  const bool low = r >= 8;
+  DecState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int rt = 0; rt < 8; ++rt) st.o[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (kbeg < kend) {
+    const int64_t region = (int64_t)a.cap * HD;  // elements per (sequence, kv head)
+    DecSrc src;
+    src.k = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.k_cache + ((int64_t)b * a.nkv + kvh) * region), 0, (int)(region * 2), 0x00020000);
+    src.v = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.vt_cache + ((int64_t)b * a.nkv + kvh) * region), 0, (int)(region * 2), 0x00020000);
+    src.k_lane = (uint32_t)((8 * (r >> 2) + (r & 3)) * HD + grp * 8) * 2;
+    src.v_lane = (uint32_t)(r * a.cap + grp * 8) * 2;
+    src.v_step = (uint32_t)(16 * a.cap) * 2;
+    // two register buffers: the next tile's loads are in flight while one is consumed.
+    // Past the run's end the "next" tile repeats the current one (cache hits, no traffic)
+    // so that the wait counts are the same on every path.
+    DecTile t0, t1;
+    int key = kbeg;
+    dec_load(t0, src, key);
+    dec_load(t1, src, key + kDecTile < kend ? key + kDecTile : key);
+    // q after the first two tiles' loads: all arrive within one memory latency
+    u32x4_t qb[4];
+    const f16_t* qrow = a.q + ((int64_t)b * a.nq + kvh * g + hh) * HD + grp * 8;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float f[8];
+      if (hh < g) {
+        unpack8_f16(ld16(qrow + c * 32), f);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        qb[c][e] = cvt_bf16x2(split_part(f[2 * e], low), split_part(f[2 * e + 1], low));
+    }
+    // t0 holds the tile at key, t1 the one after it (in flight)
+    for (;;) {
+      dec_tile(st, t0, qb, key, kv_len, lane);
+      key += kDecTile;
+      if (key >= kend) break;
+      dec_load(t0, src, key + kDecTile < kend ? key + kDecTile : key);
+      dec_tile(st, t1, qb, key, kv_len, lane);
+      key += kDecTile;
+      if (key >= kend) break;
+      dec_load(t1, src, key + kDecTile < kend ? key + kDecTile : key);
+    }
+  }
+  // fold the low-part columns into the high ones and the four row groups of the sum
+  st.l += __shfl_xor(st.l, 16, 64);
+  st.l += __shfl_xor(st.l, 32, 64);
+#pragma unroll
+  for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.o[rt][i] = add_ror8(st.o[rt][i]);
+  if (r < g) {
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) so[wave][r][rt * 16 + 4 * grp + i] = st.o[rt][i];
+    if (grp == 0) {
+      sm[wave][r] = st.m;
+      sl[wave][r] = st.l;
+    }
+  }
+  __syncthreads();
+  // merge the block's four waves into one (max, sum, output) partial per q head
   float* part = a.part + (((int64_t)b * a.nq + kvh * g) * a.splits + split) * (HD + 2);
   const int64_t hstride = (int64_t)a.splits * (HD + 2);
-
-  if (n == 0) {
-    for (int i = tid; i < g * (HD + 2); i += 256) {
-      int hh = i / (HD + 2), e = i % (HD + 2);
-      part[hh * hstride + e] = e == HD ? -INFINITY : 0.f;
-    }
-    return;
-  }
-  const bf16_t* kbase = a.k_cache + (((int64_t)b * a.nkv + kvh) * a.cap + j0) * HD;
-  const bf16_t* vbase = a.vt_cache + ((int64_t)b * a.nkv + kvh) * HD * a.cap + j0;
-
-  // phase 1: scores (log2 domain).  16 lanes per key row, 4 keys per wave step.
-  const int kg = lane >> 4, dc = lane & 15;
-  // q arrives pre-scaled by log2(e) / sqrt(hd): scores are in log2 units
-  float qv[kMaxGroup][8];
+  for (int i = tid; i < g * HD; i += 256) {
+    const int h = i / HD, d = i % HD;
+    float M = -INFINITY;
 #pragma unroll
-  for (int hh = 0; hh < kMaxGroup; ++hh) {
-    if (hh < g) {
-      float f[8];
-      unpack8_f16(ld16(a.q + ((int64_t)b * a.nq + kvh * g + hh) * HD + dc * 8), f);
+    for (int v = 0; v < kDecWaves; ++v) M = fmaxf(M, sm[v][h]);
+    float O = 0.f, L = 0.f;
+    if (M != -INFINITY) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qv[hh][e] = f[e];
-    }
-  }
-  for (int j = wave * 4 + kg; j < n; j += 16) {
-    float kf[8];
-    unpack8(ld16(kbase + (int64_t)j * HD + dc * 8), kf);
-#pragma unroll
-    for (int hh = 0; hh < kMaxGroup; ++hh) {
-      if (hh < g) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d += qv[hh][e] * kf[e];
-        d += __shfl_xor(d, 1, 64);
-        d += __shfl_xor(d, 2, 64);
-        d += __shfl_xor(d, 4, 64);
-        d += __shfl_xor(d, 8, 64);
-        if (dc == 0) sp[hh][j] = d;
+      for (int v = 0; v < kDecWaves; ++v) {
+        if (sm[v][h] == -INFINITY) continue;
+        const float f = exp2_fast(sm[v][h] - M);
+        O += so[v][h][d] * f;
+        L += sl[v][h] * f;
       }
     }
-  }
-  __syncthreads();
-  // phase 2: per-head max and exponentials
-  for (int hh = wave; hh < g; hh += 4) {
-    float m = -INFINITY;
-    for (int j = lane; j < n; j += 64) m = fmaxf(m, sp[hh][j]);
-    m = warp_max(m);
-    float s = 0.f;
-    for (int j = lane; j < kDecChunk; j += 64) {
-      float p = j < n ? exp2_fast(sp[hh][j] - m) : 0.f;
-      sp[hh][j] = p;
-      s += p;
+    part[h * hstride + d] = O;
+    if (d == 0) {
+      part[h * hstride + HD] = M;
+      part[h * hstride + HD + 1] = L;
     }
-    s = warp_sum(s);
-    if (lane == 0) { sm[hh] = m; sl[hh] = s; }
-  }
-  __syncthreads();
-  // phase 3: o[hh][d] = sum_j p[hh][j] vt[d][j]; 16 lanes per d row, 16 keys per lane
-  const int rg = tid >> 4, kl = tid & 15;
-  float pv[kMaxGroup][16];
-#pragma unroll
-  for (int hh = 0; hh < kMaxGroup; ++hh)
-    if (hh < g)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) pv[hh][e] = sp[hh][kl * 16 + e];
-  for (int r = 0; r < HD / 16; ++r) {
-    const int d = rg + 16 * r;
-    const int key = kl * 16;
-    float vf[16];
-    if (key + 16 <= n) {
-      unpack8(ld16(vbase + (int64_t)d * a.cap + key), vf);
-      unpack8(ld16(vbase + (int64_t)d * a.cap + key + 8), vf + 8);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        vf[e] = key + e < n ? bf2f(vbase[(int64_t)d * a.cap + key + e]) : 0.f;
-    }
-#pragma unroll
-    for (int hh = 0; hh < kMaxGroup; ++hh) {
-      if (hh < g) {
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc += pv[hh][e] * vf[e];
-        acc += __shfl_xor(acc, 1, 64);
-        acc += __shfl_xor(acc, 2, 64);
-        acc += __shfl_xor(acc, 4, 64);
-        acc += __shfl_xor(acc, 8, 64);
-        if (kl == 0) part[hh * hstride + d] = acc;
-      }
-    }
-  }
-  if (tid < g) {
-    part[tid * hstride + HD] = sm[tid];
-    part[tid * hstride + HD + 1] = sl[tid];
   }
 }
 
@@ -467,16 +610,23 @@ hipError_t attn_prefill(const AttnPrefillArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-void attn_decode_plan(int cap, int& splits, int& chunk) {
-  chunk = kDecChunk;
-  splits = (cap + kDecChunk - 1) / kDecChunk;
+void attn_decode_plan(int cap, int B, int nkv, int& splits, int& chunk) {
+  // about 4096 positions per block (1024 per wave), more blocks when the batch is too
+  // small for two rounds of resident waves, never fewer than 64 positions per wave
+  const int by_len = (cap + 4095) / 4096;
+  const int fill = (1024 + B * nkv - 1) / (B * nkv);
+  splits = std::min((cap + 255) / 256, std::max(by_len, fill));
+  chunk = (cap + splits - 1) / splits;
 }
 
 hipError_t attn_decode(const AttnDecodeArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
   hipLaunchKernelGGL(attn_decode_kernel, dim3(a.splits, a.nkv, a.B), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t attn_decode_combine(const AttnDecodeArgs& a, hipStream_t s) {
+  if (a.B <= 0) return hipSuccess;
   hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(a.B * a.nq), dim3(128), 0, s, a);
   return hipGetLastError();
 }

@@ -83,8 +83,9 @@ struct AttnDecodeArgs {
   float* part;         // [B][nq][splits][hd + 2]
   int B, nq, nkv, cap, max_pos, splits, chunk;
 };
-void attn_decode_plan(int cap, int& splits, int& chunk);
+void attn_decode_plan(int cap, int B, int nkv, int& splits, int& chunk);
 hipError_t attn_decode(const AttnDecodeArgs& a, hipStream_t s);
+hipError_t attn_decode_combine(const AttnDecodeArgs& a, hipStream_t s);
 
 // ---- sampling (argmax.hip)
 hipError_t argmax_rows(const float* logits, int64_t row_stride, int rows, int V, int32_t* out,

@@ -121,7 +121,7 @@ DenseLayout dense_layout(const qwen3_config* c, int op, int B, int S, int cap_hi
     L.vtf = b.take((size_t)B * nkv * L.fresh_w_max * hd * 2);
   }
   if (decode) {
-    attn_decode_plan(cap_hint, L.attn_splits, L.attn_chunk);
+    attn_decode_plan(cap_hint, B, nkv, L.attn_splits, L.attn_chunk);
     L.part_attn = b.take((size_t)B * nq * L.attn_splits * (hd + 2) * 4);
   }
   if (stack) {
@@ -308,9 +308,13 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
     d.pos = io.pos; d.out = attn; d.part = (float*)(ws + L.part_attn);
     d.B = io.B; d.nq = nq; d.nkv = nkv; d.cap = kv->capacity;
     d.max_pos = c->max_position_embeddings;
-    attn_decode_plan(kv->capacity, d.splits, d.chunk);
-    ProfScope ps("attn_decode", s);
-    CHECK_HIP(attn_decode(d, s));
+    attn_decode_plan(kv->capacity, io.B, nkv, d.splits, d.chunk);
+    {
+      ProfScope ps("attn_decode", s);
+      CHECK_HIP(attn_decode(d, s));
+    }
+    ProfScope ps("attn_decode_combine", s);
+    CHECK_HIP(attn_decode_combine(d, s));
   } else {
     AttnPrefillArgs p{};
     p.q = q; p.k_cache = (const bf16_t*)kv->k; p.vt_cache = (const bf16_t*)kv->vt;

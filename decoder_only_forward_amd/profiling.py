@@ -1,0 +1,205 @@
+"""Text summaries of rocprofv3 output for the benchmark.
+
+Two kinds of run are summarised (both write CSV with ``--output-format csv``):
+
+* kernel trace with statistics (``--kernel-trace --stats``): per kernel class, the number
+  of dispatches, total and average duration;
+* hardware counters (``--pmc FETCH_SIZE`` and, in a second run, ``--pmc WRITE_SIZE``):
+  HBM kilobytes read / written per dispatch.  The raw counter is scaled by what it reads
+  for a plain elementwise copy of known size, run first in the same process
+  (``bench.py --copy-gib``), so the figure is in real bytes.
+
+The traffic table is keyed by profile tag and stamped with a hash of the sources the
+kernel is built from; ``bench.py`` reports it only while those sources are unchanged.
+
+Usage (after the rocprofv3 runs):
+  python -m decoder_only_forward_amd.profiling stats <dir> <workload> <command> <out.md>
+  python -m decoder_only_forward_amd.profiling traffic <fetch_dir> <write_dir> <workload>
+         <copy_gib> <command_fetch> <command_write> <traffic.json>
+"""
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+
+# profile tag -> (substring of the demangled kernel name, source files of that kernel)
+_GEMM = ["gemm_kernel.h", "gemm.hip", "common.h"]
+KERNELS = {
+    "qkv_gemm": ("gemm_kernel<", _GEMM),
+    "qk_norm_rope_cache": ("qkv_rope_cache_kernel", ["norm_rope.hip", "common.h"]),
+    "attn_prefill": ("attn_prefill_kernel", ["attention.hip", "common.h"]),
+    "attn_decode": ("attn_decode_kernel", ["attention.hip", "common.h"]),
+    "gate_up_gemm": ("gemm_kernel<", _GEMM),
+    "lm_head_gemm": ("gemm_kernel<", _GEMM),
+    "moe_gate_up_gemm": ("gemm_kernel<", _GEMM),
+    "moe_down_gemm": ("gemm_kernel<", _GEMM),
+}
+
+# Template signatures that single out one GEMM use (fp16 A, B mode, epilogue, grouped,
+# split-K).  o_proj and down share one instantiation and are not told apart here.
+GEMM_SIGNATURE = {
+    "qkv_gemm": "true, 1, 1, false, false>",
+    "gate_up_gemm": "true, 2, 5, false, false>",
+    "lm_head_gemm": "true, 0, 1, false, false>",
+    "moe_gate_up_gemm": ", 2, 5, true, false>",
+    "moe_down_gemm": ", 0, 1, true, false>",
+}
+
+
+def source_hash(tag):
+    h = hashlib.sha256()
+    for f in KERNELS[tag][1]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _csv_rows(pattern):
+    rows = []
+    for f in sorted(glob.glob(pattern, recursive=True)):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def short_name(name):
+    """Demangled kernel name without its argument list and anonymous namespaces."""
+    n = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    depth = 0
+    for i, ch in enumerate(n):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return n[:i][:110]
+    return n[:110]
+
+
+def stats_markdown(rocprof_dir, workload, command):
+    rows = _csv_rows(os.path.join(rocprof_dir, "**", "*kernel_stats.csv"))
+    if not rows:
+        raise SystemExit(f"no kernel_stats.csv under {rocprof_dir}")
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    out = [f"# rocprofv3 kernel statistics: {workload}", "",
+           "Command (run from the repository root):", "", "```", command, "```", "",
+           "| kernel | calls | total ms | avg us | % time |", "|---|---:|---:|---:|---:|"]
+    for r in rows:
+        t = float(r["TotalDurationNs"])
+        if t / total < 0.002:
+            continue
+        out.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | {t / 1e6:.3f} | "
+                   f"{float(r['AverageNs']) / 1e3:.2f} | {100 * t / total:.1f} |")
+    out.append("")
+    out.append(f"All kernels: {total / 1e6:.3f} ms in total (setup kernels included).")
+    return "\n".join(out) + "\n"
+
+
+def _per_dispatch(rocprof_dir, counter):
+    rows = _csv_rows(os.path.join(rocprof_dir, "**", "*counter_collection.csv"))
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        key = (r["Dispatch_Id"], r["Kernel_Name"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    return [(name, v) for (_, name), v in per.items()]
+
+
+def _select(dispatches, tag):
+    sub, _ = KERNELS[tag]
+    sig = GEMM_SIGNATURE.get(tag)
+    vals = [v for n, v in dispatches if sub in n and (sig is None or sig in n)]
+    return vals
+
+
+def _copy_scale(dispatches, copy_bytes):
+    # the calibration copy is the largest elementwise dispatch of the run
+    cands = [v for n, v in dispatches if "elementwise" in n]
+    if not cands:
+        raise SystemExit("calibration copy dispatch not found")
+    return copy_bytes / 1024.0 / max(cands)
+
+
+def traffic_json(fetch_dir, write_dir, workload, copy_gib, cmd_fetch, cmd_write, tags,
+                 existing=None):
+    fd = _per_dispatch(fetch_dir, "FETCH_SIZE")
+    wd = _per_dispatch(write_dir, "WRITE_SIZE")
+    copy_bytes = copy_gib * (1 << 30)
+    fscale, wscale = _copy_scale(fd, copy_bytes), _copy_scale(wd, copy_bytes)
+    table = dict(existing or {})
+    for tag in tags:
+        fv, wv = _select(fd, tag), _select(wd, tag)
+        if not fv or not wv:
+            continue
+        f_kib, w_kib = sum(fv) / len(fv), sum(wv) / len(wv)
+        table[f"{workload}/{tag}"] = {
+            "fetch_kib_raw": round(f_kib, 1), "write_kib_raw": round(w_kib, 1),
+            "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4),
+            "bytes_per_launch": round((f_kib * fscale + w_kib * wscale) * 1024.0),
+            "dispatches": [len(fv), len(wv)], "source_sha": source_hash(tag),
+            "commands": [cmd_fetch, cmd_write]}
+    return table
+
+
+def traffic_for(workload, tag, path=None):
+    """HBM bytes per launch from the committed counter table, or None when absent or
+    when the kernel's sources changed since the counters were taken."""
+    path = path or os.path.join(os.path.dirname(HERE), "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            e = json.load(fh).get(f"{workload}/{tag}")
+    except (OSError, ValueError):
+        return None
+    if not e or tag not in KERNELS or e.get("source_sha") != source_hash(tag):
+        return None
+    return float(e["bytes_per_launch"])
+
+
+def traffic_markdown(table):
+    out = ["# HBM traffic per dispatch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+           "Raw counters are KiB per dispatch; each is scaled by (known bytes / counter "
+           "reading) of a plain elementwise copy run first in the same process.", "",
+           "| workload/tag | fetch KiB (raw) | write KiB (raw) | fetch scale | write scale | "
+           "HBM bytes / launch | dispatches | source sha |",
+           "|---|---:|---:|---:|---:|---:|---|---|"]
+    for k, e in sorted(table.items()):
+        out.append(f"| {k} | {e['fetch_kib_raw']} | {e['write_kib_raw']} | "
+                   f"{e['fetch_scale']} | {e['write_scale']} | {e['bytes_per_launch']:.0f} | "
+                   f"{e['dispatches']} | {e['source_sha']} |")
+    out.append("")
+    out.append("Commands:")
+    for k, e in sorted(table.items()):
+        out.append(f"- {k}: `{e['commands'][0]}` then `{e['commands'][1]}`")
+    return "\n".join(out) + "\n"
+
+
+def main(argv):
+    if argv[0] == "stats":
+        d, workload, cmd, out = argv[1:5]
+        with open(out, "w") as fh:
+            fh.write(stats_markdown(d, workload, cmd))
+    elif argv[0] == "traffic":
+        fdir, wdir, workload, gib, cf, cw, out = argv[1:8]
+        tags = argv[8].split(",") if len(argv) > 8 else list(KERNELS)
+        existing = None
+        if os.path.exists(out):
+            with open(out) as fh:
+                existing = json.load(fh)
+        table = traffic_json(fdir, wdir, workload, float(gib), cf, cw, tags, existing)
+        with open(out, "w") as fh:
+            json.dump(table, fh, indent=1, sort_keys=True)
+        with open(os.path.splitext(out)[0] + ".md", "w") as fh:
+            fh.write(traffic_markdown(table))
+    else:
+        raise SystemExit(__doc__)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])

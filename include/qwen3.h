@@ -198,7 +198,7 @@ int qwen3_stack_forward(const qwen3_config *cfg, const qwen3_model_weights *w,
 /* Opt-in kernel timing for measurement tools.  qwen3_profile_begin(tag, n) makes the
  * next (up to n) launches of the kernel class `tag` record a pair of HIP events on their
  * launch stream (tags: "qkv_gemm", "qk_norm_rope_cache", "attn_prefill", "attn_decode",
- * "o_proj_gemm", "gate_up_gemm", "down_gemm", "lm_head_gemm", "argmax",
+ * "attn_decode_combine", "o_proj_gemm", "gate_up_gemm", "down_gemm", "lm_head_gemm", "argmax",
  * "moe_router_gemm", "moe_route", "moe_gate_up_gemm", "moe_down_gemm", "moe_combine").
  * It creates 2n host-side event objects once (not on the forward path).
  * qwen3_profile_end() stops recording; after the caller has synchronised the stream it
