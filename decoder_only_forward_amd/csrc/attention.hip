@@ -7,12 +7,12 @@
 // Prefill operands: q arrives in fp16; keys/values produced by this call come from
 // unrounded fp16 copies, older ones from the bf16 cache (converted to fp16, exact in fp16's
 // normal range, as they are staged); P is rounded to fp16.  Both products run on
-// v_mfma_f32_32x32x16_f16.
+// v_mfma_f32_16x16x32_f16.
 // Prefill (flash-style, matrix cores):
-//   one block = 256 query rows of one q head, 4 waves x 64 rows; K tiles of 64 keys
+//   one block = 192 query rows of one q head, 4 waves x 48 rows; K tiles of 64 keys
 //   [64][128] and the matching V^T tile [128][64] are staged in LDS (double buffered).
 //   Scores are formed transposed, S^T = K . Q^T, so each lane owns one query column:
-//   the row max needs one cross-lane step and the rescale is per lane.  The
+//   the row max needs two cross-lane steps and the rescale is per lane.  The
 //   probabilities P^T then sit in registers exactly in the B-operand order of
 //   O^T = V^T . P^T (k-slots permuted consistently with the V^T reads), so P never
 //   leaves registers; this is why the cache keeps V transposed.  Tiles entirely above
@@ -30,42 +30,47 @@ namespace q3 {
 namespace {
 
 constexpr int HD = 128;
-constexpr int WROWS = 64;   // query rows per wave (two 32-column MFMA tiles)
+constexpr int NT = 3;                 // 16-query MFMA column tiles per wave
+constexpr int WROWS = 16 * NT;        // query rows per wave
 constexpr int PF_WAVES = 4;
 constexpr int BQ = WROWS * PF_WAVES;  // query rows per block
-constexpr int BKV = 64;     // keys per tile
+constexpr int BKV = 64;               // keys per LDS tile (two 32-key halves)
 
-// LDS layouts (16-byte chunks, XOR-swizzled so that the fragment reads of 16 consecutive
-// rows at one logical chunk hit distinct banks):
-//   K tile   [64 keys][128 dims]  = 16 chunks per row, chunk ^ (row & 15)
-//   V^T tile [128 dims][64 keys]  =  8 chunks per row, chunk ^ (row & 7) ^ (row >> 3 & 1)
-DEV int k_off(int row, int chunk) { return row * HD + ((chunk ^ (row & 15)) << 3); }
-DEV int v_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// LDS layouts, 16-byte chunks XOR-swizzled so that each 16-lane group of a fragment read
+// touches 16 distinct 4-bank groups:
+//   K tile   [64 keys][128 dims], 16 chunks per row.  A fragment read takes rows
+//            8 (r / 4) + 4 mt + r % 4 (+ 32 in the upper half), r = 0..15, at one logical
+//            chunk; row bits 0-1 and 3-4 select the swizzle, which is then r itself.
+//   V^T tile [128 dims][64 keys], 8 chunks per row, two rows per bank line.  A fragment
+//            read takes 16 consecutive rows at one chunk; rows of one parity get distinct
+//            chunks from row bits 1-3.
+DEV int k_swz(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
+DEV int k_off(int row, int chunk) { return row * HD + ((chunk ^ k_swz(row)) << 3); }
+DEV int v_swz(int row) { return (row >> 1) & 7; }
 DEV int v_off(int row, int chunk) { return row * BKV + ((chunk ^ v_swz(row)) << 3); }
 
 DEV float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-DEV f32x16_t mfma32(f16x8_t a, f16x8_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+DEV f32x4_t mfma16_f16(f16x8_t a, f16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Key order inside a 32-key MFMA tile: A-operand row rho reads key pi(rho), pi swapping
-// bits 2 and 3.  With the 32x32 accumulator layout (lane l, h = l / 32, register i ->
-// row 8(i/4) + 4h + i%4) this puts keys 16(i/8) + 8h + i%8 in register i of lane half h:
-// each 8-register group holds 8 consecutive keys, which is the B-operand k-slot order of
-// the P^T.V product, and the matching V^T fragment is one contiguous 16-byte read.
-DEV int key_perm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
-
-// 32x32x16 MFMA operand layouts (lane l, h = l / 32): A row l % 32 and B column l % 32,
-// k = 8h .. 8h + 7 for both.  S^T = K . Q^T puts one query in each lane's column, so the
-// row max needs one cross-lane step and the rescale is per lane.
+// 16x16x32 MFMA operand layouts (lane l, r = l % 16, grp = l / 16): A row r and B column r,
+// k = 8 grp .. 8 grp + 7 for both; the accumulator holds column r, rows 4 grp .. 4 grp + 3.
+// S^T = K . Q^T puts one query in each lane's column, so the row max needs two cross-lane
+// steps and the rescale is per lane.  Key order: in 32-key half h2 and 16-key m-tile mt,
+// A row r reads key 8 (r / 4) + 4 mt + r % 4, so a lane's two accumulators hold keys
+// 8 grp .. 8 grp + 7, which is the B-operand k order of O^T = V^T . P^T; P^T never leaves
+// registers and the matching V^T fragment is one 16-byte read.  48 query rows per wave keep
+// the live state (Q^T 48, O^T 96, S^T 24, P^T 12 registers) small enough for two waves per
+// SIMD, so one wave's softmax overlaps the other's matrix work.
 template <bool HAS_PAST>
-__global__ void __launch_bounds__(256) attn_prefill_kernel(AttnPrefillArgs a) {
+__global__ void __launch_bounds__(256, HAS_PAST ? 1 : 2) attn_prefill_kernel(AttnPrefillArgs a) {
   __shared__ __attribute__((aligned(16))) f16_t sK[2][BKV * HD];
   __shared__ __attribute__((aligned(16))) f16_t sV[2][HD * BKV];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, hh = lane >> 5;
+  const int r16 = lane & 15, grp = lane >> 4;
   const int nmb = (a.S + BQ - 1) / BQ;
   const int nblocks = nmb * a.B * a.nq;
   // contiguous work ranges per XCD; heavy (late) row blocks first
@@ -83,41 +88,45 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnPrefillArgs a) {
   const int kv_len = a.pos0 + min(a.S, row0 + BQ);   // keys this block may need
   const int ntiles = (kv_len + BKV - 1) / BKV;
   const int wrow0 = row0 + wave * WROWS;
-  const int wave_max_pos = a.pos0 + min(a.S - 1, wrow0 + WROWS - 1);
+  // a wave whose rows all lie past the sequence end computes nothing
+  const int wave_max_pos = wrow0 < a.S ? a.pos0 + min(a.S - 1, wrow0 + WROWS - 1) : -1;
   const int wave_min_pos = a.pos0 + wrow0;
 
   const f16_t* kfbase = a.k_fresh + ((int64_t)b * a.nkv + kvh) * a.fresh_w * HD;
   const f16_t* vfbase = a.vt_fresh + ((int64_t)b * a.nkv + kvh) * HD * a.fresh_w;
 
   // Q^T fragments (B operand): column = query row, k = head dims
-  f16x8_t qf[2][8];
-  int qpos[2];
+  f16x8_t qf[NT][4];
+  int qpos[NT];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    int s = wrow0 + nt * 32 + l32;
-    bool valid = s < a.S;
-    int sc = valid ? s : a.S - 1;
+  for (int nt = 0; nt < NT; ++nt) {
+    const int s = wrow0 + nt * 16 + r16;
+    const bool valid = s < a.S;
+    const int sc = valid ? s : a.S - 1;
     qpos[nt] = valid ? a.pos0 + s : kv_len - 1;
-    const f16_t* qp = a.q + (((int64_t)b * a.S + sc) * a.nq + h) * HD;
+    const f16_t* qp = a.q + (((int64_t)b * a.S + sc) * a.nq + h) * HD + grp * 8;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[nt][ks] = as_f16x8(ld16(qp + ks * 16 + hh * 8));
+    for (int ks = 0; ks < 4; ++ks) qf[nt][ks] = as_f16x8(ld16(qp + ks * 32));
   }
 
-  f32x16_t oacc[4][2];
+  f32x4_t oacc[8][NT];
 #pragma unroll
-  for (int md = 0; md < 4; ++md)
+  for (int md = 0; md < 8; ++md)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[md][nt][i] = 0.f;
+    for (int nt = 0; nt < NT; ++nt) oacc[md][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // q arrives pre-scaled by log2(e) / sqrt(hd): scores are in log2 units
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  float m_run[NT], l_run[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m_run[nt] = -INFINITY;
+    l_run[nt] = 0.f;
+  }
 
   // ---- tile staging
   // No past (pos0 == 0): every key/value of the block comes from the fp16 copies written
   // by this call (zero beyond the last position), loaded straight into LDS with
-  // lds_dma16: lane L of a wave instruction lands at base + 16 L, so each
-  // lane fetches the logical chunk that the swizzle places at its physical slot.
+  // lds_dma16: lane L of a wave instruction lands at base + 16 L, so each lane fetches
+  // the logical chunk that the swizzle places at its physical slot.
   // With a past: keys/values < pos0 come from the bf16 cache (converted to fp16 in
   // registers), the rest from the fp16 copies; rows/columns >= kv_len are zero.
   auto direct_load = [&](int t, int st) {
@@ -126,7 +135,7 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnPrefillArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int o = (wave * 4 + i) * 1024 + lane * 16;  // byte offset in the K tile
       const int row = o >> 8, p = (o >> 4) & 15;
-      const f16_t* src = kfbase + (int64_t)(j0 + row - a.fresh_base) * HD + ((p ^ (row & 15)) << 3);
+      const f16_t* src = kfbase + (int64_t)(j0 + row - a.fresh_base) * HD + ((p ^ k_swz(row)) << 3);
       lds_dma16(src, &sK[st][(wave * 4 + i) * 512]);
     }
 #pragma unroll
@@ -208,50 +217,48 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnPrefillArgs a) {
   }
   __syncthreads();
 
-  const int krow0 = key_perm(l32);
+  const int krow = 8 * (r16 >> 2) + (r16 & 3);  // K row of A-operand row r16 (mt = 0, h2 = 0)
   for (int t = 0; t < ntiles; ++t) {
     const int st = t & 1;
     if (t + 1 < ntiles) {
       if (HAS_PAST) gload(t + 1);
       else direct_load(t + 1, st ^ 1);
     }
-    const int j0 = t * BKV;
-    if (j0 <= wave_max_pos) {
-      // S^T[key][qrow]: 64 keys (mt) x 64 query rows (nt)
-      f32x16_t sacc[2][2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int k0 = t * BKV + 32 * h2;
+      if (k0 > wave_max_pos) continue;
+      // S^T[key][query]: 32 keys (two 16-key m-tiles) x 48 queries
+      f32x4_t sacc[2][NT];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[mt][nt][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
+      for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          f16x8_t kf = as_f16x8(ld16(&sK[st][k_off(mt * 32 + krow0, ks * 2 + hh)]));
+          const f16x8_t kf = as_f16x8(ld16(&sK[st][k_off(32 * h2 + 4 * mt + krow, 4 * ks + grp)]));
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) sacc[mt][nt] = mfma32(kf, qf[nt][ks], sacc[mt][nt]);
+          for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = mfma16_f16(kf, qf[nt][ks], sacc[mt][nt]);
         }
       }
-      const bool need_mask = j0 + BKV - 1 > wave_min_pos;
-      f16x8_t pf[2][4];
+      const bool need_mask = k0 + 31 > wave_min_pos;
+      f16x8_t pf[NT];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        float tmax = -INFINITY;
+      for (int nt = 0; nt < NT; ++nt) {
         if (need_mask) {
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              int key = j0 + mt * 32 + (i >> 3) * 16 + hh * 8 + (i & 7);
-              if (key > qpos[nt]) sacc[mt][nt][i] = -INFINITY;
-            }
+            for (int i = 0; i < 4; ++i)
+              if (k0 + 8 * grp + 4 * mt + i > qpos[nt]) sacc[mt][nt][i] = -INFINITY;
         }
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[mt][nt][i]);
+        float tmax = fmaxf(fmaxf(fmaxf(sacc[0][nt][0], sacc[0][nt][1]),
+                                 fmaxf(sacc[0][nt][2], sacc[0][nt][3])),
+                           fmaxf(fmaxf(sacc[1][nt][0], sacc[1][nt][1]),
+                                 fmaxf(sacc[1][nt][2], sacc[1][nt][3])));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
         // Lazy rescaling: the running max is only raised when a score exceeds it by more
         // than 8 (log2 units), so P <= 2^8 stays exact enough in fp16 and the output
@@ -263,36 +270,28 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnPrefillArgs a) {
           m_run[nt] = m_new;
           l_run[nt] *= alpha;
 #pragma unroll
-          for (int md = 0; md < 4; ++md)
+          for (int md = 0; md < 8; ++md)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[md][nt][i] *= alpha;
+            for (int i = 0; i < 4; ++i) oacc[md][nt][i] *= alpha;
         }
         const float m_use = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
-        float psum = 0.f;
+        float p[8];
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-          const int mt = s2 >> 1, i0 = (s2 & 1) * 8;
-          u32x4_t u;
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float p0 = exp2_fast(sacc[mt][nt][i0 + 2 * e] - m_use);
-            float p1 = exp2_fast(sacc[mt][nt][i0 + 2 * e + 1] - m_use);
-            psum += p0 + p1;
-            u[e] = pack_f16x2(p0, p1);
-          }
-          pf[nt][s2] = as_f16x8(u);
-        }
-        l_run[nt] += psum;
+          for (int i = 0; i < 4; ++i) p[4 * mt + i] = exp2_fast(sacc[mt][nt][i] - m_use);
+        l_run[nt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        u32x4_t u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = pack_f16x2(p[2 * e], p[2 * e + 1]);
+        pf[nt] = as_f16x8(u);
       }
-      // O^T[d][qrow] += V^T[d][keys] . P^T[keys][qrow]; keys 16 s2 + 8h .. +8 per lane half
+      // O^T[d][query] += V^T[d][keys] . P^T[keys][query]; keys 8 grp .. +8 per lane group
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
+      for (int md = 0; md < 8; ++md) {
+        const f16x8_t vf = as_f16x8(ld16(&sV[st][v_off(md * 16 + r16, 4 * h2 + grp)]));
 #pragma unroll
-        for (int md = 0; md < 4; ++md) {
-          f16x8_t vf = as_f16x8(ld16(&sV[st][v_off(md * 32 + l32, s2 * 2 + hh)]));
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) oacc[md][nt] = mfma32(vf, pf[nt][s2], oacc[md][nt]);
-        }
+        for (int nt = 0; nt < NT; ++nt) oacc[md][nt] = mfma16_f16(vf, pf[nt], oacc[md][nt]);
       }
     }
     if (t + 1 < ntiles) {
@@ -302,24 +301,23 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnPrefillArgs a) {
     __syncthreads();
   }
 
-  // normalise and store: lane owns query column l32 of n-tile nt, dims 32md + 8g + 4hh + i
+  // normalise and store: lane owns query column r16 of n-tile nt, dims 16 md + 4 grp + i
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
     float l = l_run[nt];
+    l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
     const float inv = 1.0f / l;
-    const int s = wrow0 + nt * 32 + l32;
+    const int s = wrow0 + nt * 16 + r16;
     if (s >= a.S) continue;
-    f16_t* op = a.out + (((int64_t)b * a.S + s) * a.nq + h) * HD;
+    f16_t* op = a.out + (((int64_t)b * a.S + s) * a.nq + h) * HD + grp * 4;
 #pragma unroll
-    for (int md = 0; md < 4; ++md)
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        u32x2_t v;
-        v[0] = pack_f16x2(oacc[md][nt][4 * gq] * inv, oacc[md][nt][4 * gq + 1] * inv);
-        v[1] = pack_f16x2(oacc[md][nt][4 * gq + 2] * inv, oacc[md][nt][4 * gq + 3] * inv);
-        *(u32x2_t*)(op + md * 32 + gq * 8 + hh * 4) = v;
-      }
+    for (int md = 0; md < 8; ++md) {
+      u32x2_t v;
+      v[0] = pack_f16x2(oacc[md][nt][0] * inv, oacc[md][nt][1] * inv);
+      v[1] = pack_f16x2(oacc[md][nt][2] * inv, oacc[md][nt][3] * inv);
+      *(u32x2_t*)(op + md * 16) = v;
+    }
   }
 }
 

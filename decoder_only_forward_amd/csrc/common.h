@@ -106,4 +106,7 @@ DEV void lds_dma16(const void* gptr, void* lds_base) {
       : "v"(gptr), "s"(lds)
       : "memory");
 }
-DEV void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// vmcnt(0) (expcnt and lgkmcnt left at their maxima), through the builtin so that the
+// compiler's own wait-count bookkeeping sees it: loads issued before it are known complete
+// afterwards, and no later vmcnt wait is inserted for them.
+DEV void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -82,8 +82,11 @@ GemmPlan gemm_plan(int M, int N, int K, int bmode, int epi, bool grouped) {
     p.partial_bytes = (size_t)p.k_splits * M * N * sizeof(float);
     return p;
   }
+  // residual epilogues stay on the 128x128 tile: with 256 accumulators per lane in the
+  // 256x256 tile the residual add does not fit the register file
+  const bool res = epi == E_RES_F32 || epi == E_RESB_F32 || epi == E_RESF_B16;
   int big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  p.tile = big_tiles >= 512 ? kBig : kMid;
+  p.tile = big_tiles >= 512 && !res ? kBig : kMid;
   return p;
 }
 
@@ -116,9 +119,6 @@ hipError_t gemm_run(const Args& a_in, bool f16, int bmode, int epi, bool grouped
   }
   // dense layers: fp16 activations x bf16->fp16 weights
   GEMM_CASE(kBig, TBig, true, B_QKV, E_F32, false)
-  GEMM_CASE(kBig, TBig, true, B_DENSE, E_RES_F32, false)
-  GEMM_CASE(kBig, TBig, true, B_DENSE, E_RESB_F32, false)
-  GEMM_CASE(kBig, TBig, true, B_DENSE, E_RESF_B16, false)
   GEMM_CASE(kBig, TBig, true, B_SWIGLU, E_SWIGLU, false)
   GEMM_CASE(kBig, TBig, true, B_DENSE, E_F32, false)
   GEMM_CASE(kMid, TMid, true, B_QKV, E_F32, false)

@@ -278,34 +278,56 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
       }
     return;
   }
+  // Residual modes walk the accumulator groups (i, j) as a pipeline: the residual values
+  // of group g + 1 are loaded before group g is stored, so only the first load latency is
+  // exposed.  The output may be the residual buffer itself: each element is read before it
+  // is written and distinct elements never overlap.
+  constexpr bool RES = EPI == E_RES_F32 || EPI == E_RESB_F32 || EPI == E_RESF_B16;
+  constexpr int NG = T::TM * T::TN;
+  auto load_res = [&](int gi, float* res) {
+    const int i = gi / T::TN, j = gi % T::TN;
+    const int col = n0 + wn * T::WN + j * 32 + ccol;
 #pragma unroll
-  for (int i = 0; i < T::TM; ++i)
+    for (int r = 0; r < 16; ++r) {
+      const int lr = wm * T::WM + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
+      const int64_t row = out_row0 + lr;
+      float v = 0.f;
+      if (col < p.N && lr < rows_valid) {
+        if (EPI == E_RESB_F32) v = bf2f(((const bf16_t*)p.R)[row * p.ldr + col]);
+        else v = ((const float*)p.R)[row * p.ldr + col];
+      }
+      res[r] = v;
+    }
+  };
+  float res_cur[16], res_next[16];
+  if (RES) load_res(0, res_next);
 #pragma unroll
-    for (int j = 0; j < T::TN; ++j) {
-      int col = n0 + wn * T::WN + j * 32 + ccol;
-      if (col >= p.N) continue;
+  for (int gi = 0; gi < NG; ++gi) {
+    const int i = gi / T::TN, j = gi % T::TN;
+    if (RES) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        int lr = wm * T::WM + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
-        if (lr >= rows_valid) continue;
-        int64_t row = out_row0 + lr;
-        float v = acc[i][j][r];
-        if (EPI == E_PARTIAL) {
-          p.partial[((int64_t)blockIdx.y * p.M + row) * p.N + col] = v;
-        } else if (EPI == E_F32) {
-          ((float*)p.C)[row * p.ldc + col] = v;
-        } else if (EPI == E_RES_F32) {
-          float res = ((const float*)p.R)[row * p.ldr + col];
-          ((float*)p.C)[row * p.ldc + col] = res + v;
-        } else if (EPI == E_RESB_F32) {
-          float res = bf2f(((const bf16_t*)p.R)[row * p.ldr + col]);
-          ((float*)p.C)[row * p.ldc + col] = res + v;
-        } else if (EPI == E_RESF_B16) {
-          float res = ((const float*)p.R)[row * p.ldr + col];
-          ((bf16_t*)p.C)[row * p.ldc + col] = f2bf(res + v);
-        }
+      for (int r = 0; r < 16; ++r) res_cur[r] = res_next[r];
+      if (gi + 1 < NG) load_res(gi + 1, res_next);
+    }
+    const int col = n0 + wn * T::WN + j * 32 + ccol;
+    if (col >= p.N) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int lr = wm * T::WM + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
+      if (lr >= rows_valid) continue;
+      const int64_t row = out_row0 + lr;
+      const float v = acc[i][j][r];
+      if (EPI == E_PARTIAL) {
+        p.partial[((int64_t)blockIdx.y * p.M + row) * p.N + col] = v;
+      } else if (EPI == E_F32) {
+        ((float*)p.C)[row * p.ldc + col] = v;
+      } else if (EPI == E_RES_F32 || EPI == E_RESB_F32) {
+        ((float*)p.C)[row * p.ldc + col] = res_cur[r] + v;
+      } else if (EPI == E_RESF_B16) {
+        ((bf16_t*)p.C)[row * p.ldc + col] = f2bf(res_cur[r] + v);
       }
     }
+  }
 }
 
 }  // namespace gemm
