@@ -11,6 +11,12 @@ BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["gemm.hip", "norm_rope.hip", "attention.hip", "argmax.hip", "moe.hip",
            "qwen3_api.cpp"]
 
+# Per-source extras.  attention.hip: its softmax takes maxima of MFMA results, which are
+# never signalling NaNs; without this the compiler quiets every fmaxf operand first.  The
+# file's handling of positions past a sequence's end (possibly NaN-filled cache slots) uses
+# integer position compares and bit masks only, never float comparisons.
+SOURCE_FLAGS = {"attention.hip": ["-fno-honor-nans"]}
+
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU ops are kept off: hand-written v_pk_* forms are avoided entirely
@@ -26,7 +32,7 @@ def build(verbose=False):
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".", "_") + ".o")
         objs.append(obj)
-        cmd = ["hipcc", *HIP_FLAGS]
+        cmd = ["hipcc", *HIP_FLAGS, *SOURCE_FLAGS.get(src, [])]
         if src.endswith(".cpp"):
             cmd += ["-x", "hip"]
         cmd += ["-c", os.path.join(CSRC, src), "-o", obj]

@@ -114,13 +114,15 @@ __global__ void __launch_bounds__(256, HAS_PAST ? 1 : 2) attn_prefill_kernel(Att
   for (int md = 0; md < 8; ++md)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) oacc[md][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // q arrives pre-scaled by log2(e) / sqrt(hd): scores are in log2 units
-  float m_run[NT], l_run[NT];
+  // q arrives pre-scaled by log2(e) / sqrt(hd): scores are in log2 units.  m_ref is the
+  // reference max the exponentials are taken against (set on the wave's first half).
+  float m_ref[NT], l_run[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    m_run[nt] = -INFINITY;
+    m_ref[nt] = 0.f;
     l_run[nt] = 0.f;
   }
+  bool first = true;
 
   // ---- tile staging
   // No past (pos0 == 0): every key/value of the block comes from the fp16 copies written
@@ -228,14 +230,21 @@ __global__ void __launch_bounds__(256, HAS_PAST ? 1 : 2) attn_prefill_kernel(Att
     for (int h2 = 0; h2 < 2; ++h2) {
       const int k0 = t * BKV + 32 * h2;
       if (k0 > wave_max_pos) continue;
-      // S^T[key][query]: 32 keys (two 16-key m-tiles) x 48 queries
+      // S^T[key][query] - m: 32 keys (two 16-key m-tiles) x 48 queries.  The running
+      // reference max enters as the accumulator's initial value, so the scores come out
+      // already shifted.
       f32x4_t sacc[2][NT];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int nt = 0; nt < NT; ++nt) {
+        const f32x4_t negm = {-m_ref[nt], -m_ref[nt], -m_ref[nt], -m_ref[nt]};
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < 2; ++mt) {
+          const f16x8_t kf = as_f16x8(ld16(&sK[st][k_off(32 * h2 + 4 * mt + krow, grp)]));
+          sacc[mt][nt] = mfma16_f16(kf, qf[nt][0], negm);
+        }
+      }
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 1; ks < 4; ++ks) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
           const f16x8_t kf = as_f16x8(ld16(&sK[st][k_off(32 * h2 + 4 * mt + krow, 4 * ks + grp)]));
@@ -243,43 +252,55 @@ __global__ void __launch_bounds__(256, HAS_PAST ? 1 : 2) attn_prefill_kernel(Att
           for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = mfma16_f16(kf, qf[nt][ks], sacc[mt][nt]);
         }
       }
-      const bool need_mask = k0 + 31 > wave_min_pos;
-      f16x8_t pf[NT];
+      if (k0 + 31 > wave_min_pos) {  // the causal diagonal crosses this half
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        if (need_mask) {
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               if (k0 + 8 * grp + 4 * mt + i > qpos[nt]) sacc[mt][nt][i] = -INFINITY;
-        }
-        float tmax = fmaxf(fmaxf(fmaxf(sacc[0][nt][0], sacc[0][nt][1]),
-                                 fmaxf(sacc[0][nt][2], sacc[0][nt][3])),
-                           fmaxf(fmaxf(sacc[1][nt][0], sacc[1][nt][1]),
-                                 fmaxf(sacc[1][nt][2], sacc[1][nt][3])));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        // Lazy rescaling: the running max is only raised when a score exceeds it by more
-        // than 8 (log2 units), so P <= 2^8 stays exact enough in fp16 and the output
-        // accumulators are rescaled only when some lane's max moved that far.
-        const bool raise = tmax > m_run[nt] + 8.0f;
-        if (__any(raise)) {
-          const float m_new = raise ? tmax : m_run[nt];
-          const float alpha = exp2_fast(m_run[nt] - m_new);
-          m_run[nt] = m_new;
+      }
+      float tmax[NT];
+      bool raise = false;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float x = fmaxf(fmaxf(fmaxf(sacc[0][nt][0], sacc[0][nt][1]), sacc[0][nt][2]),
+                        fmaxf(fmaxf(sacc[0][nt][3], sacc[1][nt][0]), sacc[1][nt][1]));
+        x = fmaxf(x, fmaxf(sacc[1][nt][2], sacc[1][nt][3]));
+        tmax[nt] = rows4_max(x);
+        raise |= tmax[nt] > 8.0f;
+      }
+      // Lazy rescaling: the reference max moves (to this half's max) only on a wave's
+      // first half or when a score exceeds it by more than 8 (log2 units), so P <= 2^8
+      // stays exact enough in fp16 and the accumulators are rescaled rarely.
+      if (first || __any(raise)) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const bool mv = (first && tmax[nt] > -INFINITY) || tmax[nt] > 8.0f;
+          const float delta = mv ? tmax[nt] : 0.f;
+          const float alpha = exp2_fast(-delta);
+          m_ref[nt] += delta;
           l_run[nt] *= alpha;
 #pragma unroll
           for (int md = 0; md < 8; ++md)
 #pragma unroll
             for (int i = 0; i < 4; ++i) oacc[md][nt][i] *= alpha;
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sacc[mt][nt][i] -= delta;
         }
-        const float m_use = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
+        first = false;
+      }
+      f16x8_t pf[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
         float p[8];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) p[4 * mt + i] = exp2_fast(sacc[mt][nt][i] - m_use);
+          for (int i = 0; i < 4; ++i) p[4 * mt + i] = exp2_fast(sacc[mt][nt][i]);
         l_run[nt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         u32x4_t u;
 #pragma unroll
@@ -304,10 +325,7 @@ __global__ void __launch_bounds__(256, HAS_PAST ? 1 : 2) attn_prefill_kernel(Att
   // normalise and store: lane owns query column r16 of n-tile nt, dims 16 md + 4 grp + i
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    float l = l_run[nt];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    const float inv = 1.0f / l;
+    const float inv = 1.0f / rows4_sum(l_run[nt]);
     const int s = wrow0 + nt * 16 + r16;
     if (s >= a.S) continue;
     f16_t* op = a.out + (((int64_t)b * a.S + s) * a.nq + h) * HD + grp * 4;
@@ -420,8 +438,7 @@ DEV void dec_tile(DecState& st, const DecTile& t, const u32x4_t* qb, int key0, i
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[s][i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  mx = rows4_max(mx);
   // lazy rescale: move the reference max only when a score exceeds it by 2^8
   if (__any(mx > st.m + 8.f)) {
     const float mn = fmaxf(st.m, mx);
@@ -531,8 +548,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDecodeArgs a) {
     }
   }
   // fold the low-part columns into the high ones and the four row groups of the sum
-  st.l += __shfl_xor(st.l, 16, 64);
-  st.l += __shfl_xor(st.l, 32, 64);
+  st.l = rows4_sum(st.l);
 #pragma unroll
   for (int rt = 0; rt < 8; ++rt)
 #pragma unroll

@@ -33,8 +33,11 @@ DEV uint32_t pack_bf16x2(float lo, float hi) {
 // fp16 <-> fp32 (round to nearest even)
 DEV float h2f(f16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 DEV f16_t f2h(float f) { return __builtin_bit_cast(f16_t, (_Float16)f); }
+// two floats -> packed fp16 pair, round to nearest even (one v_cvt_pk_f16_f32)
 DEV uint32_t pack_f16x2(float lo, float hi) {
-  return (uint32_t)f2h(lo) | ((uint32_t)f2h(hi) << 16);
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{lo, hi}), h2));
 }
 DEV void unpack8_f16(const u32x4_t v, float* f) {
 #pragma unroll
@@ -73,6 +76,22 @@ DEV float warp_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
+}
+
+// Reductions over the four 16-lane rows of a wave (lanes r, r + 16, r + 32, r + 48) with
+// the gfx950 row-swap permutes (VALU only, no LDS round trip).  Every lane receives the
+// same result, formed in the same order.
+DEV float rows4_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+DEV float rows4_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 DEV float silu(float z) { return z / (1.0f + __expf(-z)); }
