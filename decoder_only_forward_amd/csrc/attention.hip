@@ -33,7 +33,9 @@ constexpr int HD = 128;
 constexpr int NT = 3;                 // 16-query MFMA column tiles per wave
 constexpr int WROWS = 16 * NT;        // query rows per wave
 constexpr int PF_WAVES = 4;
+constexpr int PF_THREADS = 64 * PF_WAVES;
 constexpr int BQ = WROWS * PF_WAVES;  // query rows per block
+constexpr int STAGE_WAVES = 4;        // waves that copy K/V tiles (16 KB = 4 x 4 x 1 KB each)
 constexpr int BKV = 64;               // keys per LDS tile (two 32-key halves)
 
 // LDS layouts, 16-byte chunks XOR-swizzled so that each 16-lane group of a fragment read
@@ -63,9 +65,10 @@ DEV f32x4_t mfma16_f16(f16x8_t a, f16x8_t b, f32x4_t c) {
 // 8 grp .. 8 grp + 7, which is the B-operand k order of O^T = V^T . P^T; P^T never leaves
 // registers and the matching V^T fragment is one 16-byte read.  48 query rows per wave keep
 // the live state (Q^T 48, O^T 96, S^T 24, P^T 12 registers) small enough for two waves per
-// SIMD, so one wave's softmax overlaps the other's matrix work.
+// SIMD, so one wave's softmax overlaps the other's matrix work.  (32 rows per wave at three
+// waves per SIMD measured slower: less reuse of each K/V fragment, more per-wave overhead.)
 template <bool HAS_PAST>
-__global__ void __launch_bounds__(256, HAS_PAST ? 1 : 2) attn_prefill_kernel(AttnPrefillArgs a) {
+__global__ void __launch_bounds__(PF_THREADS, HAS_PAST ? 1 : 2) attn_prefill_kernel(AttnPrefillArgs a) {
   __shared__ __attribute__((aligned(16))) f16_t sK[2][BKV * HD];
   __shared__ __attribute__((aligned(16))) f16_t sV[2][HD * BKV];
 
@@ -116,13 +119,16 @@ __global__ void __launch_bounds__(256, HAS_PAST ? 1 : 2) attn_prefill_kernel(Att
     for (int nt = 0; nt < NT; ++nt) oacc[md][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // q arrives pre-scaled by log2(e) / sqrt(hd): scores are in log2 units.  m_ref is the
   // reference max the exponentials are taken against (set on the wave's first half).
-  float m_ref[NT], l_run[NT];
+  // lacc accumulates the softmax denominators with the matrix cores (ones . P^T).
+  float m_ref[NT];
+  f32x4_t lacc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     m_ref[nt] = 0.f;
-    l_run[nt] = 0.f;
+    lacc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   bool first = true;
+  const f16x8_t ones = as_f16x8(u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u});
 
   // ---- tile staging
   // No past (pos0 == 0): every key/value of the block comes from the fp16 copies written
@@ -132,6 +138,7 @@ __global__ void __launch_bounds__(256, HAS_PAST ? 1 : 2) attn_prefill_kernel(Att
   // With a past: keys/values < pos0 come from the bf16 cache (converted to fp16 in
   // registers), the rest from the fp16 copies; rows/columns >= kv_len are zero.
   auto direct_load = [&](int t, int st) {
+    if (wave >= STAGE_WAVES) return;
     const int j0 = t * BKV;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -153,6 +160,7 @@ __global__ void __launch_bounds__(256, HAS_PAST ? 1 : 2) attn_prefill_kernel(Att
   u32x4_t rk[HAS_PAST ? 4 : 1], rv[HAS_PAST ? 4 : 1];
   const u32x4_t zero4 = {0u, 0u, 0u, 0u};
   auto gload = [&](int t) {
+    if (tid >= 64 * STAGE_WAVES) return;
     const int j0 = t * BKV;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -198,6 +206,7 @@ __global__ void __launch_bounds__(256, HAS_PAST ? 1 : 2) attn_prefill_kernel(Att
     }
   };
   auto sstore = [&](int st) {
+    if (tid >= 64 * STAGE_WAVES) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int c = tid & 15, r = (tid >> 4) + 16 * i;
@@ -261,27 +270,32 @@ __global__ void __launch_bounds__(256, HAS_PAST ? 1 : 2) attn_prefill_kernel(Att
             for (int i = 0; i < 4; ++i)
               if (k0 + 8 * grp + 4 * mt + i > qpos[nt]) sacc[mt][nt][i] = -INFINITY;
       }
-      float tmax[NT];
-      bool raise = false;
+      // Lazy rescaling: the reference max moves (to this half's column max) only on a
+      // wave's first half or when a score exceeds it by more than 8 (log2 units), so
+      // P <= 2^8 stays exact enough in fp16 and the accumulators are rescaled rarely.  The
+      // test needs only each lane's own maximum; column maxima are formed in the rare path.
+      float lmax = sacc[0][0][0];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        float x = fmaxf(fmaxf(fmaxf(sacc[0][nt][0], sacc[0][nt][1]), sacc[0][nt][2]),
-                        fmaxf(fmaxf(sacc[0][nt][3], sacc[1][nt][0]), sacc[1][nt][1]));
-        x = fmaxf(x, fmaxf(sacc[1][nt][2], sacc[1][nt][3]));
-        tmax[nt] = rows4_max(x);
-        raise |= tmax[nt] > 8.0f;
-      }
-      // Lazy rescaling: the reference max moves (to this half's max) only on a wave's
-      // first half or when a score exceeds it by more than 8 (log2 units), so P <= 2^8
-      // stays exact enough in fp16 and the accumulators are rescaled rarely.
-      if (first || __any(raise)) {
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, sacc[mt][nt][i]);
+      if (first || __any(lmax > 8.0f)) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const bool mv = (first && tmax[nt] > -INFINITY) || tmax[nt] > 8.0f;
-          const float delta = mv ? tmax[nt] : 0.f;
+          float x = sacc[0][nt][0];
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x = fmaxf(x, sacc[mt][nt][i]);
+          const float tmax = rows4_max(x);
+          const bool mv = (first && tmax > -INFINITY) || tmax > 8.0f;
+          const float delta = mv ? tmax : 0.f;
           const float alpha = exp2_fast(-delta);
           m_ref[nt] += delta;
-          l_run[nt] *= alpha;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lacc[nt][i] *= alpha;
 #pragma unroll
           for (int md = 0; md < 8; ++md)
 #pragma unroll
@@ -296,16 +310,14 @@ __global__ void __launch_bounds__(256, HAS_PAST ? 1 : 2) attn_prefill_kernel(Att
       f16x8_t pf[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        float p[8];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) p[4 * mt + i] = exp2_fast(sacc[mt][nt][i]);
-        l_run[nt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         u32x4_t u;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) u[e] = pack_f16x2(p[2 * e], p[2 * e + 1]);
+        for (int e = 0; e < 4; ++e)
+          u[e] = pack_f16x2(exp2_fast(sacc[e >> 1][nt][2 * (e & 1)]),
+                            exp2_fast(sacc[e >> 1][nt][2 * (e & 1) + 1]));
         pf[nt] = as_f16x8(u);
+        // row sums of the rounded P (every accumulator row gets the column's sum)
+        lacc[nt] = mfma16_f16(ones, pf[nt], lacc[nt]);
       }
       // O^T[d][query] += V^T[d][keys] . P^T[keys][query]; keys 8 grp .. +8 per lane group
 #pragma unroll
@@ -325,7 +337,7 @@ __global__ void __launch_bounds__(256, HAS_PAST ? 1 : 2) attn_prefill_kernel(Att
   // normalise and store: lane owns query column r16 of n-tile nt, dims 16 md + 4 grp + i
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const float inv = 1.0f / rows4_sum(l_run[nt]);
+    const float inv = 1.0f / lacc[nt][0];
     const int s = wrow0 + nt * 16 + r16;
     if (s >= a.S) continue;
     f16_t* op = a.out + (((int64_t)b * a.S + s) * a.nq + h) * HD + grp * 4;
@@ -618,9 +630,9 @@ hipError_t attn_prefill(const AttnPrefillArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.S <= 0) return hipSuccess;
   const int nmb = (a.S + BQ - 1) / BQ;
   if (a.pos0 > 0)
-    hipLaunchKernelGGL(attn_prefill_kernel<true>, dim3(nmb * a.B * a.nq), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_prefill_kernel<true>, dim3(nmb * a.B * a.nq), dim3(PF_THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3(nmb * a.B * a.nq), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3(nmb * a.B * a.nq), dim3(PF_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
