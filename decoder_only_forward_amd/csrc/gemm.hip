@@ -8,7 +8,7 @@ namespace {
 
 using namespace gemm;
 
-using TBig = Tile<256, 256, 2, 2>;   // 4 waves, 128x128 per wave, 128 KB LDS
+using TBig = Tile<256, 256, 2, 4>;   // 8 waves (2 per SIMD), 128x64 per wave, 128 KB LDS
 using TMid = Tile<128, 128, 2, 2>;   // 4 waves, 64x64 per wave, 32 KB LDS
 using TSkin = Tile<64, 128, 2, 2>;   // 4 waves, 32x64 per wave: decode (M <= 64)
 
@@ -82,11 +82,8 @@ GemmPlan gemm_plan(int M, int N, int K, int bmode, int epi, bool grouped) {
     p.partial_bytes = (size_t)p.k_splits * M * N * sizeof(float);
     return p;
   }
-  // residual epilogues stay on the 128x128 tile: with 256 accumulators per lane in the
-  // 256x256 tile the residual add does not fit the register file
-  const bool res = epi == E_RES_F32 || epi == E_RESB_F32 || epi == E_RESF_B16;
   int big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  p.tile = big_tiles >= 512 && !res ? kBig : kMid;
+  p.tile = big_tiles >= 512 ? kBig : kMid;
   return p;
 }
 
@@ -119,6 +116,9 @@ hipError_t gemm_run(const Args& a_in, bool f16, int bmode, int epi, bool grouped
   }
   // dense layers: fp16 activations x bf16->fp16 weights
   GEMM_CASE(kBig, TBig, true, B_QKV, E_F32, false)
+  GEMM_CASE(kBig, TBig, true, B_DENSE, E_RES_F32, false)
+  GEMM_CASE(kBig, TBig, true, B_DENSE, E_RESB_F32, false)
+  GEMM_CASE(kBig, TBig, true, B_DENSE, E_RESF_B16, false)
   GEMM_CASE(kBig, TBig, true, B_SWIGLU, E_SWIGLU, false)
   GEMM_CASE(kBig, TBig, true, B_DENSE, E_F32, false)
   GEMM_CASE(kMid, TMid, true, B_QKV, E_F32, false)

@@ -65,9 +65,10 @@ struct Tile {
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 32, TN = WN / 32;
-  static constexpr int THREADS = WAVES_M * WAVES_N * 64;
+  static constexpr int NWAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = NWAVES * 64;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(THREADS == 256 && BM % 32 == 0 && BN % 32 == 0, "4 waves, 8 rows per load");
+  static_assert(BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0, "8 rows per copy per wave");
 };
 
 // Blocks are dispatched round-robin over the 8 XCDs; give each XCD a contiguous run of
@@ -146,7 +147,7 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
   // row 8q + L/8, physical chunk L%8 of the tile, so each lane fetches the logical chunk
   // the swizzle stores there.  Rows past the valid range are clamped to the last valid
   // row: they only feed accumulator rows / columns the epilogue never stores.
-  constexpr int A_INSTS = T::BM / 32, B_INSTS = T::BN / 32;  // per wave, per stage
+  constexpr int A_INSTS = T::BM / (8 * T::NWAVES), B_INSTS = T::BN / (8 * T::NWAVES);  // per wave
   const int lrow = lane >> 3, pchunk = lane & 7;
   const uint16_t* aptr[A_INSTS];
   const bf16_t* bptr[B_INSTS];
@@ -284,19 +285,23 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
   // is written and distinct elements never overlap.
   constexpr bool RES = EPI == E_RES_F32 || EPI == E_RESB_F32 || EPI == E_RESF_B16;
   constexpr int NG = T::TM * T::TN;
+  // Rows / columns past the valid range are clamped to the last valid one: every load is
+  // in bounds and unconditional (so they issue back to back), and those elements are
+  // never stored.
   auto load_res = [&](int gi, float* res) {
     const int i = gi / T::TN, j = gi % T::TN;
-    const int col = n0 + wn * T::WN + j * 32 + ccol;
+    const int col = min(n0 + wn * T::WN + j * 32 + ccol, p.N - 1);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int lr = wm * T::WM + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
+      const int lr = min(wm * T::WM + i * 32 + (r >> 2) * 8 + rsub + (r & 3), rows_valid - 1);
       const int64_t row = out_row0 + lr;
-      float v = 0.f;
-      if (col < p.N && lr < rows_valid) {
-        if (EPI == E_RESB_F32) v = bf2f(((const bf16_t*)p.R)[row * p.ldr + col]);
-        else v = ((const float*)p.R)[row * p.ldr + col];
+      if (EPI == E_RESB_F32) {
+        // the aligned 32-bit word holding this bf16 and its neighbour's
+        const uint32_t w = *(const uint32_t*)((const bf16_t*)p.R + row * p.ldr + (col & ~1));
+        res[r] = __uint_as_float((col & 1) ? (w & 0xffff0000u) : (w << 16));
+      } else {
+        res[r] = ((const float*)p.R)[row * p.ldr + col];
       }
-      res[r] = v;
     }
   };
   float res_cur[16], res_next[16];
