@@ -139,12 +139,12 @@ def wl_prefill(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown):
 def dense_units(cfg, B, S, launches):
     """Algorithmic work per launch of each dense-block kernel class for a prefill of B x S
     tokens from position 0 (causal pairs only; the q/k-norm + RoPE + cache-write pass is
-    priced at the bytes this design moves: fp32 q/k/v in, fp16 q and bf16 cache plus fp16
+    priced at the bytes this design moves: fp16 q/k/v in, fp16 q and bf16 cache plus fp16
     fresh K/V out)."""
     H, nq, nkv, hd, I = (cfg["hidden_size"], cfg["num_attention_heads"],
                          cfg["num_key_value_heads"], cfg["head_dim"], cfg["intermediate_size"])
     T = B * S
-    rope_bytes = T * (nq + 2 * nkv) * hd * 4 + T * nq * hd * 2 + 4.0 * T * nkv * hd * 2
+    rope_bytes = T * (nq + 2 * nkv) * hd * 2 + T * nq * hd * 2 + 4.0 * T * nkv * hd * 2
     return {
         "qkv_gemm": ("mfma", 2.0 * T * H * (nq + 2 * nkv) * hd, launches),
         "qk_norm_rope_cache": ("hbm", float(rope_bytes), launches),
@@ -233,8 +233,8 @@ def wl_decode(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown):
     units = {
         # weights dominate the skinny GEMMs; activations in/out are counted too
         "qkv_gemm": ("hbm", 2.0 * H * (nq + 2 * nkv) * hd + 2.0 * B * H
-                     + 4.0 * B * (nq + 2 * nkv) * hd, L),
-        "qk_norm_rope_cache": ("hbm", 4.0 * B * (nq + 2 * nkv) * hd + 2.0 * B * nq * hd
+                     + 2.0 * B * (nq + 2 * nkv) * hd, L),
+        "qk_norm_rope_cache": ("hbm", 2.0 * B * (nq + 2 * nkv) * hd + 2.0 * B * nq * hd
                                + 2.0 * B * 2 * nkv * hd, L),
         "attn_decode": ("hbm", kv_bytes + 2.0 * B * nq * hd, L),
         "attn_decode_combine": ("hbm", part_bytes + 2.0 * B * nq * hd, L),

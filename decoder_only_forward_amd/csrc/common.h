@@ -26,8 +26,11 @@ DEV bf16_t f2bf(float f) {
   return (bf16_t)(u >> 16);
 }
 
+// two floats -> packed bf16 pair, round to nearest even, NaN stays NaN (v_cvt_pk_bf16_f32)
 DEV uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{lo, hi}), b2));
 }
 
 // fp16 <-> fp32 (round to nearest even)

@@ -54,6 +54,7 @@ splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N, i
     for (int z = 0; z < splits; ++z) v += part[((int64_t)z * M + m) * N + c];
     switch (epi) {
       case E_F32: ((float*)C)[m * ldc + c] = v; break;
+      case E_F16: ((f16_t*)C)[m * ldc + c] = f2h(v); break;
       case E_RES_F32: ((float*)C)[m * ldc + c] = ((const float*)R)[m * ldr + c] + v; break;
       case E_RESB_F32:
         ((float*)C)[m * ldc + c] = bf2f(((const bf16_t*)R)[m * ldr + c]) + v;
@@ -115,13 +116,13 @@ hipError_t gemm_run(const Args& a_in, bool f16, int bmode, int epi, bool grouped
     return hipGetLastError();
   }
   // dense layers: fp16 activations x bf16->fp16 weights
-  GEMM_CASE(kBig, TBig, true, B_QKV, E_F32, false)
+  GEMM_CASE(kBig, TBig, true, B_QKV, E_F16, false)
   GEMM_CASE(kBig, TBig, true, B_DENSE, E_RES_F32, false)
   GEMM_CASE(kBig, TBig, true, B_DENSE, E_RESB_F32, false)
   GEMM_CASE(kBig, TBig, true, B_DENSE, E_RESF_B16, false)
   GEMM_CASE(kBig, TBig, true, B_SWIGLU, E_SWIGLU, false)
   GEMM_CASE(kBig, TBig, true, B_DENSE, E_F32, false)
-  GEMM_CASE(kMid, TMid, true, B_QKV, E_F32, false)
+  GEMM_CASE(kMid, TMid, true, B_QKV, E_F16, false)
   GEMM_CASE(kMid, TMid, true, B_DENSE, E_RES_F32, false)
   GEMM_CASE(kMid, TMid, true, B_DENSE, E_RESB_F32, false)
   GEMM_CASE(kMid, TMid, true, B_DENSE, E_RESF_B16, false)

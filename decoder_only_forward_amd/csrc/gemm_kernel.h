@@ -7,14 +7,16 @@
 // activations they are kept in fp16 (8x finer rounding than bf16) and the weight tile
 // is converted bf16 -> fp16 on its way into LDS (exact in fp16's normal range), so the
 // fp16 MFMA runs at the same rate.
-// Block tile BM x BN x 64 staged through LDS, double buffered (one barrier per
-// k-step).  Each 128-byte tile row is stored with its eight 16-byte chunks XOR-swizzled
-// (lds_off), so the 16-byte fragment reads of consecutive lanes (consecutive rows, same
-// chunk) hit distinct banks, and the row-contiguous tile stores stay contiguous.
+// Block tile BM x BN x BK staged through a ring of STAGES LDS slots filled by direct
+// global -> LDS copies issued STAGES - 1 k-steps ahead (one barrier per k-step).  Tile
+// rows are stored with their 16-byte chunks XOR-swizzled (lds_off), so the 16-byte
+// fragment reads of consecutive lanes (consecutive rows, same chunk) hit distinct banks,
+// and each copy instruction still fills 1 KB of contiguous LDS.
 // Every wave owns a WM x WN sub-tile made of 32x32 MFMA tiles.
 //
 // Fused epilogues (one per projection of the decoder block):
-//   E_F32       fp32 store                               (QKV, LM head, router, MoE down)
+//   E_F32       fp32 store                               (LM head, router, MoE down)
+//   E_F16       fp16 store                               (QKV projections)
 //   E_RES_F32   out_f32 = res_f32 + acc (in place ok)    (o_proj / down in the stack)
 //   E_RESB_F32  out_f32 = float(res_bf16) + acc          (o_proj in the block API)
 //   E_RESF_B16  out_bf16 = bf16(res_f32 + acc)           (down in the block API)
@@ -33,7 +35,7 @@
 namespace gemm {
 
 enum BMode { B_DENSE = 0, B_QKV = 1, B_SWIGLU = 2 };
-enum EpiMode { E_F32 = 1, E_RES_F32, E_RESB_F32, E_RESF_B16, E_SWIGLU, E_PARTIAL };
+enum EpiMode { E_F32 = 1, E_RES_F32, E_RESB_F32, E_RESF_B16, E_SWIGLU, E_PARTIAL, E_F16 };
 
 struct Args {
   int M, N, K;  // N counts virtual columns (gate|up: 2 * I)
@@ -59,16 +61,19 @@ struct Args {
   int64_t g_b_stride;            // elements between experts' B matrices
 };
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_ = 64, int STAGES_ = 2>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, BK = 64;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int ROWS_PER_COPY = 1024 / (2 * BK);  // tile rows per 1 KB copy
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr int NWAVES = WAVES_M * WAVES_N;
   static constexpr int THREADS = NWAVES * 64;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(BM % (8 * NWAVES) == 0 && BN % (8 * NWAVES) == 0, "8 rows per copy per wave");
+  static_assert(BK == 32 || BK == 64, "k-step");
+  static_assert(BM % (ROWS_PER_COPY * NWAVES) == 0 && BN % (ROWS_PER_COPY * NWAVES) == 0,
+                "whole copies per wave");
 };
 
 // Blocks are dispatched round-robin over the 8 XCDs; give each XCD a contiguous run of
@@ -91,18 +96,31 @@ DEV void tile_coords(int t, int m_tiles, int n_tiles, int& tm, int& tn) {
   tn = rem / gm;
 }
 
-// 16-byte chunk c of tile row `row` (128-byte rows).  The XOR spreads any 16 consecutive
-// rows' fragment reads (same logical chunk) over distinct banks whether the LDS serves 8
-// lanes (128 B) or 16 lanes (256 B) of a 16-byte read per cycle: rows r and r+8 differ in
-// bit 0 of the swizzle and rows of opposite parity sit in opposite 128-byte halves.
-DEV int lds_off(int row, int chunk) {
-  return row * 64 + ((chunk ^ (row & 7) ^ ((row >> 3) & 1)) << 3);
+// 16-byte chunk c of tile row `row`.
+// 128-byte rows (BK = 64): the XOR spreads any 16 consecutive rows' fragment reads (same
+// logical chunk) over distinct banks whether the LDS serves 8 lanes (128 B) or 16 lanes
+// (256 B) of a 16-byte read per cycle: rows r and r+8 differ in bit 0 of the swizzle and
+// rows of opposite parity sit in opposite 128-byte halves.
+// 64-byte rows (BK = 32, four rows per 256-byte bank line): rows r, r+4, r+8, r+12 share
+// bank positions; XOR-ing the chunk with (r / 4) % 4 gives them distinct chunks.
+template <int BK>
+DEV int lds_swz(int row) {
+  return BK == 64 ? ((row & 7) ^ ((row >> 3) & 1)) : ((row >> 2) & 3);
+}
+template <int BK>
+DEV int lds_off(int row, int chunk) { return row * BK + ((chunk ^ lds_swz<BK>(row)) << 3); }
+
+// s_waitcnt vmcnt(N) through the builtin (expcnt and lgkmcnt at their maxima).
+template <int N>
+DEV void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | 0x0F70);
 }
 
 template <class T, bool F16, int BMODE, int EPI, bool GROUPED, bool SPLITK>
 __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][T::BM * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][T::BN * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t sA[T::STAGES][T::BM * T::BK];
+  __shared__ __attribute__((aligned(16))) bf16_t sB[T::STAGES][T::BN * T::BK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -133,7 +151,7 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
   const int n0 = tn * T::BN;
 
   // K range of this block (split-K over gridDim.y)
-  const int nk_total = p.K / 64;
+  const int nk_total = p.K / T::BK;
   int kt0 = 0, kt1 = nk_total;
   if (SPLITK) {
     int per = (nk_total + p.k_splits - 1) / p.k_splits;
@@ -144,26 +162,29 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
 
   // ---- operand tiles go global -> LDS directly (lds_dma16): lane L of a
   // wave instruction lands at 16 L bytes past that instruction's 1 KB LDS slot, i.e. at
-  // row 8q + L/8, physical chunk L%8 of the tile, so each lane fetches the logical chunk
-  // the swizzle stores there.  Rows past the valid range are clamped to the last valid
-  // row: they only feed accumulator rows / columns the epilogue never stores.
-  constexpr int A_INSTS = T::BM / (8 * T::NWAVES), B_INSTS = T::BN / (8 * T::NWAVES);  // per wave
-  const int lrow = lane >> 3, pchunk = lane & 7;
+  // row R q + L / C, physical chunk L % C of the tile (R rows of C chunks per copy), so
+  // each lane fetches the logical chunk the swizzle stores there.  Rows past the valid
+  // range are clamped to the last valid row: they only feed accumulator rows / columns
+  // the epilogue never stores.
+  constexpr int RPC = T::ROWS_PER_COPY, CPR = T::BK / 8;
+  constexpr int A_INSTS = T::BM / (RPC * T::NWAVES), B_INSTS = T::BN / (RPC * T::NWAVES);
+  constexpr int STAGE_INSTS = A_INSTS + B_INSTS;  // copies per wave per stage
+  const int lrow = lane / CPR, pchunk = lane % CPR;
   const uint16_t* aptr[A_INSTS];
   const bf16_t* bptr[B_INSTS];
 #pragma unroll
   for (int i = 0; i < A_INSTS; ++i) {
-    int r = 8 * (wave * A_INSTS + i) + lrow;
+    int r = RPC * (wave * A_INSTS + i) + lrow;
     int rc = min(r, rows_valid - 1);
     int orow = out_row0 + rc;
     int64_t arow = p.a_rows ? (int64_t)p.a_rows[orow] : (int64_t)orow;
-    int c = pchunk ^ (r & 7) ^ ((r >> 3) & 1);
+    int c = pchunk ^ lds_swz<T::BK>(r);
     aptr[i] = p.A + arow * p.lda + c * 8;
   }
 #pragma unroll
   for (int i = 0; i < B_INSTS; ++i) {
-    int r = 8 * (wave * B_INSTS + i) + lrow;
-    int c = pchunk ^ (r & 7) ^ ((r >> 3) & 1);
+    int r = RPC * (wave * B_INSTS + i) + lrow;
+    int c = pchunk ^ lds_swz<T::BK>(r);
     const bf16_t* ptr;
     if (BMODE == B_SWIGLU) {
       const int half = T::WN / 2;
@@ -192,7 +213,7 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   auto load_stage = [&](int kt, int st) {
-    const int koff = kt * 64;
+    const int koff = kt * T::BK;
 #pragma unroll
     for (int i = 0; i < A_INSTS; ++i)
       lds_dma16(aptr[i] + koff, &sA[st][(wave * A_INSTS + i) * 512]);
@@ -201,25 +222,27 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
       lds_dma16(bptr[i] + koff, &sB[st][(wave * B_INSTS + i) * 512]);
   };
 
-  if (nk > 0) {
-    load_stage(kt0, 0);
-    wait_dma();
-  }
+  // prologue: the first STAGES - 1 k-steps in flight, then wait for the first one
+#pragma unroll
+  for (int j = 0; j < T::STAGES - 1; ++j)
+    if (j < nk) load_stage(kt0 + j, j);
+  if (nk >= T::STAGES - 1) wait_vm<(T::STAGES - 2) * STAGE_INSTS>();
+  else wait_vm<0>();
   __syncthreads();
 
   const int frow = lane & 31, fhalf = lane >> 5;
-  // Inside a stage the fragments of k-step kk+1 are read from LDS while the MFMAs of
-  // k-step kk run; the next stage streams into the other buffer meanwhile.  bf16 weight
+  // Inside a stage the fragments of k-slice kk+1 are read from LDS while the MFMAs of
+  // k-slice kk run; later stages stream into the other ring slots meanwhile.  bf16 weight
   // fragments are converted to fp16 after the LDS read when the activations are fp16.
   u32x4_t fa[2][T::TM], fb[2][T::TN];
   auto read = [&](int s, int kk, int slot) {
     const int c = 2 * kk + fhalf;
 #pragma unroll
     for (int i = 0; i < T::TM; ++i)
-      fa[slot][i] = ld16(&sA[s][lds_off(wm * T::WM + i * 32 + frow, c)]);
+      fa[slot][i] = ld16(&sA[s][lds_off<T::BK>(wm * T::WM + i * 32 + frow, c)]);
 #pragma unroll
     for (int j = 0; j < T::TN; ++j) {
-      u32x4_t v = ld16(&sB[s][lds_off(wn * T::WN + j * 32 + frow, c)]);
+      u32x4_t v = ld16(&sB[s][lds_off<T::BK>(wn * T::WN + j * 32 + frow, c)]);
       fb[slot][j] = F16 ? bf16x8_to_f16x8(v) : v;
     }
   };
@@ -238,20 +261,23 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
                                                               0, 0, 0);
       }
   };
+  constexpr int KK = T::BK / 16;  // MFMA k-slices per stage
   for (int it = 0; it < nk; ++it) {
-    const int s = it & 1;
-    const bool more = it + 1 < nk;
-    // the other buffer was last read before the previous barrier
-    if (more) load_stage(kt0 + it + 1, s ^ 1);
+    const int s = it % T::STAGES;
+    // ring slot (it - 1) % STAGES was last read before the previous barrier
+    const bool issue = it + T::STAGES - 1 < nk;
+    if (issue) load_stage(kt0 + it + T::STAGES - 1, (it + T::STAGES - 1) % T::STAGES);
     read(s, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (kk < 3) read(s, kk + 1, (kk + 1) & 1);
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + 1 < KK) read(s, kk + 1, (kk + 1) & 1);
       mma(kk & 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) wait_dma();
+    // k-step it + 1 must have landed: at most the copies issued after it may be pending
+    if (issue) wait_vm<(T::STAGES - 2) * STAGE_INSTS>();
+    else wait_vm<0>();
     __syncthreads();
   }
 
@@ -326,6 +352,8 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
         p.partial[((int64_t)blockIdx.y * p.M + row) * p.N + col] = v;
       } else if (EPI == E_F32) {
         ((float*)p.C)[row * p.ldc + col] = v;
+      } else if (EPI == E_F16) {
+        ((f16_t*)p.C)[row * p.ldc + col] = f2h(v);
       } else if (EPI == E_RES_F32 || EPI == E_RESB_F32) {
         ((float*)p.C)[row * p.ldc + col] = res_cur[r] + v;
       } else if (EPI == E_RESF_B16) {

@@ -41,7 +41,7 @@ hipError_t embed_gather(const int32_t* ids, const bf16_t* table, float* out, int
 hipError_t rope_table(float* rope, int max_pos, int hd, double theta, hipStream_t s);
 
 struct RopeCacheArgs {
-  const float* qkv;  // [T][(nq + 2 nkv) * hd] fp32 projections, token t = b * S + s
+  const f16_t* qkv;  // [T][(nq + 2 nkv) * hd] fp16 projections, token t = b * S + s
   const float* rope;  // [2][max_pos][hd/2]
   const bf16_t* q_norm;
   const bf16_t* k_norm;
@@ -49,7 +49,7 @@ struct RopeCacheArgs {
   bf16_t* k_cache;  // [B][nkv][cap][hd]
   bf16_t* vt_cache; // [B][nkv][hd][cap]
   const int32_t* pos;  // decode: device [B] (S == 1); prefill: nullptr
-  // prefill only: unrounded fp16 copies of the new keys / values for the attention,
+  // prefill only: fp16 copies of the new keys / values (not rounded to bf16) for the attention,
   // indexed by absolute position - fresh_base; k_fresh [B][nkv][fresh_w][hd],
   // vt_fresh [B][nkv][hd][fresh_w] (nullptr: not written)
   f16_t* k_fresh;

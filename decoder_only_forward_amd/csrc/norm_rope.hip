@@ -89,14 +89,22 @@ rope_table_kernel(float* __restrict__ rope, int max_pos, int half, double theta,
 //   v heads:  v -> vt_cache[b][h][:][pos]  (transposed through LDS)
 // ([P3] "GQA 注意力": per-head q/k RMSNorm before RoPE, offset = cached length;
 // "RoPE": pairs (i, i + hd/2) rotated by pos * theta_i.)
-// Lane l of a wave holds dims l and l + 64 of one token: exactly one RoPE plane.
+// q / k heads: 16 lanes per token row, lane j holding dims 8j .. 8j + 7 (16-byte loads and
+// stores); the RoPE partner of dim d is dim d ^ 64, held by lane j ^ 8 of the same 16-lane
+// row, so the exchange and the sum of squares are row-local DPP rotations.
 constexpr int kRopeTile = 64;
+
+// rotate within 16-lane rows by n (n in 1..15)
+template <int N>
+DEV float ror16(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+}
 
 __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
   const int HD = 128;
   const int tile = blockIdx.x, b = blockIdx.y, slot = blockIdx.z;
   const int s0 = tile * kRopeTile;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row_elems = (a.nq + 2 * a.nkv) * HD;
   const int half = HD / 2;
 
@@ -106,7 +114,7 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
     const bool is_k = slot < a.nq + a.nkv;
     const int h = is_k ? slot - a.nq : slot - a.nq - a.nkv;
     const int t0 = a.pos0 + a.S - a.fresh_base, nt = a.fresh_w - t0;
-    for (int i = threadIdx.x; i < nt * HD; i += 256) {
+    for (int i = tid; i < nt * HD; i += 256) {
       const int r = t0 + i / HD, d = i % HD;
       if (is_k)
         a.k_fresh[(((int64_t)b * a.nkv + h) * a.fresh_w + r) * HD + d] = 0;
@@ -118,80 +126,131 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
   if (slot < a.nq + a.nkv) {
     const bool is_q = slot < a.nq;
     const int h = is_q ? slot : slot - a.nq;
-    const bf16_t* nw = is_q ? a.q_norm : a.k_norm;
-    const float w0 = a.qk_norm ? bf2f(nw[lane]) : 1.f;
-    const float w1 = a.qk_norm ? bf2f(nw[lane + half]) : 1.f;
-    for (int j = wave; j < kRopeTile; j += 4) {
-      const int s = s0 + j;
+    const int j = lane & 15, sub = lane >> 4;  // 4 token rows per wave step
+    const int d0 = 8 * j;                       // first dim of this lane
+    const int i0 = d0 & (half - 1);             // its RoPE frequency index
+    const float sgn = d0 < half ? -1.f : 1.f;   // y = x c + sgn * partner * s
+    float w[8];
+    if (a.qk_norm) {
+      unpack8(ld16((is_q ? a.q_norm : a.k_norm) + d0), w);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = 1.f;
+    }
+    for (int r = wave * 4 + sub; r < kRopeTile; r += 16) {
+      const int s = s0 + r;
       if (s >= a.S) break;
       const int64_t t = (int64_t)b * a.S + s;
       const int pos = a.pos ? a.pos[b] : a.pos0 + s;
       const bool ok = pos >= 0 && pos < a.cap && pos < a.max_pos;
-      const float* src = a.qkv + t * row_elems + slot * HD;
-      float x0 = src[lane], x1 = src[lane + half];
+      float x[8];
+      unpack8_f16(ld16(a.qkv + t * row_elems + slot * HD + d0), x);
       if (a.qk_norm) {
-        float ss = warp_sum(x0 * x0 + x1 * x1);
-        float inv = rsqrtf(ss / (float)HD + a.eps);
-        x0 = x0 * inv * w0;
-        x1 = x1 * inv * w1;
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+        ss += ror16<8>(ss);
+        ss += ror16<4>(ss);
+        ss += ror16<2>(ss);
+        ss += ror16<1>(ss);
+        const float inv = rsqrtf(ss / (float)HD + a.eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = x[e] * inv * w[e];
       }
-      float c = 0.f, sn = 0.f;
+      float c[8], sn[8];
       if (ok) {
-        c = a.rope[(int64_t)pos * half + lane];
-        sn = a.rope[(int64_t)a.max_pos * half + (int64_t)pos * half + lane];
+        const float* cp = a.rope + (int64_t)pos * half + i0;
+        const float* sp = a.rope + ((int64_t)a.max_pos + pos) * half + i0;
+        const f32x4_t c0 = *(const f32x4_t*)cp, c1 = *(const f32x4_t*)(cp + 4);
+        const f32x4_t s0v = *(const f32x4_t*)sp, s1v = *(const f32x4_t*)(sp + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          c[e] = c0[e]; c[e + 4] = c1[e];
+          sn[e] = s0v[e]; sn[e + 4] = s1v[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c[e] = sn[e] = 0.f;
       }
-      float y0 = x0 * c - x1 * sn;
-      float y1 = x0 * sn + x1 * c;
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = x[e] * c[e] + sgn * ror16<8>(x[e]) * sn[e];
       if (is_q) {
         // q carries the softmax scale log2(e) / sqrt(hd) for the attention kernels
         const float qs = 0.08838834764831845f * kLog2e;
-        y0 *= qs;
-        y1 *= qs;
-        if (!ok) y0 = y1 = __int_as_float(0x7FC00000);
-        f16_t* dst = a.q_out + (t * a.nq + h) * HD;
-        dst[lane] = f2h(y0);
-        dst[lane + half] = f2h(y1);
+        u32x4_t o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = ok ? pack_f16x2(y[2 * e] * qs, y[2 * e + 1] * qs) : 0x7E007E00u;
+        st16(a.q_out + (t * a.nq + h) * HD + d0, o);
       } else if (ok) {
-        bf16_t* dst = a.k_cache + (((int64_t)b * a.nkv + h) * a.cap + pos) * HD;
-        dst[lane] = f2bf(y0);
-        dst[lane + half] = f2bf(y1);
-        if (a.k_fresh) {
-          f16_t* kf = a.k_fresh +
-                      (((int64_t)b * a.nkv + h) * a.fresh_w + (pos - a.fresh_base)) * HD;
-          kf[lane] = f2h(y0);
-          kf[lane + half] = f2h(y1);
+        u32x4_t kb, kh;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kb[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
+          kh[e] = pack_f16x2(y[2 * e], y[2 * e + 1]);
         }
+        st16(a.k_cache + (((int64_t)b * a.nkv + h) * a.cap + pos) * HD + d0, kb);
+        if (a.k_fresh)
+          st16(a.k_fresh + (((int64_t)b * a.nkv + h) * a.fresh_w + (pos - a.fresh_base)) * HD + d0,
+               kh);
       }
     }
     return;
   }
 
-  // value head: stage [64 tokens][128] in LDS, write 64 consecutive positions per d row
+  // value head: stage [64 tokens][128] in LDS (fp32, padded rows), then write V^T rows of
+  // 8 consecutive positions per lane (16-byte stores)
   __shared__ float sv[kRopeTile][HD + 1];
   const int h = slot - a.nq - a.nkv;
-  for (int i = threadIdx.x; i < kRopeTile * (HD / 2); i += 256) {
-    int j = i / (HD / 2), d2 = (i % (HD / 2)) * 2;
-    int s = s0 + j;
-    float v0 = 0.f, v1 = 0.f;
+  for (int i = tid; i < kRopeTile * (HD / 8); i += 256) {
+    const int r = i / (HD / 8), d = (i % (HD / 8)) * 8;
+    const int s = s0 + r;
+    float v[8];
     if (s < a.S) {
-      const int64_t t = (int64_t)b * a.S + s;
-      const float* src = a.qkv + t * row_elems + slot * HD + d2;
-      v0 = src[0];
-      v1 = src[1];
+      unpack8_f16(ld16(a.qkv + ((int64_t)b * a.S + s) * row_elems + slot * HD + d), v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
     }
-    sv[j][d2] = v0;
-    sv[j][d2 + 1] = v1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sv[r][d + e] = v[e];
   }
   __syncthreads();
-  const int s = s0 + lane;
-  if (s < a.S) {
-    const int pos = a.pos ? a.pos[b] : a.pos0 + s;
-    if (pos >= 0 && pos < a.cap && pos < a.max_pos) {
-      bf16_t* base = a.vt_cache + ((int64_t)b * a.nkv + h) * HD * a.cap + pos;
-      for (int d = wave; d < HD; d += 4) base[(int64_t)d * a.cap] = f2bf(sv[lane][d]);
-      if (a.vt_fresh) {
-        f16_t* fb = a.vt_fresh + ((int64_t)b * a.nkv + h) * HD * a.fresh_w + (pos - a.fresh_base);
-        for (int d = wave; d < HD; d += 4) fb[(int64_t)d * a.fresh_w] = f2h(sv[lane][d]);
+  if (a.pos) {
+    // decode: one token per sequence, each at its own position
+    for (int d = tid; d < HD; d += 256) {
+      if (a.S < 1) break;
+      const int pos = a.pos[b];
+      if (pos < 0 || pos >= a.cap || pos >= a.max_pos) break;
+      a.vt_cache[(((int64_t)b * a.nkv + h) * HD + d) * a.cap + pos] = f2bf(sv[0][d]);
+    }
+    return;
+  }
+  // prefill: positions pos0 + s0 .. contiguous
+  for (int i = tid; i < HD * (kRopeTile / 8); i += 256) {
+    const int d = i / (kRopeTile / 8), r0 = (i % (kRopeTile / 8)) * 8;
+    const int s = s0 + r0;
+    if (s >= a.S) continue;
+    const int pos = a.pos0 + s;
+    const int n = min(8, a.S - s);  // valid tokens in this group
+    bf16_t* vb = a.vt_cache + (((int64_t)b * a.nkv + h) * HD + d) * a.cap + pos;
+    f16_t* vf = a.vt_fresh ? a.vt_fresh + (((int64_t)b * a.nkv + h) * HD + d) * a.fresh_w +
+                                 (pos - a.fresh_base)
+                           : nullptr;
+    if (n == 8 && (pos & 7) == 0 && (!vf || ((pos - a.fresh_base) & 7) == 0)) {
+      u32x4_t ob, oh;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ob[e] = pack_bf16x2(sv[r0 + 2 * e][d], sv[r0 + 2 * e + 1][d]);
+        oh[e] = pack_f16x2(sv[r0 + 2 * e][d], sv[r0 + 2 * e + 1][d]);
+      }
+      st16(vb, ob);
+      if (vf) st16(vf, oh);
+    } else {
+      for (int e = 0; e < n; ++e) {
+        vb[e] = f2bf(sv[r0 + e][d]);
+        if (vf) vf[e] = f2h(sv[r0 + e][d]);
       }
     }
   }

@@ -90,7 +90,7 @@ size_t max_gemm_partial(const qwen3_config* c, int T) {
   const int H = c->hidden_size, nq = c->num_attention_heads, nkv = c->num_key_value_heads,
             hd = c->head_dim, I = c->intermediate_size;
   size_t m = 0;
-  m = std::max(m, gemm_plan(T, (nq + 2 * nkv) * hd, H, gemm::B_QKV, gemm::E_F32, false).partial_bytes);
+  m = std::max(m, gemm_plan(T, (nq + 2 * nkv) * hd, H, gemm::B_QKV, gemm::E_F16, false).partial_bytes);
   m = std::max(m, gemm_plan(T, H, nq * hd, gemm::B_DENSE, gemm::E_RES_F32, false).partial_bytes);
   m = std::max(m, gemm_plan(T, 2 * I, H, gemm::B_SWIGLU, gemm::E_SWIGLU, false).partial_bytes);
   m = std::max(m, gemm_plan(T, H, I, gemm::B_DENSE, gemm::E_RES_F32, false).partial_bytes);
@@ -108,7 +108,7 @@ DenseLayout dense_layout(const qwen3_config* c, int op, int B, int S, int cap_hi
   L.T = T;
   Bump b;
   L.xn = b.take((size_t)T * H * 2);
-  L.qkv = b.take((size_t)T * (nq + 2 * nkv) * hd * 4);
+  L.qkv = b.take((size_t)T * (nq + 2 * nkv) * hd * 2);
   L.q = b.take((size_t)T * nq * hd * 2);
   L.attn = b.take((size_t)T * nq * hd * 2);
   L.act = b.take((size_t)T * I * 2);
@@ -255,7 +255,7 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
             hd = c->head_dim, I = c->intermediate_size, T = io.T;
   // transient activations feeding the matrix cores are fp16
   f16_t* xn = (f16_t*)(ws + L.xn);
-  float* qkv = (float*)(ws + L.qkv);
+  f16_t* qkv = (f16_t*)(ws + L.qkv);
   f16_t* q = (f16_t*)(ws + L.q);
   f16_t* attn = (f16_t*)(ws + L.attn);
   f16_t* act = (f16_t*)(ws + L.act);
@@ -269,8 +269,8 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
   else
     CHECK_HIP(rmsnorm_bf16(io.x_bf16, 1, 0, (const bf16_t*)w->input_layernorm, xn, T, H, eps, s));
 
-  // QKV projection (q, k, v weights stacked along N without a copy), fp32 out so the
-  // q/k RMSNorm sees unrounded projections
+  // QKV projection (q, k, v weights stacked along N without a copy), fp16 out: one
+  // rounding 4x finer than the bf16 cache that the keys end in
   {
     Args a{};
     a.M = T; a.N = (nq + 2 * nkv) * hd; a.K = H;
@@ -279,9 +279,9 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
     a.B2 = (const bf16_t*)w->v_proj; a.ldb = H;
     a.seg1 = nq * hd; a.seg2 = (nq + nkv) * hd;
     a.C = qkv; a.ldc = a.N;
-    GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_QKV, gemm::E_F32, false);
+    GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_QKV, gemm::E_F16, false);
     ProfScope ps("qkv_gemm", s);
-    CHECK_HIP(gemm_run(a, true, gemm::B_QKV, gemm::E_F32, false, p, part, s));
+    CHECK_HIP(gemm_run(a, true, gemm::B_QKV, gemm::E_F16, false, p, part, s));
   }
   // q/k RMSNorm + RoPE, K/V into the cache
   {
