@@ -2,12 +2,14 @@
 // ([P3] "MoE": fp32 router softmax, top-k, renormalisation, hit experts only,
 // weighted index_add back to the token rows).
 //
-// Dispatch order: experts ascending, tokens ascending within an expert.  It is built
-// without atomics (counting sort over fixed token chunks), so it is bit-reproducible:
-//   hist    per chunk, thread e counts the chunk's choices of expert e
+// Dispatch order: experts ascending, tokens ascending within an expert.  It is a counting
+// sort over fixed token chunks whose result does not depend on thread timing (the only
+// atomics are order-free bit sets), so it is bit-reproducible:
+//   hist    per chunk, per-expert token bitmasks in LDS; counts are popcounts
 //   scan    per expert: chunk bases, totals, offsets, and the m-tile table the grouped
 //           GEMM walks (tile -> expert, first row)
-//   scatter per chunk, thread e walks the chunk in token order and assigns rows
+//   scatter per chunk, one thread per token: its row for expert e is the expert's base
+//           plus the popcount of e's mask bits below the token
 #include <algorithm>
 
 #include "launch.h"
@@ -82,16 +84,34 @@ __global__ void __launch_bounds__(256) topk_kernel(MoeRouteArgs a) {
   }
 }
 
+// Per 256-token chunk: bit t of word w of expert e's mask says token 32 w + t of the chunk
+// selected e.  Counts are popcounts; the stable (token-ascending) rank of an entry among
+// its expert's entries in the chunk is the popcount of the bits below its token.
+constexpr int kMaskWords = kChunk / 32;
+
+DEV void build_masks(const MoeRouteArgs& a, int t0, int nt, uint32_t (*smask)[kMaskWords]) {
+  for (int i = threadIdx.x; i < a.E * kMaskWords; i += 256) smask[i / kMaskWords][i % kMaskWords] = 0u;
+  __syncthreads();
+  const int tl = threadIdx.x;
+  if (tl < nt) {
+    for (int j = 0; j < a.k; ++j) {
+      const int e = a.idx[(int64_t)(t0 + tl) * a.k + j];
+      if (e >= 0 && e < a.E) atomicOr(&smask[e][tl >> 5], 1u << (tl & 31));
+    }
+  }
+  __syncthreads();
+}
+
 __global__ void __launch_bounds__(256) hist_kernel(MoeRouteArgs a) {
-  __shared__ int sidx[kChunk * kMaxK];
+  __shared__ uint32_t smask[kMaxE][kMaskWords];
   const int c = blockIdx.x;
   const int t0 = c * kChunk, nt = min(kChunk, a.T - t0);
-  for (int i = threadIdx.x; i < nt * a.k; i += 256) sidx[i] = a.idx[(int64_t)t0 * a.k + i];
-  __syncthreads();
+  build_masks(a, t0, nt, smask);
   const int e = threadIdx.x;
   if (e >= a.E) return;
   int cnt = 0;
-  for (int i = 0; i < nt * a.k; ++i) cnt += sidx[i] == e;
+#pragma unroll
+  for (int w = 0; w < kMaskWords; ++w) cnt += __popc(smask[e][w]);
   a.chunk_counts[(int64_t)c * a.E + e] = cnt;
 }
 
@@ -140,21 +160,22 @@ __global__ void __launch_bounds__(256) scan_kernel(MoeRouteArgs a, int nchunks) 
 }
 
 __global__ void __launch_bounds__(256) scatter_kernel(MoeRouteArgs a) {
-  __shared__ int sidx[kChunk * kMaxK];
+  __shared__ uint32_t smask[kMaxE][kMaskWords];
   const int c = blockIdx.x;
   const int t0 = c * kChunk, nt = min(kChunk, a.T - t0);
-  for (int i = threadIdx.x; i < nt * a.k; i += 256) sidx[i] = a.idx[(int64_t)t0 * a.k + i];
-  __syncthreads();
-  const int e = threadIdx.x;
-  if (e >= a.E) return;
-  int row = a.offsets[e] + a.chunk_counts[(int64_t)c * a.E + e];
-  for (int i = 0; i < nt * a.k; ++i) {
-    if (sidx[i] == e) {
-      int t = t0 + i / a.k;
-      a.perm_token[row] = t;
-      a.inv_row[(int64_t)t0 * a.k + i] = row;
-      ++row;
-    }
+  build_masks(a, t0, nt, smask);
+  const int tl = threadIdx.x;
+  if (tl >= nt) return;
+  const int t = t0 + tl, w0 = tl >> 5;
+  const uint32_t below = (1u << (tl & 31)) - 1u;
+  for (int j = 0; j < a.k; ++j) {
+    const int e = a.idx[(int64_t)t * a.k + j];
+    if (e < 0 || e >= a.E) continue;
+    int rank = __popc(smask[e][w0] & below);
+    for (int w = 0; w < w0; ++w) rank += __popc(smask[e][w]);
+    const int row = a.offsets[e] + a.chunk_counts[(int64_t)c * a.E + e] + rank;
+    a.perm_token[row] = t;
+    a.inv_row[(int64_t)t * a.k + j] = row;
   }
 }
 
