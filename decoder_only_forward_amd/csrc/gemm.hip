@@ -9,7 +9,7 @@ namespace {
 using namespace gemm;
 
 using TBig = Tile<256, 256, 2, 4>;   // 8 waves (2 per SIMD), 128x64 per wave, 128 KB LDS
-using TMid = Tile<128, 128, 2, 2>;   // 4 waves, 64x64 per wave, 32 KB LDS
+using TMid = Tile<128, 128, 2, 2>;   // 4 waves, 64x64 per wave, 64 KB LDS
 using TSkin = Tile<64, 128, 2, 2>;   // 4 waves, 32x64 per wave: decode (M <= 64)
 
 template <class T>
@@ -19,68 +19,136 @@ int tiles_n(int N, int bmode) {
   return (N + T::BN - 1) / T::BN;
 }
 
-template <class T, bool F16, int BMODE, int EPI, bool G, bool SK>
-hipError_t launch_t(Args a, int splits, hipStream_t s) {
+template <class T, bool F16, int BMODE, int EPI, bool G>
+hipError_t launch_t(Args a, hipStream_t s) {
   if (!G) a.m_tiles = tiles_m<T>(a.M);
   a.n_tiles = tiles_n<T>(a.N, BMODE);
-  a.k_splits = splits;
-  dim3 grid(a.m_tiles * a.n_tiles, SK ? splits : 1);
-  hipLaunchKernelGGL((gemm_kernel<T, F16, BMODE, EPI, G, SK>), grid, dim3(T::THREADS), 0, s, a);
+  dim3 grid(a.m_tiles * a.n_tiles);
+  hipLaunchKernelGGL((gemm_kernel<T, F16, BMODE, EPI, G>), grid, dim3(T::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
-// Sum the split-K partials and apply the epilogue.
-__global__ void __launch_bounds__(256)
-splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N, int epi,
-                     void* C, int64_t ldc, const void* R, int64_t ldr, int BN, int WN) {
-  const int ncols = epi == E_SWIGLU ? N / 2 : N;
-  const int64_t total = (int64_t)M * ncols;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    int m = (int)(i / ncols), c = (int)(i % ncols);
-    if (epi == E_SWIGLU) {
-      int half = WN / 2;
-      int vg = (c / (BN / 2)) * BN + ((c % (BN / 2)) / half) * WN + (c % half);
-      int vu = vg + half;
-      float g = 0.f, u = 0.f;
-      for (int z = 0; z < splits; ++z) {
-        g += part[((int64_t)z * M + m) * N + vg];
-        u += part[((int64_t)z * M + m) * N + vu];
-      }
-      ((f16_t*)C)[m * ldc + c] = f2h(silu(g) * u);
-      continue;
-    }
-    float v = 0.f;
-    for (int z = 0; z < splits; ++z) v += part[((int64_t)z * M + m) * N + c];
-    switch (epi) {
-      case E_F32: ((float*)C)[m * ldc + c] = v; break;
-      case E_F16: ((f16_t*)C)[m * ldc + c] = f2h(v); break;
-      case E_RES_F32: ((float*)C)[m * ldc + c] = ((const float*)R)[m * ldr + c] + v; break;
-      case E_RESB_F32:
-        ((float*)C)[m * ldc + c] = bf2f(((const bf16_t*)R)[m * ldr + c]) + v;
-        break;
-      case E_RESF_B16:
-        ((bf16_t*)C)[m * ldc + c] = f2bf(((const float*)R)[m * ldr + c] + v);
-        break;
-      default: break;
+// Decode-size products (M <= 64 rows): one block per 16 output columns (SwiGLU: 16 gate
+// columns and the matching 16 up columns) over all rows, the K range split across the
+// block's 8 waves.  Each wave streams its slice of the weights straight from memory into
+// 16x16x32 fp16 MFMAs (every weight is read once; bf16 -> fp16 is exact in fp16's normal
+// range); the activations come through L2.  The waves' partial sums are added in LDS in a
+// fixed order and the epilogue applied once: no partial sums in memory, one launch.
+// MFMA layouts (lane l, r = l % 16, g = l / 16): A row r, B column r, k = 8 g .. 8 g + 7;
+// the accumulator holds column r, rows 4 g .. 4 g + 3.
+constexpr int kDecWaves = 8;
+constexpr int kDecBatch = 4;  // k-steps of 32 loaded per batch
+
+DEV f32x4_t mfma16h(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a), as_f16x8(b), c, 0, 0, 0);
+}
+
+template <int BMODE, int EPI>
+__global__ void __launch_bounds__(64 * kDecWaves) decode_gemm_kernel(Args p) {
+  constexpr int NT = BMODE == B_SWIGLU ? 2 : 1;
+  __shared__ float red[kDecWaves][4][NT][256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, grp = lane >> 4;
+  const int c0 = blockIdx.x * 16;
+  const int ncols = BMODE == B_SWIGLU ? p.N / 2 : p.N;
+
+  const bf16_t* bp[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int col = min(c0 + r16, ncols - 1);
+    if (BMODE == B_SWIGLU) {
+      bp[nt] = (nt == 0 ? p.B0 : p.B1) + (int64_t)col * p.ldb;
+    } else if (BMODE == B_QKV) {
+      bp[nt] = col < p.seg1 ? p.B0 + (int64_t)col * p.ldb
+             : col < p.seg2 ? p.B1 + (int64_t)(col - p.seg1) * p.ldb
+                            : p.B2 + (int64_t)(col - p.seg2) * p.ldb;
+    } else {
+      bp[nt] = p.B0 + (int64_t)col * p.ldb;
     }
   }
+  const uint16_t* ap[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) ap[mt] = p.A + (int64_t)min(mt * 16 + r16, p.M - 1) * p.lda;
+
+  const int nks = p.K / 32;
+  const int per = (nks + kDecWaves - 1) / kDecWaves;
+  const int ks0 = min(nks, wave * per), ks1 = min(nks, ks0 + per);
+  f32x4_t acc[4][NT];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int kb = ks0; kb < ks1; kb += kDecBatch) {
+    u32x4_t fa[kDecBatch][4], fb[kDecBatch][NT];
+#pragma unroll
+    for (int u = 0; u < kDecBatch; ++u) {
+      if (kb + u < ks1) {
+        const int ko = (kb + u) * 32 + grp * 8;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) fb[u][nt] = ld16(bp[nt] + ko);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) fa[u][mt] = ld16(ap[mt] + ko);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kDecBatch; ++u) {
+      if (kb + u < ks1) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const u32x4_t b = bf16x8_to_f16x8(fb[u][nt]);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mfma16h(fa[u][mt], b, acc[mt][nt]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      *(f32x4_t*)&red[wave][mt][nt][lane * 4] = acc[mt][nt];
+  __syncthreads();
+  for (int o = tid; o < 64 * 16; o += 64 * kDecWaves) {
+    const int m = o >> 4, n = o & 15;
+    if (m >= p.M) continue;
+    const int col = c0 + n;
+    if (col >= ncols) continue;
+    const int mt = m >> 4, rr = m & 15;
+    const int slot = (n + 16 * (rr >> 2)) * 4 + (rr & 3);
+    float v[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) sum += red[w][mt][nt][slot];
+      v[nt] = sum;
+    }
+    const int64_t ci = (int64_t)m * p.ldc + col, ri = (int64_t)m * p.ldr + col;
+    if (EPI == E_SWIGLU) ((f16_t*)p.C)[ci] = f2h(silu(v[0]) * v[NT - 1]);
+    else if (EPI == E_F16) ((f16_t*)p.C)[ci] = f2h(v[0]);
+    else if (EPI == E_RES_F32) ((float*)p.C)[ci] = ((const float*)p.R)[ri] + v[0];
+    else if (EPI == E_RESB_F32) ((float*)p.C)[ci] = bf2f(((const bf16_t*)p.R)[ri]) + v[0];
+    else if (EPI == E_RESF_B16) ((bf16_t*)p.C)[ci] = f2bf(((const float*)p.R)[ri] + v[0]);
+  }
+}
+
+template <int BMODE, int EPI>
+hipError_t launch_decode(const Args& a, hipStream_t s) {
+  const int ncols = BMODE == B_SWIGLU ? a.N / 2 : a.N;
+  hipLaunchKernelGGL((decode_gemm_kernel<BMODE, EPI>), dim3((ncols + 15) / 16),
+                     dim3(64 * kDecWaves), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 GemmPlan gemm_plan(int M, int N, int K, int bmode, int epi, bool grouped) {
-  GemmPlan p{kMid, 1, 0};
+  GemmPlan p{kMid};
   if (grouped) return p;
-  const int nk = K / 64;
   if (M <= 64) {
-    p.tile = kSkinny;
-    int tiles = (N + TSkin::BN - 1) / TSkin::BN;
-    if (epi == E_F32 && tiles >= 512) return p;  // wide output (LM head): no split
-    int splits = (512 + tiles - 1) / tiles;
-    splits = std::min(splits, std::max(1, nk / 2));
-    p.k_splits = std::max(1, splits);
-    p.partial_bytes = (size_t)p.k_splits * M * N * sizeof(float);
+    // fp32 outputs (LM head, router) keep the 64x128 tile: its k order is that of the
+    // larger tiles, so last-position logits equal the corresponding rows of a full pass
+    p.tile = epi == E_F32 ? kSkinny : kDecode;
     return p;
   }
   int big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
@@ -89,31 +157,21 @@ GemmPlan gemm_plan(int M, int N, int K, int bmode, int epi, bool grouped) {
 }
 
 #define GEMM_CASE(TT, TCFG, F16, BM, EP, G)                                          \
-  if (plan.tile == TT && f16 == F16 && bmode == BM && epi == EP && grouped == G)        \
-    return launch_t<TCFG, F16, BM, EP, G, false>(a, plan.k_splits, s);
+  if (pl.tile == TT && f16 == F16 && bmode == BM && epi == EP && grouped == G)          \
+    return launch_t<TCFG, F16, BM, EP, G>(a, s);
 
 hipError_t gemm_run(const Args& a_in, bool f16, int bmode, int epi, bool grouped,
-                    const GemmPlan& plan, float* partial, hipStream_t s) {
+                    const GemmPlan& plan, hipStream_t s) {
   Args a = a_in;
-  if (plan.tile == kSkinny && !(epi == E_F32 && plan.k_splits == 1)) {
-    // split-K: fp32 partial sums, then one reduce + epilogue pass
-    if (grouped || partial == nullptr || !f16) return hipErrorInvalidValue;
-    a.partial = partial;
-    hipError_t e;
-    if (bmode == B_QKV)
-      e = launch_t<TSkin, true, B_QKV, E_PARTIAL, false, true>(a, plan.k_splits, s);
-    else if (bmode == B_SWIGLU)
-      e = launch_t<TSkin, true, B_SWIGLU, E_PARTIAL, false, true>(a, plan.k_splits, s);
-    else
-      e = launch_t<TSkin, true, B_DENSE, E_PARTIAL, false, true>(a, plan.k_splits, s);
-    if (e != hipSuccess) return e;
-    const int ncols = epi == E_SWIGLU ? a.N / 2 : a.N;
-    const int64_t total = (int64_t)a.M * ncols;
-    const int blocks = (int)std::min<int64_t>(4096, (total + 255) / 256);
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, partial,
-                       plan.k_splits, a.M, a.N, epi, a.C, a.ldc, a.R, a.ldr, TSkin::BN,
-                       TSkin::WN);
-    return hipGetLastError();
+  const GemmPlan& pl = plan;
+  if (pl.tile == kDecode) {
+    if (grouped || !f16 || a.M > 64) return hipErrorInvalidValue;
+    if (bmode == B_QKV && epi == E_F16) return launch_decode<B_QKV, E_F16>(a, s);
+    if (bmode == B_SWIGLU && epi == E_SWIGLU) return launch_decode<B_SWIGLU, E_SWIGLU>(a, s);
+    if (bmode == B_DENSE && epi == E_RES_F32) return launch_decode<B_DENSE, E_RES_F32>(a, s);
+    if (bmode == B_DENSE && epi == E_RESB_F32) return launch_decode<B_DENSE, E_RESB_F32>(a, s);
+    if (bmode == B_DENSE && epi == E_RESF_B16) return launch_decode<B_DENSE, E_RESF_B16>(a, s);
+    return hipErrorInvalidValue;
   }
   // dense layers: fp16 activations x bf16->fp16 weights
   GEMM_CASE(kBig, TBig, true, B_QKV, E_F16, false)

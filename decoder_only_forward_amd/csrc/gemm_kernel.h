@@ -21,7 +21,6 @@
 //   E_RESB_F32  out_f32 = float(res_bf16) + acc          (o_proj in the block API)
 //   E_RESF_B16  out_bf16 = bf16(res_f32 + acc)           (down in the block API)
 //   E_SWIGLU    out_f16[:, c] = f16(silu(g) * u)         (gate|up with SwiGLU)
-//   E_PARTIAL   fp32 partial sums of one K split         (skinny decode GEMMs)
 // B row sources:
 //   B_DENSE   one matrix;  B_QKV  q/k/v weights stacked along N without a copy;
 //   B_SWIGLU  gate and up rows interleaved per wave so that a lane holds the gate and
@@ -35,7 +34,7 @@
 namespace gemm {
 
 enum BMode { B_DENSE = 0, B_QKV = 1, B_SWIGLU = 2 };
-enum EpiMode { E_F32 = 1, E_RES_F32, E_RESB_F32, E_RESF_B16, E_SWIGLU, E_PARTIAL, E_F16 };
+enum EpiMode { E_F32 = 1, E_RES_F32, E_RESB_F32, E_RESF_B16, E_SWIGLU, E_F16 };
 
 struct Args {
   int M, N, K;  // N counts virtual columns (gate|up: 2 * I)
@@ -51,8 +50,6 @@ struct Args {
   int64_t ldc;
   const void* R;  // residual input
   int64_t ldr;
-  float* partial;  // E_PARTIAL: [k_splits][M][N]
-  int k_splits;
   int m_tiles, n_tiles;
   // grouped mode
   const int32_t* g_offsets;      // [E + 1] first output row of each expert
@@ -117,7 +114,7 @@ DEV void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | 0x0F70);
 }
 
-template <class T, bool F16, int BMODE, int EPI, bool GROUPED, bool SPLITK>
+template <class T, bool F16, int BMODE, int EPI, bool GROUPED>
 __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
   __shared__ __attribute__((aligned(16))) bf16_t sA[T::STAGES][T::BM * T::BK];
   __shared__ __attribute__((aligned(16))) bf16_t sB[T::STAGES][T::BN * T::BK];
@@ -150,15 +147,7 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
   }
   const int n0 = tn * T::BN;
 
-  // K range of this block (split-K over gridDim.y)
-  const int nk_total = p.K / T::BK;
-  int kt0 = 0, kt1 = nk_total;
-  if (SPLITK) {
-    int per = (nk_total + p.k_splits - 1) / p.k_splits;
-    kt0 = blockIdx.y * per;
-    kt1 = min(nk_total, kt0 + per);
-  }
-  const int nk = kt1 - kt0;
+  const int kt0 = 0, nk = p.K / T::BK;
 
   // ---- operand tiles go global -> LDS directly (lds_dma16): lane L of a
   // wave instruction lands at 16 L bytes past that instruction's 1 KB LDS slot, i.e. at
@@ -348,9 +337,7 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
       if (lr >= rows_valid) continue;
       const int64_t row = out_row0 + lr;
       const float v = acc[i][j][r];
-      if (EPI == E_PARTIAL) {
-        p.partial[((int64_t)blockIdx.y * p.M + row) * p.N + col] = v;
-      } else if (EPI == E_F32) {
+      if (EPI == E_F32) {
         ((float*)p.C)[row * p.ldc + col] = v;
       } else if (EPI == E_F16) {
         ((f16_t*)p.C)[row * p.ldc + col] = f2h(v);

@@ -11,24 +11,22 @@ namespace q3 {
 
 // ---- GEMM (gemm.hip)
 // Tile families; kAuto picks by problem size.
-enum GemmTile { kAuto = 0, kBig = 1, kMid = 2, kSkinny = 3 };
+enum GemmTile { kAuto = 0, kBig = 1, kMid = 2, kSkinny = 3, kDecode = 4 };
 
 struct GemmPlan {
-  int tile;      // GemmTile actually used
-  int k_splits;  // > 1: split-K with fp32 partials + reduce kernel
-  size_t partial_bytes;
+  int tile;  // GemmTile actually used
 };
 
-// Chooses tile family and split count for an (M, N, K) problem; partial_bytes is the
-// split-K scratch it needs (0 without split-K).
+// Chooses the tile family for an (M, N, K) problem: for M <= 64 the decode kernel (the
+// 64x128 tile for fp32 outputs), else 256x256 when that gives >= 512 tiles, else
+// 128x128 (grouped problems always 128x128).
 GemmPlan gemm_plan(int M, int N, int K, int bmode, int epi, bool grouped);
 
-// Runs C = A . B^T with the given B source and epilogue.  `partial` must hold
-// plan.partial_bytes when plan.k_splits > 1.
+// Runs C = A . B^T with the given B source and epilogue.
 // f16: A holds fp16 activations and the bf16 weights are converted to fp16 (otherwise
 // both operands are bf16).
 hipError_t gemm_run(const gemm::Args& a, bool f16, int bmode, int epi, bool grouped,
-                    const GemmPlan& plan, float* partial, hipStream_t s);
+                    const GemmPlan& plan, hipStream_t s);
 
 // ---- norms, embedding, RoPE (norm_rope.hip)
 // out[r] = f16(rmsnorm(in[r_in])) with r_in = r * in_row_stride + in_row_offset.

@@ -78,7 +78,7 @@ struct Bump {
 };
 
 struct DenseLayout {
-  size_t xn, qkv, q, attn, h1, act, res, hf, part_attn, part_gemm, am_val, am_idx, lg_scratch;
+  size_t xn, qkv, q, attn, h1, act, res, hf, part_attn, am_val, am_idx, lg_scratch;
   size_t kf, vtf;  // prefill: fp16 copies of the new keys / values
   size_t total;
   int T, rows_out, attn_splits, attn_chunk, am_chunks, fresh_w_max;
@@ -86,16 +86,6 @@ struct DenseLayout {
 
 constexpr int kArgmaxChunks = 64;
 
-size_t max_gemm_partial(const qwen3_config* c, int T) {
-  const int H = c->hidden_size, nq = c->num_attention_heads, nkv = c->num_key_value_heads,
-            hd = c->head_dim, I = c->intermediate_size;
-  size_t m = 0;
-  m = std::max(m, gemm_plan(T, (nq + 2 * nkv) * hd, H, gemm::B_QKV, gemm::E_F16, false).partial_bytes);
-  m = std::max(m, gemm_plan(T, H, nq * hd, gemm::B_DENSE, gemm::E_RES_F32, false).partial_bytes);
-  m = std::max(m, gemm_plan(T, 2 * I, H, gemm::B_SWIGLU, gemm::E_SWIGLU, false).partial_bytes);
-  m = std::max(m, gemm_plan(T, H, I, gemm::B_DENSE, gemm::E_RES_F32, false).partial_bytes);
-  return m;
-}
 
 // op: block prefill / decode (bf16 block I/O) or stack prefill / decode
 DenseLayout dense_layout(const qwen3_config* c, int op, int B, int S, int cap_hint) {
@@ -114,7 +104,6 @@ DenseLayout dense_layout(const qwen3_config* c, int op, int B, int S, int cap_hi
   L.act = b.take((size_t)T * I * 2);
   L.h1 = stack ? 0 : b.take((size_t)T * H * 4);
   L.res = stack ? b.take((size_t)T * H * 4) : 0;
-  L.part_gemm = b.take(max_gemm_partial(c, T));
   if (!decode) {
     L.fresh_w_max = ((S + 63 + 63) / 64) * 64;
     L.kf = b.take((size_t)B * nkv * L.fresh_w_max * hd * 2);
@@ -259,7 +248,6 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
   f16_t* q = (f16_t*)(ws + L.q);
   f16_t* attn = (f16_t*)(ws + L.attn);
   f16_t* act = (f16_t*)(ws + L.act);
-  float* part = (float*)(ws + L.part_gemm);
   float* h1 = io.res ? io.res : (float*)(ws + L.h1);
   const float eps = c->rms_norm_eps;
 
@@ -281,7 +269,7 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
     a.C = qkv; a.ldc = a.N;
     GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_QKV, gemm::E_F16, false);
     ProfScope ps("qkv_gemm", s);
-    CHECK_HIP(gemm_run(a, true, gemm::B_QKV, gemm::E_F16, false, p, part, s));
+    CHECK_HIP(gemm_run(a, true, gemm::B_QKV, gemm::E_F16, false, p, s));
   }
   // q/k RMSNorm + RoPE, K/V into the cache
   {
@@ -338,7 +326,7 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
     a.R = io.res ? (const void*)io.res : (const void*)io.x_bf16; a.ldr = H;
     GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_DENSE, epi, false);
     ProfScope ps("o_proj_gemm", s);
-    CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, epi, false, p, part, s));
+    CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, epi, false, p, s));
   }
   // post-attention RMSNorm
   CHECK_HIP(rmsnorm_f32(h1, 1, 0, (const bf16_t*)w->post_attention_layernorm, xn, T, H, eps, s));
@@ -351,7 +339,7 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
     a.C = act; a.ldc = I;
     GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_SWIGLU, gemm::E_SWIGLU, false);
     ProfScope ps("gate_up_gemm", s);
-    CHECK_HIP(gemm_run(a, true, gemm::B_SWIGLU, gemm::E_SWIGLU, false, p, part, s));
+    CHECK_HIP(gemm_run(a, true, gemm::B_SWIGLU, gemm::E_SWIGLU, false, p, s));
   }
   // down + residual
   {
@@ -371,7 +359,7 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
     a.ldc = H;
     GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_DENSE, epi, false);
     ProfScope ps("down_gemm", s);
-    CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, epi, false, p, part, s));
+    CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, epi, false, p, s));
   }
   return QWEN3_OK;
 }
@@ -592,9 +580,8 @@ int qwen3_stack_forward(const qwen3_config* c, const qwen3_model_weights* w, con
     a.B0 = head; a.ldb = H;
     a.C = out; a.ldc = V;
     GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_DENSE, gemm::E_F32, false);
-    if (p.partial_bytes > 0) p = GemmPlan{kSkinny, 1, 0};
     ProfScope ps("lm_head_gemm", s);
-    CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, gemm::E_F32, false, p, nullptr, s));
+    CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, gemm::E_F32, false, p, s));
   }
   if (next_ids) {
     const float* last = out;
@@ -658,9 +645,8 @@ int qwen3_moe_ffn(const qwen3_config* c, const qwen3_moe_weights* w, const void*
     a.B0 = (const bf16_t*)w->router; a.ldb = H;
     a.C = lg; a.ldc = E;
     GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_DENSE, gemm::E_F32, false);
-    if (p.partial_bytes > 0) p = GemmPlan{kSkinny, 1, 0};
     ProfScope ps("moe_router_gemm", s);
-    CHECK_HIP(gemm_run(a, false, gemm::B_DENSE, gemm::E_F32, false, p, nullptr, s));
+    CHECK_HIP(gemm_run(a, false, gemm::B_DENSE, gemm::E_F32, false, p, s));
   }
   // top-k, weights, dispatch order, tile table
   {
@@ -687,9 +673,9 @@ int qwen3_moe_ffn(const qwen3_config* c, const qwen3_moe_weights* w, const void*
     a.g_b_stride = (int64_t)2 * I * H;
     a.m_tiles = L.max_tiles;
     a.C = act; a.ldc = I;
-    GemmPlan p{kMid, 1, 0};
+    GemmPlan p{kMid};
     ProfScope ps("moe_gate_up_gemm", s);
-    CHECK_HIP(gemm_run(a, false, gemm::B_SWIGLU, gemm::E_SWIGLU, true, p, nullptr, s));
+    CHECK_HIP(gemm_run(a, false, gemm::B_SWIGLU, gemm::E_SWIGLU, true, p, s));
   }
   // grouped down -> per-row fp32 outputs in dispatch order
   {
@@ -701,9 +687,9 @@ int qwen3_moe_ffn(const qwen3_config* c, const qwen3_moe_weights* w, const void*
     a.g_b_stride = (int64_t)H * I;
     a.m_tiles = L.max_tiles;
     a.C = yrows; a.ldc = H;
-    GemmPlan p{kMid, 1, 0};
+    GemmPlan p{kMid};
     ProfScope ps("moe_down_gemm", s);
-    CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, gemm::E_F32, true, p, nullptr, s));
+    CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, gemm::E_F32, true, p, s));
   }
   {
     ProfScope ps("moe_combine", s);
