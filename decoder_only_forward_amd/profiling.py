@@ -40,14 +40,14 @@ KERNELS = {
     "moe_down_gemm": ("gemm_kernel<", _GEMM),
 }
 
-# Template signatures that single out one GEMM use (fp16 A, B mode, epilogue, grouped,
-# split-K).  o_proj and down share one instantiation and are not told apart here.
+# Template signatures that single out one GEMM use (fp16 A, B mode, epilogue, grouped).
+# o_proj and down share one instantiation and are not told apart here.
 GEMM_SIGNATURE = {
-    "qkv_gemm": "true, 1, 7, false, false>",
-    "gate_up_gemm": "true, 2, 5, false, false>",
-    "lm_head_gemm": "true, 0, 1, false, false>",
-    "moe_gate_up_gemm": ", 2, 5, true, false>",
-    "moe_down_gemm": ", 0, 1, true, false>",
+    "qkv_gemm": "true, 1, 6, false>",
+    "gate_up_gemm": "true, 2, 5, false>",
+    "lm_head_gemm": "true, 0, 1, false>",
+    "moe_gate_up_gemm": ", 2, 5, true>",
+    "moe_down_gemm": ", 0, 1, true>",
 }
 
 
