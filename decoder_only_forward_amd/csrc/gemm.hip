@@ -43,7 +43,10 @@ DEV f32x4_t mfma16h(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a), as_f16x8(b), c, 0, 0, 0);
 }
 
-template <int BMODE, int EPI>
+// With PART the K range is further split over gridDim.y blocks, each writing its fp32
+// partial sums to p.partial[blockIdx.y] for a separate reduction (used when N alone gives
+// too few blocks).
+template <int BMODE, int EPI, bool PART>
 __global__ void __launch_bounds__(64 * kDecWaves) decode_gemm_kernel(Args p) {
   constexpr int NT = BMODE == B_SWIGLU ? 2 : 1;
   __shared__ float red[kDecWaves][4][NT][256];
@@ -70,9 +73,12 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_gemm_kernel(Args p) {
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) ap[mt] = p.A + (int64_t)min(mt * 16 + r16, p.M - 1) * p.lda;
 
-  const int nks = p.K / 32;
+  const int nks_all = p.K / 32;
+  const int per_split = (nks_all + gridDim.y - 1) / gridDim.y;
+  const int kbase = min(nks_all, (int)blockIdx.y * per_split);
+  const int nks = min(nks_all, kbase + per_split) - kbase;
   const int per = (nks + kDecWaves - 1) / kDecWaves;
-  const int ks0 = min(nks, wave * per), ks1 = min(nks, ks0 + per);
+  const int ks0 = kbase + min(nks, wave * per), ks1 = kbase + min(nks, min(nks, wave * per) + per);
   f32x4_t acc[4][NT];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -123,6 +129,10 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_gemm_kernel(Args p) {
       for (int w = 0; w < kDecWaves; ++w) sum += red[w][mt][nt][slot];
       v[nt] = sum;
     }
+    if (PART) {
+      p.partial[((int64_t)blockIdx.y * p.M + m) * ncols + col] = v[0];
+      continue;
+    }
     const int64_t ci = (int64_t)m * p.ldc + col, ri = (int64_t)m * p.ldr + col;
     if (EPI == E_SWIGLU) ((f16_t*)p.C)[ci] = f2h(silu(v[0]) * v[NT - 1]);
     else if (EPI == E_F16) ((f16_t*)p.C)[ci] = f2h(v[0]);
@@ -133,22 +143,34 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_gemm_kernel(Args p) {
 }
 
 template <int BMODE, int EPI>
-hipError_t launch_decode(const Args& a, hipStream_t s) {
+hipError_t launch_decode(const Args& a, int splits, hipStream_t s) {
   const int ncols = BMODE == B_SWIGLU ? a.N / 2 : a.N;
-  hipLaunchKernelGGL((decode_gemm_kernel<BMODE, EPI>), dim3((ncols + 15) / 16),
-                     dim3(64 * kDecWaves), 0, s, a);
+  if (splits > 1)
+    hipLaunchKernelGGL((decode_gemm_kernel<BMODE, EPI, true>), dim3((ncols + 15) / 16, splits),
+                       dim3(64 * kDecWaves), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_gemm_kernel<BMODE, EPI, false>), dim3((ncols + 15) / 16),
+                       dim3(64 * kDecWaves), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 GemmPlan gemm_plan(int M, int N, int K, int bmode, int epi, bool grouped) {
-  GemmPlan p{kMid};
+  GemmPlan p{kMid, 1};
   if (grouped) return p;
   if (M <= 64) {
     // fp32 outputs (LM head, router) keep the 64x128 tile: its k order is that of the
     // larger tiles, so last-position logits equal the corresponding rows of a full pass
     p.tile = epi == E_F32 ? kSkinny : kDecode;
+    // residual projections with few output columns split K over extra blocks; the caller
+    // reduces the partials (fused with the residual add and the following RMSNorm)
+    const bool res = epi == E_RES_F32 || epi == E_RESB_F32 || epi == E_RESF_B16;
+    const int blocks = (N + 15) / 16;
+    if (p.tile == kDecode && res && blocks < 128) {
+      const int want = (256 + blocks - 1) / blocks;
+      p.k_splits = std::max(1, std::min(want, K / (32 * kDecWaves)));
+    }
     return p;
   }
   int big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
@@ -166,11 +188,15 @@ hipError_t gemm_run(const Args& a_in, bool f16, int bmode, int epi, bool grouped
   const GemmPlan& pl = plan;
   if (pl.tile == kDecode) {
     if (grouped || !f16 || a.M > 64) return hipErrorInvalidValue;
-    if (bmode == B_QKV && epi == E_F16) return launch_decode<B_QKV, E_F16>(a, s);
-    if (bmode == B_SWIGLU && epi == E_SWIGLU) return launch_decode<B_SWIGLU, E_SWIGLU>(a, s);
-    if (bmode == B_DENSE && epi == E_RES_F32) return launch_decode<B_DENSE, E_RES_F32>(a, s);
-    if (bmode == B_DENSE && epi == E_RESB_F32) return launch_decode<B_DENSE, E_RESB_F32>(a, s);
-    if (bmode == B_DENSE && epi == E_RESF_B16) return launch_decode<B_DENSE, E_RESF_B16>(a, s);
+    if (pl.k_splits > 1) {  // partial sums only (bmode dense, any residual epilogue)
+      if (bmode != B_DENSE || a.partial == nullptr) return hipErrorInvalidValue;
+      return launch_decode<B_DENSE, E_RES_F32>(a, pl.k_splits, s);
+    }
+    if (bmode == B_QKV && epi == E_F16) return launch_decode<B_QKV, E_F16>(a, 1, s);
+    if (bmode == B_SWIGLU && epi == E_SWIGLU) return launch_decode<B_SWIGLU, E_SWIGLU>(a, 1, s);
+    if (bmode == B_DENSE && epi == E_RES_F32) return launch_decode<B_DENSE, E_RES_F32>(a, 1, s);
+    if (bmode == B_DENSE && epi == E_RESB_F32) return launch_decode<B_DENSE, E_RESB_F32>(a, 1, s);
+    if (bmode == B_DENSE && epi == E_RESF_B16) return launch_decode<B_DENSE, E_RESF_B16>(a, 1, s);
     return hipErrorInvalidValue;
   }
   // dense layers: fp16 activations x bf16->fp16 weights

@@ -50,6 +50,7 @@ struct Args {
   int64_t ldc;
   const void* R;  // residual input
   int64_t ldr;
+  float* partial;  // decode K-split: fp32 partial sums [splits][M][N] (no epilogue)
   int m_tiles, n_tiles;
   // grouped mode
   const int32_t* g_offsets;      // [E + 1] first output row of each expert

@@ -14,7 +14,9 @@ namespace q3 {
 enum GemmTile { kAuto = 0, kBig = 1, kMid = 2, kSkinny = 3, kDecode = 4 };
 
 struct GemmPlan {
-  int tile;  // GemmTile actually used
+  int tile;      // GemmTile actually used
+  int k_splits;  // decode residual projections: > 1 means fp32 partial sums
+                 // [k_splits][M][N] in a.partial, reduced by splitk_res_norm()
 };
 
 // Chooses the tile family for an (M, N, K) problem: for M <= 64 the decode kernel (the
@@ -34,6 +36,11 @@ hipError_t rmsnorm_f32(const float* in, int64_t in_row_stride, int64_t in_row_of
                        const bf16_t* w, f16_t* out, int rows, int H, float eps, hipStream_t s);
 hipError_t rmsnorm_bf16(const bf16_t* in, int64_t in_row_stride, int64_t in_row_offset,
                         const bf16_t* w, f16_t* out, int rows, int H, float eps, hipStream_t s);
+// out[m] = residual[m] + sum_s part[s][m] (fixed order), then, if norm_w is given,
+// xn[m] = rmsnorm(out[m]) * norm_w (fp16).  residual / out may be fp32 or bf16; N <= 2048.
+hipError_t splitk_res_norm(const float* part, int splits, int M, int N, const void* residual,
+                           bool residual_bf16, void* out, bool out_bf16, const bf16_t* norm_w,
+                           f16_t* xn, float eps, hipStream_t s);
 hipError_t embed_gather(const int32_t* ids, const bf16_t* table, float* out, int T, int H, int V,
                         hipStream_t s);
 hipError_t rope_table(float* rope, int max_pos, int hd, double theta, hipStream_t s);

@@ -256,6 +256,66 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
   }
 }
 
+// Decode residual projections split over K: one block per row sums the partials in a fixed
+// order, adds the residual, writes the residual stream and (optionally) the RMSNorm of the
+// new row that the next projection consumes ([P3] "TransformerBlock": x + sublayer(x),
+// then the next pre-norm).  Thread t owns columns 4 t .. 4 t + 3 (+ 1024 for N > 1024).
+constexpr int kResMaxIter = 2;  // N <= 2048
+
+__global__ void __launch_bounds__(256)
+splitk_res_norm_kernel(const float* __restrict__ part, int splits, int M, int N,
+                       const void* residual, bool residual_bf16, void* out, bool out_bf16,
+                       const bf16_t* __restrict__ norm_w, f16_t* __restrict__ xn, float eps) {
+  __shared__ float sred[4];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  float v[kResMaxIter][4];
+  float ss = 0.f;
+#pragma unroll
+  for (int it = 0; it < kResMaxIter; ++it) {
+    const int c = (it * 256 + tid) * 4;
+    if (c >= N) continue;
+    const int64_t o = (int64_t)m * N + c;
+    f32x4_t acc;
+    if (residual_bf16) {
+      const u32x2_t r = *(const u32x2_t*)((const bf16_t*)residual + o);
+      acc = f32x4_t{__uint_as_float(r[0] << 16), __uint_as_float(r[0] & 0xffff0000u),
+                    __uint_as_float(r[1] << 16), __uint_as_float(r[1] & 0xffff0000u)};
+    } else {
+      acc = *(const f32x4_t*)((const float*)residual + o);
+    }
+    for (int sp = 0; sp < splits; ++sp) {
+      const f32x4_t pv = *(const f32x4_t*)(part + ((int64_t)sp * M + m) * N + c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += pv[e];
+    }
+    if (out_bf16)
+      *(u32x2_t*)((bf16_t*)out + o) = u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    else
+      *(f32x4_t*)((float*)out + o) = acc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[it][e] = acc[e];
+      ss += acc[e] * acc[e];
+    }
+  }
+  if (norm_w == nullptr) return;
+  ss = warp_sum(ss);
+  if ((tid & 63) == 0) sred[tid >> 6] = ss;
+  __syncthreads();
+  const float inv = rsqrtf((sred[0] + sred[1] + sred[2] + sred[3]) / (float)N + eps);
+#pragma unroll
+  for (int it = 0; it < kResMaxIter; ++it) {
+    const int c = (it * 256 + tid) * 4;
+    if (c >= N) continue;
+    const u32x2_t wv = *(const u32x2_t*)(norm_w + c);
+    const float w0 = __uint_as_float(wv[0] << 16), w1 = __uint_as_float(wv[0] & 0xffff0000u);
+    const float w2 = __uint_as_float(wv[1] << 16), w3 = __uint_as_float(wv[1] & 0xffff0000u);
+    *(u32x2_t*)(xn + (int64_t)m * N + c) =
+        u32x2_t{pack_f16x2(v[it][0] * inv * w0, v[it][1] * inv * w1),
+                pack_f16x2(v[it][2] * inv * w2, v[it][3] * inv * w3)};
+  }
+}
+
 int blocks_for(int64_t work, int per_block, int cap = 65536) {
   int64_t b = (work + per_block - 1) / per_block;
   if (b < 1) b = 1;
@@ -279,6 +339,16 @@ hipError_t rmsnorm_bf16(const bf16_t* in, int64_t in_row_stride, int64_t in_row_
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3((rows + 3) / 4), dim3(256), 0, s, in,
                      in_row_stride, in_row_offset, w, out, rows, H, eps);
+  return hipGetLastError();
+}
+
+hipError_t splitk_res_norm(const float* part, int splits, int M, int N, const void* residual,
+                           bool residual_bf16, void* out, bool out_bf16, const bf16_t* norm_w,
+                           f16_t* xn, float eps, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (N % 4 || N > 256 * 4 * kResMaxIter) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(splitk_res_norm_kernel, dim3(M), dim3(256), 0, s, part, splits, M, N,
+                     residual, residual_bf16, out, out_bf16, norm_w, xn, eps);
   return hipGetLastError();
 }
 

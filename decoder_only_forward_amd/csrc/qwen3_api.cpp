@@ -78,7 +78,7 @@ struct Bump {
 };
 
 struct DenseLayout {
-  size_t xn, qkv, q, attn, h1, act, res, hf, part_attn, am_val, am_idx, lg_scratch;
+  size_t xn, qkv, q, attn, h1, act, res, hf, part_attn, part_res, am_val, am_idx, lg_scratch;
   size_t kf, vtf;  // prefill: fp16 copies of the new keys / values
   size_t total;
   int T, rows_out, attn_splits, attn_chunk, am_chunks, fresh_w_max;
@@ -112,6 +112,13 @@ DenseLayout dense_layout(const qwen3_config* c, int op, int B, int S, int cap_hi
   if (decode) {
     attn_decode_plan(cap_hint, B, nkv, L.attn_splits, L.attn_chunk);
     L.part_attn = b.take((size_t)B * nq * L.attn_splits * (hd + 2) * 4);
+  }
+  {
+    // K-split partial sums of the residual projections (decode sizes only)
+    const int so = gemm_plan(T, H, nq * hd, gemm::B_DENSE, gemm::E_RES_F32, false).k_splits;
+    const int sd = gemm_plan(T, H, I, gemm::B_DENSE, gemm::E_RES_F32, false).k_splits;
+    const int sm = std::max(so, sd);
+    L.part_res = sm > 1 ? b.take((size_t)sm * T * H * 4) : 0;
   }
   if (stack) {
     L.rows_out = T;  // upper bound: ALL mode needs every row normalised
@@ -235,11 +242,16 @@ struct LayerIO {
   const bf16_t* x_bf16;  // block API input (nullptr in the stack)
   float* res;            // stack residual (in/out) (nullptr in the block API)
   bf16_t* x_out;         // block API output
+  bool input_normed;        // stack: xn already holds this layer's normalised input
+  const bf16_t* next_norm;  // stack: next layer's input RMSNorm weight (nullptr: none)
 };
 
+// *next_normed is set when the layer's last reduction also wrote the next layer's
+// normalised input into xn (decode sizes, stack only).
 int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* rope,
               const qwen3_kv_layer* kv, const LayerIO& io, char* ws, const DenseLayout& L,
-              hipStream_t s) {
+              hipStream_t s, bool* next_normed = nullptr) {
+  if (next_normed) *next_normed = false;
   const int H = c->hidden_size, nq = c->num_attention_heads, nkv = c->num_key_value_heads,
             hd = c->head_dim, I = c->intermediate_size, T = io.T;
   // transient activations feeding the matrix cores are fp16
@@ -251,11 +263,15 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
   float* h1 = io.res ? io.res : (float*)(ws + L.h1);
   const float eps = c->rms_norm_eps;
 
-  // input RMSNorm
-  if (io.res)
-    CHECK_HIP(rmsnorm_f32(io.res, 1, 0, (const bf16_t*)w->input_layernorm, xn, T, H, eps, s));
-  else
+  float* part_res = L.part_res ? (float*)(ws + L.part_res) : nullptr;
+
+  // input RMSNorm (unless the previous layer's last reduction produced it)
+  if (io.res) {
+    if (!io.input_normed)
+      CHECK_HIP(rmsnorm_f32(io.res, 1, 0, (const bf16_t*)w->input_layernorm, xn, T, H, eps, s));
+  } else {
     CHECK_HIP(rmsnorm_bf16(io.x_bf16, 1, 0, (const bf16_t*)w->input_layernorm, xn, T, H, eps, s));
+  }
 
   // QKV projection (q, k, v weights stacked along N without a copy), fp16 out: one
   // rounding 4x finer than the bf16 cache that the keys end in
@@ -325,11 +341,25 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
     int epi = io.res ? gemm::E_RES_F32 : gemm::E_RESB_F32;
     a.R = io.res ? (const void*)io.res : (const void*)io.x_bf16; a.ldr = H;
     GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_DENSE, epi, false);
-    ProfScope ps("o_proj_gemm", s);
-    CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, epi, false, p, s));
+    if (p.k_splits > 1) {
+      // partial sums; then residual add and the post-attention RMSNorm in one pass
+      a.partial = part_res;
+      {
+        ProfScope ps("o_proj_gemm", s);
+        CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, epi, false, p, s));
+      }
+      CHECK_HIP(splitk_res_norm(part_res, p.k_splits, T, H, a.R, io.res == nullptr, h1, false,
+                                (const bf16_t*)w->post_attention_layernorm, xn, eps, s));
+    } else {
+      {
+        ProfScope ps("o_proj_gemm", s);
+        CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, epi, false, p, s));
+      }
+      // post-attention RMSNorm
+      CHECK_HIP(rmsnorm_f32(h1, 1, 0, (const bf16_t*)w->post_attention_layernorm, xn, T, H,
+                            eps, s));
+    }
   }
-  // post-attention RMSNorm
-  CHECK_HIP(rmsnorm_f32(h1, 1, 0, (const bf16_t*)w->post_attention_layernorm, xn, T, H, eps, s));
   // gate | up with SwiGLU
   {
     Args a{};
@@ -358,8 +388,21 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
     }
     a.ldc = H;
     GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_DENSE, epi, false);
-    ProfScope ps("down_gemm", s);
-    CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, epi, false, p, s));
+    if (p.k_splits > 1) {
+      // partial sums; then residual add (and the next layer's input RMSNorm) in one pass
+      a.partial = part_res;
+      {
+        ProfScope ps("down_gemm", s);
+        CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, epi, false, p, s));
+      }
+      const bf16_t* nn = io.res ? io.next_norm : nullptr;
+      CHECK_HIP(splitk_res_norm(part_res, p.k_splits, T, H, h1, false, a.C, io.res == nullptr,
+                                nn, xn, eps, s));
+      if (next_normed) *next_normed = nn != nullptr;
+    } else {
+      ProfScope ps("down_gemm", s);
+      CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, epi, false, p, s));
+    }
   }
   return QWEN3_OK;
 }
@@ -554,8 +597,13 @@ int qwen3_stack_forward(const qwen3_config* c, const qwen3_model_weights* w, con
   LayerIO io{};
   io.T = T; io.B = batch; io.S = decode ? 1 : seq_len; io.pos0 = pos0;
   io.pos = decode ? pos : nullptr; io.res = res;
-  for (int l = 0; l < c->num_hidden_layers; ++l)
-    TRY(run_layer(c, &w->layers[l], rope, &caches[l], io, ws, L, s));
+  bool normed = false;
+  for (int l = 0; l < c->num_hidden_layers; ++l) {
+    io.input_normed = normed;
+    io.next_norm = l + 1 < c->num_hidden_layers
+                       ? (const bf16_t*)w->layers[l + 1].input_layernorm : nullptr;
+    TRY(run_layer(c, &w->layers[l], rope, &caches[l], io, ws, L, s, &normed));
+  }
 
   // final RMSNorm on the rows that need logits, LM head (tied: embed_tokens)
   const bf16_t* head = (const bf16_t*)(c->tie_word_embeddings ? w->embed_tokens : w->lm_head);
