@@ -75,13 +75,12 @@ __global__ void __launch_bounds__(PF_THREADS, HAS_PAST ? 1 : 2) attn_prefill_ker
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, grp = lane >> 4;
   const int nmb = (a.S + BQ - 1) / BQ;
-  const int nblocks = nmb * a.B * a.nq;
-  // contiguous work ranges per XCD; heavy (late) row blocks first
-  int wid;
-  {
-    int q = nblocks >> 3, r = nblocks & 7, x = blockIdx.x & 7, i = blockIdx.x >> 3;
-    wid = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
-  }
+  // Heavy (late) row blocks first.  Workgroups reach the eight XCDs round-robin, so with
+  // this order every XCD receives every eighth block of each causal row level: the XCDs
+  // get equal work, and when B * nq is a multiple of 8 each keeps the same heads (and
+  // their K/V) for all levels.  (Contiguous block ranges per XCD would hand one XCD all
+  // the longest rows.)
+  const int wid = blockIdx.x;
   const int mb = nmb - 1 - wid / (a.B * a.nq);
   const int rem = wid % (a.B * a.nq);
   const int b = rem / a.nq, h = rem % a.nq;
