@@ -56,6 +56,7 @@ struct Args {
   const int32_t* g_offsets;      // [E + 1] first output row of each expert
   const int32_t* g_tile_expert;  // [m_tiles] expert of each m tile (-1: idle)
   const int32_t* g_tile_row0;    // [m_tiles] first row within the expert
+  const int32_t* g_tile_count;   // [1] m tiles in use (nullptr: all m_tiles)
   int64_t g_b_stride;            // elements between experts' B matrices
 };
 
@@ -124,10 +125,14 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
 
-  const int nblocks_mn = p.m_tiles * p.n_tiles;
+  // Grouped mode: the grid covers every possible m tile, but only the first tile_count
+  // are in use; the used tiles are spread over the XCDs and surplus blocks leave at once.
+  const int m_tiles = GROUPED && p.g_tile_count ? min(p.m_tiles, *p.g_tile_count) : p.m_tiles;
+  const int nblocks_mn = m_tiles * p.n_tiles;
+  if ((int)blockIdx.x >= nblocks_mn) return;
   const int t = xcd_remap(blockIdx.x, nblocks_mn);
   int tm, tn;
-  tile_coords(t, p.m_tiles, p.n_tiles, tm, tn);
+  tile_coords(t, m_tiles, p.n_tiles, tm, tn);
 
   // rows handled by this block
   int out_row0, rows_valid;

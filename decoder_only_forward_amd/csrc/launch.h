@@ -109,6 +109,7 @@ struct MoeRouteArgs {
   int32_t* inv_row;       // [T][k]
   int32_t* tile_expert;   // [max_tiles]
   int32_t* tile_row0;     // [max_tiles]
+  int32_t* tile_count;    // [1] number of tiles in use (the first entries of the table)
   int max_tiles, tile_m;
 };
 int moe_route_chunks(int T);

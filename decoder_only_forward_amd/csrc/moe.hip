@@ -141,9 +141,10 @@ __global__ void __launch_bounds__(256) scan_kernel(MoeRouteArgs a, int nchunks) 
       toff += tl;
     }
     a.offsets[a.E] = off;
+    a.tile_count[0] = toff;
   }
   __syncthreads();
-  // tile table: idle entries first, then each expert's tiles
+  // tile table: each expert's tiles in order (tile_count of them), then idle entries
   for (int i = e; i < a.max_tiles; i += 256) {
     a.tile_expert[i] = -1;
     a.tile_row0[i] = 0;

@@ -133,7 +133,8 @@ DenseLayout dense_layout(const qwen3_config* c, int op, int B, int S, int cap_hi
 }
 
 struct MoeLayout {
-  size_t logits, idx, w, chunk_counts, counts, offsets, perm, inv, tile_e, tile_r, act, yrows;
+  size_t logits, idx, w, chunk_counts, counts, offsets, perm, inv, tile_e, tile_r, tile_n, act,
+      yrows;
   size_t total;
   int max_tiles, tile_m;
 };
@@ -155,6 +156,7 @@ MoeLayout moe_layout(const qwen3_config* c, int T) {
   L.inv = b.take((size_t)T * k * 4);
   L.tile_e = b.take((size_t)L.max_tiles * 4);
   L.tile_r = b.take((size_t)L.max_tiles * 4);
+  L.tile_n = b.take(4);
   L.act = b.take((size_t)T * k * I * 2);
   L.yrows = b.take((size_t)T * k * H * 4);
   L.total = b.off;
@@ -682,6 +684,7 @@ int qwen3_moe_ffn(const qwen3_config* c, const qwen3_moe_weights* w, const void*
   int32_t* inv = inv_row ? inv_row : (int32_t*)(ws + L.inv);
   int32_t* tile_e = (int32_t*)(ws + L.tile_e);
   int32_t* tile_r = (int32_t*)(ws + L.tile_r);
+  int32_t* tile_n = (int32_t*)(ws + L.tile_n);
   f16_t* act = (f16_t*)(ws + L.act);
   float* yrows = (float*)(ws + L.yrows);
 
@@ -704,7 +707,7 @@ int qwen3_moe_ffn(const qwen3_config* c, const qwen3_moe_weights* w, const void*
     r.chunk_counts = (int32_t*)(ws + L.chunk_counts);
     r.counts = (int32_t*)(ws + L.counts);
     r.offsets = offs; r.perm_token = perm; r.inv_row = inv;
-    r.tile_expert = tile_e; r.tile_row0 = tile_r;
+    r.tile_expert = tile_e; r.tile_row0 = tile_r; r.tile_count = tile_n;
     r.max_tiles = L.max_tiles; r.tile_m = L.tile_m;
     ProfScope ps("moe_route", s);
     CHECK_HIP(moe_route(r, s));
@@ -718,6 +721,7 @@ int qwen3_moe_ffn(const qwen3_config* c, const qwen3_moe_weights* w, const void*
     a.B1 = (const bf16_t*)w->gate_up_proj + (int64_t)I * H;
     a.ldb = H;
     a.g_offsets = offs; a.g_tile_expert = tile_e; a.g_tile_row0 = tile_r;
+    a.g_tile_count = tile_n;
     a.g_b_stride = (int64_t)2 * I * H;
     a.m_tiles = L.max_tiles;
     a.C = act; a.ldc = I;
@@ -732,6 +736,7 @@ int qwen3_moe_ffn(const qwen3_config* c, const qwen3_moe_weights* w, const void*
     a.A = act; a.lda = I;
     a.B0 = (const bf16_t*)w->down_proj; a.B1 = a.B0; a.ldb = I;
     a.g_offsets = offs; a.g_tile_expert = tile_e; a.g_tile_row0 = tile_r;
+    a.g_tile_count = tile_n;
     a.g_b_stride = (int64_t)H * I;
     a.m_tiles = L.max_tiles;
     a.C = yrows; a.ldc = H;
