@@ -100,6 +100,9 @@ DEV float ror16(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
 }
 
+// DECODE: one token per sequence at its own position (a.pos); the kernel is compiled
+// separately for it so the prefill path keeps all of its loads unconditional.
+template <bool DECODE>
 __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
   const int HD = 128;
   const int tile = blockIdx.x, b = blockIdx.y, slot = blockIdx.z;
@@ -137,14 +140,42 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) w[e] = 1.f;
     }
-    for (int r = wave * 4 + sub; r < kRopeTile; r += 16) {
-      const int s = s0 + r;
-      if (s >= a.S) break;
+    // all rows' loads (activations and RoPE table) are issued before any is used
+    constexpr int RPL = kRopeTile / 16;  // token rows per lane
+    u32x4_t raw[RPL];
+    f32x4_t tc[RPL][2], ts[RPL][2];
+    int pos_r[RPL];
+    bool ok_r[RPL], live_r[RPL];
+#pragma unroll
+    for (int k = 0; k < RPL; ++k) {
+      const int s = s0 + wave * 4 + sub + 16 * k;
+      live_r[k] = s < a.S;
+      const int sc = live_r[k] ? s : a.S - 1;
+      const int64_t t = (int64_t)b * a.S + sc;
+      const int pos = DECODE ? a.pos[b] : a.pos0 + sc;
+      pos_r[k] = pos;
+      ok_r[k] = pos >= 0 && pos < a.cap && pos < a.max_pos;
+      // decode: rows other than the one token load nothing; prefill rows past the end
+      // load a clamped row so that every load is unconditional
+      if (DECODE && !live_r[k]) continue;
+      raw[k] = ld16(a.qkv + t * row_elems + slot * HD + d0);
+      const int pc = ok_r[k] ? pos : 0;
+      const float* cp = a.rope + (int64_t)pc * half + i0;
+      const float* sp = a.rope + ((int64_t)a.max_pos + pc) * half + i0;
+      tc[k][0] = *(const f32x4_t*)cp;
+      tc[k][1] = *(const f32x4_t*)(cp + 4);
+      ts[k][0] = *(const f32x4_t*)sp;
+      ts[k][1] = *(const f32x4_t*)(sp + 4);
+    }
+#pragma unroll
+    for (int k = 0; k < RPL; ++k) {
+      if (!live_r[k]) break;
+      const int s = s0 + wave * 4 + sub + 16 * k;
       const int64_t t = (int64_t)b * a.S + s;
-      const int pos = a.pos ? a.pos[b] : a.pos0 + s;
-      const bool ok = pos >= 0 && pos < a.cap && pos < a.max_pos;
+      const int pos = pos_r[k];
+      const bool ok = ok_r[k];
       float x[8];
-      unpack8_f16(ld16(a.qkv + t * row_elems + slot * HD + d0), x);
+      unpack8_f16(raw[k], x);
       if (a.qk_norm) {
         float ss = 0.f;
 #pragma unroll
@@ -158,19 +189,12 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
         for (int e = 0; e < 8; ++e) x[e] = x[e] * inv * w[e];
       }
       float c[8], sn[8];
-      if (ok) {
-        const float* cp = a.rope + (int64_t)pos * half + i0;
-        const float* sp = a.rope + ((int64_t)a.max_pos + pos) * half + i0;
-        const f32x4_t c0 = *(const f32x4_t*)cp, c1 = *(const f32x4_t*)(cp + 4);
-        const f32x4_t s0v = *(const f32x4_t*)sp, s1v = *(const f32x4_t*)(sp + 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          c[e] = c0[e]; c[e + 4] = c1[e];
-          sn[e] = s0v[e]; sn[e + 4] = s1v[e];
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) c[e] = sn[e] = 0.f;
+      for (int e = 0; e < 4; ++e) {
+        c[e] = ok ? tc[k][0][e] : 0.f;
+        c[e + 4] = ok ? tc[k][1][e] : 0.f;
+        sn[e] = ok ? ts[k][0][e] : 0.f;
+        sn[e + 4] = ok ? ts[k][1][e] : 0.f;
       }
       float y[8];
 #pragma unroll
@@ -203,21 +227,29 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
   // 8 consecutive positions per lane (16-byte stores)
   __shared__ float sv[kRopeTile][HD + 1];
   const int h = slot - a.nq - a.nkv;
-  for (int i = tid; i < kRopeTile * (HD / 8); i += 256) {
-    const int r = i / (HD / 8), d = (i % (HD / 8)) * 8;
-    const int s = s0 + r;
-    float v[8];
-    if (s < a.S) {
-      unpack8_f16(ld16(a.qkv + ((int64_t)b * a.S + s) * row_elems + slot * HD + d), v);
-    } else {
+  {
+    constexpr int PER = kRopeTile * (HD / 8) / 256;  // 16-byte chunks per thread
+    u32x4_t raw[PER];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    for (int k = 0; k < PER; ++k) {
+      const int i = tid + 256 * k;
+      const int r = i / (HD / 8), d = (i % (HD / 8)) * 8;
+      const int s = min(s0 + r, a.S - 1);
+      raw[k] = ld16(a.qkv + ((int64_t)b * a.S + s) * row_elems + slot * HD + d);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sv[r][d + e] = v[e];
+    for (int k = 0; k < PER; ++k) {
+      const int i = tid + 256 * k;
+      const int r = i / (HD / 8), d = (i % (HD / 8)) * 8;
+      float v[8];
+      unpack8_f16(raw[k], v);
+      const bool live = s0 + r < a.S;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sv[r][d + e] = live ? v[e] : 0.f;
+    }
   }
   __syncthreads();
-  if (a.pos) {
+  if (DECODE) {
     // decode: one token per sequence, each at its own position
     for (int d = tid; d < HD; d += 256) {
       if (a.S < 1) break;
@@ -369,7 +401,10 @@ hipError_t rope_table(float* rope, int max_pos, int hd, double theta, hipStream_
 hipError_t qkv_rope_cache(const RopeCacheArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.S <= 0) return hipSuccess;
   dim3 grid((a.S + kRopeTile - 1) / kRopeTile, a.B, a.nq + 2 * a.nkv);
-  hipLaunchKernelGGL(qkv_rope_cache_kernel, grid, dim3(256), 0, s, a);
+  if (a.pos)
+    hipLaunchKernelGGL(qkv_rope_cache_kernel<true>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(qkv_rope_cache_kernel<false>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
