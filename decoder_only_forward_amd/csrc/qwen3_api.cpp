@@ -143,7 +143,7 @@ MoeLayout moe_layout(const qwen3_config* c, int T) {
   MoeLayout L{};
   const int E = c->num_experts, k = c->num_experts_per_tok, H = c->hidden_size,
             I = c->moe_intermediate_size;
-  L.tile_m = 128;
+  L.tile_m = 256;
   L.max_tiles = (int)(((int64_t)T * k + L.tile_m - 1) / L.tile_m) + E;
   Bump b;
   L.logits = b.take((size_t)T * E * 4);
@@ -725,7 +725,7 @@ int qwen3_moe_ffn(const qwen3_config* c, const qwen3_moe_weights* w, const void*
     a.g_b_stride = (int64_t)2 * I * H;
     a.m_tiles = L.max_tiles;
     a.C = act; a.ldc = I;
-    GemmPlan p{kMid};
+    GemmPlan p{kBig};
     ProfScope ps("moe_gate_up_gemm", s);
     CHECK_HIP(gemm_run(a, false, gemm::B_SWIGLU, gemm::E_SWIGLU, true, p, s));
   }
@@ -740,7 +740,7 @@ int qwen3_moe_ffn(const qwen3_config* c, const qwen3_moe_weights* w, const void*
     a.g_b_stride = (int64_t)H * I;
     a.m_tiles = L.max_tiles;
     a.C = yrows; a.ldc = H;
-    GemmPlan p{kMid};
+    GemmPlan p{kBig};
     ProfScope ps("moe_down_gemm", s);
     CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, gemm::E_F32, true, p, s));
   }
