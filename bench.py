@@ -313,8 +313,10 @@ def wl_moe(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown):
     return out
 
 
-def wl_block(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, big):
+def wl_block(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, big,
+             rope_interleaved=0):
     cfg = dict(recipes.QWEN_7B_BLOCK if big else recipes.QWEN3_0P6B)
+    cfg["rope_interleaved"] = rope_interleaved
     B, S = (1, 32768) if big else (1, 128)
     seed = 5 if big else 1
     w = recipes.layer_device(seed, cfg, 0, dev)
@@ -338,13 +340,14 @@ def wl_block(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, bi
     c1 = dict(cfg, num_hidden_layers=1, vocab_size=0)
     flops = stack_prefill_flops(c1, B, S)
     nq = cfg["num_attention_heads"]
-    name = "block_7b" if big else "block_0p6b"
+    name = ("block_7b" if big else "block_0p6b") + ("_rope_interleaved" if rope_interleaved else "")
     units = dense_units(cfg, B, S, 1)
     ms, dom, rf, kernels = measure(timer, step, steps, warmup, name, units, "attn_prefill",
                                    breakdown)
     out = {"name": name, "tokens_per_s": B * S / (ms * 1e-3), "ms_per_step": ms,
            "config": {"workload": name, "batch": B, "seq_len": S, "hidden": H,
-                      "heads": f"{nq}q/{nkv}kv x128", "intermediate": cfg["intermediate_size"]},
+                      "heads": f"{nq}q/{nkv}kv x128", "intermediate": cfg["intermediate_size"],
+                      "rope": "interleaved pairs" if rope_interleaved else "rotate-half"},
            "dominant_kernel": dom, "roofline": rf,
            "whole_step_mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
            "algorithmic_tflop_per_step": round(flops / 1e12, 3)}
@@ -386,7 +389,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="prefill,decode,moe,block7b,block")
+    ap.add_argument("--workloads", default="prefill,decode,moe,block7b,block7b_irope,block")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=512,
                     help="prefix length for the oracle CPU baseline (0 = skip)")
@@ -424,6 +427,9 @@ def main():
                                  timer, bd),
            "block7b": lambda: wl_block(torch, q3, recipes, synth, dev, max(2, args.steps // 3),
                                        1, timer, bd, True),
+           "block7b_irope": lambda: wl_block(torch, q3, recipes, synth, dev,
+                                             max(2, args.steps // 3), 1, timer, bd, True,
+                                             rope_interleaved=1),
            "block": lambda: wl_block(torch, q3, recipes, synth, dev, 10 * args.steps,
                                      args.warmup, timer, bd, False)}
     for w in wls:

@@ -45,7 +45,8 @@ class Config(ctypes.Structure):
                 ("rms_norm_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
                 ("qk_norm", ctypes.c_int32), ("tie_word_embeddings", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("num_experts_per_tok", ctypes.c_int32),
-                ("moe_intermediate_size", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32)]
+                ("moe_intermediate_size", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32),
+                ("rope_interleaved", ctypes.c_int32)]
 
 
 LAYER_FIELDS = ("input_layernorm", "q_proj", "k_proj", "v_proj", "q_norm", "k_norm", "o_proj",

@@ -61,6 +61,7 @@ struct RopeCacheArgs {
   f16_t* vt_fresh;
   int fresh_base, fresh_w;
   int pos0, B, S, nq, nkv, cap, max_pos, qk_norm;
+  int interleaved;  // RoPE planes (2i, 2i + 1) instead of (i, i + hd/2)
   float eps;
 };
 hipError_t qkv_rope_cache(const RopeCacheArgs& a, hipStream_t s);

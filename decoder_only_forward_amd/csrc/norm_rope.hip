@@ -88,10 +88,12 @@ rope_table_kernel(float* __restrict__ rope, int max_pos, int half, double theta,
 //   k heads:  k = rope(rmsnorm_hd(k)) -> k_cache[b][h][pos][:]
 //   v heads:  v -> vt_cache[b][h][:][pos]  (transposed through LDS)
 // ([P3] "GQA 注意力": per-head q/k RMSNorm before RoPE, offset = cached length;
-// "RoPE": pairs (i, i + hd/2) rotated by pos * theta_i.)
+// "RoPE": pairs (i, i + hd/2) rotated by pos * theta_i; with a.interleaved the planes are
+// (2i, 2i + 1) instead, the complex-number form of [P1] section 8.)
 // q / k heads: 16 lanes per token row, lane j holding dims 8j .. 8j + 7 (16-byte loads and
-// stores); the RoPE partner of dim d is dim d ^ 64, held by lane j ^ 8 of the same 16-lane
-// row, so the exchange and the sum of squares are row-local DPP rotations.
+// stores); the rotate-half partner of dim d is dim d ^ 64, held by lane j ^ 8 of the same
+// 16-lane row, so the exchange and the sum of squares are row-local DPP rotations; the
+// interleaved partner d ^ 1 is in the same lane.
 constexpr int kRopeTile = 64;
 
 // rotate within 16-lane rows by n (n in 1..15)
@@ -131,7 +133,9 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
     const int h = is_q ? slot : slot - a.nq;
     const int j = lane & 15, sub = lane >> 4;  // 4 token rows per wave step
     const int d0 = 8 * j;                       // first dim of this lane
-    const int i0 = d0 & (half - 1);             // its RoPE frequency index
+    // first RoPE frequency index of this lane's dims: 8 consecutive (rotate-half) or the
+    // 4 planes (2i, 2i + 1) its 8 dims form (interleaved)
+    const int i0 = a.interleaved ? d0 / 2 : d0 & (half - 1);
     const float sgn = d0 < half ? -1.f : 1.f;   // y = x c + sgn * partner * s
     float w[8];
     if (a.qk_norm) {
@@ -163,9 +167,11 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
       const float* cp = a.rope + (int64_t)pc * half + i0;
       const float* sp = a.rope + ((int64_t)a.max_pos + pc) * half + i0;
       tc[k][0] = *(const f32x4_t*)cp;
-      tc[k][1] = *(const f32x4_t*)(cp + 4);
       ts[k][0] = *(const f32x4_t*)sp;
-      ts[k][1] = *(const f32x4_t*)(sp + 4);
+      if (!a.interleaved) {
+        tc[k][1] = *(const f32x4_t*)(cp + 4);
+        ts[k][1] = *(const f32x4_t*)(sp + 4);
+      }
     }
 #pragma unroll
     for (int k = 0; k < RPL; ++k) {
@@ -188,17 +194,26 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = x[e] * inv * w[e];
       }
-      float c[8], sn[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        c[e] = ok ? tc[k][0][e] : 0.f;
-        c[e + 4] = ok ? tc[k][1][e] : 0.f;
-        sn[e] = ok ? ts[k][0][e] : 0.f;
-        sn[e + 4] = ok ? ts[k][1][e] : 0.f;
-      }
       float y[8];
+      if (a.interleaved) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = x[e] * c[e] + sgn * ror16<8>(x[e]) * sn[e];
+        for (int e = 0; e < 4; ++e) {
+          const float c = ok ? tc[k][0][e] : 0.f, sn = ok ? ts[k][0][e] : 0.f;
+          y[2 * e] = x[2 * e] * c - x[2 * e + 1] * sn;
+          y[2 * e + 1] = x[2 * e] * sn + x[2 * e + 1] * c;
+        }
+      } else {
+        float c[8], sn[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          c[e] = ok ? tc[k][0][e] : 0.f;
+          c[e + 4] = ok ? tc[k][1][e] : 0.f;
+          sn[e] = ok ? ts[k][0][e] : 0.f;
+          sn[e + 4] = ok ? ts[k][1][e] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = x[e] * c[e] + sgn * ror16<8>(x[e]) * sn[e];
+      }
       if (is_q) {
         // q carries the softmax scale log2(e) / sqrt(hd) for the attention kernels
         const float qs = 0.08838834764831845f * kLog2e;

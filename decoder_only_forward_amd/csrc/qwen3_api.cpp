@@ -186,6 +186,8 @@ int check_dense_cfg(const qwen3_config* c) {
     return fail(QWEN3_EINVAL, "max_position_embeddings=%d", c->max_position_embeddings);
   if (!(c->rms_norm_eps >= 0.f)) return fail(QWEN3_EINVAL, "rms_norm_eps must be >= 0");
   if (!(c->rope_theta > 0.f)) return fail(QWEN3_EINVAL, "rope_theta must be > 0");
+  if (c->rope_interleaved != 0 && c->rope_interleaved != 1)
+    return fail(QWEN3_EINVAL, "rope_interleaved=%d must be 0 or 1", c->rope_interleaved);
   return QWEN3_OK;
 }
 
@@ -298,6 +300,7 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
     r.pos = io.pos; r.pos0 = io.pos0; r.B = io.B; r.S = io.pos ? 1 : io.S;
     r.nq = nq; r.nkv = nkv; r.cap = kv->capacity; r.max_pos = c->max_position_embeddings;
     r.qk_norm = c->qk_norm; r.eps = eps;
+    r.interleaved = c->rope_interleaved;
     if (!io.pos) {
       r.k_fresh = (f16_t*)(ws + L.kf);
       r.vt_fresh = (f16_t*)(ws + L.vtf);

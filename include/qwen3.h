@@ -73,6 +73,10 @@ typedef struct qwen3_config {
   int32_t num_experts_per_tok;     /* k (MoE only), 1 <= k <= min(E, 8) */
   int32_t moe_intermediate_size;   /* I_moe (MoE only) */
   int32_t norm_topk_prob;          /* 1: renormalise the k selected probabilities */
+  int32_t rope_interleaved;        /* RoPE pairing. 0: planes (i, i + hd/2) (rotate-half,
+                                      Qwen3 "RoPE" section of the build-it-yourself pages);
+                                      1: planes (2i, 2i + 1) (the complex-number form of
+                                      the first page's RoPE section). Other values: EINVAL */
 } qwen3_config;
 
 /* One decoder layer's weights (device, bf16). */

@@ -25,7 +25,7 @@ class OracleCfg(ctypes.Structure):
         "hidden", "n_heads", "n_kv_heads", "head_dim", "inter", "n_layers", "vocab", "max_pos")] + [
         ("eps", ctypes.c_double), ("theta", ctypes.c_double), ("qk_norm", ctypes.c_int32),
         ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("moe_inter", ctypes.c_int32),
-        ("norm_topk", ctypes.c_int32)]
+        ("norm_topk", ctypes.c_int32), ("rope_interleaved", ctypes.c_int32)]
 
 
 LAYER_FIELDS = ("in_norm", "q", "k", "v", "q_norm", "k_norm", "o", "post_norm", "gate", "up",
@@ -65,7 +65,8 @@ def make_cfg(c):
         eps=c.get("rms_norm_eps", 1e-6), theta=c.get("rope_theta", 1e6),
         qk_norm=int(c.get("qk_norm", 1)), n_experts=c.get("num_experts", 0),
         top_k=c.get("num_experts_per_tok", 0), moe_inter=c.get("moe_intermediate_size", 0),
-        norm_topk=int(c.get("norm_topk_prob", 1)))
+        norm_topk=int(c.get("norm_topk_prob", 1)),
+        rope_interleaved=int(c.get("rope_interleaved", 0)))
 
 
 def _p(a):
@@ -96,13 +97,13 @@ def rmsnorm_rows(x, w, eps):
     return y
 
 
-def rope(x, pos, theta):
+def rope(x, pos, theta, interleaved=False):
     x = _f64(x)
     hd = x.shape[-1]
     pos = np.ascontiguousarray(np.broadcast_to(pos, (x.size // hd,)), dtype=np.int64)
     y = np.empty_like(x)
     lib().oracle_rope(_p(x), ctypes.c_int64(x.size // hd), hd, _p(pos), ctypes.c_double(theta),
-                      _p(y))
+                      int(interleaved), _p(y))
     return y
 
 

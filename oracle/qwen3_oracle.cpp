@@ -69,19 +69,21 @@ void rmsnorm_vec(const double *x, int n, const uint16_t *w, double eps, double *
   for (int i = 0; i < n; ++i) y[i] = x[i] * inv * bf(w[i]);
 }
 
-// Rotate-half RoPE of one head vector at absolute position pos:
-// theta_i = base^(-2i/hd), i < hd/2; dims (i, i + hd/2) form one plane;
-// [a, b] -> [a cos(pos theta_i) - b sin(pos theta_i), a sin + b cos]
-// ([P3] "RoPE" formula and apply_rope; [P4] 3.4).
-void rope_vec(const double *x, int hd, int64_t pos, double theta, double *y) {
+// RoPE of one head vector at absolute position pos: theta_i = base^(-2i/hd), i < hd/2;
+// plane i is rotated by pos theta_i: [a, b] -> [a cos - b sin, a sin + b cos].
+// Rotate-half pairing (the default): plane i = dims (i, i + hd/2) ([P3] "RoPE" formula
+// and apply_rope; [P4] 3.4).  Interleaved pairing: plane i = dims (2i, 2i + 1), the
+// complex-number form of [P1] section 8.
+void rope_vec(const double *x, int hd, int64_t pos, double theta, int interleaved, double *y) {
   int half = hd / 2;
   for (int i = 0; i < half; ++i) {
     double inv_freq = std::pow(theta, -(2.0 * i) / hd);
     double ang = (double)pos * inv_freq;
     double c = std::cos(ang), s = std::sin(ang);
-    double a = x[i], b = x[i + half];
-    y[i] = a * c - b * s;
-    y[i + half] = a * s + b * c;
+    int ia = interleaved ? 2 * i : i, ib = interleaved ? 2 * i + 1 : i + half;
+    double a = x[ia], b = x[ib];
+    y[ia] = a * c - b * s;
+    y[ib] = a * s + b * c;
   }
 }
 
@@ -131,8 +133,10 @@ void oracle_rmsnorm_rows(const double *x, int64_t rows, int n, const uint16_t *w
 }
 
 void oracle_rope(const double *x, int64_t nvec, int hd, const int64_t *pos, double theta,
-                 double *y) {
-  parallel_for(nvec, [&](int64_t i) { rope_vec(x + i * hd, hd, pos[i], theta, y + i * hd); });
+                 int interleaved, double *y) {
+  parallel_for(nvec, [&](int64_t i) {
+    rope_vec(x + i * hd, hd, pos[i], theta, interleaved, y + i * hd);
+  });
 }
 
 // Grouped-query attention: q head h reads kv head h / (nq / nkv)
@@ -211,7 +215,7 @@ void oracle_block(const oracle_cfg *c, const oracle_layer *w, const double *x, i
         rmsnorm_vec(kh, hd, w->k_norm, c->eps, t.data());
         std::copy(t.begin(), t.end(), kh);
       }
-      rope_vec(kh, hd, pos0 + s, c->theta, t.data());
+      rope_vec(kh, hd, pos0 + s, c->theta, c->rope_interleaved, t.data());
       for (int e = 0; e < hd; ++e) {
         K[((pos0 + s) * nkv + h) * hd + e] = t[e];
         V[((pos0 + s) * nkv + h) * hd + e] = vr[(size_t)h * hd + e];
@@ -239,7 +243,7 @@ void oracle_block(const oracle_cfg *c, const oracle_layer *w, const double *x, i
         rmsnorm_vec(qh, hd, w->q_norm, c->eps, t.data());
         std::copy(t.begin(), t.end(), qh);
       }
-      rope_vec(qh, hd, pos0 + s, c->theta, t.data());
+      rope_vec(qh, hd, pos0 + s, c->theta, c->rope_interleaved, t.data());
       std::copy(t.begin(), t.end(), qh);
       attend_row(qh, K.data(), V.data(), pos0 + s, h / g, nkv, hd, o.data() + (size_t)h * hd, sc);
     }

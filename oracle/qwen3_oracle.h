@@ -35,6 +35,7 @@ typedef struct {
   double eps, theta;
   int32_t qk_norm;
   int32_t n_experts, top_k, moe_inter, norm_topk;
+  int32_t rope_interleaved; /* 1: planes (2i, 2i + 1); 0: planes (i, i + hd/2) */
 } oracle_cfg;
 
 typedef struct { /* bf16 bits */
@@ -47,7 +48,7 @@ int oracle_get_threads(void);
 void oracle_rmsnorm_rows(const double *x, int64_t rows, int n, const uint16_t *w, double eps,
                          double *y);
 void oracle_rope(const double *x, int64_t nvec, int hd, const int64_t *pos, double theta,
-                 double *y);
+                 int interleaved, double *y);
 void oracle_attention(const double *q, const double *k, const double *v, const int64_t *qpos,
                       int64_t S, int64_t L, int nq, int nkv, int hd, double *o);
 void oracle_linear_rows(const double *x, int64_t T, int64_t K, const uint16_t *W, int64_t N,

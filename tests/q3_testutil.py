@@ -93,8 +93,9 @@ def cache_v_logical(vt, b, n_pos):
     return f64(bf16_host(vt[b, :, :, :n_pos])).transpose(0, 2, 1)
 
 
-def small_cfg(H=256, nq=4, nkv=2, I=512, L=2, V=512, qk_norm=1, max_pos=4096):
+def small_cfg(H=256, nq=4, nkv=2, I=512, L=2, V=512, qk_norm=1, max_pos=4096,
+              rope_interleaved=0):
     return dict(hidden_size=H, num_attention_heads=nq, num_key_value_heads=nkv, head_dim=128,
                 intermediate_size=I, num_hidden_layers=L, vocab_size=V,
                 max_position_embeddings=max_pos, rms_norm_eps=1e-6, rope_theta=1e6,
-                qk_norm=qk_norm, tie_word_embeddings=1)
+                qk_norm=qk_norm, tie_word_embeddings=1, rope_interleaved=rope_interleaved)

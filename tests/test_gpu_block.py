@@ -26,6 +26,8 @@ PREFILL_CASES = {
     "group7": (dict(nq=7, nkv=1), 1, 130, 0),
     "no_qk_norm": (dict(qk_norm=0), 1, 64, 0),
     "one_token": (dict(), 3, 1, 0),
+    "interleaved_rope": (dict(rope_interleaved=1), 2, 150, 0),
+    "interleaved_rope_chunked": (dict(rope_interleaved=1), 1, 70, 60),
     "cfg1_0p6b": (None, 1, 128, 0),
 }
 
@@ -90,6 +92,7 @@ def test_block_prefill_deterministic(gpu):
 DECODE_CASES = {
     "small": (dict(), [0, 100, 255, 37], 256),
     "group7": (dict(nq=7, nkv=1), [300, 5], 320),
+    "interleaved_rope": (dict(rope_interleaved=1), [0, 77, 200], 256),
     "cfg_0p6b": (None, [4096, 1000], 4160),
 }
 

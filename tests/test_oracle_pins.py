@@ -117,6 +117,46 @@ def test_rope_dot_product_depends_on_relative_position_only():
     assert abs(d1 - d2) < 1e-10 and abs(d1 - d3) < 1e-10
 
 
+def test_rope_interleaved_rotates_adjacent_planes():
+    # Interleaved pairing (the complex-number form): a unit vector on dim 2i moves only
+    # within the plane (2i, 2i + 1), by pos * theta_i with the same frequency ladder.
+    hd, base, pos = 128, 1e6, 11
+    for i in (0, 1, 31, 63):
+        ang = pos * base ** (-2.0 * i / hd)
+        e = np.zeros((1, hd))
+        e[0, 2 * i] = 1.0
+        want = np.zeros(hd)
+        want[2 * i], want[2 * i + 1] = math.cos(ang), math.sin(ang)
+        np.testing.assert_allclose(oracle.rope(e, pos, base, interleaved=True)[0], want,
+                                   atol=1e-15)
+        e2 = np.zeros((1, hd))
+        e2[0, 2 * i + 1] = 1.0
+        want2 = np.zeros(hd)
+        want2[2 * i], want2[2 * i + 1] = -math.sin(ang), math.cos(ang)
+        np.testing.assert_allclose(oracle.rope(e2, pos, base, interleaved=True)[0], want2,
+                                   atol=1e-15)
+
+
+def test_rope_interleaved_is_rotate_half_under_a_dim_permutation():
+    # Moving dims (2i, 2i + 1) to (i, i + 64) turns one pairing into the other, so both
+    # compute the same rotation of the same planes; identity at 0, composition and the
+    # relative-position property carry over.
+    hd = 128
+    perm = np.empty(hd, dtype=np.int64)  # perm[rotate-half index] = interleaved index
+    perm[:64] = np.arange(0, hd, 2)
+    perm[64:] = np.arange(1, hd, 2)
+    x = rng.standard_normal((5, hd))
+    for pos in (0, 1, 777, 40000):
+        yi = oracle.rope(x, pos, 1e6, interleaved=True)
+        yh = oracle.rope(x[:, perm], pos, 1e6)
+        np.testing.assert_allclose(yi[:, perm], yh, atol=1e-13)
+    np.testing.assert_array_equal(oracle.rope(x, 0, 1e6, interleaved=True), x)
+    q, k = rng.standard_normal((1, hd)), rng.standard_normal((1, hd))
+    d1 = (oracle.rope(q, 10, 1e6, True) @ oracle.rope(k, 3, 1e6, True).T).item()
+    d2 = (oracle.rope(q, 2010, 1e6, True) @ oracle.rope(k, 2003, 1e6, True).T).item()
+    assert abs(d1 - d2) < 1e-10
+
+
 # ---------------------------------------------------------------- attention
 
 def _onehot_values(L, nkv, hd):
