@@ -260,6 +260,45 @@ def wl_decode(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown):
     return out
 
 
+def wl_generate(torch, q3, recipes, synth, dev, steps, warmup, timer, sampled):
+    """Generation on the device: a 512-token prompt per sequence, then 64 new tokens each
+    (prefill + 63 decode steps inside one qwen3_generate call), greedy or sampled."""
+    cfg = dict(recipes.QWEN3_0P6B)
+    B, S, n_new = 64, 512, 64
+    cap = ((S + n_new - 1 + 63) // 64) * 64
+    model, mw, keep, rope, caches = setup_stack(torch, q3, recipes, dev, cfg, B, S, cap,
+                                                recipes.MODEL_SEED_0P6B, 4)
+    kvs = [q3.make_kv_layer(k, vt, cap) for k, vt in caches]
+    ids = torch.empty((B, S), dtype=torch.int32, device=dev)
+    synth.uniform_i32_device(ids, 4, "input.ids", 0, cfg["vocab_size"])
+    out = torch.empty((B, n_new), dtype=torch.int32, device=dev)
+    ws = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_GENERATE, B, S),
+                     dtype=torch.uint8, device=dev)
+    T, top_p, uni = 0.0, 1.0, None
+    if sampled:
+        T, top_p = 0.8, 0.95
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(4)
+        uni = torch.rand((n_new, B), generator=gen, device=dev, dtype=torch.float32)
+
+    def step():
+        q3.qwen3_generate(cfg, mw, rope, ids, B, S, n_new, kvs, out, ws, temperature=T,
+                          top_p=top_p, uniforms=uni)
+
+    ms, _ = timer.run(step, steps, warmup)
+    name = "generate_0p6b" + ("_sampled" if sampled else "_greedy")
+    res = {"name": name, "tokens_per_s": B * n_new / (ms * 1e-3), "ms_per_step": ms,
+           "config": {"workload": name, "batch": B, "prompt": S, "new_tokens_per_seq": n_new,
+                      "layers": cfg["num_hidden_layers"],
+                      "selection": (f"sampled (temperature {T}, top_p {top_p})" if sampled
+                                    else "greedy")},
+           "note": "tokens_per_s counts generated tokens; ms_per_step is one whole generation "
+                   "(prompt prefill + 63 decode steps)"}
+    del caches, kvs, model, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def decode_step_bytes(cfg, B, ctx):
     H, nq, nkv, hd, I, L, V = (cfg["hidden_size"], cfg["num_attention_heads"],
                                cfg["num_key_value_heads"], cfg["head_dim"],
@@ -389,7 +428,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="prefill,decode,moe,block7b,block7b_irope,block")
+    ap.add_argument("--workloads",
+                    default="prefill,decode,moe,block7b,block7b_irope,block,generate,"
+                            "generate_sampled")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=512,
                     help="prefix length for the oracle CPU baseline (0 = skip)")
@@ -431,7 +472,10 @@ def main():
                                              max(2, args.steps // 3), 1, timer, bd, True,
                                              rope_interleaved=1),
            "block": lambda: wl_block(torch, q3, recipes, synth, dev, 10 * args.steps,
-                                     args.warmup, timer, bd, False)}
+                                     args.warmup, timer, bd, False),
+           "generate": lambda: wl_generate(torch, q3, recipes, synth, dev, 3, 1, timer, False),
+           "generate_sampled": lambda: wl_generate(torch, q3, recipes, synth, dev, 3, 1, timer,
+                                                   True)}
     for w in wls:
         log(f"workload {w} ...")
         t0 = time.time()
@@ -446,7 +490,7 @@ def main():
             "ms_per_step": round(m["ms_per_step"], 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "f16",
             "data": "synthetic (seeded counter-based generator, random-init weights)",
-            "config": m["config"], "roofline": m["roofline"]}
+            "config": m["config"], "roofline": m.get("roofline")}
     if "decode" in results:
         line["decode_tokens_per_s"] = round(results["decode"]["tokens_per_s"], 1)
     if args.cpu_tokens > 0 and main_wl == "prefill":

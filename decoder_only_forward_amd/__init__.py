@@ -26,13 +26,14 @@ QWEN3_OP_BLOCK_DECODE = 2
 QWEN3_OP_MOE_FFN = 3
 QWEN3_OP_STACK_PREFILL = 4
 QWEN3_OP_STACK_DECODE = 5
+QWEN3_OP_GENERATE = 6
 
 QWEN3_LOGITS_NONE = 0
 QWEN3_LOGITS_ALL = 1
 QWEN3_LOGITS_LAST = 2
 
 EXPORTS = ("qwen3_workspace_bytes", "qwen3_rope_table_init", "qwen3_block_prefill",
-           "qwen3_block_decode", "qwen3_moe_ffn", "qwen3_stack_forward",
+           "qwen3_block_decode", "qwen3_moe_ffn", "qwen3_stack_forward", "qwen3_generate",
            "qwen3_status_string", "qwen3_last_error", "qwen3_profile_begin",
            "qwen3_profile_end")
 
@@ -95,6 +96,9 @@ def lib():
         L.qwen3_stack_forward.restype = ctypes.c_int
         L.qwen3_stack_forward.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, i32, vp, vp,
                                           sz, vp]
+        L.qwen3_generate.restype = ctypes.c_int
+        L.qwen3_generate.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, ctypes.c_float,
+                                     ctypes.c_float, vp, vp, vp, sz, vp]
         L.qwen3_status_string.restype = ctypes.c_char_p
         L.qwen3_status_string.argtypes = [ctypes.c_int]
         L.qwen3_last_error.restype = ctypes.c_char_p
@@ -228,6 +232,18 @@ def qwen3_stack_forward(cfg, w, rope, ids, batch, seq_len, pos0, pos, caches, lo
                                      _ptr(ids), batch, seq_len, pos0, _ptr(pos), arr,
                                      _ptr(logits), logits_mode, _ptr(next_ids), wp, wb,
                                      _stream(stream)))
+
+
+def qwen3_generate(cfg, w, rope, prompt_ids, batch, prompt_len, n_new, caches, out_ids,
+                   workspace, temperature=0.0, top_p=1.0, uniforms=None, stream=None):
+    """caches: list of KVLayer (one per layer); out_ids: device int32 [batch][n_new];
+    uniforms: device float32 [n_new][batch] when temperature > 0."""
+    arr = (KVLayer * len(caches))(*caches)
+    wp, wb = _ws(workspace)
+    _check(lib().qwen3_generate(ctypes.byref(_cfg(cfg)), ctypes.byref(w), _ptr(rope),
+                                _ptr(prompt_ids), batch, prompt_len, n_new, arr,
+                                float(temperature), float(top_p), _ptr(uniforms),
+                                _ptr(out_ids), wp, wb, _stream(stream)))
 
 
 def qwen3_profile_begin(tag, max_launches):

@@ -8,7 +8,7 @@ CSRC = os.path.join(HERE, "csrc")
 SO = os.path.join(HERE, "libqwen3.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["gemm.hip", "norm_rope.hip", "attention.hip", "argmax.hip", "moe.hip",
+SOURCES = ["gemm.hip", "norm_rope.hip", "attention.hip", "argmax.hip", "sample.hip", "moe.hip",
            "qwen3_api.cpp"]
 
 # Per-source extras.  attention.hip: its softmax takes maxima of MFMA results, which are

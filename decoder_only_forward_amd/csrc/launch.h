@@ -97,6 +97,15 @@ hipError_t attn_decode_combine(const AttnDecodeArgs& a, hipStream_t s);
 hipError_t argmax_rows(const float* logits, int64_t row_stride, int rows, int V, int32_t* out,
                        float* part_val, int32_t* part_idx, int chunks, hipStream_t s);
 
+// ---- sampling and generation bookkeeping (sample.hip)
+// temperature > 0, top_p in (0, 1]; u: device [rows] uniforms in [0, 1)
+hipError_t sample_rows(const float* logits, int64_t row_stride, int rows, int V,
+                       float temperature, float top_p, const float* u, int32_t* out,
+                       hipStream_t s);
+// out_ids[b][col] = ids[b] (out_ids [B][n_new]); pos[b] = next_pos
+hipError_t gen_feed(const int32_t* ids, int32_t* out_ids, int n_new, int col, int32_t* pos,
+                    int next_pos, int B, hipStream_t s);
+
 // ---- MoE (moe.hip)
 struct MoeRouteArgs {
   const float* logits;  // [T][E]

@@ -132,6 +132,26 @@ DenseLayout dense_layout(const qwen3_config* c, int op, int B, int S, int cap_hi
   return L;
 }
 
+// Generation workspace: per-step buffers, then one region shared by the prefill and the
+// decode steps of the stack.
+struct GenLayout {
+  size_t logits, ids, pos, stack, total;
+  DenseLayout prefill, decode;
+};
+
+GenLayout gen_layout(const qwen3_config* c, int B, int S, int cap) {
+  GenLayout G{};
+  Bump b;
+  G.logits = b.take((size_t)B * c->vocab_size * 4);
+  G.ids = b.take((size_t)B * 4);
+  G.pos = b.take((size_t)B * 4);
+  G.stack = b.off;
+  G.prefill = dense_layout(c, QWEN3_OP_STACK_PREFILL, B, S, cap);
+  G.decode = dense_layout(c, QWEN3_OP_STACK_DECODE, B, 1, cap);
+  G.total = G.stack + std::max(G.prefill.total, G.decode.total);
+  return G;
+}
+
 struct MoeLayout {
   size_t logits, idx, w, chunk_counts, counts, offsets, perm, inv, tile_e, tile_r, tile_n, act,
       yrows;
@@ -471,6 +491,12 @@ size_t qwen3_workspace_bytes(const qwen3_config* c, int32_t op, int32_t batch, i
     return moe_layout(c, batch).total;
   }
   if (check_dense_cfg(c) != QWEN3_OK) return 0;
+  if (op == QWEN3_OP_GENERATE) {
+    if (seq_len <= 0) { fail(QWEN3_EINVAL, "seq_len=%d", seq_len); return 0; }
+    if (c->vocab_size <= 0) { fail(QWEN3_EINVAL, "vocab_size=%d", c->vocab_size); return 0; }
+    int cap = ((c->max_position_embeddings + 63) / 64) * 64;
+    return gen_layout(c, batch, seq_len, cap).total;
+  }
   if (op == QWEN3_OP_BLOCK_DECODE || op == QWEN3_OP_STACK_DECODE) {
     // decode partials scale with the cache capacity; size for max_position_embeddings
     int cap = ((c->max_position_embeddings + 63) / 64) * 64;
@@ -552,12 +578,13 @@ int qwen3_block_decode(const qwen3_config* c, const qwen3_layer_weights* w, cons
   return run_layer(c, w, rope, cache, io, (char*)workspace, L, (hipStream_t)stream);
 }
 
-int qwen3_stack_forward(const qwen3_config* c, const qwen3_model_weights* w, const float* rope,
-                        const int32_t* ids, int32_t batch, int32_t seq_len, int32_t pos0,
-                        const int32_t* pos, const qwen3_kv_layer* caches, float* logits,
-                        int32_t logits_mode, int32_t* next_ids, void* workspace,
-                        size_t workspace_bytes, void* stream) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+
+// Model-level argument checks shared by the stack forward and generation.
+int check_stack(const qwen3_config* c, const qwen3_model_weights* w, const float* rope,
+                const qwen3_kv_layer* caches) {
   TRY(check_dense_cfg(c));
   if (!w) return fail(QWEN3_EINVAL, "model weights are NULL");
   if (c->num_hidden_layers <= 0 || !w->layers)
@@ -572,30 +599,22 @@ int qwen3_stack_forward(const qwen3_config* c, const qwen3_model_weights* w, con
     if (rc) return fail(rc, "layer %d: %s", l, g_err.c_str());
   }
   REQ_PTR(rope, "rope");
-  if (!ids) return fail(QWEN3_EINVAL, "ids is NULL");
-  if (batch <= 0 || seq_len <= 0)
-    return fail(QWEN3_EINVAL, "batch=%d seq_len=%d must be positive", batch, seq_len);
-  if (logits_mode != QWEN3_LOGITS_NONE && logits_mode != QWEN3_LOGITS_ALL &&
-      logits_mode != QWEN3_LOGITS_LAST)
-    return fail(QWEN3_EINVAL, "logits_mode=%d", logits_mode);
-  if (logits_mode != QWEN3_LOGITS_NONE) REQ_PTR(logits, "logits");
   if (!caches) return fail(QWEN3_EINVAL, "caches is NULL");
-  const bool decode = seq_len == 1 && pos != nullptr;
   for (int l = 0; l < c->num_hidden_layers; ++l) {
     TRY(check_cache(c, &caches[l], "caches[l]"));
-    if (!decode) TRY(check_range(c, &caches[l], pos0, seq_len));
-  }
-  const int op = decode ? QWEN3_OP_STACK_DECODE : QWEN3_OP_STACK_PREFILL;
-  DenseLayout L = dense_layout(c, op, batch, seq_len, caches[0].capacity);
-  for (int l = 1; l < c->num_hidden_layers; ++l)
     if (caches[l].capacity != caches[0].capacity)
       return fail(QWEN3_EINVAL, "all layers' caches must share one capacity");
-  if (!aligned16(workspace) || workspace_bytes < L.total)
-    return fail(QWEN3_EWORKSPACE, "workspace needs %zu bytes (got %zu)", L.total,
-                workspace_bytes);
+  }
+  return QWEN3_OK;
+}
 
-  hipStream_t s = (hipStream_t)stream;
-  char* ws = (char*)workspace;
+// Embedding, the layers, final norm, LM head and optional argmax (arguments checked).
+int stack_run(const qwen3_config* c, const qwen3_model_weights* w, const float* rope,
+              const int32_t* ids, int32_t batch, int32_t seq_len, int32_t pos0,
+              const int32_t* pos, const qwen3_kv_layer* caches, float* logits,
+              int32_t logits_mode, int32_t* next_ids, char* ws, const DenseLayout& L,
+              hipStream_t s) {
+  const bool decode = seq_len == 1 && pos != nullptr;
   const int H = c->hidden_size, V = c->vocab_size, T = L.T;
   float* res = (float*)(ws + L.res);
   CHECK_HIP(embed_gather(ids, (const bf16_t*)w->embed_tokens, res, T, H, V, s));
@@ -646,6 +665,86 @@ int qwen3_stack_forward(const qwen3_config* c, const qwen3_model_weights* w, con
     ProfScope ps("argmax", s);
     CHECK_HIP(argmax_rows(last, stride, batch, V, next_ids, (float*)(ws + L.am_val),
                           (int32_t*)(ws + L.am_idx), L.am_chunks, s));
+  }
+  return QWEN3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qwen3_stack_forward(const qwen3_config* c, const qwen3_model_weights* w, const float* rope,
+                        const int32_t* ids, int32_t batch, int32_t seq_len, int32_t pos0,
+                        const int32_t* pos, const qwen3_kv_layer* caches, float* logits,
+                        int32_t logits_mode, int32_t* next_ids, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  TRY(check_stack(c, w, rope, caches));
+  if (!ids) return fail(QWEN3_EINVAL, "ids is NULL");
+  if (batch <= 0 || seq_len <= 0)
+    return fail(QWEN3_EINVAL, "batch=%d seq_len=%d must be positive", batch, seq_len);
+  if (logits_mode != QWEN3_LOGITS_NONE && logits_mode != QWEN3_LOGITS_ALL &&
+      logits_mode != QWEN3_LOGITS_LAST)
+    return fail(QWEN3_EINVAL, "logits_mode=%d", logits_mode);
+  if (logits_mode != QWEN3_LOGITS_NONE) REQ_PTR(logits, "logits");
+  const bool decode = seq_len == 1 && pos != nullptr;
+  if (!decode)
+    for (int l = 0; l < c->num_hidden_layers; ++l) TRY(check_range(c, &caches[l], pos0, seq_len));
+  const int op = decode ? QWEN3_OP_STACK_DECODE : QWEN3_OP_STACK_PREFILL;
+  DenseLayout L = dense_layout(c, op, batch, seq_len, caches[0].capacity);
+  if (!aligned16(workspace) || workspace_bytes < L.total)
+    return fail(QWEN3_EWORKSPACE, "workspace needs %zu bytes (got %zu)", L.total,
+                workspace_bytes);
+  return stack_run(c, w, rope, ids, batch, seq_len, pos0, pos, caches, logits, logits_mode,
+                   next_ids, (char*)workspace, L, (hipStream_t)stream);
+}
+
+int qwen3_generate(const qwen3_config* c, const qwen3_model_weights* w, const float* rope,
+                   const int32_t* prompt_ids, int32_t batch, int32_t prompt_len, int32_t n_new,
+                   const qwen3_kv_layer* caches, float temperature, float top_p,
+                   const float* uniforms, int32_t* out_ids, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  TRY(check_stack(c, w, rope, caches));
+  if (!prompt_ids) return fail(QWEN3_EINVAL, "prompt_ids is NULL");
+  if (!out_ids) return fail(QWEN3_EINVAL, "out_ids is NULL");
+  if (batch <= 0 || prompt_len <= 0 || n_new <= 0)
+    return fail(QWEN3_EINVAL, "batch=%d prompt_len=%d n_new=%d must be positive", batch,
+                prompt_len, n_new);
+  const bool sampling = temperature != 0.f;
+  if (sampling) {
+    if (!(temperature > 0.f)) return fail(QWEN3_EINVAL, "temperature must be >= 0");
+    if (!(top_p > 0.f && top_p <= 1.f)) return fail(QWEN3_EINVAL, "top_p must be in (0, 1]");
+    if (!uniforms) return fail(QWEN3_EINVAL, "uniforms is NULL (needed when temperature > 0)");
+  }
+  // the prompt and every generated token but the last take a cache position
+  for (int l = 0; l < c->num_hidden_layers; ++l)
+    TRY(check_range(c, &caches[l], 0, prompt_len + n_new - 1));
+  const GenLayout G = gen_layout(c, batch, prompt_len, caches[0].capacity);
+  if (!aligned16(workspace) || workspace_bytes < G.total)
+    return fail(QWEN3_EWORKSPACE, "workspace needs %zu bytes (got %zu)", G.total,
+                workspace_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* logits = (float*)(ws + G.logits);
+  int32_t* ids = (int32_t*)(ws + G.ids);
+  int32_t* pos = (int32_t*)(ws + G.pos);
+  char* sws = ws + G.stack;
+  const int V = c->vocab_size;
+  for (int i = 0; i < n_new; ++i) {
+    // step 0: prefill of the prompt; step i: decode of token i - 1 at prompt_len + i - 1
+    if (i == 0)
+      TRY(stack_run(c, w, rope, prompt_ids, batch, prompt_len, 0, nullptr, caches, logits,
+                    QWEN3_LOGITS_LAST, sampling ? nullptr : ids, sws, G.prefill, s));
+    else
+      TRY(stack_run(c, w, rope, ids, batch, 1, 0, pos, caches, logits, QWEN3_LOGITS_LAST,
+                    sampling ? nullptr : ids, sws, G.decode, s));
+    if (sampling) {
+      ProfScope ps("sample", s);
+      CHECK_HIP(sample_rows(logits, V, batch, V, temperature, top_p,
+                            uniforms + (int64_t)i * batch, ids, s));
+    }
+    CHECK_HIP(gen_feed(ids, out_ids, n_new, i, pos, prompt_len + i, batch, s));
   }
   return QWEN3_OK;
 }

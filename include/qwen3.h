@@ -122,6 +122,7 @@ typedef struct qwen3_kv_layer {
 #define QWEN3_OP_MOE_FFN 3
 #define QWEN3_OP_STACK_PREFILL 4
 #define QWEN3_OP_STACK_DECODE 5
+#define QWEN3_OP_GENERATE 6 /* qwen3_generate: batch, seq_len = prompt length */
 
 /* Logits selection for qwen3_stack_forward. */
 #define QWEN3_LOGITS_NONE 0 /* no logits (next_ids still allowed) */
@@ -199,11 +200,35 @@ int qwen3_stack_forward(const qwen3_config *cfg, const qwen3_model_weights *w,
                         float *logits, int32_t logits_mode, int32_t *next_ids, void *workspace,
                         size_t workspace_bytes, void *stream);
 
+/* Generation on the device (the pages' generation loops, [P3] and [P4]; [P1] section 13):
+ * a prefill of prompt_ids [batch][prompt_len] (device int32, positions 0..prompt_len-1)
+ * picks token 0 of each sequence from its last-position logits; then n_new - 1 decode steps
+ * each feed the previous token back at position prompt_len + i - 1 and pick token i.
+ * All steps run on `stream` without host synchronisation.
+ *   temperature == 0: greedy, the largest logit, lowest index on ties (uniforms unused).
+ *   temperature > 0: e_v = exp((l_v - max) / temperature); the nucleus keeps every token with
+ *     e_v >= tau, tau the largest value whose kept mass reaches top_p (in (0, 1]) of the
+ *     total; r = u * kept mass; the token is the smallest index v whose running kept mass
+ *     over tokens <= v exceeds r.  uniforms: device float [n_new][batch] in [0, 1), the
+ *     caller's random numbers (u for step i, sequence b at uniforms[i * batch + b]).
+ *   caches: HOST array [L] of per-layer caches (one capacity, >= prompt_len + n_new - 1,
+ *     <= max_position_embeddings); positions 0 .. prompt_len + n_new - 2 are written.
+ *   out_ids: device int32 [batch][n_new].
+ *   workspace: qwen3_workspace_bytes(cfg, QWEN3_OP_GENERATE, batch, prompt_len) bytes.
+ * Errors as for qwen3_stack_forward; EINVAL for temperature < 0, top_p outside (0, 1] or
+ * missing uniforms when sampling. */
+int qwen3_generate(const qwen3_config *cfg, const qwen3_model_weights *w, const float *rope,
+                   const int32_t *prompt_ids, int32_t batch, int32_t prompt_len, int32_t n_new,
+                   const qwen3_kv_layer *caches, float temperature, float top_p,
+                   const float *uniforms, int32_t *out_ids, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
 /* Opt-in kernel timing for measurement tools.  qwen3_profile_begin(tag, n) makes the
  * next (up to n) launches of the kernel class `tag` record a pair of HIP events on their
  * launch stream (tags: "qkv_gemm", "qk_norm_rope_cache", "attn_prefill", "attn_decode",
  * "attn_decode_combine", "o_proj_gemm", "gate_up_gemm", "down_gemm", "lm_head_gemm", "argmax",
- * "moe_router_gemm", "moe_route", "moe_gate_up_gemm", "moe_down_gemm", "moe_combine").
+ * "moe_router_gemm", "moe_route", "moe_gate_up_gemm", "moe_down_gemm", "moe_combine",
+ * "sample").
  * It creates 2n host-side event objects once (not on the forward path).
  * qwen3_profile_end() stops recording; after the caller has synchronised the stream it
  * returns the summed duration (ms) and the number of timed launches. */

@@ -264,6 +264,69 @@ def permute(idx, E):
     return counts, offsets, perm, inv
 
 
+def sample(logits, temperature, top_p, u):
+    """One draw per row by the sampling rule of the generation loops ([P3] generation and
+    [P4] sampling sections: softmax of logits / temperature, optionally cut to the top-p
+    nucleus, then a multinomial draw), made exact so that two implementations agree:
+      e_v = exp((l_v - max) / temperature), non-finite logits give e_v = 0;
+      sort e descending (ties by index); the nucleus is cut at the first sorted entry where
+      the running sum reaches top_p * sum(e), and every e_v >= that entry's value is kept
+      (top_p >= 1 keeps every e_v > 0);
+      K = kept mass; r = u K; the token is the smallest index v whose running kept mass over
+      tokens <= v (ascending index order) exceeds r, else the last kept index.
+    logits [rows, V] (or [V]); u [rows] in [0, 1).  Returns (tokens int32 [rows], details),
+    details per row: dict(e, tau, kept, K, r, cum) for tolerance checks."""
+    lg = np.asarray(logits, dtype=np.float64)
+    if lg.ndim == 1:
+        lg = lg[None]
+    u = np.broadcast_to(np.asarray(u, dtype=np.float64), (lg.shape[0],))
+    toks = np.empty((lg.shape[0],), np.int32)
+    details = []
+    for r_i in range(lg.shape[0]):
+        l = lg[r_i]
+        fin = np.isfinite(l)
+        if not fin.any():
+            toks[r_i] = 0
+            details.append(None)
+            continue
+        m = l[fin].max()
+        e = np.zeros_like(l)
+        e[fin] = np.exp((l[fin] - m) / temperature)
+        if top_p < 1.0:
+            order = np.argsort(-e, kind="stable")
+            cs = np.cumsum(e[order])
+            k = int(np.argmax(cs >= top_p * e.sum()))
+            tau = e[order[k]]
+        else:
+            tau = e[e > 0].min()
+        kept = (e >= tau) & (e > 0)
+        K = e[kept].sum()
+        r = min(max(float(u[r_i]), 0.0), 1.0) * K
+        cum = np.cumsum(np.where(kept, e, 0.0))
+        hit = np.nonzero(kept & (cum > r))[0]
+        toks[r_i] = hit[0] if hit.size else np.nonzero(kept)[0][-1]
+        details.append(dict(e=e, tau=tau, kept=kept, K=K, r=r, cum=cum))
+    return toks, details
+
+
+def generate(cfg, model, prompt, n_new, temperature=0.0, top_p=1.0, uniforms=None):
+    """Generation by full recompute, as in the pages' generation loops ([P1] section 13,
+    [P3] generation): every step runs the whole model over prompt + tokens so far and takes
+    the last row's logits; greedy (argmax, lowest index on ties) when temperature == 0, else
+    sample() with uniforms[i].  prompt: int sequence.  Returns int32 [n_new]."""
+    seq = [int(t) for t in prompt]
+    out = []
+    for i in range(n_new):
+        lg = stack_prefill(cfg, model, np.array(seq, np.int32), rows=[len(seq) - 1])[0]
+        if temperature == 0.0:
+            t = int(argmax(lg)[0])
+        else:
+            t = int(sample(lg, temperature, top_p, [uniforms[i]])[0][0])
+        out.append(t)
+        seq.append(t)
+    return np.array(out, np.int32)
+
+
 def argmax(logits):
     lg = np.asarray(logits)
     if lg.ndim == 1:

@@ -506,3 +506,49 @@ def test_argmax_ties_go_to_lowest_index():
     lg = np.array([[0.0, 5.0, 5.0, -1.0], [7.0, 7.0, 7.0, 7.0]], np.float32)
     np.testing.assert_array_equal(oracle.argmax(lg), [1, 0])
     np.testing.assert_array_equal(oracle.argmax(lg.astype(np.float64)), [1, 0])
+
+
+# ---------------------------------------------------------------- sampling
+
+def test_sample_inverse_cdf_on_a_worked_distribution():
+    # logits 0, ln 2, ln 3, -inf at temperature 1: probabilities 1/6, 2/6, 3/6, 0; the
+    # cumulative boundaries in index order are 1, 3, 6 (times 1/6)
+    lg = np.array([0.0, math.log(2.0), math.log(3.0), -np.inf])
+    cases = {0.0: 0, 0.16: 0, 0.17: 1, 0.49: 1, 0.51: 2, 0.99: 2}
+    for u, want in cases.items():
+        assert oracle.sample(lg, 1.0, 1.0, [u])[0][0] == want, u
+
+
+def test_sample_top_p_cut_keeps_ties_and_renormalises():
+    lg = np.log(np.array([1.0, 2.0, 3.0]))
+    # top_p 0.5: the largest entry (3 of 6) already reaches the target -> only token 2
+    for u in (0.0, 0.3, 0.9):
+        assert oracle.sample(lg, 1.0, 0.5, [u])[0][0] == 2
+    # top_p 0.6: target 3.6 needs 3 + 2 -> kept {1, 2}, mass 5, boundaries 2 and 5
+    assert oracle.sample(lg, 1.0, 0.6, [0.39])[0][0] == 1
+    assert oracle.sample(lg, 1.0, 0.6, [0.41])[0][0] == 2
+    # ties at the cut are all kept: e = 2, 2, 1 with top_p 0.4 keeps tokens 0 and 1
+    lt = np.log(np.array([2.0, 2.0, 1.0]))
+    toks = [oracle.sample(lt, 1.0, 0.4, [u])[0][0] for u in np.linspace(0, 0.999, 50)]
+    assert set(toks) == {0, 1}
+
+
+def test_sample_frequencies_match_tempered_probabilities():
+    # a regular grid of u gives each kept token a share equal to its probability
+    lg = rng.standard_normal(40) * 2.0
+    T = 0.7
+    grid = (np.arange(20000) + 0.5) / 20000
+    toks = oracle.sample(np.tile(lg, (len(grid), 1)), T, 1.0, grid)[0]
+    p = np.exp((lg - lg.max()) / T)
+    p /= p.sum()
+    freq = np.bincount(toks, minlength=40) / len(grid)
+    np.testing.assert_allclose(freq, p, atol=2.0 / len(grid) + 1e-12)
+
+
+def test_sample_low_temperature_or_tiny_nucleus_is_greedy():
+    lg = rng.standard_normal((5, 64))
+    g = oracle.argmax(lg)
+    lg[np.arange(5), g] += 1.0  # a clear maximum: at temperature 1e-4 the rest weigh e^-10^4
+    for u in (0.0, 0.5, 0.999):
+        np.testing.assert_array_equal(oracle.sample(lg, 1.0, 1e-9, [u] * 5)[0], g)
+        np.testing.assert_array_equal(oracle.sample(lg, 1e-4, 1.0, [u] * 5)[0], g)
