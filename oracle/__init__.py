@@ -25,15 +25,19 @@ class OracleCfg(ctypes.Structure):
         "hidden", "n_heads", "n_kv_heads", "head_dim", "inter", "n_layers", "vocab", "max_pos")] + [
         ("eps", ctypes.c_double), ("theta", ctypes.c_double), ("qk_norm", ctypes.c_int32),
         ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("moe_inter", ctypes.c_int32),
-        ("norm_topk", ctypes.c_int32), ("rope_interleaved", ctypes.c_int32)]
+        ("norm_topk", ctypes.c_int32), ("rope_interleaved", ctypes.c_int32),
+        ("sparse_step", ctypes.c_int32), ("router_bf16", ctypes.c_int32)]
 
 
 LAYER_FIELDS = ("in_norm", "q", "k", "v", "q_norm", "k_norm", "o", "post_norm", "gate", "up",
                 "down")
 
 
+MOE_LAYER_FIELDS = ("router", "experts_gate_up", "experts_down")
+
+
 class OracleLayer(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_FIELDS]
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_FIELDS + MOE_LAYER_FIELDS]
 
 
 def lib():
@@ -66,7 +70,9 @@ def make_cfg(c):
         qk_norm=int(c.get("qk_norm", 1)), n_experts=c.get("num_experts", 0),
         top_k=c.get("num_experts_per_tok", 0), moe_inter=c.get("moe_intermediate_size", 0),
         norm_topk=int(c.get("norm_topk_prob", 1)),
-        rope_interleaved=int(c.get("rope_interleaved", 0)))
+        rope_interleaved=int(c.get("rope_interleaved", 0)),
+        sparse_step=int(c.get("decoder_sparse_step", 0)),
+        router_bf16=int(c.get("router_weights_bf16", 0)))
 
 
 def _p(a):
@@ -82,9 +88,10 @@ def _u16(a):
 
 
 def make_layer(w):
-    """``w``: dict with keys LAYER_FIELDS -> uint16 arrays.  Returns (struct, keepalive)."""
-    keep = {k: _u16(w[k]) for k in LAYER_FIELDS}
-    return OracleLayer(**{k: keep[k].ctypes.data for k in LAYER_FIELDS}), keep
+    """``w``: dict with keys LAYER_FIELDS (and, for routed layers, MOE_LAYER_FIELDS) ->
+    uint16 arrays.  Returns (struct, keepalive)."""
+    keep = {k: _u16(w[k]) for k in LAYER_FIELDS + MOE_LAYER_FIELDS if w.get(k) is not None}
+    return OracleLayer(**{k: keep[k].ctypes.data for k in keep}), keep
 
 
 def rmsnorm_rows(x, w, eps):
@@ -141,8 +148,9 @@ def swiglu_ffn(x, gate, up, down):
     return y
 
 
-def block(cfg, layer, x, pos0=0, past_k=None, past_v=None, rows=None):
+def block(cfg, layer, x, pos0=0, past_k=None, past_v=None, rows=None, routed=False):
     """One decoder block on one sequence.  x [S, H] (float); past_k/v [nkv, pos0, hd].
+    routed: the FFN is the layer's routed MoE.
     Returns (x_out [len(rows) or S, H], new_k [nkv, S, hd], new_v)."""
     c = make_cfg(cfg)
     lw, keep = make_layer(layer)
@@ -161,7 +169,7 @@ def block(cfg, layer, x, pos0=0, past_k=None, past_v=None, rows=None):
     nv = np.empty((nkv, S, hd), dtype=np.float64)
     lib().oracle_block(ctypes.byref(c), ctypes.byref(lw), _p(x), ctypes.c_int64(S),
                        ctypes.c_int64(pos0), _p(pk), _p(pv), _p(rows), ctypes.c_int64(nr), _p(out),
-                       _p(nk), _p(nv))
+                       _p(nk), _p(nv), int(routed), ctypes.c_void_p(0))
     return out, nk, nv
 
 
@@ -175,9 +183,10 @@ def _layers(model):
     return arr, keep
 
 
-def stack_prefill(cfg, model, ids, rows=None, want_kv=False):
+def stack_prefill(cfg, model, ids, rows=None, want_kv=False, want_router=False):
     """Whole model on one sequence from position 0.  model: dict(embed, norm, lm_head or None,
-    layers=[layer dicts]).  Returns logits [len(rows), V] (and per-layer k, v when asked)."""
+    layers=[layer dicts]).  Returns logits [len(rows), V] (and per-layer k, v when asked;
+    with want_router also the routed layers' router logits [L, S, E], NaN elsewhere)."""
     c = make_cfg(cfg)
     arr, keep = _layers(model)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
@@ -190,15 +199,20 @@ def stack_prefill(cfg, model, ids, rows=None, want_kv=False):
     if want_kv:
         ko = np.empty((c.n_layers, c.n_kv_heads, S, c.head_dim), dtype=np.float64)
         vo = np.empty_like(ko)
+    ro = np.full((c.n_layers, S, c.n_experts), np.nan) if want_router else None
     lib().oracle_stack_prefill(ctypes.byref(c), _p(embed), _p(norm), _p(head), arr, _p(ids),
                                ctypes.c_int64(S), _p(rows), ctypes.c_int64(len(rows)), _p(logits),
-                               _p(ko), _p(vo))
-    return (logits, ko, vo) if want_kv else logits
+                               _p(ko), _p(vo), _p(ro))
+    out = (logits, ko, vo) if want_kv else (logits,)
+    if want_router:
+        out = out + (ro,)
+    return out if len(out) > 1 else out[0]
 
 
-def stack_decode(cfg, model, token_id, pos, cache_k, cache_v):
+def stack_decode(cfg, model, token_id, pos, cache_k, cache_v, want_router=False):
     """One decode step of one sequence.  cache_k/v: per-layer arrays [nkv, pos, hd], either
-    uint16 (bf16 bits) or float64.  Returns logits [V]."""
+    uint16 (bf16 bits) or float64.  Returns logits [V] (and, with want_router, the routed
+    layers' router logits [L, E], NaN elsewhere)."""
     c = make_cfg(cfg)
     arr, keep = _layers(model)
     embed, norm = _u16(model["embed"]), _u16(model["norm"])
@@ -211,11 +225,12 @@ def stack_decode(cfg, model, token_id, pos, cache_k, cache_v):
     pv = (ctypes.c_void_p * L)(*[a.ctypes.data for a in cv])
     null = ctypes.c_void_p(0)
     logits = np.empty((c.vocab,), dtype=np.float64)
+    ro = np.full((L, c.n_experts), np.nan) if want_router else None
     lib().oracle_stack_decode(ctypes.byref(c), _p(embed), _p(norm), _p(head), arr,
                               ctypes.c_int32(int(token_id)), ctypes.c_int64(pos),
                               null if f64 else pk, null if f64 else pv,
-                              pk if f64 else null, pv if f64 else null, _p(logits))
-    return logits
+                              pk if f64 else null, pv if f64 else null, _p(logits), _p(ro))
+    return (logits, ro) if want_router else logits
 
 
 def moe_ffn(cfg, router, gate_up, down, x):
@@ -325,6 +340,14 @@ def generate(cfg, model, prompt, n_new, temperature=0.0, top_p=1.0, uniforms=Non
         out.append(t)
         seq.append(t)
     return np.array(out, np.int32)
+
+
+def bf16_round(x):
+    """fp32 values rounded to bf16 (round to nearest, ties to even), returned as float64."""
+    a = np.atleast_1d(np.asarray(x, dtype=np.float32))
+    lib().oracle_bf16_round.restype = ctypes.c_float
+    lib().oracle_bf16_round.argtypes = [ctypes.c_float]
+    return np.array([lib().oracle_bf16_round(float(v)) for v in a], dtype=np.float64)
 
 
 def argmax(logits):

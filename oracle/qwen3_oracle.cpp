@@ -87,6 +87,21 @@ void rope_vec(const double *x, int hd, int64_t pos, double theta, int interleave
   }
 }
 
+// fp32 -> bf16 -> fp32 with round-to-nearest-even: keep the top 16 bits of the fp32
+// pattern, rounding on the dropped 16 (a NaN stays a NaN).
+float bf16_round_impl(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, 4);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return x;
+  const uint32_t dropped = u & 0xffffu, keep = u & 0xffff0000u;
+  const uint32_t half = 0x8000u;
+  uint32_t r = keep;
+  if (dropped > half || (dropped == half && (keep & 0x10000u))) r += 0x10000u;
+  float y;
+  std::memcpy(&y, &r, 4);
+  return y;
+}
+
 // silu(z) = z / (1 + e^-z) ([P3] "SwiGLU FFN"; [P1] section 11).
 inline double silu(double z) { return z / (1.0 + std::exp(-z)); }
 
@@ -173,6 +188,10 @@ void oracle_swiglu_ffn(const double *x, int64_t T, int H, int I, const uint16_t 
   });
 }
 
+static void moe_row(const oracle_cfg *c, const uint16_t *router, const uint16_t *gate_up,
+                    const uint16_t *down, const double *xt, double *y, int32_t *idx, double *w,
+                    double *r);
+
 // One pre-norm decoder block for one sequence ([P3] "TransformerBlock" and
 // "GQA 注意力"; [P4] decoder layer):
 //   n  = rmsnorm(x, in_norm)
@@ -181,12 +200,15 @@ void oracle_swiglu_ffn(const double *x, int64_t T, int H, int I, const uint16_t 
 //           absolute position pos0 + s (the offset is the cached length)
 //   keys/values = past cache (positions < pos0) followed by the new k, v
 //   h1 = x + attention(q, keys, values) Wo^T
-//   h2 = h1 + swiglu(rmsnorm(h1, post_norm))
+//   h2 = h1 + swiglu(rmsnorm(h1, post_norm))   (routed: h1 + moe(rmsnorm(h1, post_norm)))
 // rows != NULL restricts the attention/FFN outputs to those token rows (the K/V
-// of every row are still produced, as every later row needs them).
+// of every row are still produced, as every later row needs them).  routed selects the
+// routed MoE FFN ([P1] section 11, [P3] "MoE") with the layer's router and experts;
+// router_logits (nullable) then receives each output row's router logits [n_rows][E].
 void oracle_block(const oracle_cfg *c, const oracle_layer *w, const double *x, int64_t S,
                   int64_t pos0, const double *past_k, const double *past_v, const int64_t *rows,
-                  int64_t n_rows, double *x_out, double *new_k, double *new_v) {
+                  int64_t n_rows, double *x_out, double *new_k, double *new_v, int routed,
+                  double *router_logits) {
   const int H = c->hidden, nq = c->n_heads, nkv = c->n_kv_heads, hd = c->head_dim;
   const int64_t L = pos0 + S;
   std::vector<int64_t> all;
@@ -250,10 +272,19 @@ void oracle_block(const oracle_cfg *c, const oracle_layer *w, const double *x, i
     linear_row(o.data(), w->o, H, (int64_t)nq * hd, h1.data());
     for (int i = 0; i < H; ++i) h1[i] += x[s * H + i];
     rmsnorm_vec(h1.data(), H, w->post_norm, c->eps, n2.data());
-    linear_row(n2.data(), w->gate, I, H, gg.data());
-    linear_row(n2.data(), w->up, I, H, uu.data());
-    for (int i = 0; i < I; ++i) gg[i] = silu(gg[i]) * uu[i];
-    linear_row(gg.data(), w->down, H, I, y.data());
+    if (routed) {
+      const int E = c->n_experts, k = c->top_k;
+      std::vector<int32_t> idx(k);
+      std::vector<double> wt(k), r(E);
+      moe_row(c, w->router, w->experts_gate_up, w->experts_down, n2.data(), y.data(),
+              idx.data(), wt.data(), r.data());
+      if (router_logits) std::copy(r.begin(), r.end(), router_logits + ri * E);
+    } else {
+      linear_row(n2.data(), w->gate, I, H, gg.data());
+      linear_row(n2.data(), w->up, I, H, uu.data());
+      for (int i = 0; i < I; ++i) gg[i] = silu(gg[i]) * uu[i];
+      linear_row(gg.data(), w->down, H, I, y.data());
+    }
     for (int i = 0; i < H; ++i) x_out[ri * H + i] = h1[i] + y[i];
   });
 }
@@ -262,11 +293,18 @@ void oracle_block(const oracle_cfg *c, const oracle_layer *w, const double *x, i
 // [P1] sections 12-13): embedding lookup, every block in order, final RMSNorm,
 // LM head (lm_head == NULL means tied: the embedding matrix is reused).
 // logits are produced for the requested token rows; k_out / v_out (nullable)
-// receive each layer's new keys / values, layout [layer][nkv][S][hd].
+// receive each layer's new keys / values, layout [layer][nkv][S][hd].  Layer l is routed
+// when the config has experts and (l + 1) % sparse_step == 0 (the Qwen-MoE convention
+// behind [P1]'s decoder_sparse_step); router_out (nullable) receives the routed layers'
+// router logits [layer][S][E].
+static bool routed_layer(const oracle_cfg *c, int l) {
+  return c->n_experts > 0 && c->sparse_step > 0 && (l + 1) % c->sparse_step == 0;
+}
+
 void oracle_stack_prefill(const oracle_cfg *c, const uint16_t *embed, const uint16_t *final_norm,
                           const uint16_t *lm_head, const oracle_layer *layers, const int32_t *ids,
                           int64_t S, const int64_t *rows, int64_t n_rows, double *logits,
-                          double *k_out, double *v_out) {
+                          double *k_out, double *v_out, double *router_out) {
   const int H = c->hidden, nkv = c->n_kv_heads, hd = c->head_dim;
   std::vector<double> x((size_t)S * H), y((size_t)S * H);
   for (int64_t s = 0; s < S; ++s)
@@ -274,7 +312,9 @@ void oracle_stack_prefill(const oracle_cfg *c, const uint16_t *embed, const uint
   for (int l = 0; l < c->n_layers; ++l) {
     double *kk = k_out ? k_out + (int64_t)l * nkv * S * hd : nullptr;
     double *vv = v_out ? v_out + (int64_t)l * nkv * S * hd : nullptr;
-    oracle_block(c, &layers[l], x.data(), S, 0, nullptr, nullptr, nullptr, 0, y.data(), kk, vv);
+    double *ro = router_out ? router_out + (int64_t)l * S * c->n_experts : nullptr;
+    oracle_block(c, &layers[l], x.data(), S, 0, nullptr, nullptr, nullptr, 0, y.data(), kk, vv,
+                 routed_layer(c, l), ro);
     x.swap(y);
   }
   const uint16_t *head = lm_head ? lm_head : embed;
@@ -298,7 +338,7 @@ void oracle_stack_decode(const oracle_cfg *c, const uint16_t *embed, const uint1
                          const uint16_t *lm_head, const oracle_layer *layers, int32_t id,
                          int64_t pos, const uint16_t *const *cache_k,
                          const uint16_t *const *cache_v, const double *const *cache_k64,
-                         const double *const *cache_v64, double *logits) {
+                         const double *const *cache_v64, double *logits, double *router_out) {
   const int H = c->hidden, nkv = c->n_kv_heads, hd = c->head_dim;
   std::vector<double> x(H), y(H), pk((size_t)nkv * pos * hd), pv((size_t)nkv * pos * hd);
   for (int i = 0; i < H; ++i) x[i] = bf(embed[(int64_t)id * H + i]);
@@ -308,7 +348,8 @@ void oracle_stack_decode(const oracle_cfg *c, const uint16_t *embed, const uint1
       pv[i] = cache_v64 ? cache_v64[l][i] : bf(cache_v[l][i]);
     }
     oracle_block(c, &layers[l], x.data(), 1, pos, pk.data(), pv.data(), nullptr, 0, y.data(),
-                 nullptr, nullptr);
+                 nullptr, nullptr, routed_layer(c, l),
+                 router_out ? router_out + (int64_t)l * c->n_experts : nullptr);
     x.swap(y);
   }
   std::vector<double> hf(H);
@@ -356,34 +397,62 @@ void oracle_route_weights(const double *logits, const int32_t *idx, int64_t T, i
   }
 }
 
-// Routed MoE FFN, token by token ([P3] "MoE": router linear, fp32 softmax,
-// top-k, optional renormalisation; each selected expert is a SwiGLU whose
-// fused gate_up_proj [2I, H] splits into gate = rows [0, I) and up = rows
-// [I, 2I) (chunk(2)); outputs are summed with the routing weights).
+// Routed MoE FFN of one token ([P3] "MoE": router linear, fp32 softmax, top-k, optional
+// renormalisation; each selected expert is a SwiGLU whose fused gate_up_proj [2I, H]
+// splits into gate = rows [0, I) and up = rows [I, 2I) (chunk(2)); outputs are summed with
+// the routing weights).  With router_bf16 the selection follows [P1] section 11 instead:
+// the softmax (fp32, as that page computes it) is rounded to bf16, the experts with the
+// largest rounded probabilities are taken (lower index first on ties) and each weight is
+// its rounded probability (renormalised over the selection only with norm_topk).
+static void moe_row(const oracle_cfg *c, const uint16_t *router, const uint16_t *gate_up,
+                    const uint16_t *down, const double *xt, double *y, int32_t *idx, double *w,
+                    double *r) {
+  const int H = c->hidden, E = c->n_experts, k = c->top_k, I = c->moe_inter;
+  linear_row(xt, router, E, H, r);
+  std::vector<int> order(E);
+  for (int e = 0; e < E; ++e) order[e] = e;
+  if (c->router_bf16) {
+    float m = -std::numeric_limits<float>::infinity();
+    for (int e = 0; e < E; ++e) m = std::max(m, (float)r[e]);
+    float z = 0.f;
+    for (int e = 0; e < E; ++e) z += std::exp((float)r[e] - m);
+    std::vector<double> p(E);
+    for (int e = 0; e < E; ++e) p[e] = oracle_bf16_round(std::exp((float)r[e] - m) / z);
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return p[a] > p[b]; });
+    double sel = 0.0;
+    for (int j = 0; j < k; ++j) {
+      idx[j] = order[j];
+      w[j] = p[order[j]];
+      sel += w[j];
+    }
+    if (c->norm_topk)
+      for (int j = 0; j < k; ++j) w[j] /= sel;
+  } else {
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return r[a] > r[b]; });
+    for (int j = 0; j < k; ++j) idx[j] = order[j];
+    oracle_route_weights(r, idx, 1, E, k, c->norm_topk, w);
+  }
+  std::vector<double> g(I), u(I), o(H);
+  for (int i = 0; i < H; ++i) y[i] = 0.0;
+  for (int j = 0; j < k; ++j) {
+    int e = idx[j];
+    const uint16_t *gu = gate_up + (int64_t)e * 2 * I * H;
+    linear_row(xt, gu, I, H, g.data());
+    linear_row(xt, gu + (int64_t)I * H, I, H, u.data());
+    for (int i = 0; i < I; ++i) g[i] = silu(g[i]) * u[i];
+    linear_row(g.data(), down + (int64_t)e * H * I, H, I, o.data());
+    for (int i = 0; i < H; ++i) y[i] += w[j] * o[i];
+  }
+}
+
+// Routed MoE FFN over T tokens, token by token (see moe_row).
 void oracle_moe_ffn(const oracle_cfg *c, const uint16_t *router, const uint16_t *gate_up,
                     const uint16_t *down, const double *x, int64_t T, double *y, int32_t *idx,
                     double *w, double *logits) {
-  const int H = c->hidden, E = c->n_experts, k = c->top_k, I = c->moe_inter;
+  const int H = c->hidden, E = c->n_experts, k = c->top_k;
   parallel_for(T, [&](int64_t t) {
-    const double *xt = x + t * H;
-    double *r = logits + t * E;
-    linear_row(xt, router, E, H, r);
-    std::vector<int> order(E);
-    for (int e = 0; e < E; ++e) order[e] = e;
-    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return r[a] > r[b]; });
-    for (int j = 0; j < k; ++j) idx[t * k + j] = order[j];
-    oracle_route_weights(r, idx + t * k, 1, E, k, c->norm_topk, w + t * k);
-    std::vector<double> g(I), u(I), o(H);
-    for (int i = 0; i < H; ++i) y[t * H + i] = 0.0;
-    for (int j = 0; j < k; ++j) {
-      int e = idx[t * k + j];
-      const uint16_t *gu = gate_up + (int64_t)e * 2 * I * H;
-      linear_row(xt, gu, I, H, g.data());
-      linear_row(xt, gu + (int64_t)I * H, I, H, u.data());
-      for (int i = 0; i < I; ++i) g[i] = silu(g[i]) * u[i];
-      linear_row(g.data(), down + (int64_t)e * H * I, H, I, o.data());
-      for (int i = 0; i < H; ++i) y[t * H + i] += w[t * k + j] * o[i];
-    }
+    moe_row(c, router, gate_up, down, x + t * H, y + t * H, idx + t * k, w + t * k,
+            logits + t * E);
   });
 }
 
@@ -421,6 +490,8 @@ void oracle_argmax_f32(const float *logits, int64_t rows, int64_t V, int32_t *ou
     out[r] = (int32_t)best;
   }
 }
+
+float oracle_bf16_round(float x) { return bf16_round_impl(x); }
 
 void oracle_argmax_f64(const double *logits, int64_t rows, int64_t V, int32_t *out) {
   for (int64_t r = 0; r < rows; ++r) {

@@ -36,10 +36,15 @@ typedef struct {
   int32_t qk_norm;
   int32_t n_experts, top_k, moe_inter, norm_topk;
   int32_t rope_interleaved; /* 1: planes (2i, 2i + 1); 0: planes (i, i + hd/2) */
+  int32_t sparse_step;      /* stack: layer l is routed when n_experts > 0 and
+                               (l + 1) % sparse_step == 0; 0: no routed layers */
+  int32_t router_bf16;      /* 1: routing probabilities rounded to bf16 before selection */
 } oracle_cfg;
 
 typedef struct { /* bf16 bits */
   const uint16_t *in_norm, *q, *k, *v, *q_norm, *k_norm, *o, *post_norm, *gate, *up, *down;
+  /* routed layers: router [E][H], experts' fused gate|up [E][2I][H], down [E][H][I] */
+  const uint16_t *router, *experts_gate_up, *experts_down;
 } oracle_layer;
 
 void oracle_set_threads(int n);
@@ -57,16 +62,17 @@ void oracle_swiglu_ffn(const double *x, int64_t T, int H, int I, const uint16_t 
                        const uint16_t *up, const uint16_t *down, double *y);
 void oracle_block(const oracle_cfg *c, const oracle_layer *w, const double *x, int64_t S,
                   int64_t pos0, const double *past_k, const double *past_v, const int64_t *rows,
-                  int64_t n_rows, double *x_out, double *new_k, double *new_v);
+                  int64_t n_rows, double *x_out, double *new_k, double *new_v, int routed,
+                  double *router_logits);
 void oracle_stack_prefill(const oracle_cfg *c, const uint16_t *embed, const uint16_t *final_norm,
                           const uint16_t *lm_head, const oracle_layer *layers, const int32_t *ids,
                           int64_t S, const int64_t *rows, int64_t n_rows, double *logits,
-                          double *k_out, double *v_out);
+                          double *k_out, double *v_out, double *router_out);
 void oracle_stack_decode(const oracle_cfg *c, const uint16_t *embed, const uint16_t *final_norm,
                          const uint16_t *lm_head, const oracle_layer *layers, int32_t id,
                          int64_t pos, const uint16_t *const *cache_k,
                          const uint16_t *const *cache_v, const double *const *cache_k64,
-                         const double *const *cache_v64, double *logits);
+                         const double *const *cache_v64, double *logits, double *router_out);
 void oracle_moe_ffn(const oracle_cfg *c, const uint16_t *router, const uint16_t *gate_up,
                     const uint16_t *down, const double *x, int64_t T, double *y, int32_t *idx,
                     double *w, double *logits);
@@ -77,6 +83,7 @@ void oracle_permute(const int32_t *idx, int64_t T, int k, int E, int32_t *counts
                     int32_t *offsets, int32_t *perm_token, int32_t *inv_row);
 void oracle_argmax_f32(const float *logits, int64_t rows, int64_t V, int32_t *out);
 void oracle_argmax_f64(const double *logits, int64_t rows, int64_t V, int32_t *out);
+float oracle_bf16_round(float x);
 
 #ifdef __cplusplus
 }

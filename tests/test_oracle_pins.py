@@ -552,3 +552,64 @@ def test_sample_low_temperature_or_tiny_nucleus_is_greedy():
     for u in (0.0, 0.5, 0.999):
         np.testing.assert_array_equal(oracle.sample(lg, 1.0, 1e-9, [u] * 5)[0], g)
         np.testing.assert_array_equal(oracle.sample(lg, 1e-4, 1.0, [u] * 5)[0], g)
+
+
+# ---------------------------------------------------------------- routed layers
+
+def test_bf16_round_to_nearest_even():
+    u = 2.0 ** -7  # bf16 spacing just above 1
+    got = oracle.bf16_round([1.0, 1 + u / 2, 1 + 1.5 * u, 1 + u / 2 + 2.0 ** -20, -3.0, 0.0])
+    np.testing.assert_array_equal(got, [1.0, 1.0, 1 + 2 * u, 1 + u, -3.0, 0.0])
+
+
+def _two_expert_cfg(H=64, I=64, bf16_router=1, norm=0):
+    return dict(hidden_size=H, num_experts=2, num_experts_per_tok=1, moe_intermediate_size=I,
+                norm_topk_prob=norm, rms_norm_eps=1e-6, router_weights_bf16=bf16_router)
+
+
+def test_router_bf16_tie_goes_to_the_lower_expert():
+    # Router logits (0, d) with d = 0.0016: fp32 softmax gives 0.4996 / 0.5004, both rounding
+    # to bf16 0.5.  The page's rule (argmax over the rounded probabilities, first on ties)
+    # picks expert 0 with weight 0.5; the fp32 top-k rule picks expert 1 with 0.5004.
+    H, I = 64, 64
+    d = 0.0016
+    x = np.zeros((1, H)); x[0, 0] = 1.0
+    router = np.zeros((2, H), np.uint16)
+    router[1, 0] = np.float32(d).view(np.uint32) >> 16  # bf16 bits of d (truncated)
+    dval = float(np.array([int(router[1, 0]) << 16], np.uint32).view(np.float32)[0])
+    gu = synth.normal_bf16(3, "t.gu", (2, 2 * I, H), 0.0, 0.05)
+    dn = synth.normal_bf16(3, "t.dn", (2, H, I), 0.0, 0.05)
+    y, idx, w, lg = oracle.moe_ffn(_two_expert_cfg(), router, gu, dn, x)
+    assert idx[0, 0] == 0 and w[0, 0] == 0.5
+    y2, idx2, w2, _ = oracle.moe_ffn(_two_expert_cfg(bf16_router=0), router, gu, dn, x)
+    assert idx2[0, 0] == 1
+    np.testing.assert_allclose(w2[0, 0], 1.0 / (1.0 + math.exp(-dval)), rtol=1e-12)
+    # a clear winner is selected by both rules, the bf16 weight being its rounded probability
+    router[1, 0] = np.float32(1.0).view(np.uint32) >> 16
+    _, idx3, w3, _ = oracle.moe_ffn(_two_expert_cfg(), router, gu, dn, x)
+    p1 = np.float32(1.0) / (np.float32(1.0) + np.exp(np.float32(-1.0)))
+    assert idx3[0, 0] == 1 and w3[0, 0] == oracle.bf16_round(p1)[0]
+
+
+def test_stack_routed_layers_with_one_expert_equal_the_dense_stack():
+    # decoder_sparse_step = 1 routes every layer; with a single expert (k = 1, renormalised
+    # weight 1) holding the dense FFN's weights, the routed stack is the dense stack.
+    from q3_testutil import small_cfg
+    cfg = small_cfg(L=2, V=300)
+    model = recipes.model_host(5, cfg)
+    ids = synth.uniform_i32(5, "input.ids", (9,), 0, 300)
+    dense = oracle.stack_prefill(cfg, model, ids)
+    rcfg = dict(cfg, num_experts=1, num_experts_per_tok=1,
+                moe_intermediate_size=cfg["intermediate_size"], norm_topk_prob=1,
+                decoder_sparse_step=1)
+    H = cfg["hidden_size"]
+    for lw in model["layers"]:
+        lw["router"] = synth.normal_bf16(5, "t.router", (1, H), 0.0, 0.02)
+        lw["experts_gate_up"] = np.concatenate([lw["gate"], lw["up"]])[None]
+        lw["experts_down"] = lw["down"][None]
+    routed, rl = oracle.stack_prefill(rcfg, model, ids, want_router=True)
+    np.testing.assert_allclose(routed, dense, rtol=0, atol=1e-12)
+    assert np.isfinite(rl).all()
+    # sparse step 2: only layer 1 is routed
+    _, rl2 = oracle.stack_prefill(dict(rcfg, decoder_sparse_step=2), model, ids, want_router=True)
+    assert np.isnan(rl2[0]).all() and np.isfinite(rl2[1]).all()
