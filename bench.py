@@ -95,8 +95,14 @@ def setup_stack(torch, q3, recipes, dev, cfg, B, S, cap, seed_model, seed_in):
     return model, mw, keep, rope, caches
 
 
-def wl_prefill(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown):
+def wl_prefill(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, routed=False):
     cfg = dict(recipes.QWEN3_0P6B)
+    name = "stack_0p6b_prefill"
+    if routed:
+        # the two-expert variant of the 0.6B model: every layer's MLP is a top-1 routed
+        # pair of experts of the dense MLP's shape, gated by bf16 probabilities
+        cfg.update(recipes.MOE_2E)
+        name = "stack_0p8b_2e_prefill"
     B, S = 4, 2048
     model, mw, keep, rope, caches = setup_stack(torch, q3, recipes, dev, cfg, B, S, S,
                                                 recipes.MODEL_SEED_0P6B, 2)
@@ -118,14 +124,23 @@ def wl_prefill(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown):
     units = dense_units(cfg, B, S, L)
     units["lm_head_gemm"] = ("mfma", 2.0 * T * H * V, 1)
     units["argmax"] = ("hbm", 4.0 * B * V, 1)
-    ms, dom, rf, kernels = measure(timer, step, steps, warmup, "stack_0p6b_prefill", units,
-                                   "attn_prefill", breakdown)
-    out = {"name": "stack_0p6b_prefill", "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms,
-           "config": {"workload": "stack_0p6b_prefill", "batch": B, "seq_len": S, "layers": L,
+    if routed:
+        for tag in ("gate_up_gemm", "down_gemm"):
+            del units[tag]
+        units.update(moe_units(cfg, T, L))
+    ms, dom, rf, kernels = measure(timer, step, steps, warmup, name, units, "attn_prefill",
+                                   breakdown)
+    out = {"name": name, "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms,
+           "config": {"workload": name, "batch": B, "seq_len": S, "layers": L,
                       "hidden": H, "heads": "16q/8kv x128", "intermediate": I, "vocab": V,
                       "lm_head": "tied, fp32 logits for all positions",
                       "greedy_next_token": True},
            "dominant_kernel": dom, "roofline": rf}
+    if routed:
+        out["config"].update(experts=cfg["num_experts"], top_k=cfg["num_experts_per_tok"],
+                             expert_intermediate=cfg["moe_intermediate_size"],
+                             gating="bf16 probabilities, not renormalised")
+        del out["config"]["intermediate"]
     total_flops = stack_prefill_flops(cfg, B, S)
     out["whole_step_mfma_frac"] = round(total_flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)
     out["algorithmic_tflop_per_step"] = round(total_flops / 1e12, 3)
@@ -155,13 +170,29 @@ def dense_units(cfg, B, S, launches):
     }
 
 
+def moe_units(cfg, T, launches):
+    """Algorithmic work per launch of the routed-FFN kernel classes for T tokens."""
+    H, E, k, I = (cfg["hidden_size"], cfg["num_experts"], cfg["num_experts_per_tok"],
+                  cfg["moe_intermediate_size"])
+    return {
+        "moe_router_gemm": ("mfma", 2.0 * T * E * H, launches),
+        "moe_route": ("hbm", 4.0 * T * E + 8.0 * T * k * 3, launches),
+        "moe_gate_up_gemm": ("mfma", 2.0 * T * k * 2 * I * H, launches),
+        "moe_down_gemm": ("mfma", 2.0 * T * k * I * H, launches),
+        "moe_combine": ("hbm", 4.0 * T * k * H + 2.0 * T * H, launches),
+    }
+
+
 def stack_prefill_flops(cfg, B, S):
     H, nq, nkv, hd, I, L, V = (cfg["hidden_size"], cfg["num_attention_heads"],
                                cfg["num_key_value_heads"], cfg["head_dim"],
                                cfg["intermediate_size"], cfg["num_hidden_layers"],
                                cfg["vocab_size"])
     T = B * S
-    gemm = 2.0 * T * H * ((nq + 2 * nkv) * hd + nq * hd + 3 * I)
+    ffn = 3 * I
+    if cfg.get("num_experts", 0) > 0 and cfg.get("decoder_sparse_step", 0) == 1:
+        ffn = cfg["num_experts"] + 3 * cfg["num_experts_per_tok"] * cfg["moe_intermediate_size"]
+    gemm = 2.0 * T * H * ((nq + 2 * nkv) * hd + nq * hd + ffn)
     attn = 4.0 * hd * nq * B * S * (S + 1) / 2
     return L * (gemm + attn) + 2.0 * T * H * V
 
@@ -327,13 +358,7 @@ def wl_moe(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown):
         q3.qwen3_moe_ffn(cfg, w, x, y, T, None, None, None, offsets, None, None, ws)
 
     H, I = cfg["hidden_size"], cfg["moe_intermediate_size"]
-    units = {
-        "moe_router_gemm": ("mfma", 2.0 * T * E * H, 1),
-        "moe_route": ("hbm", 4.0 * T * E + 8.0 * T * k * 3, 1),
-        "moe_gate_up_gemm": ("mfma", 2.0 * T * k * 2 * I * H, 1),
-        "moe_down_gemm": ("mfma", 2.0 * T * k * I * H, 1),
-        "moe_combine": ("hbm", 4.0 * T * k * H + 2.0 * T * H, 1),
-    }
+    units = moe_units(cfg, T, 1)
     ms, dom, rf, kernels = measure(timer, step, steps, warmup, "moe_ffn", units,
                                    "moe_gate_up_gemm", breakdown)
     counts = (offsets[1:] - offsets[:-1]).cpu().numpy()
@@ -429,8 +454,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads",
-                    default="prefill,decode,moe,block7b,block7b_irope,block,generate,"
-                            "generate_sampled")
+                    default="prefill,decode,moe,prefill_2e,block7b,block7b_irope,block,"
+                            "generate,generate_sampled")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=512,
                     help="prefix length for the oracle CPU baseline (0 = skip)")
@@ -462,6 +487,8 @@ def main():
     results = {}
     fns = {"prefill": lambda: wl_prefill(torch, q3, recipes, synth, dev, args.steps, args.warmup,
                                          timer, bd),
+           "prefill_2e": lambda: wl_prefill(torch, q3, recipes, synth, dev, args.steps,
+                                            args.warmup, timer, bd, routed=True),
            "decode": lambda: wl_decode(torch, q3, recipes, synth, dev, 2 * args.steps,
                                        args.warmup, timer, bd),
            "moe": lambda: wl_moe(torch, q3, recipes, synth, dev, 2 * args.steps, args.warmup,

@@ -47,11 +47,13 @@ class Config(ctypes.Structure):
                 ("qk_norm", ctypes.c_int32), ("tie_word_embeddings", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("num_experts_per_tok", ctypes.c_int32),
                 ("moe_intermediate_size", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32),
-                ("rope_interleaved", ctypes.c_int32)]
+                ("rope_interleaved", ctypes.c_int32), ("decoder_sparse_step", ctypes.c_int32),
+                ("router_weights_bf16", ctypes.c_int32)]
 
 
 LAYER_FIELDS = ("input_layernorm", "q_proj", "k_proj", "v_proj", "q_norm", "k_norm", "o_proj",
-                "post_attention_layernorm", "gate_proj", "up_proj", "down_proj")
+                "post_attention_layernorm", "gate_proj", "up_proj", "down_proj", "router",
+                "experts_gate_up_proj", "experts_down_proj")
 
 
 class LayerWeights(ctypes.Structure):

@@ -220,6 +220,8 @@ hipError_t gemm_run(const Args& a_in, bool f16, int bmode, int epi, bool grouped
   GEMM_CASE(kMid, TMid, false, B_SWIGLU, E_SWIGLU, true)
   GEMM_CASE(kMid, TMid, true, B_DENSE, E_F32, true)
   GEMM_CASE(kBig, TBig, false, B_SWIGLU, E_SWIGLU, true)
+  // routed layers inside the stack read fp16 normalised rows
+  GEMM_CASE(kBig, TBig, true, B_SWIGLU, E_SWIGLU, true)
   GEMM_CASE(kBig, TBig, true, B_DENSE, E_F32, true)
   return hipErrorInvalidValue;
 }

@@ -110,6 +110,7 @@ hipError_t gen_feed(const int32_t* ids, int32_t* out_ids, int n_new, int col, in
 struct MoeRouteArgs {
   const float* logits;  // [T][E]
   int T, E, k, norm_topk;
+  int router_bf16;  // select on (and weight by) bf16-rounded softmax probabilities
   int32_t* idx;   // [T][k]
   float* w;       // [T][k]
   int32_t* chunk_counts;  // [nchunks][E]
@@ -124,7 +125,10 @@ struct MoeRouteArgs {
 };
 int moe_route_chunks(int T);
 hipError_t moe_route(const MoeRouteArgs& a, hipStream_t s);
-hipError_t moe_combine(const float* y_rows, const int32_t* inv_row, const float* w, bf16_t* y,
-                       int T, int k, int H, hipStream_t s);
+// out[t] = (residual[t] +) sum_j w[t][j] y_rows[inv_row[t][j]]; out fp32 or bf16
+// (residual nullable; out may be the residual itself)
+hipError_t moe_combine(const float* y_rows, const int32_t* inv_row, const float* w,
+                       const float* residual, void* out, bool out_f32, int T, int k, int H,
+                       hipStream_t s);
 
 }  // namespace q3

@@ -1,6 +1,8 @@
 // Routed MoE: top-k routing, deterministic dispatch order, weighted combine
 // ([P3] "MoE": fp32 router softmax, top-k, renormalisation, hit experts only,
-// weighted index_add back to the token rows).
+// weighted index_add back to the token rows).  With router_bf16 the selection follows
+// [P1] section 11: the fp32 softmax over all experts is rounded to bf16, the largest
+// rounded probabilities are selected (lower index first on ties) and serve as the weights.
 //
 // Dispatch order: experts ascending, tokens ascending within an expert.  It is a counting
 // sort over fixed token chunks whose result does not depend on thread timing (the only
@@ -35,6 +37,20 @@ __global__ void __launch_bounds__(256) topk_kernel(MoeRouteArgs a) {
     e_of[i] = e;
     v[i] = e < a.E ? r[e] : -INFINITY;
   }
+  if (a.router_bf16) {
+    // selection keys: the bf16-rounded fp32 softmax probabilities
+    float m = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    float ex[4], s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ex[i] = e_of[i] < a.E ? expf(v[i] - m) : 0.f;
+      s += ex[i];
+    }
+    s = warp_sum(s);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = e_of[i] < a.E ? bf2f(f2bf(ex[i] / s)) : -INFINITY;
+  }
   bool taken[4] = {false, false, false, false};
   float sel_v[kMaxK];
   int sel_e[kMaxK];
@@ -59,6 +75,22 @@ __global__ void __launch_bounds__(256) topk_kernel(MoeRouteArgs a) {
       if (e_of[i] == be) taken[i] = true;
     sel_v[j] = bv;
     sel_e[j] = be;
+  }
+  if (a.router_bf16) {  // the selected rounded probabilities are the weights
+    float sel = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < a.k) sel += sel_v[j];
+    if (lane < a.k) {
+      float sv = sel_v[0];
+      int se = sel_e[0];
+#pragma unroll
+      for (int j = 1; j < kMaxK; ++j)
+        if (j == lane && j < a.k) { sv = sel_v[j]; se = sel_e[j]; }
+      a.idx[(int64_t)t * a.k + lane] = se;
+      a.w[(int64_t)t * a.k + lane] = a.norm_topk ? sv / sel : sv;
+    }
+    return;
   }
   // probabilities: softmax over all experts (max = sel_v[0]); renormalised over the k
   float denom = 0.f;
@@ -183,7 +215,8 @@ __global__ void __launch_bounds__(256) scatter_kernel(MoeRouteArgs a) {
 // y[t] = sum_j w[t][j] * y_rows[inv_row[t][j]], in slot order, rounded once to bf16.
 __global__ void __launch_bounds__(256)
 combine_kernel(const float* __restrict__ y_rows, const int32_t* __restrict__ inv_row,
-               const float* __restrict__ w, bf16_t* __restrict__ y, int T, int k, int H) {
+               const float* __restrict__ w, const float* residual, void* out, bool out_f32,
+               int T, int k, int H) {
   const int nchunk = H / 8;
   const int64_t total = (int64_t)T * nchunk;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
@@ -199,9 +232,22 @@ combine_kernel(const float* __restrict__ y_rows, const int32_t* __restrict__ inv
         acc[4 + e] += wj * a1[e];
       }
     }
-    u32x4_t o;
-    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
-    st16(y + (int64_t)t * H + c * 8, o);
+    const int64_t off = (int64_t)t * H + c * 8;
+    if (residual) {  // out = residual + sum (in place allowed: read before written)
+      const f32x4_t r0 = *(const f32x4_t*)(residual + off), r1 = *(const f32x4_t*)(residual + off + 4);
+      for (int e = 0; e < 4; ++e) {
+        acc[e] = r0[e] + acc[e];
+        acc[4 + e] = r1[e] + acc[4 + e];
+      }
+    }
+    if (out_f32) {
+      *(f32x4_t*)((float*)out + off) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+      *(f32x4_t*)((float*)out + off + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
+    } else {
+      u32x4_t o;
+      for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+      st16((bf16_t*)out + off, o);
+    }
   }
 }
 
@@ -219,13 +265,14 @@ hipError_t moe_route(const MoeRouteArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t moe_combine(const float* y_rows, const int32_t* inv_row, const float* w, bf16_t* y,
-                       int T, int k, int H, hipStream_t s) {
+hipError_t moe_combine(const float* y_rows, const int32_t* inv_row, const float* w,
+                       const float* residual, void* out, bool out_f32, int T, int k, int H,
+                       hipStream_t s) {
   if (T <= 0) return hipSuccess;
   int64_t work = (int64_t)T * H / 8;
   int blocks = (int)std::min<int64_t>(65536, (work + 255) / 256);
-  hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, s, y_rows, inv_row, w, y, T,
-                     k, H);
+  hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, s, y_rows, inv_row, w, residual,
+                     out, out_f32, T, k, H);
   return hipGetLastError();
 }
 

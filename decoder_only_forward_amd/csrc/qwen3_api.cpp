@@ -77,8 +77,48 @@ struct Bump {
   }
 };
 
+struct MoeLayout {
+  size_t logits, idx, w, chunk_counts, counts, offsets, perm, inv, tile_e, tile_r, tile_n, act,
+      yrows;
+  size_t total;
+  int max_tiles, tile_m;
+};
+
+MoeLayout moe_layout(const qwen3_config* c, int T) {
+  MoeLayout L{};
+  const int E = c->num_experts, k = c->num_experts_per_tok, H = c->hidden_size,
+            I = c->moe_intermediate_size;
+  L.tile_m = 256;
+  L.max_tiles = (int)(((int64_t)T * k + L.tile_m - 1) / L.tile_m) + E;
+  Bump b;
+  L.logits = b.take((size_t)T * E * 4);
+  L.idx = b.take((size_t)T * k * 4);
+  L.w = b.take((size_t)T * k * 4);
+  L.chunk_counts = b.take((size_t)moe_route_chunks(T) * E * 4);
+  L.counts = b.take((size_t)E * 4);
+  L.offsets = b.take((size_t)(E + 1) * 4);
+  L.perm = b.take((size_t)T * k * 4);
+  L.inv = b.take((size_t)T * k * 4);
+  L.tile_e = b.take((size_t)L.max_tiles * 4);
+  L.tile_r = b.take((size_t)L.max_tiles * 4);
+  L.tile_n = b.take(4);
+  L.act = b.take((size_t)T * k * I * 2);
+  L.yrows = b.take((size_t)T * k * H * 4);
+  L.total = b.off;
+  return L;
+}
+
+// Stack layer l runs the routed MoE FFN when the config has experts and
+// (l + 1) % decoder_sparse_step == 0.
+bool has_routed(const qwen3_config* c) { return c->num_experts > 0 && c->decoder_sparse_step > 0; }
+bool routed_layer(const qwen3_config* c, int l) {
+  return has_routed(c) && (l + 1) % c->decoder_sparse_step == 0;
+}
+
 struct DenseLayout {
   size_t xn, qkv, q, attn, h1, act, res, hf, part_attn, part_res, am_val, am_idx, lg_scratch;
+  size_t moe;      // stack with routed layers: the MoE FFN's workspace (layout ml)
+  MoeLayout ml;
   size_t kf, vtf;  // prefill: fp16 copies of the new keys / values
   size_t total;
   int T, rows_out, attn_splits, attn_chunk, am_chunks, fresh_w_max;
@@ -120,6 +160,10 @@ DenseLayout dense_layout(const qwen3_config* c, int op, int B, int S, int cap_hi
     const int sm = std::max(so, sd);
     L.part_res = sm > 1 ? b.take((size_t)sm * T * H * 4) : 0;
   }
+  if (stack && has_routed(c)) {
+    L.ml = moe_layout(c, T);
+    L.moe = b.take(L.ml.total);
+  }
   if (stack) {
     L.rows_out = T;  // upper bound: ALL mode needs every row normalised
     L.hf = b.take((size_t)T * H * 2);
@@ -152,36 +196,6 @@ GenLayout gen_layout(const qwen3_config* c, int B, int S, int cap) {
   return G;
 }
 
-struct MoeLayout {
-  size_t logits, idx, w, chunk_counts, counts, offsets, perm, inv, tile_e, tile_r, tile_n, act,
-      yrows;
-  size_t total;
-  int max_tiles, tile_m;
-};
-
-MoeLayout moe_layout(const qwen3_config* c, int T) {
-  MoeLayout L{};
-  const int E = c->num_experts, k = c->num_experts_per_tok, H = c->hidden_size,
-            I = c->moe_intermediate_size;
-  L.tile_m = 256;
-  L.max_tiles = (int)(((int64_t)T * k + L.tile_m - 1) / L.tile_m) + E;
-  Bump b;
-  L.logits = b.take((size_t)T * E * 4);
-  L.idx = b.take((size_t)T * k * 4);
-  L.w = b.take((size_t)T * k * 4);
-  L.chunk_counts = b.take((size_t)moe_route_chunks(T) * E * 4);
-  L.counts = b.take((size_t)E * 4);
-  L.offsets = b.take((size_t)(E + 1) * 4);
-  L.perm = b.take((size_t)T * k * 4);
-  L.inv = b.take((size_t)T * k * 4);
-  L.tile_e = b.take((size_t)L.max_tiles * 4);
-  L.tile_r = b.take((size_t)L.max_tiles * 4);
-  L.tile_n = b.take(4);
-  L.act = b.take((size_t)T * k * I * 2);
-  L.yrows = b.take((size_t)T * k * H * 4);
-  L.total = b.off;
-  return L;
-}
 
 // ---------------------------------------------------------------- validation
 int check_dense_cfg(const qwen3_config* c) {
@@ -211,7 +225,7 @@ int check_dense_cfg(const qwen3_config* c) {
   return QWEN3_OK;
 }
 
-int check_layer(const qwen3_config* c, const qwen3_layer_weights* w) {
+int check_layer(const qwen3_config* c, const qwen3_layer_weights* w, bool routed = false) {
   if (!w) return fail(QWEN3_EINVAL, "layer weights are NULL");
   REQ_PTR(w->input_layernorm, "input_layernorm");
   REQ_PTR(w->q_proj, "q_proj");
@@ -223,9 +237,29 @@ int check_layer(const qwen3_config* c, const qwen3_layer_weights* w) {
   }
   REQ_PTR(w->o_proj, "o_proj");
   REQ_PTR(w->post_attention_layernorm, "post_attention_layernorm");
-  REQ_PTR(w->gate_proj, "gate_proj");
-  REQ_PTR(w->up_proj, "up_proj");
-  REQ_PTR(w->down_proj, "down_proj");
+  if (routed) {
+    REQ_PTR(w->router, "router");
+    REQ_PTR(w->experts_gate_up_proj, "experts_gate_up_proj");
+    REQ_PTR(w->experts_down_proj, "experts_down_proj");
+  } else {
+    REQ_PTR(w->gate_proj, "gate_proj");
+    REQ_PTR(w->up_proj, "up_proj");
+    REQ_PTR(w->down_proj, "down_proj");
+  }
+  return QWEN3_OK;
+}
+
+int check_moe_cfg(const qwen3_config* c) {
+  const int E = c->num_experts, k = c->num_experts_per_tok, H = c->hidden_size,
+            I = c->moe_intermediate_size;
+  if (E <= 0 || E > 256) return fail(QWEN3_EUNSUPPORTED, "num_experts=%d must be in [1, 256]", E);
+  if (k <= 0 || k > 8 || k > E)
+    return fail(QWEN3_EUNSUPPORTED, "num_experts_per_tok=%d must be in [1, min(E, 8)]", k);
+  if (H <= 0 || H % 64) return fail(QWEN3_EUNSUPPORTED, "hidden_size=%d must be a multiple of 64", H);
+  if (I <= 0 || I % 64)
+    return fail(QWEN3_EUNSUPPORTED, "moe_intermediate_size=%d must be a multiple of 64", I);
+  if (c->router_weights_bf16 != 0 && c->router_weights_bf16 != 1)
+    return fail(QWEN3_EINVAL, "router_weights_bf16=%d must be 0 or 1", c->router_weights_bf16);
   return QWEN3_OK;
 }
 
@@ -270,11 +304,111 @@ struct LayerIO {
   const bf16_t* next_norm;  // stack: next layer's input RMSNorm weight (nullptr: none)
 };
 
+// Routed MoE FFN ([P3] "MoE"; [P1] section 11 with router_weights_bf16): router GEMM,
+// top-k routing and dispatch order, grouped gate|up + SwiGLU, grouped down, weighted
+// combine (plus the residual when given).  Arguments are checked by the callers.
+struct MoeIO {
+  const void* x;  // [T][H] input rows: the caller's bf16 tokens or fp16 normalised rows
+  bool x_f16;
+  int T;
+  const float* residual;  // nullable: out = residual + moe(x)
+  void* out;              // [T][H], fp32 or bf16 (may be the residual itself)
+  bool out_f32;
+  // optional outputs (nullptr: workspace)
+  float* lg;
+  int32_t* idx;
+  float* wt;
+  int32_t* offs;
+  int32_t* perm;
+  int32_t* inv;
+};
+
+int moe_run(const qwen3_config* c, const void* router, const void* gate_up, const void* down,
+            const MoeIO& io, char* ws, const MoeLayout& L, hipStream_t s) {
+  const int T = io.T;
+  const int E = c->num_experts, k = c->num_experts_per_tok, H = c->hidden_size,
+            I = c->moe_intermediate_size;
+  float* lg = io.lg ? io.lg : (float*)(ws + L.logits);
+  int32_t* idx = io.idx ? io.idx : (int32_t*)(ws + L.idx);
+  float* wt = io.wt ? io.wt : (float*)(ws + L.w);
+  int32_t* offs = io.offs ? io.offs : (int32_t*)(ws + L.offsets);
+  int32_t* perm = io.perm ? io.perm : (int32_t*)(ws + L.perm);
+  int32_t* inv = io.inv ? io.inv : (int32_t*)(ws + L.inv);
+  int32_t* tile_e = (int32_t*)(ws + L.tile_e);
+  int32_t* tile_r = (int32_t*)(ws + L.tile_r);
+  int32_t* tile_n = (int32_t*)(ws + L.tile_n);
+  f16_t* act = (f16_t*)(ws + L.act);
+  float* yrows = (float*)(ws + L.yrows);
+
+  // router logits (fp32)
+  {
+    Args a{};
+    a.M = T; a.N = E; a.K = H;
+    a.A = (const uint16_t*)io.x; a.lda = H;
+    a.B0 = (const bf16_t*)router; a.ldb = H;
+    a.C = lg; a.ldc = E;
+    GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_DENSE, gemm::E_F32, false);
+    ProfScope ps("moe_router_gemm", s);
+    CHECK_HIP(gemm_run(a, io.x_f16, gemm::B_DENSE, gemm::E_F32, false, p, s));
+  }
+  // top-k, weights, dispatch order, tile table
+  {
+    MoeRouteArgs r{};
+    r.logits = lg; r.T = T; r.E = E; r.k = k; r.norm_topk = c->norm_topk_prob;
+    r.router_bf16 = c->router_weights_bf16;
+    r.idx = idx; r.w = wt;
+    r.chunk_counts = (int32_t*)(ws + L.chunk_counts);
+    r.counts = (int32_t*)(ws + L.counts);
+    r.offsets = offs; r.perm_token = perm; r.inv_row = inv;
+    r.tile_expert = tile_e; r.tile_row0 = tile_r; r.tile_count = tile_n;
+    r.max_tiles = L.max_tiles; r.tile_m = L.tile_m;
+    ProfScope ps("moe_route", s);
+    CHECK_HIP(moe_route(r, s));
+  }
+  // grouped gate|up + SwiGLU over gathered token rows
+  {
+    Args a{};
+    a.M = T * k; a.N = 2 * I; a.K = H;
+    a.A = (const uint16_t*)io.x; a.lda = H; a.a_rows = perm;
+    a.B0 = (const bf16_t*)gate_up;
+    a.B1 = (const bf16_t*)gate_up + (int64_t)I * H;
+    a.ldb = H;
+    a.g_offsets = offs; a.g_tile_expert = tile_e; a.g_tile_row0 = tile_r;
+    a.g_tile_count = tile_n;
+    a.g_b_stride = (int64_t)2 * I * H;
+    a.m_tiles = L.max_tiles;
+    a.C = act; a.ldc = I;
+    GemmPlan p{kBig};
+    ProfScope ps("moe_gate_up_gemm", s);
+    CHECK_HIP(gemm_run(a, io.x_f16, gemm::B_SWIGLU, gemm::E_SWIGLU, true, p, s));
+  }
+  // grouped down -> per-row fp32 outputs in dispatch order
+  {
+    Args a{};
+    a.M = T * k; a.N = H; a.K = I;
+    a.A = act; a.lda = I;
+    a.B0 = (const bf16_t*)down; a.B1 = a.B0; a.ldb = I;
+    a.g_offsets = offs; a.g_tile_expert = tile_e; a.g_tile_row0 = tile_r;
+    a.g_tile_count = tile_n;
+    a.g_b_stride = (int64_t)H * I;
+    a.m_tiles = L.max_tiles;
+    a.C = yrows; a.ldc = H;
+    GemmPlan p{kBig};
+    ProfScope ps("moe_down_gemm", s);
+    CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, gemm::E_F32, true, p, s));
+  }
+  {
+    ProfScope ps("moe_combine", s);
+    CHECK_HIP(moe_combine(yrows, inv, wt, io.residual, io.out, io.out_f32, T, k, H, s));
+  }
+  return QWEN3_OK;
+}
+
 // *next_normed is set when the layer's last reduction also wrote the next layer's
 // normalised input into xn (decode sizes, stack only).
 int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* rope,
               const qwen3_kv_layer* kv, const LayerIO& io, char* ws, const DenseLayout& L,
-              hipStream_t s, bool* next_normed = nullptr) {
+              hipStream_t s, bool* next_normed = nullptr, bool routed = false) {
   if (next_normed) *next_normed = false;
   const int H = c->hidden_size, nq = c->num_attention_heads, nkv = c->num_key_value_heads,
             hd = c->head_dim, I = c->intermediate_size, T = io.T;
@@ -384,6 +518,16 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
       CHECK_HIP(rmsnorm_f32(h1, 1, 0, (const bf16_t*)w->post_attention_layernorm, xn, T, H,
                             eps, s));
     }
+  }
+  if (routed) {
+    // routed MoE FFN on the normalised rows; the combine adds the residual h1
+    MoeIO m{};
+    m.x = xn; m.x_f16 = true; m.T = T;
+    m.residual = h1;
+    m.out = io.res ? (void*)io.res : (void*)io.x_out;
+    m.out_f32 = io.res != nullptr;
+    return moe_run(c, w->router, w->experts_gate_up_proj, w->experts_down_proj, m,
+                   ws + L.moe, L.ml, s);
   }
   // gate | up with SwiGLU
   {
@@ -594,8 +738,11 @@ int check_stack(const qwen3_config* c, const qwen3_model_weights* w, const float
   REQ_PTR(w->embed_tokens, "embed_tokens");
   REQ_PTR(w->norm, "norm");
   if (!c->tie_word_embeddings) REQ_PTR(w->lm_head, "lm_head");
+  if (c->decoder_sparse_step < 0)
+    return fail(QWEN3_EINVAL, "decoder_sparse_step=%d must be >= 0", c->decoder_sparse_step);
+  if (has_routed(c)) TRY(check_moe_cfg(c));
   for (int l = 0; l < c->num_hidden_layers; ++l) {
-    int rc = check_layer(c, &w->layers[l]);
+    int rc = check_layer(c, &w->layers[l], routed_layer(c, l));
     if (rc) return fail(rc, "layer %d: %s", l, g_err.c_str());
   }
   REQ_PTR(rope, "rope");
@@ -626,7 +773,8 @@ int stack_run(const qwen3_config* c, const qwen3_model_weights* w, const float* 
     io.input_normed = normed;
     io.next_norm = l + 1 < c->num_hidden_layers
                        ? (const bf16_t*)w->layers[l + 1].input_layernorm : nullptr;
-    TRY(run_layer(c, &w->layers[l], rope, &caches[l], io, ws, L, s, &normed));
+    TRY(run_layer(c, &w->layers[l], rope, &caches[l], io, ws, L, s, &normed,
+                  routed_layer(c, l)));
   }
 
   // final RMSNorm on the rows that need logits, LM head (tied: embed_tokens)
@@ -755,14 +903,8 @@ int qwen3_moe_ffn(const qwen3_config* c, const qwen3_moe_weights* w, const void*
                   void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   if (!c) return fail(QWEN3_EINVAL, "cfg is NULL");
-  const int E = c->num_experts, k = c->num_experts_per_tok, H = c->hidden_size,
-            I = c->moe_intermediate_size;
-  if (E <= 0 || E > 256) return fail(QWEN3_EUNSUPPORTED, "num_experts=%d must be in [1, 256]", E);
-  if (k <= 0 || k > 8 || k > E)
-    return fail(QWEN3_EUNSUPPORTED, "num_experts_per_tok=%d must be in [1, min(E, 8)]", k);
-  if (H <= 0 || H % 64) return fail(QWEN3_EUNSUPPORTED, "hidden_size=%d must be a multiple of 64", H);
-  if (I <= 0 || I % 64)
-    return fail(QWEN3_EUNSUPPORTED, "moe_intermediate_size=%d must be a multiple of 64", I);
+  TRY(check_moe_cfg(c));
+  const int k = c->num_experts_per_tok;
   if (n_tokens <= 0) return fail(QWEN3_EINVAL, "n_tokens=%d must be positive", n_tokens);
   if ((int64_t)n_tokens * k > (1 << 30)) return fail(QWEN3_EINVAL, "too many tokens");
   if (!w) return fail(QWEN3_EINVAL, "MoE weights are NULL");
@@ -775,82 +917,13 @@ int qwen3_moe_ffn(const qwen3_config* c, const qwen3_moe_weights* w, const void*
   if (!aligned16(workspace) || workspace_bytes < L.total)
     return fail(QWEN3_EWORKSPACE, "workspace needs %zu bytes (got %zu)", L.total,
                 workspace_bytes);
-  hipStream_t s = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  const int T = n_tokens;
-  float* lg = router_logits ? router_logits : (float*)(ws + L.logits);
-  int32_t* idx = topk_idx ? topk_idx : (int32_t*)(ws + L.idx);
-  float* wt = topk_w ? topk_w : (float*)(ws + L.w);
-  int32_t* offs = expert_offsets ? expert_offsets : (int32_t*)(ws + L.offsets);
-  int32_t* perm = perm_token ? perm_token : (int32_t*)(ws + L.perm);
-  int32_t* inv = inv_row ? inv_row : (int32_t*)(ws + L.inv);
-  int32_t* tile_e = (int32_t*)(ws + L.tile_e);
-  int32_t* tile_r = (int32_t*)(ws + L.tile_r);
-  int32_t* tile_n = (int32_t*)(ws + L.tile_n);
-  f16_t* act = (f16_t*)(ws + L.act);
-  float* yrows = (float*)(ws + L.yrows);
-
-  // router logits (fp32)
-  {
-    Args a{};
-    a.M = T; a.N = E; a.K = H;
-    a.A = (const bf16_t*)x; a.lda = H;
-    a.B0 = (const bf16_t*)w->router; a.ldb = H;
-    a.C = lg; a.ldc = E;
-    GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_DENSE, gemm::E_F32, false);
-    ProfScope ps("moe_router_gemm", s);
-    CHECK_HIP(gemm_run(a, false, gemm::B_DENSE, gemm::E_F32, false, p, s));
-  }
-  // top-k, weights, dispatch order, tile table
-  {
-    MoeRouteArgs r{};
-    r.logits = lg; r.T = T; r.E = E; r.k = k; r.norm_topk = c->norm_topk_prob;
-    r.idx = idx; r.w = wt;
-    r.chunk_counts = (int32_t*)(ws + L.chunk_counts);
-    r.counts = (int32_t*)(ws + L.counts);
-    r.offsets = offs; r.perm_token = perm; r.inv_row = inv;
-    r.tile_expert = tile_e; r.tile_row0 = tile_r; r.tile_count = tile_n;
-    r.max_tiles = L.max_tiles; r.tile_m = L.tile_m;
-    ProfScope ps("moe_route", s);
-    CHECK_HIP(moe_route(r, s));
-  }
-  // grouped gate|up + SwiGLU over gathered token rows
-  {
-    Args a{};
-    a.M = T * k; a.N = 2 * I; a.K = H;
-    a.A = (const uint16_t*)x; a.lda = H; a.a_rows = perm;
-    a.B0 = (const bf16_t*)w->gate_up_proj;
-    a.B1 = (const bf16_t*)w->gate_up_proj + (int64_t)I * H;
-    a.ldb = H;
-    a.g_offsets = offs; a.g_tile_expert = tile_e; a.g_tile_row0 = tile_r;
-    a.g_tile_count = tile_n;
-    a.g_b_stride = (int64_t)2 * I * H;
-    a.m_tiles = L.max_tiles;
-    a.C = act; a.ldc = I;
-    GemmPlan p{kBig};
-    ProfScope ps("moe_gate_up_gemm", s);
-    CHECK_HIP(gemm_run(a, false, gemm::B_SWIGLU, gemm::E_SWIGLU, true, p, s));
-  }
-  // grouped down -> per-row fp32 outputs in dispatch order
-  {
-    Args a{};
-    a.M = T * k; a.N = H; a.K = I;
-    a.A = act; a.lda = I;
-    a.B0 = (const bf16_t*)w->down_proj; a.B1 = a.B0; a.ldb = I;
-    a.g_offsets = offs; a.g_tile_expert = tile_e; a.g_tile_row0 = tile_r;
-    a.g_tile_count = tile_n;
-    a.g_b_stride = (int64_t)H * I;
-    a.m_tiles = L.max_tiles;
-    a.C = yrows; a.ldc = H;
-    GemmPlan p{kBig};
-    ProfScope ps("moe_down_gemm", s);
-    CHECK_HIP(gemm_run(a, true, gemm::B_DENSE, gemm::E_F32, true, p, s));
-  }
-  {
-    ProfScope ps("moe_combine", s);
-    CHECK_HIP(moe_combine(yrows, inv, wt, (bf16_t*)y, T, k, H, s));
-  }
-  return QWEN3_OK;
+  MoeIO m{};
+  m.x = x; m.x_f16 = false; m.T = n_tokens;
+  m.out = y; m.out_f32 = false;
+  m.lg = router_logits; m.idx = topk_idx; m.wt = topk_w; m.offs = expert_offsets;
+  m.perm = perm_token; m.inv = inv_row;
+  return moe_run(c, w->router, w->gate_up_proj, w->down_proj, m, (char*)workspace, L,
+                 (hipStream_t)stream);
 }
 
 }  // extern "C"

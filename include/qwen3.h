@@ -77,6 +77,16 @@ typedef struct qwen3_config {
                                       Qwen3 "RoPE" section of the build-it-yourself pages);
                                       1: planes (2i, 2i + 1) (the complex-number form of
                                       the first page's RoPE section). Other values: EINVAL */
+  int32_t decoder_sparse_step;     /* stack: layer l runs the routed MoE FFN (num_experts,
+                                      num_experts_per_tok, moe_intermediate_size,
+                                      norm_topk_prob) when num_experts > 0 and
+                                      (l + 1) % decoder_sparse_step == 0 (the first page's
+                                      Qwen-MoE config); 0: every layer dense. The block entry
+                                      points always run the dense FFN. */
+  int32_t router_weights_bf16;     /* routed FFN: 1 rounds the fp32 softmax probabilities to
+                                      bf16, selects the largest rounded values (lower expert
+                                      first on ties) and uses them as the weights (the first
+                                      page's MoE section); 0: fp32 selection and weights */
 } qwen3_config;
 
 /* One decoder layer's weights (device, bf16). */
@@ -92,6 +102,11 @@ typedef struct qwen3_layer_weights {
   const void *gate_proj;                /* [I, H] */
   const void *up_proj;                  /* [I, H] */
   const void *down_proj;                /* [H, I] */
+  /* routed layers of the stack (see decoder_sparse_step); such a layer needs only these
+     three for its FFN (gate_proj, up_proj, down_proj may be NULL there) */
+  const void *router;                   /* [E, H] */
+  const void *experts_gate_up_proj;     /* [E, 2*I_moe, H]; rows [0, I_moe) gate, rest up */
+  const void *experts_down_proj;        /* [E, H, I_moe] */
 } qwen3_layer_weights;
 
 /* Whole-model weights. `layers` is a HOST array of num_hidden_layers entries. */

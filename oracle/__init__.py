@@ -267,6 +267,19 @@ def route_weights(logits, idx, norm_topk=True):
     return w
 
 
+def route_bf16(logits, k, norm_topk=False):
+    """Routing with bf16-rounded probabilities ([P1] section 11) on given router logits
+    [T, E]: fp32 softmax rounded to bf16, the k largest rounded values (lower index first
+    on ties), weights = rounded probabilities (renormalised with norm_topk).
+    Returns idx [T, k] int32, w [T, k]."""
+    lg = _f64(logits)
+    T, E = lg.shape
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    lib().oracle_route_bf16(_p(lg), ctypes.c_int64(T), E, k, int(norm_topk), _p(idx), _p(w))
+    return idx, w
+
+
 def permute(idx, E):
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     T, k = idx.shape

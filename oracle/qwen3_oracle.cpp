@@ -397,6 +397,34 @@ void oracle_route_weights(const double *logits, const int32_t *idx, int64_t T, i
   }
 }
 
+// Routing with bf16 probabilities ([P1] section 11): the softmax over all experts, in
+// fp32 as that page computes it, is rounded to bf16; the k experts with the largest
+// rounded probabilities are taken (the lower index first among equal values) and each
+// weight is its rounded probability, divided by the selection's sum with norm_topk.
+void oracle_route_bf16(const double *logits, int64_t T, int E, int k, int norm_topk,
+                       int32_t *idx, double *w) {
+  std::vector<int> order(E);
+  std::vector<double> p(E);
+  for (int64_t t = 0; t < T; ++t) {
+    const double *r = logits + t * E;
+    float m = -std::numeric_limits<float>::infinity();
+    for (int e = 0; e < E; ++e) m = std::max(m, (float)r[e]);
+    float z = 0.f;
+    for (int e = 0; e < E; ++e) z += std::exp((float)r[e] - m);
+    for (int e = 0; e < E; ++e) p[e] = oracle_bf16_round(std::exp((float)r[e] - m) / z);
+    for (int e = 0; e < E; ++e) order[e] = e;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return p[a] > p[b]; });
+    double sel = 0.0;
+    for (int j = 0; j < k; ++j) {
+      idx[t * k + j] = order[j];
+      w[t * k + j] = p[order[j]];
+      sel += w[t * k + j];
+    }
+    if (norm_topk)
+      for (int j = 0; j < k; ++j) w[t * k + j] /= sel;
+  }
+}
+
 // Routed MoE FFN of one token ([P3] "MoE": router linear, fp32 softmax, top-k, optional
 // renormalisation; each selected expert is a SwiGLU whose fused gate_up_proj [2I, H]
 // splits into gate = rows [0, I) and up = rows [I, 2I) (chunk(2)); outputs are summed with
@@ -412,21 +440,7 @@ static void moe_row(const oracle_cfg *c, const uint16_t *router, const uint16_t 
   std::vector<int> order(E);
   for (int e = 0; e < E; ++e) order[e] = e;
   if (c->router_bf16) {
-    float m = -std::numeric_limits<float>::infinity();
-    for (int e = 0; e < E; ++e) m = std::max(m, (float)r[e]);
-    float z = 0.f;
-    for (int e = 0; e < E; ++e) z += std::exp((float)r[e] - m);
-    std::vector<double> p(E);
-    for (int e = 0; e < E; ++e) p[e] = oracle_bf16_round(std::exp((float)r[e] - m) / z);
-    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return p[a] > p[b]; });
-    double sel = 0.0;
-    for (int j = 0; j < k; ++j) {
-      idx[j] = order[j];
-      w[j] = p[order[j]];
-      sel += w[j];
-    }
-    if (c->norm_topk)
-      for (int j = 0; j < k; ++j) w[j] /= sel;
+    oracle_route_bf16(r, 1, E, k, c->norm_topk, idx, w);
   } else {
     std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return r[a] > r[b]; });
     for (int j = 0; j < k; ++j) idx[j] = order[j];

@@ -79,6 +79,8 @@ void oracle_moe_ffn(const oracle_cfg *c, const uint16_t *router, const uint16_t 
 void oracle_topk(const float *logits, int64_t T, int E, int k, int32_t *idx);
 void oracle_route_weights(const double *logits, const int32_t *idx, int64_t T, int E, int k,
                           int norm_topk, double *w);
+void oracle_route_bf16(const double *logits, int64_t T, int E, int k, int norm_topk,
+                       int32_t *idx, double *w);
 void oracle_permute(const int32_t *idx, int64_t T, int k, int E, int32_t *counts,
                     int32_t *offsets, int32_t *perm_token, int32_t *inv_row);
 void oracle_argmax_f32(const float *logits, int64_t rows, int64_t V, int32_t *out);

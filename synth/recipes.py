@@ -12,8 +12,10 @@ from (seed, HF-style tensor name, element index)):
                  top-8 with renormalised weights, 8192 tokens, Zipf-skewed load
   5 block_7b     one 7B-shaped block (hidden 3584, 28 q / 4 kv heads, I=18944),
                  prefill batch 1 x 32768
+  and the two-expert stack: workload 2 with every layer's MLP replaced by a
+                 top-1 pair of routed experts (I=3072 each, bf16 gating)
 
-Distributions: linear weights ~N(0, 0.02); every RMSNorm weight (input, post,
+Distributions: linear weights ~N(0, 0.02) (routers of routed layers too); every RMSNorm weight (input, post,
 final, q_norm, k_norm) ~1 + N(0, 0.05); activations ~N(0, 1); token ids
 uniform in [0, vocab).  "N" is the generator's Irwin-Hall(12) normal.
 """
@@ -39,6 +41,12 @@ QWEN_7B_BLOCK = dict(
 MOE_2048 = dict(
     hidden_size=2048, num_experts=128, num_experts_per_tok=8, moe_intermediate_size=768,
     norm_topk_prob=1, rms_norm_eps=1e-6)
+
+# Two-expert routed variant of the 0.6B model ([P1]: every layer's MLP replaced by two
+# experts, top-1, weight = the bf16-rounded router probability, no renormalisation; the
+# experts keep the dense MLP's shape)
+MOE_2E = dict(num_experts=2, num_experts_per_tok=1, moe_intermediate_size=3072,
+              norm_topk_prob=0, decoder_sparse_step=1, router_weights_bf16=1)
 
 WORKLOADS = {
     1: dict(name="block_0p6b", cfg=QWEN3_0P6B, batch=1, seq_len=128, layers=1),
@@ -88,8 +96,21 @@ def model_specs(cfg):
     return out
 
 
+def has_experts(cfg, l):
+    """Whether layer l's MLP is a routed expert set (the Hugging Face Qwen3-MoE layout:
+    every decoder_sparse_step-th layer when num_experts > 0); such a layer has no dense
+    gate/up/down projections."""
+    step = cfg.get("decoder_sparse_step", 0)
+    return cfg.get("num_experts", 0) > 0 and step > 0 and (l + 1) % step == 0
+
+
 def layer_host(seed, cfg, l):
-    return {f: normal_bf16(seed, n, s, m, sd) for f, n, s, m, sd in layer_specs(cfg, l)}
+    routed = has_experts(cfg, l)
+    d = {f: normal_bf16(seed, n, s, m, sd) for f, n, s, m, sd in layer_specs(cfg, l)
+         if not (routed and f in ("gate", "up", "down"))}
+    if routed:
+        d["router"], d["experts_gate_up"], d["experts_down"] = moe_host(seed, cfg, l=l)
+    return d
 
 
 def model_host(seed, cfg, n_layers=None):
@@ -148,17 +169,17 @@ def router_row_scales(n_experts=128):
     return np.ones(n_experts)
 
 
-def moe_specs(cfg):
+def moe_specs(cfg, l=0):
     H, E, I = cfg["hidden_size"], cfg["num_experts"], cfg["moe_intermediate_size"]
-    p = "model.layers.0.mlp."
+    p = f"model.layers.{l}.mlp."
     return [("router", p + "gate.weight", (E, H)),
             ("gate_up", p + "experts.gate_up_proj", (E, 2 * I, H)),
             ("down", p + "experts.down_proj", (E, H, I))]
 
 
-def moe_host(seed, cfg, skew=True):
+def moe_host(seed, cfg, skew=True, l=0):
     H, E = cfg["hidden_size"], cfg["num_experts"]
-    specs = dict((f, (n, s)) for f, n, s in moe_specs(cfg))
+    specs = dict((f, (n, s)) for f, n, s in moe_specs(cfg, l))
     g = router_row_scales(E) if skew else np.ones(E)
     n, _ = specs["router"]
     router = np.empty((E, H), np.uint16)
@@ -203,8 +224,14 @@ def _dev_normal(shape, seed, name, mean, std, device):
 
 def layer_device(seed, cfg, l, device):
     """One layer's weights on the device, keyed by the library's field names."""
-    return {LIB_LAYER_NAMES[f]: _dev_normal(s, seed, n, m, sd, device)
-            for f, n, s, m, sd in layer_specs(cfg, l)}
+    routed = has_experts(cfg, l)
+    d = {LIB_LAYER_NAMES[f]: _dev_normal(s, seed, n, m, sd, device)
+         for f, n, s, m, sd in layer_specs(cfg, l)
+         if not (routed and f in ("gate", "up", "down"))}
+    if routed:
+        d["router"], d["experts_gate_up_proj"], d["experts_down_proj"] = \
+            moe_device(seed, cfg, device, l=l)
+    return d
 
 
 def model_device(seed, cfg, device, n_layers=None):
@@ -236,11 +263,11 @@ def kv_fill_device(k, vt, seed, l, n_pos, ctx):
                            logical=(1, n_pos, hd), strides=(0, 1, cap))
 
 
-def moe_device(seed, cfg, device, skew=True):
+def moe_device(seed, cfg, device, skew=True, l=0):
     import torch
     from . import normal_bf16_device
     H, E = cfg["hidden_size"], cfg["num_experts"]
-    specs = dict((f, (n, s)) for f, n, s in moe_specs(cfg))
+    specs = dict((f, (n, s)) for f, n, s in moe_specs(cfg, l))
     g = router_row_scales(E) if skew else np.ones(E)
     n, _ = specs["router"]
     router = torch.empty((E, H), dtype=torch.bfloat16, device=device)

@@ -56,7 +56,8 @@ def layer_to_dev(layer_host, device):
     m = {"in_norm": "input_layernorm", "q": "q_proj", "k": "k_proj", "v": "v_proj",
          "q_norm": "q_norm", "k_norm": "k_norm", "o": "o_proj",
          "post_norm": "post_attention_layernorm", "gate": "gate_proj", "up": "up_proj",
-         "down": "down_proj"}
+         "down": "down_proj", "router": "router", "experts_gate_up": "experts_gate_up_proj",
+         "experts_down": "experts_down_proj"}
     return {m[k]: to_dev_bf16(v, device) for k, v in layer_host.items()}
 
 

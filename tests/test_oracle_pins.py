@@ -613,3 +613,19 @@ def test_stack_routed_layers_with_one_expert_equal_the_dense_stack():
     # sparse step 2: only layer 1 is routed
     _, rl2 = oracle.stack_prefill(dict(rcfg, decoder_sparse_step=2), model, ids, want_router=True)
     assert np.isnan(rl2[0]).all() and np.isfinite(rl2[1]).all()
+
+
+def test_route_bf16_closed_form():
+    # logits (0, ln 2, ln 2): probabilities 1/5, 2/5, 2/5; bf16 rounds 2/5 up to
+    # 0.400390625 (fp32 0x3ECCCCCD, low half above the midpoint).  Top-1 takes the lower
+    # index of the tie with that rounded weight; top-2 renormalised gives 1/2 each.
+    lg = np.array([[0.0, math.log(2.0), math.log(2.0)]])
+    idx, w = oracle.route_bf16(lg, 1)
+    assert idx[0, 0] == 1 and w[0, 0] == 0.400390625
+    idx, w = oracle.route_bf16(lg, 2, norm_topk=True)
+    np.testing.assert_array_equal(idx[0], [1, 2])
+    np.testing.assert_array_equal(w[0], [0.5, 0.5])
+    # unrenormalised top-2 of (0, 0, -inf-like): bf16(1/2) each
+    idx, w = oracle.route_bf16(np.array([[0.0, 0.0, -100.0]]), 2)
+    np.testing.assert_array_equal(idx[0], [0, 1])
+    np.testing.assert_array_equal(w[0], [0.5, 0.5])
