@@ -210,26 +210,34 @@ def stack_prefill(cfg, model, ids, rows=None, want_kv=False, want_router=False):
 
 
 def stack_decode(cfg, model, token_id, pos, cache_k, cache_v, want_router=False):
-    """One decode step of one sequence.  cache_k/v: per-layer arrays [nkv, pos, hd], either
-    uint16 (bf16 bits) or float64.  Returns logits [V] (and, with want_router, the routed
-    layers' router logits [L, E], NaN elsewhere)."""
+    """Decode of one sequence: token_id (an int: one token, or a sequence of n tokens taking
+    positions pos .. pos + n - 1, each seeing the cache and the new tokens up to itself).
+    cache_k/v: per-layer arrays [nkv, pos, hd], uint16 (bf16 bits) or float64.  Returns
+    logits [V] for an int, [n, V] for a sequence (and, with want_router, the routed layers'
+    router logits [L, E] or [L, n, E], NaN elsewhere)."""
     c = make_cfg(cfg)
     arr, keep = _layers(model)
     embed, norm = _u16(model["embed"]), _u16(model["norm"])
     head = _u16(model["lm_head"]) if model.get("lm_head") is not None else None
     L = c.n_layers
+    single = np.ndim(token_id) == 0
+    ids = np.ascontiguousarray(np.atleast_1d(token_id), dtype=np.int32)
+    n = ids.shape[0]
     f64 = cache_k[0].dtype == np.float64
     ck = [(_f64(a) if f64 else _u16(a)) for a in cache_k]
     cv = [(_f64(a) if f64 else _u16(a)) for a in cache_v]
     pk = (ctypes.c_void_p * L)(*[a.ctypes.data for a in ck])
     pv = (ctypes.c_void_p * L)(*[a.ctypes.data for a in cv])
     null = ctypes.c_void_p(0)
-    logits = np.empty((c.vocab,), dtype=np.float64)
-    ro = np.full((L, c.n_experts), np.nan) if want_router else None
-    lib().oracle_stack_decode(ctypes.byref(c), _p(embed), _p(norm), _p(head), arr,
-                              ctypes.c_int32(int(token_id)), ctypes.c_int64(pos),
+    logits = np.empty((n, c.vocab), dtype=np.float64)
+    ro = np.full((L, n, c.n_experts), np.nan) if want_router else None
+    lib().oracle_stack_decode(ctypes.byref(c), _p(embed), _p(norm), _p(head), arr, _p(ids),
+                              ctypes.c_int64(n), ctypes.c_int64(pos),
                               null if f64 else pk, null if f64 else pv,
                               pk if f64 else null, pv if f64 else null, _p(logits), _p(ro))
+    if single:
+        logits = logits[0]
+        ro = ro[:, 0] if ro is not None else None
     return (logits, ro) if want_router else logits
 
 

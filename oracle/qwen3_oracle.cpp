@@ -334,32 +334,41 @@ void oracle_stack_prefill(const oracle_cfg *c, const uint16_t *embed, const uint
 // attends to cached keys/values 0..pos-1 plus its own ([P3] "prefill 与
 // decode": the last mask row sees all history).  Caches per layer are
 // [nkv][pos][hd], either bf16 (cache_k/cache_v) or double (cache_k64/...).
+// Decode of n new tokens of one sequence at positions pos .. pos + n - 1 ([P3] "prefill 与
+// decode"; [P2] section 4's mask slice: token i sees the cached positions and new tokens
+// 0..i): every layer is the block over the n rows with the given cache as its past, then
+// the final norm and the LM head on each row.  logits [n][V]; router_out [L][n][E].
 void oracle_stack_decode(const oracle_cfg *c, const uint16_t *embed, const uint16_t *final_norm,
-                         const uint16_t *lm_head, const oracle_layer *layers, int32_t id,
-                         int64_t pos, const uint16_t *const *cache_k,
+                         const uint16_t *lm_head, const oracle_layer *layers, const int32_t *ids,
+                         int64_t n, int64_t pos, const uint16_t *const *cache_k,
                          const uint16_t *const *cache_v, const double *const *cache_k64,
                          const double *const *cache_v64, double *logits, double *router_out) {
   const int H = c->hidden, nkv = c->n_kv_heads, hd = c->head_dim;
-  std::vector<double> x(H), y(H), pk((size_t)nkv * pos * hd), pv((size_t)nkv * pos * hd);
-  for (int i = 0; i < H; ++i) x[i] = bf(embed[(int64_t)id * H + i]);
+  std::vector<double> x((size_t)n * H), y((size_t)n * H), pk((size_t)nkv * pos * hd),
+      pv((size_t)nkv * pos * hd);
+  for (int64_t t = 0; t < n; ++t)
+    for (int i = 0; i < H; ++i) x[t * H + i] = bf(embed[(int64_t)ids[t] * H + i]);
   for (int l = 0; l < c->n_layers; ++l) {
     for (size_t i = 0; i < pk.size(); ++i) {
       pk[i] = cache_k64 ? cache_k64[l][i] : bf(cache_k[l][i]);
       pv[i] = cache_v64 ? cache_v64[l][i] : bf(cache_v[l][i]);
     }
-    oracle_block(c, &layers[l], x.data(), 1, pos, pk.data(), pv.data(), nullptr, 0, y.data(),
+    oracle_block(c, &layers[l], x.data(), n, pos, pk.data(), pv.data(), nullptr, 0, y.data(),
                  nullptr, nullptr, routed_layer(c, l),
-                 router_out ? router_out + (int64_t)l * c->n_experts : nullptr);
+                 router_out ? router_out + (int64_t)l * n * c->n_experts : nullptr);
     x.swap(y);
   }
-  std::vector<double> hf(H);
-  rmsnorm_vec(x.data(), H, final_norm, c->eps, hf.data());
   const uint16_t *head = lm_head ? lm_head : embed;
   const int64_t V = c->vocab, chunk = 1024, nchunk = (V + chunk - 1) / chunk;
-  parallel_for(nchunk, [&](int64_t i) {
-    int64_t v0 = i * chunk, n = std::min(chunk, V - v0);
-    linear_row(hf.data(), head + v0 * H, n, H, logits + v0);
-  });
+  std::vector<double> hf(H);
+  for (int64_t t = 0; t < n; ++t) {
+    rmsnorm_vec(x.data() + t * H, H, final_norm, c->eps, hf.data());
+    double *lg = logits + t * V;
+    parallel_for(nchunk, [&](int64_t i) {
+      int64_t v0 = i * chunk, m = std::min(chunk, V - v0);
+      linear_row(hf.data(), head + v0 * H, m, H, lg + v0);
+    });
+  }
 }
 
 // Top-k selection on given scores: the k largest, in descending order, ties

@@ -69,8 +69,8 @@ void oracle_stack_prefill(const oracle_cfg *c, const uint16_t *embed, const uint
                           int64_t S, const int64_t *rows, int64_t n_rows, double *logits,
                           double *k_out, double *v_out, double *router_out);
 void oracle_stack_decode(const oracle_cfg *c, const uint16_t *embed, const uint16_t *final_norm,
-                         const uint16_t *lm_head, const oracle_layer *layers, int32_t id,
-                         int64_t pos, const uint16_t *const *cache_k,
+                         const uint16_t *lm_head, const oracle_layer *layers, const int32_t *ids,
+                         int64_t n, int64_t pos, const uint16_t *const *cache_k,
                          const uint16_t *const *cache_v, const double *const *cache_k64,
                          const double *const *cache_v64, double *logits, double *router_out);
 void oracle_moe_ffn(const oracle_cfg *c, const uint16_t *router, const uint16_t *gate_up,

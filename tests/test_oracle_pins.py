@@ -375,6 +375,32 @@ def test_stack_decode_equals_last_prefill_row():
     np.testing.assert_allclose(dec, lg[p], atol=1e-11)
 
 
+def test_multi_token_decode_equals_prefill_rows():
+    # n new tokens decoded onto the cache of the first p positions give the full prefill's
+    # rows p .. p + n - 1; and one step at a time (the cache grown by each step's own K/V)
+    # gives the same rows
+    cfg = _small_cfg()
+    model = recipes.model_host(7, cfg)
+    ids = np.array([5, 9, 250, 1, 77, 13, 40, 2, 311], np.int32)
+    lg, ko, vo = oracle.stack_prefill(cfg, model, ids, want_kv=True)
+    p, n = 4, 5
+    dec = oracle.stack_decode(cfg, model, ids[p:p + n], p, [k[:, :p] for k in ko],
+                              [v[:, :p] for v in vo])
+    assert dec.shape == (n, cfg["vocab_size"])
+    np.testing.assert_allclose(dec, lg[p:p + n], atol=1e-11)
+    for i in range(n):
+        one = oracle.stack_decode(cfg, model, ids[p + i], p + i, [k[:, :p + i] for k in ko],
+                                  [v[:, :p + i] for v in vo])
+        np.testing.assert_allclose(one, dec[i], atol=1e-11)
+    # a later token changes nothing before it (causal), but does change its own row
+    ids2 = ids.copy()
+    ids2[p + n - 1] = 123
+    dec2 = oracle.stack_decode(cfg, model, ids2[p:p + n], p, [k[:, :p] for k in ko],
+                               [v[:, :p] for v in vo])
+    np.testing.assert_array_equal(dec2[:n - 1], dec[:n - 1])
+    assert np.abs(dec2[n - 1] - dec[n - 1]).max() > 1e-3
+
+
 def test_config_shapes_match_page_facts():
     with open(os.path.join(GOLDEN, "qwen3_0p6b_page_facts.json")) as f:
         facts = json.load(f)
