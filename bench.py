@@ -230,10 +230,13 @@ def measure(timer, step, steps, warmup, workload, units, default_tag, breakdown)
     return ms, dom, rf, kernels
 
 
-def wl_decode(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown):
+def wl_decode(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, S=1):
+    """Decode of S new tokens per sequence (S = 1: one step; S > 1: the tokens of one
+    sequence are decoded together, each seeing the cache and the new tokens before it)."""
     cfg = dict(recipes.QWEN3_0P6B)
     B, ctx = 64, 4096
     cap = 4160
+    name = "stack_0p6b_decode" if S == 1 else f"stack_0p6b_decode_{S}tok"
     model, mw, keep, rope, caches = setup_stack(torch, q3, recipes, dev, cfg, B, 1, cap,
                                                 recipes.MODEL_SEED_0P6B, 3)
     t0 = time.time()
@@ -243,44 +246,47 @@ def wl_decode(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown):
     log(f"  decode: KV cache {len(caches)} x 2 x {tuple(caches[0][0].shape)} filled in "
         f"{time.time() - t0:.1f}s")
     kvs = [q3.make_kv_layer(k, vt, cap) for k, vt in caches]
-    ids = torch.empty((B,), dtype=torch.int32, device=dev)
+    ids = torch.empty((B, S), dtype=torch.int32, device=dev)
     synth.uniform_i32_device(ids, 3, "input.ids", 0, cfg["vocab_size"])
     pos = torch.full((B,), ctx, dtype=torch.int32, device=dev)
     V = cfg["vocab_size"]
-    logits = torch.empty((B, V), dtype=torch.float32, device=dev)
+    mode = q3.QWEN3_LOGITS_LAST if S == 1 else q3.QWEN3_LOGITS_ALL
+    logits = torch.empty((B * S, V), dtype=torch.float32, device=dev)
     nxt = torch.empty((B,), dtype=torch.int32, device=dev)
-    ws = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_STACK_DECODE, B),
+    ws = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_STACK_DECODE, B, S),
                      dtype=torch.uint8, device=dev)
 
     def step():
-        q3.qwen3_stack_forward(cfg, mw, rope, ids, B, 1, 0, pos, kvs, logits,
-                               q3.QWEN3_LOGITS_LAST, nxt, ws)
+        q3.qwen3_stack_forward(cfg, mw, rope, ids, B, S, 0, pos, kvs, logits, mode, nxt, ws)
 
     L, nkv, nq = cfg["num_hidden_layers"], cfg["num_key_value_heads"], cfg["num_attention_heads"]
     H, hd, I = cfg["hidden_size"], cfg["head_dim"], cfg["intermediate_size"]
-    kv_bytes = 2.0 * B * nkv * (ctx + 1) * hd * 2
-    nsplit = min(-(-cap // 256), max(-(-cap // 4096), -(-1024 // (B * nkv))))
-    part_bytes = 4.0 * B * nq * nsplit * (hd + 2)  # split partials: design bytes, not algorithmic
+    T = B * S
+    kv_bytes = 2.0 * B * nkv * (ctx + S) * hd * 2
+    g = nq // nkv
+    nqg = -(-(S * g) // 8)
+    nsplit = min(-(-cap // 256), max(-(-cap // 4096), -(-1024 // (B * nqg * nkv))))
+    part_bytes = 4.0 * T * nq * nsplit * (hd + 2)  # split partials: design bytes, not algorithmic
     units = {
         # weights dominate the skinny GEMMs; activations in/out are counted too
-        "qkv_gemm": ("hbm", 2.0 * H * (nq + 2 * nkv) * hd + 2.0 * B * H
-                     + 2.0 * B * (nq + 2 * nkv) * hd, L),
-        "qk_norm_rope_cache": ("hbm", 2.0 * B * (nq + 2 * nkv) * hd + 2.0 * B * nq * hd
-                               + 2.0 * B * 2 * nkv * hd, L),
-        "attn_decode": ("hbm", kv_bytes + 2.0 * B * nq * hd, L),
-        "attn_decode_combine": ("hbm", part_bytes + 2.0 * B * nq * hd, L),
-        "o_proj_gemm": ("hbm", 2.0 * nq * hd * H + 2.0 * B * nq * hd + 8.0 * B * H, L),
-        "gate_up_gemm": ("hbm", 2.0 * 2 * I * H + 2.0 * B * H + 2.0 * B * I, L),
-        "down_gemm": ("hbm", 2.0 * I * H + 2.0 * B * I + 8.0 * B * H, L),
-        "lm_head_gemm": ("hbm", 2.0 * V * H + 4.0 * B * V, 1),
+        "qkv_gemm": ("hbm", 2.0 * H * (nq + 2 * nkv) * hd + 2.0 * T * H
+                     + 2.0 * T * (nq + 2 * nkv) * hd, L),
+        "qk_norm_rope_cache": ("hbm", 2.0 * T * (nq + 2 * nkv) * hd + 2.0 * T * nq * hd
+                               + 2.0 * T * 2 * nkv * hd, L),
+        "attn_decode": ("hbm", kv_bytes + 2.0 * T * nq * hd, L),
+        "attn_decode_combine": ("hbm", part_bytes + 2.0 * T * nq * hd, L),
+        "o_proj_gemm": ("hbm", 2.0 * nq * hd * H + 2.0 * T * nq * hd + 8.0 * T * H, L),
+        "gate_up_gemm": ("hbm", 2.0 * 2 * I * H + 2.0 * T * H + 2.0 * T * I, L),
+        "down_gemm": ("hbm", 2.0 * I * H + 2.0 * T * I + 8.0 * T * H, L),
+        "lm_head_gemm": ("hbm", 2.0 * V * H + 4.0 * T * V, 1),
         "argmax": ("hbm", 4.0 * B * V, 1),
     }
-    ms, dom, rf, kernels = measure(timer, step, steps, warmup, "stack_0p6b_decode", units,
-                                   "attn_decode", breakdown)
-    step_bytes = decode_step_bytes(cfg, B, ctx)
-    out = {"name": "stack_0p6b_decode", "tokens_per_s": B / (ms * 1e-3), "ms_per_step": ms,
-           "config": {"workload": "stack_0p6b_decode", "batch": B, "context": ctx,
-                      "new_tokens_per_seq": 1, "layers": L, "greedy_next_token": True},
+    ms, dom, rf, kernels = measure(timer, step, steps, warmup, name, units, "attn_decode",
+                                   breakdown)
+    step_bytes = decode_step_bytes(cfg, B, ctx, S)
+    out = {"name": name, "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms,
+           "config": {"workload": name, "batch": B, "context": ctx,
+                      "new_tokens_per_seq": S, "layers": L, "greedy_next_token": True},
            "dominant_kernel": dom, "roofline": rf,
            "whole_step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
            "algorithmic_gb_per_step": round(step_bytes / 1e9, 3)}
@@ -330,15 +336,16 @@ def wl_generate(torch, q3, recipes, synth, dev, steps, warmup, timer, sampled):
     return res
 
 
-def decode_step_bytes(cfg, B, ctx):
+def decode_step_bytes(cfg, B, ctx, S=1):
     H, nq, nkv, hd, I, L, V = (cfg["hidden_size"], cfg["num_attention_heads"],
                                cfg["num_key_value_heads"], cfg["head_dim"],
                                cfg["intermediate_size"], cfg["num_hidden_layers"],
                                cfg["vocab_size"])
     layer_w = 2.0 * (H * (nq + 2 * nkv) * hd + nq * hd * H + 3 * I * H + 2 * H + 2 * hd)
-    kv_read = 2.0 * B * nkv * (ctx + 1) * hd * 2
-    kv_write = 2.0 * B * nkv * hd * 2
-    return L * (layer_w + kv_read + kv_write) + 2.0 * V * H + 4.0 * B * V
+    kv_read = 2.0 * B * nkv * (ctx + S) * hd * 2
+    kv_write = 2.0 * B * S * nkv * hd * 2
+    logits = 4.0 * B * S * V if S > 1 else 4.0 * B * V
+    return L * (layer_w + kv_read + kv_write) + 2.0 * V * H + logits
 
 
 def wl_moe(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown):
@@ -454,8 +461,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads",
-                    default="prefill,decode,moe,prefill_2e,block7b,block7b_irope,block,"
-                            "generate,generate_sampled")
+                    default="prefill,decode,decode_4tok,moe,prefill_2e,block7b,block7b_irope,"
+                            "block,generate,generate_sampled")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=512,
                     help="prefix length for the oracle CPU baseline (0 = skip)")
@@ -491,6 +498,8 @@ def main():
                                             args.warmup, timer, bd, routed=True),
            "decode": lambda: wl_decode(torch, q3, recipes, synth, dev, 2 * args.steps,
                                        args.warmup, timer, bd),
+           "decode_4tok": lambda: wl_decode(torch, q3, recipes, synth, dev, 2 * args.steps,
+                                            args.warmup, timer, bd, S=4),
            "moe": lambda: wl_moe(torch, q3, recipes, synth, dev, 2 * args.steps, args.warmup,
                                  timer, bd),
            "block7b": lambda: wl_block(torch, q3, recipes, synth, dev, max(2, args.steps // 3),

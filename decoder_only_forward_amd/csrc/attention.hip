@@ -422,8 +422,11 @@ struct DecState {
   float m, l;    // running max (log2 units) and sum for column r's head
 };
 
+// Keys at or past kv_len (the last new token's limit) hold anything and are zeroed in V;
+// column r's query sees keys below col_len (<= kv_len; mask_from is the smallest col_len
+// of the block, so tiles wholly below it need no masking).
 DEV void dec_tile(DecState& st, const DecTile& t, const u32x4_t* qb, int key0, int kv_len,
-                  int lane) {
+                  int col_len, int mask_from, int lane) {
   const int grp = lane >> 4;
   const bool low = (lane & 15) >= 8;
   f32x4_t sc[2];
@@ -436,14 +439,15 @@ DEV void dec_tile(DecState& st, const DecTile& t, const u32x4_t* qb, int key0, i
     for (int i = 0; i < 4; ++i) acc[i] = add_ror8(acc[i]);
     sc[s] = acc;
   }
-  const bool tail = key0 + kDecTile > kv_len;
-  if (tail) {
+  const bool masked = key0 + kDecTile > mask_from;
+  if (masked) {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (key0 + 8 * grp + 4 * s + i >= kv_len) sc[s][i] = -INFINITY;
+        if (key0 + 8 * grp + 4 * s + i >= col_len) sc[s][i] = -INFINITY;
   }
+  const bool tail = key0 + kDecTile > kv_len;
   float mx = sc[0][0];
 #pragma unroll
   for (int s = 0; s < 2; ++s)
@@ -461,12 +465,14 @@ DEV void dec_tile(DecState& st, const DecTile& t, const u32x4_t* qb, int key0, i
 #pragma unroll
       for (int i = 0; i < 4; ++i) st.o[rt][i] *= f;
   }
+  // a column with no visible key yet keeps m = -inf; its weights are all zero
+  const float mref = st.m == -INFINITY ? 0.f : st.m;
   float p[8];
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[4 * s + i] = exp2_fast(sc[s][i] - st.m);
+      p[4 * s + i] = exp2_fast(sc[s][i] - mref);
       st.l += p[4 * s + i];
     }
   u32x4_t pb;
@@ -489,15 +495,21 @@ DEV void dec_tile(DecState& st, const DecTile& t, const u32x4_t* qb, int key0, i
   }
 }
 
+// Queries of one (sequence, kv head): its S new tokens times the g q heads of the group,
+// listed token-major (query i = token i / g, head i % g), eight per block (blockIdx.z
+// = sequence * nqg + query group).  Token s of the sequence sees keys 0 .. pos + s.
 __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDecodeArgs a) {
   __shared__ float so[kDecWaves][kMaxGroup][HD];
   __shared__ float sm[kDecWaves][kMaxGroup], sl[kDecWaves][kMaxGroup];
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z / a.nqg;
+  const int qg = blockIdx.z % a.nqg;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = a.nq / a.nkv;
+  const int nqry = a.S * g;                           // queries of this (sequence, kv head)
+  const int ncols = min(kMaxGroup, nqry - qg * kMaxGroup);  // in this block
   const int pos = a.pos[b];
-  const bool ok = pos >= 0 && pos < a.cap && pos < a.max_pos;
-  const int kv_len = ok ? pos + 1 : 0;
+  const bool ok = pos >= 0 && pos + a.S <= a.cap && pos + a.S <= a.max_pos;
+  const int kv_len = ok ? pos + a.S : 0;
   // 64-key units spread evenly over all waves serving this (sequence, kv head)
   const int n64 = (kv_len + 63) / 64;
   const int nw = a.splits * kDecWaves, w = split * kDecWaves + wave;
@@ -505,8 +517,12 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDecodeArgs a) {
   const int kend = min((int)((int64_t)(w + 1) * n64 / nw) * 64, kv_len);
 
   const int r = lane & 15, grp = lane >> 4;
-  const int hh = r & 7;
+  const int hh = r & 7;  // query column within the block
   const bool low = r >= 8;
+  const int qi = qg * kMaxGroup + hh;
+  const bool qlive = hh < ncols;
+  const int q_tok = qlive ? qi / g : 0, q_head = qlive ? qi % g : 0;
+  const int col_len = qlive ? pos + 1 + q_tok : kv_len;
   DecState st;
   st.m = -INFINITY;
   st.l = 0.f;
@@ -532,11 +548,12 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDecodeArgs a) {
     dec_load(t1, src, key + kDecTile < kend ? key + kDecTile : key);
     // q after the first two tiles' loads: all arrive within one memory latency
     u32x4_t qb[4];
-    const f16_t* qrow = a.q + ((int64_t)b * a.nq + kvh * g + hh) * HD + grp * 8;
+    const f16_t* qrow =
+        a.q + (((int64_t)b * a.S + q_tok) * a.nq + kvh * g + q_head) * HD + grp * 8;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       float f[8];
-      if (hh < g) {
+      if (qlive) {
         unpack8_f16(ld16(qrow + c * 32), f);
       } else {
 #pragma unroll
@@ -548,11 +565,11 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDecodeArgs a) {
     }
     // t0 holds the tile at key, t1 the one after it (in flight)
     for (;;) {
-      dec_tile(st, t0, qb, key, kv_len, lane);
+      dec_tile(st, t0, qb, key, kv_len, col_len, pos + 1, lane);
       key += kDecTile;
       if (key >= kend) break;
       dec_load(t0, src, key + kDecTile < kend ? key + kDecTile : key);
-      dec_tile(st, t1, qb, key, kv_len, lane);
+      dec_tile(st, t1, qb, key, kv_len, col_len, pos + 1, lane);
       key += kDecTile;
       if (key >= kend) break;
       dec_load(t1, src, key + kDecTile < kend ? key + kDecTile : key);
@@ -564,7 +581,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDecodeArgs a) {
   for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) st.o[rt][i] = add_ror8(st.o[rt][i]);
-  if (r < g) {
+  if (r < ncols) {
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
@@ -575,11 +592,12 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDecodeArgs a) {
     }
   }
   __syncthreads();
-  // merge the block's four waves into one (max, sum, output) partial per q head
-  float* part = a.part + (((int64_t)b * a.nq + kvh * g) * a.splits + split) * (HD + 2);
-  const int64_t hstride = (int64_t)a.splits * (HD + 2);
-  for (int i = tid; i < g * HD; i += 256) {
+  // merge the block's four waves into one (max, sum, output) partial per query
+  for (int i = tid; i < ncols * HD; i += 256) {
     const int h = i / HD, d = i % HD;
+    const int qh = qg * kMaxGroup + h;
+    float* part = a.part + ((((int64_t)b * a.S + qh / g) * a.nq + kvh * g + qh % g) * a.splits +
+                            split) * (HD + 2);
     float M = -INFINITY;
 #pragma unroll
     for (int v = 0; v < kDecWaves; ++v) M = fmaxf(M, sm[v][h]);
@@ -593,20 +611,20 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDecodeArgs a) {
         L += sl[v][h] * f;
       }
     }
-    part[h * hstride + d] = O;
+    part[d] = O;
     if (d == 0) {
-      part[h * hstride + HD] = M;
-      part[h * hstride + HD + 1] = L;
+      part[HD] = M;
+      part[HD + 1] = L;
     }
   }
 }
 
 __global__ void __launch_bounds__(128) attn_decode_combine_kernel(AttnDecodeArgs a) {
-  const int bh = blockIdx.x;
-  const int b = bh / a.nq;
+  const int bh = blockIdx.x;  // (token row, q head)
+  const int b = bh / a.nq / a.S;
   const int d = threadIdx.x;
   const int pos = a.pos[b];
-  const bool ok = pos >= 0 && pos < a.cap && pos < a.max_pos;
+  const bool ok = pos >= 0 && pos + a.S <= a.cap && pos + a.S <= a.max_pos;
   const float* part = a.part + (int64_t)bh * a.splits * (HD + 2);
   float M = -INFINITY;
   for (int s = 0; s < a.splits; ++s) M = fmaxf(M, part[s * (HD + 2) + HD]);
@@ -644,15 +662,18 @@ void attn_decode_plan(int cap, int B, int nkv, int& splits, int& chunk) {
   chunk = (cap + splits - 1) / splits;
 }
 
+int attn_decode_groups(int S, int g) { return (S * g + kMaxGroup - 1) / kMaxGroup; }
+
 hipError_t attn_decode(const AttnDecodeArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_decode_kernel, dim3(a.splits, a.nkv, a.B), dim3(256), 0, s, a);
+  if (a.S <= 0 || a.nqg != attn_decode_groups(a.S, a.nq / a.nkv)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_decode_kernel, dim3(a.splits, a.nkv, a.B * a.nqg), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t attn_decode_combine(const AttnDecodeArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(a.B * a.nq), dim3(128), 0, s, a);
+  hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(a.B * a.S * a.nq), dim3(128), 0, s, a);
   return hipGetLastError();
 }
 

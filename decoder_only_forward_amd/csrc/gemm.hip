@@ -28,9 +28,9 @@ hipError_t launch_t(Args a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Decode-size products (M <= 64 rows): one block per 16 output columns (SwiGLU: 16 gate
-// columns and the matching 16 up columns) over all rows, the K range split across the
-// block's 8 waves.  Each wave streams its slice of the weights straight from memory into
+// Decode-size products (M <= 256 rows): one block per 16 output columns (SwiGLU: 16 gate
+// columns and the matching 16 up columns) and 64 rows (blockIdx.z), the K range split
+// across the block's 8 waves.  Each wave streams its slice of the weights straight from memory into
 // 16x16x32 fp16 MFMAs (every weight is read once; bf16 -> fp16 is exact in fp16's normal
 // range); the activations come through L2.  The waves' partial sums are added in LDS in a
 // fixed order and the epilogue applied once: no partial sums in memory, one launch.
@@ -38,6 +38,7 @@ hipError_t launch_t(Args a, hipStream_t s) {
 // the accumulator holds column r, rows 4 g .. 4 g + 3.
 constexpr int kDecWaves = 8;
 constexpr int kDecBatch = 4;  // k-steps of 32 loaded per batch
+constexpr int kDecMaxRows = 256;
 
 DEV f32x4_t mfma16h(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a), as_f16x8(b), c, 0, 0, 0);
@@ -69,9 +70,11 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_gemm_kernel(Args p) {
       bp[nt] = p.B0 + (int64_t)col * p.ldb;
     }
   }
+  const int row0 = blockIdx.z * 64;
   const uint16_t* ap[4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) ap[mt] = p.A + (int64_t)min(mt * 16 + r16, p.M - 1) * p.lda;
+  for (int mt = 0; mt < 4; ++mt)
+    ap[mt] = p.A + (int64_t)min(row0 + mt * 16 + r16, p.M - 1) * p.lda;
 
   const int nks_all = p.K / 32;
   const int per_split = (nks_all + gridDim.y - 1) / gridDim.y;
@@ -115,11 +118,11 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_gemm_kernel(Args p) {
       *(f32x4_t*)&red[wave][mt][nt][lane * 4] = acc[mt][nt];
   __syncthreads();
   for (int o = tid; o < 64 * 16; o += 64 * kDecWaves) {
-    const int m = o >> 4, n = o & 15;
+    const int ml = o >> 4, n = o & 15, m = row0 + ml;
     if (m >= p.M) continue;
     const int col = c0 + n;
     if (col >= ncols) continue;
-    const int mt = m >> 4, rr = m & 15;
+    const int mt = ml >> 4, rr = ml & 15;
     const int slot = (n + 16 * (rr >> 2)) * 4 + (rr & 3);
     float v[NT];
 #pragma unroll
@@ -145,11 +148,12 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_gemm_kernel(Args p) {
 template <int BMODE, int EPI>
 hipError_t launch_decode(const Args& a, int splits, hipStream_t s) {
   const int ncols = BMODE == B_SWIGLU ? a.N / 2 : a.N;
+  const int chunks = (a.M + 63) / 64;
   if (splits > 1)
-    hipLaunchKernelGGL((decode_gemm_kernel<BMODE, EPI, true>), dim3((ncols + 15) / 16, splits),
-                       dim3(64 * kDecWaves), 0, s, a);
+    hipLaunchKernelGGL((decode_gemm_kernel<BMODE, EPI, true>),
+                       dim3((ncols + 15) / 16, splits, chunks), dim3(64 * kDecWaves), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_gemm_kernel<BMODE, EPI, false>), dim3((ncols + 15) / 16),
+    hipLaunchKernelGGL((decode_gemm_kernel<BMODE, EPI, false>), dim3((ncols + 15) / 16, 1, chunks),
                        dim3(64 * kDecWaves), 0, s, a);
   return hipGetLastError();
 }
@@ -159,14 +163,15 @@ hipError_t launch_decode(const Args& a, int splits, hipStream_t s) {
 GemmPlan gemm_plan(int M, int N, int K, int bmode, int epi, bool grouped) {
   GemmPlan p{kMid, 1};
   if (grouped) return p;
-  if (M <= 64) {
-    // fp32 outputs (LM head, router) keep the 64x128 tile: its k order is that of the
-    // larger tiles, so last-position logits equal the corresponding rows of a full pass
+  if (M <= 64 || (M <= kDecMaxRows && epi != E_F32)) {
+    // fp32 outputs (LM head, router) keep the 64x128 tile (the larger tiles above 64
+    // rows): its k order is that of the larger tiles, so last-position logits equal the
+    // corresponding rows of a full pass
     p.tile = epi == E_F32 ? kSkinny : kDecode;
     // residual projections with few output columns split K over extra blocks; the caller
     // reduces the partials (fused with the residual add and the following RMSNorm)
     const bool res = epi == E_RES_F32 || epi == E_RESB_F32 || epi == E_RESF_B16;
-    const int blocks = (N + 15) / 16;
+    const int blocks = (N + 15) / 16 * ((M + 63) / 64);
     if (p.tile == kDecode && res && blocks < 128) {
       const int want = (256 + blocks - 1) / blocks;
       p.k_splits = std::max(1, std::min(want, K / (32 * kDecWaves)));
@@ -187,7 +192,7 @@ hipError_t gemm_run(const Args& a_in, bool f16, int bmode, int epi, bool grouped
   Args a = a_in;
   const GemmPlan& pl = plan;
   if (pl.tile == kDecode) {
-    if (grouped || !f16 || a.M > 64) return hipErrorInvalidValue;
+    if (grouped || !f16 || a.M > kDecMaxRows) return hipErrorInvalidValue;
     if (pl.k_splits > 1) {  // partial sums only (bmode dense, any residual epilogue)
       if (bmode != B_DENSE || a.partial == nullptr) return hipErrorInvalidValue;
       return launch_decode<B_DENSE, E_RES_F32>(a, pl.k_splits, s);

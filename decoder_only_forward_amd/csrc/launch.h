@@ -53,7 +53,7 @@ struct RopeCacheArgs {
   f16_t* q_out;  // [T][nq][hd] fp16, pre-scaled by log2(e) / sqrt(hd)
   bf16_t* k_cache;  // [B][nkv][cap][hd]
   bf16_t* vt_cache; // [B][nkv][hd][cap]
-  const int32_t* pos;  // decode: device [B] (S == 1); prefill: nullptr
+  const int32_t* pos;  // decode: device [B], token s at pos[b] + s; prefill: nullptr
   // prefill only: fp16 copies of the new keys / values (not rounded to bf16) for the attention,
   // indexed by absolute position - fresh_base; k_fresh [B][nkv][fresh_w][hd],
   // vt_fresh [B][nkv][hd][fresh_w] (nullptr: not written)
@@ -81,14 +81,17 @@ struct AttnPrefillArgs {
 hipError_t attn_prefill(const AttnPrefillArgs& a, hipStream_t s);
 
 struct AttnDecodeArgs {
-  const f16_t* q;   // [B][nq][hd] fp16
+  const f16_t* q;   // [B][S][nq][hd] fp16
   const bf16_t* k_cache;
   const bf16_t* vt_cache;
-  const int32_t* pos;  // device [B]
-  f16_t* out;          // [B][nq][hd] fp16
-  float* part;         // [B][nq][splits][hd + 2]
-  int B, nq, nkv, cap, max_pos, splits, chunk;
+  const int32_t* pos;  // device [B]: token s of sequence b sits at pos[b] + s
+  f16_t* out;          // [B][S][nq][hd] fp16
+  float* part;         // [B][S][nq][splits][hd + 2]
+  int B, S, nq, nkv, cap, max_pos, splits, chunk;
+  int nqg;  // query groups of 8 per (sequence, kv head): attn_decode_groups(S, nq / nkv)
 };
+int attn_decode_groups(int S, int g);
+// blocks: B * attn_decode_groups(S, g) per kv head
 void attn_decode_plan(int cap, int B, int nkv, int& splits, int& chunk);
 hipError_t attn_decode(const AttnDecodeArgs& a, hipStream_t s);
 hipError_t attn_decode_combine(const AttnDecodeArgs& a, hipStream_t s);

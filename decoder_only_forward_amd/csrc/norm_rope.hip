@@ -102,8 +102,10 @@ DEV float ror16(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
 }
 
-// DECODE: one token per sequence at its own position (a.pos); the kernel is compiled
-// separately for it so the prefill path keeps all of its loads unconditional.
+// DECODE: the S new tokens of sequence b at positions pos[b] .. pos[b] + S - 1 (a sequence
+// whose last position falls outside the cache or the RoPE table writes nothing and gets NaN
+// q rows); the kernel is compiled separately for it so the prefill path keeps all of its
+// loads unconditional.
 template <bool DECODE>
 __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
   const int HD = 128;
@@ -156,9 +158,16 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
       live_r[k] = s < a.S;
       const int sc = live_r[k] ? s : a.S - 1;
       const int64_t t = (int64_t)b * a.S + sc;
-      const int pos = DECODE ? a.pos[b] : a.pos0 + sc;
+      int pos;
+      if (DECODE) {
+        const int p0 = a.pos[b];
+        pos = p0 + sc;
+        ok_r[k] = p0 >= 0 && p0 + a.S <= a.cap && p0 + a.S <= a.max_pos;
+      } else {
+        pos = a.pos0 + sc;
+        ok_r[k] = pos >= 0 && pos < a.cap && pos < a.max_pos;
+      }
       pos_r[k] = pos;
-      ok_r[k] = pos >= 0 && pos < a.cap && pos < a.max_pos;
       // decode: rows other than the one token load nothing; prefill rows past the end
       // load a clamped row so that every load is unconditional
       if (DECODE && !live_r[k]) continue;
@@ -265,12 +274,13 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
   }
   __syncthreads();
   if (DECODE) {
-    // decode: one token per sequence, each at its own position
-    for (int d = tid; d < HD; d += 256) {
-      if (a.S < 1) break;
-      const int pos = a.pos[b];
-      if (pos < 0 || pos >= a.cap || pos >= a.max_pos) break;
-      a.vt_cache[(((int64_t)b * a.nkv + h) * HD + d) * a.cap + pos] = f2bf(sv[0][d]);
+    // decode: this tile's tokens of the sequence, from its own position on
+    const int p0 = a.pos[b];
+    if (p0 < 0 || p0 + a.S > a.cap || p0 + a.S > a.max_pos) return;
+    const int n = min(kRopeTile, a.S - s0);
+    for (int i = tid; i < HD * n; i += 256) {
+      const int d = i / n, r = i % n;
+      a.vt_cache[(((int64_t)b * a.nkv + h) * HD + d) * a.cap + p0 + s0 + r] = f2bf(sv[r][d]);
     }
     return;
   }

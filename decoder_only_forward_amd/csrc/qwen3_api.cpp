@@ -132,7 +132,7 @@ DenseLayout dense_layout(const qwen3_config* c, int op, int B, int S, int cap_hi
   DenseLayout L{};
   const bool decode = op == QWEN3_OP_BLOCK_DECODE || op == QWEN3_OP_STACK_DECODE;
   const bool stack = op == QWEN3_OP_STACK_PREFILL || op == QWEN3_OP_STACK_DECODE;
-  const int T = decode ? B : B * S;
+  const int T = B * S;  // decode: S new tokens per sequence
   const int H = c->hidden_size, nq = c->num_attention_heads, nkv = c->num_key_value_heads,
             hd = c->head_dim, I = c->intermediate_size;
   L.T = T;
@@ -150,8 +150,9 @@ DenseLayout dense_layout(const qwen3_config* c, int op, int B, int S, int cap_hi
     L.vtf = b.take((size_t)B * nkv * L.fresh_w_max * hd * 2);
   }
   if (decode) {
-    attn_decode_plan(cap_hint, B, nkv, L.attn_splits, L.attn_chunk);
-    L.part_attn = b.take((size_t)B * nq * L.attn_splits * (hd + 2) * 4);
+    attn_decode_plan(cap_hint, B * attn_decode_groups(S, nq / nkv), nkv, L.attn_splits,
+                     L.attn_chunk);
+    L.part_attn = b.take((size_t)T * nq * L.attn_splits * (hd + 2) * 4);
   }
   {
     // K-split partial sums of the residual projections (decode sizes only)
@@ -451,7 +452,7 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
     r.qkv = qkv; r.rope = rope;
     r.q_norm = (const bf16_t*)w->q_norm; r.k_norm = (const bf16_t*)w->k_norm;
     r.q_out = q; r.k_cache = (bf16_t*)kv->k; r.vt_cache = (bf16_t*)kv->vt;
-    r.pos = io.pos; r.pos0 = io.pos0; r.B = io.B; r.S = io.pos ? 1 : io.S;
+    r.pos = io.pos; r.pos0 = io.pos0; r.B = io.B; r.S = io.S;
     r.nq = nq; r.nkv = nkv; r.cap = kv->capacity; r.max_pos = c->max_position_embeddings;
     r.qk_norm = c->qk_norm; r.eps = eps;
     r.interleaved = c->rope_interleaved;
@@ -469,9 +470,10 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
     AttnDecodeArgs d{};
     d.q = q; d.k_cache = (const bf16_t*)kv->k; d.vt_cache = (const bf16_t*)kv->vt;
     d.pos = io.pos; d.out = attn; d.part = (float*)(ws + L.part_attn);
-    d.B = io.B; d.nq = nq; d.nkv = nkv; d.cap = kv->capacity;
+    d.B = io.B; d.S = io.S; d.nq = nq; d.nkv = nkv; d.cap = kv->capacity;
     d.max_pos = c->max_position_embeddings;
-    attn_decode_plan(kv->capacity, io.B, nkv, d.splits, d.chunk);
+    d.nqg = attn_decode_groups(io.S, nq / nkv);
+    attn_decode_plan(kv->capacity, io.B * d.nqg, nkv, d.splits, d.chunk);
     {
       ProfScope ps("attn_decode", s);
       CHECK_HIP(attn_decode(d, s));
@@ -642,9 +644,11 @@ size_t qwen3_workspace_bytes(const qwen3_config* c, int32_t op, int32_t batch, i
     return gen_layout(c, batch, seq_len, cap).total;
   }
   if (op == QWEN3_OP_BLOCK_DECODE || op == QWEN3_OP_STACK_DECODE) {
-    // decode partials scale with the cache capacity; size for max_position_embeddings
+    // decode partials scale with the cache capacity; size for max_position_embeddings.
+    // The stack decodes seq_len new tokens per sequence (at least one).
     int cap = ((c->max_position_embeddings + 63) / 64) * 64;
-    return dense_layout(c, op, batch, 1, cap).total;
+    const int S = op == QWEN3_OP_STACK_DECODE ? std::max(1, (int)seq_len) : 1;
+    return dense_layout(c, op, batch, S, cap).total;
   }
   if (op != QWEN3_OP_BLOCK_PREFILL && op != QWEN3_OP_STACK_PREFILL) {
     fail(QWEN3_EINVAL, "unknown op %d", op);
@@ -761,13 +765,13 @@ int stack_run(const qwen3_config* c, const qwen3_model_weights* w, const float* 
               const int32_t* pos, const qwen3_kv_layer* caches, float* logits,
               int32_t logits_mode, int32_t* next_ids, char* ws, const DenseLayout& L,
               hipStream_t s) {
-  const bool decode = seq_len == 1 && pos != nullptr;
+  const bool decode = pos != nullptr;
   const int H = c->hidden_size, V = c->vocab_size, T = L.T;
   float* res = (float*)(ws + L.res);
   CHECK_HIP(embed_gather(ids, (const bf16_t*)w->embed_tokens, res, T, H, V, s));
   LayerIO io{};
-  io.T = T; io.B = batch; io.S = decode ? 1 : seq_len; io.pos0 = pos0;
-  io.pos = decode ? pos : nullptr; io.res = res;
+  io.T = T; io.B = batch; io.S = seq_len; io.pos0 = decode ? 0 : pos0;
+  io.pos = pos; io.res = res;
   bool normed = false;
   for (int l = 0; l < c->num_hidden_layers; ++l) {
     io.input_normed = normed;
@@ -835,9 +839,15 @@ int qwen3_stack_forward(const qwen3_config* c, const qwen3_model_weights* w, con
       logits_mode != QWEN3_LOGITS_LAST)
     return fail(QWEN3_EINVAL, "logits_mode=%d", logits_mode);
   if (logits_mode != QWEN3_LOGITS_NONE) REQ_PTR(logits, "logits");
-  const bool decode = seq_len == 1 && pos != nullptr;
-  if (!decode)
+  const bool decode = pos != nullptr;
+  if (decode) {
+    // the positions live on the device: the kernels check them (NaN rows, no writes)
+    if (seq_len > std::min(caches[0].capacity, c->max_position_embeddings))
+      return fail(QWEN3_ERANGE, "seq_len=%d exceeds the cache capacity %d", seq_len,
+                  caches[0].capacity);
+  } else {
     for (int l = 0; l < c->num_hidden_layers; ++l) TRY(check_range(c, &caches[l], pos0, seq_len));
+  }
   const int op = decode ? QWEN3_OP_STACK_DECODE : QWEN3_OP_STACK_PREFILL;
   DenseLayout L = dense_layout(c, op, batch, seq_len, caches[0].capacity);
   if (!aligned16(workspace) || workspace_bytes < L.total)

@@ -4,6 +4,7 @@
  * The operations follow the hand-built Qwen3 described on these web pages
  * (sections named as on the pages):
  *   [P1] "Building Qwen-3 MoE from scratch" (adg.csdn.net), sections 5-13.
+ *   [P2] "手搓一个Qwen3" (news.43b.com.cn), section 4 (KV cache and offset mask).
  *   [P3] "从零实现 Qwen3：拆解 mini-qwen3 的 0.6B Dense 架构" (quarkcode.cn):
  *        config table, "骨架", "prefill 与 decode", "RMSNorm", "GQA 注意力",
  *        "RoPE", "SwiGLU FFN", "TransformerBlock", "MoE".
@@ -145,8 +146,10 @@ typedef struct qwen3_kv_layer {
 #define QWEN3_LOGITS_LAST 2 /* [B][V]: last position of each sequence */
 
 /* Bytes of workspace needed by `op` for `batch` sequences of `seq_len` new tokens
- * (for QWEN3_OP_MOE_FFN: batch = number of tokens, seq_len ignored).  Returns 0 for an
- * invalid configuration (qwen3_last_error() says why). */
+ * (QWEN3_OP_MOE_FFN: batch = number of tokens, seq_len ignored; QWEN3_OP_BLOCK_DECODE: one
+ * token per sequence; QWEN3_OP_STACK_DECODE: seq_len new tokens per sequence, at least 1;
+ * decode sizes hold for any cache capacity up to max_position_embeddings).  Returns 0 for
+ * an invalid configuration (qwen3_last_error() says why). */
 size_t qwen3_workspace_bytes(const qwen3_config *cfg, int32_t op, int32_t batch,
                              int32_t seq_len);
 
@@ -202,9 +205,14 @@ int qwen3_moe_ffn(const qwen3_config *cfg, const qwen3_moe_weights *w, const voi
  * blocks with an fp32 residual stream, final RMSNorm, LM head (tied unless
  * tie_word_embeddings == 0), optional greedy argmax.
  *   ids: device int32 [batch][seq_len], each in [0, V) (an out-of-range id gives a NaN row)
- *   seq_len > 1 or pos == NULL: prefill of every sequence from position pos0
- *     (pos0 + seq_len <= capacity, <= max_position_embeddings).
- *   seq_len == 1 and pos != NULL: decode step, sequence b at device position pos[b].
+ *   pos == NULL: prefill of every sequence from position pos0 (pos0 + seq_len <= capacity,
+ *     <= max_position_embeddings).
+ *   pos != NULL: decode of seq_len new tokens per sequence; token s of sequence b takes
+ *     position pos[b] + s (device int32 [batch]) and sees cache slots 0 .. pos[b] - 1 and
+ *     the new tokens 0 .. s ([P3] "prefill 与 decode", [P2] section 4's mask slice).  A
+ *     sequence with pos[b] < 0 or pos[b] + seq_len beyond the capacity or
+ *     max_position_embeddings is not written and yields NaN rows; seq_len itself must fit
+ *     the capacity (ERANGE).
  *   caches: HOST array [L] of per-layer caches (required).
  *   logits: fp32, layout by logits_mode (NULL only with QWEN3_LOGITS_NONE).
  *   next_ids: device int32 [batch] (nullable): argmax of each sequence's last-position
