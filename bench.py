@@ -153,21 +153,23 @@ def wl_prefill(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, 
 
 def dense_units(cfg, B, S, launches):
     """Algorithmic work per launch of each dense-block kernel class for a prefill of B x S
-    tokens from position 0 (causal pairs only; the q/k-norm + RoPE + cache-write pass is
-    priced at the bytes this design moves: fp16 q/k/v in, fp16 q and bf16 cache plus fp16
-    fresh K/V out)."""
+    tokens from position 0 (causal pairs only).  Above 256 tokens the q/k-norm + RoPE +
+    cache writes run in the QKV projection's epilogue; below, as a separate pass priced at
+    the bytes it moves: fp16 q/k/v in, fp16 q and bf16 cache plus fp16 fresh K/V out."""
     H, nq, nkv, hd, I = (cfg["hidden_size"], cfg["num_attention_heads"],
                          cfg["num_key_value_heads"], cfg["head_dim"], cfg["intermediate_size"])
     T = B * S
     rope_bytes = T * (nq + 2 * nkv) * hd * 2 + T * nq * hd * 2 + 4.0 * T * nkv * hd * 2
-    return {
+    units = {
         "qkv_gemm": ("mfma", 2.0 * T * H * (nq + 2 * nkv) * hd, launches),
-        "qk_norm_rope_cache": ("hbm", float(rope_bytes), launches),
         "attn_prefill": ("mfma", 4.0 * hd * nq * B * S * (S + 1) / 2, launches),
         "o_proj_gemm": ("mfma", 2.0 * T * nq * hd * H, launches),
         "gate_up_gemm": ("mfma", 2.0 * T * H * 2 * I, launches),
         "down_gemm": ("mfma", 2.0 * T * I * H, launches),
     }
+    if T <= 256:
+        units["qk_norm_rope_cache"] = ("hbm", float(rope_bytes), launches)
+    return units
 
 
 def moe_units(cfg, T, launches):

@@ -108,6 +108,12 @@ DEV void st16(void* p, u32x4_t v) { *(u32x4_t*)p = v; }
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// x from the lane N places round the same 16-lane row (DPP row_ror)
+template <int N>
+DEV float ror16(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+}
+
 // Asynchronous 16-byte global -> LDS copy (global_load_lds_dwordx4): the 64 lanes of the
 // wave write 1 KB at lds_base + 16 * lane (lds_base must be wave-uniform).  It is issued
 // from inline asm so that the compiler does not make every later LDS read wait for it

@@ -206,6 +206,8 @@ hipError_t gemm_run(const Args& a_in, bool f16, int bmode, int epi, bool grouped
   }
   // dense layers: fp16 activations x bf16->fp16 weights
   GEMM_CASE(kBig, TBig, true, B_QKV, E_F16, false)
+  GEMM_CASE(kBig, TBig, true, B_QKV, E_QKROPE, false)
+  GEMM_CASE(kMid, TMid, true, B_QKV, E_QKROPE, false)
   GEMM_CASE(kBig, TBig, true, B_DENSE, E_RES_F32, false)
   GEMM_CASE(kBig, TBig, true, B_DENSE, E_RESB_F32, false)
   GEMM_CASE(kBig, TBig, true, B_DENSE, E_RESF_B16, false)

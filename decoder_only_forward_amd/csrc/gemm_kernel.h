@@ -21,6 +21,10 @@
 //   E_RESB_F32  out_f32 = float(res_bf16) + acc          (o_proj in the block API)
 //   E_RESF_B16  out_bf16 = bf16(res_f32 + acc)           (down in the block API)
 //   E_SWIGLU    out_f16[:, c] = f16(silu(g) * u)         (gate|up with SwiGLU)
+//   E_QKROPE    QKV projections of a prefill: the tile is rounded to fp16 and staged in
+//               LDS, then per (token, head): q/k RMSNorm, RoPE, q to q_out (pre-scaled
+//               fp16), k to the bf16 cache and its fp16 copy, v transposed to the V^T
+//               cache and its fp16 copy (see RopeEpi)
 // B row sources:
 //   B_DENSE   one matrix;  B_QKV  q/k/v weights stacked along N without a copy;
 //   B_SWIGLU  gate and up rows interleaved per wave so that a lane holds the gate and
@@ -34,7 +38,22 @@
 namespace gemm {
 
 enum BMode { B_DENSE = 0, B_QKV = 1, B_SWIGLU = 2 };
-enum EpiMode { E_F32 = 1, E_RES_F32, E_RESB_F32, E_RESF_B16, E_SWIGLU, E_F16 };
+enum EpiMode { E_F32 = 1, E_RES_F32, E_RESB_F32, E_RESF_B16, E_SWIGLU, E_F16, E_QKROPE };
+
+// Destination of the E_QKROPE epilogue (a prefill of B sequences of S tokens from pos0;
+// output row t is token t % S of sequence t / S at position pos0 + t % S).
+struct RopeEpi {
+  const float* table;  // [2][max_pos][hd/2]: cos, then sin
+  const bf16_t* q_norm;
+  const bf16_t* k_norm;
+  f16_t* q_out;      // [T][nq][hd], pre-scaled by log2(e) / sqrt(hd)
+  bf16_t* k_cache;   // [B][nkv][cap][hd]
+  bf16_t* vt_cache;  // [B][nkv][hd][cap]
+  f16_t* k_fresh;    // [B][nkv][fresh_w][hd], position - fresh_base
+  f16_t* vt_fresh;   // [B][nkv][hd][fresh_w]
+  int fresh_base, fresh_w, pos0, S, nq, nkv, cap, max_pos, qk_norm, interleaved;
+  float eps;
+};
 
 struct Args {
   int M, N, K;  // N counts virtual columns (gate|up: 2 * I)
@@ -58,6 +77,7 @@ struct Args {
   const int32_t* g_tile_row0;    // [m_tiles] first row within the expert
   const int32_t* g_tile_count;   // [1] m tiles in use (nullptr: all m_tiles)
   int64_t g_b_stride;            // elements between experts' B matrices
+  RopeEpi re;                    // E_QKROPE only
 };
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_ = 64, int STAGES_ = 2>
@@ -116,10 +136,195 @@ DEV void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | 0x0F70);
 }
 
+// E_QKROPE epilogue.  Columns n0 .. n0 + BN of the B_QKV product lie in one segment (q, k or
+// v heads: BN divides the segment boundaries), each 128 columns one head.  The block's fp16
+// tile is staged in LDS ([BM][BN + 8], rows padded by 16 bytes), then
+//   q / k heads: 16 lanes per (token, head), 8 dims each: RMSNorm over the head (sum of
+//     squares by row-local DPP rotations), RoPE (rotate-half: dim d pairs with d ^ 64, held
+//     by lane j ^ 8; interleaved: planes (2i, 2i + 1) inside a lane), 16-byte stores;
+//   v heads: one lane per (dim, 8 consecutive tokens), transposed 16-byte stores where the
+//     8 tokens are one sequence's aligned positions, element stores otherwise.
+template <class T>
+DEV void qkrope_epilogue(const Args& p, const f32x16_t (&acc)[T::TM][T::TN], f16_t* st,
+                         int out_row0, int rows_valid, int n0, int wm, int wn, int lane,
+                         int wave) {
+  constexpr int HD = 128, LDT = T::BN + 8, HEADS = T::BN / HD;
+  const RopeEpi& e = p.re;
+  const int ccol = lane & 31, rsub = (lane >> 5) * 4;
+  __syncthreads();  // every wave is done with the operand ring
+#pragma unroll
+  for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lr = wm * T::WM + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
+        st[lr * LDT + wn * T::WN + j * 32 + ccol] = f2h(acc[i][j][r]);
+      }
+  __syncthreads();
+  const int tid = threadIdx.x;
+  if (n0 < p.seg2) {
+    const bool is_q = n0 < p.seg1;
+    const int head0 = is_q ? n0 / HD : (n0 - p.seg1) / HD;
+    const int nh = is_q ? e.nq : e.nkv;
+    const int j16 = lane & 15, sub = lane >> 4, d0 = 8 * j16;
+    const int half = HD / 2;
+    const int i0 = e.interleaved ? d0 / 2 : d0 & (half - 1);
+    const float sgn = d0 < half ? -1.f : 1.f;
+    const float qs = 0.08838834764831845f * kLog2e;
+    float w[8];
+    if (e.qk_norm) {
+      unpack8(ld16((is_q ? e.q_norm : e.k_norm) + d0), w);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w[k] = 1.f;
+    }
+    // NB items per lane at a time: all their LDS reads and RoPE table loads are issued
+    // before any is used, so one table latency covers the batch
+    constexpr int NB = 8, STEP = T::NWAVES * 4;
+    const int n_items = rows_valid * HEADS;
+    for (int base = wave * 4 + sub; base < n_items; base += NB * STEP) {
+      u32x4_t raw[NB];
+      f32x4_t tc[NB][2], ts[NB][2];
+      int pos_k[NB];
+      bool ok_k[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int item = min(base + u * STEP, n_items - 1);
+        const int lr = item / HEADS, hl = item % HEADS;
+        const int64_t t = out_row0 + lr;
+        const int pos = e.pos0 + (int)(t % e.S);
+        pos_k[u] = pos;
+        ok_k[u] = pos >= 0 && pos < e.cap && pos < e.max_pos;
+        raw[u] = ld16(st + lr * LDT + hl * HD + d0);
+        const int pc = ok_k[u] ? pos : 0;
+        const float* cp = e.table + (int64_t)pc * half + i0;
+        const float* sp = e.table + ((int64_t)e.max_pos + pc) * half + i0;
+        tc[u][0] = *(const f32x4_t*)cp;
+        ts[u][0] = *(const f32x4_t*)sp;
+        if (!e.interleaved) {
+          tc[u][1] = *(const f32x4_t*)(cp + 4);
+          ts[u][1] = *(const f32x4_t*)(sp + 4);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int item = base + u * STEP;
+        if (item >= n_items) break;
+        const int lr = item / HEADS, hl = item % HEADS;
+        const int h = head0 + hl;
+        const int64_t t = out_row0 + lr;
+        const int b = (int)(t / e.S);
+        const int pos = pos_k[u];
+        const bool ok = ok_k[u];
+        float x[8];
+        unpack8_f16(raw[u], x);
+        if (e.qk_norm) {
+          float ss = 0.f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) ss += x[k] * x[k];
+          ss += ror16<8>(ss);
+          ss += ror16<4>(ss);
+          ss += ror16<2>(ss);
+          ss += ror16<1>(ss);
+          const float inv = rsqrtf(ss / (float)HD + e.eps);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) x[k] = x[k] * inv * w[k];
+        }
+        float y[8];
+        if (e.interleaved) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float c = ok ? tc[u][0][k] : 0.f, sn = ok ? ts[u][0][k] : 0.f;
+            y[2 * k] = x[2 * k] * c - x[2 * k + 1] * sn;
+            y[2 * k + 1] = x[2 * k] * sn + x[2 * k + 1] * c;
+          }
+        } else {
+          float c[8], sn[8];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            c[k] = ok ? tc[u][0][k] : 0.f;
+            c[k + 4] = ok ? tc[u][1][k] : 0.f;
+            sn[k] = ok ? ts[u][0][k] : 0.f;
+            sn[k + 4] = ok ? ts[u][1][k] : 0.f;
+          }
+#pragma unroll
+          for (int k = 0; k < 8; ++k) y[k] = x[k] * c[k] + sgn * ror16<8>(x[k]) * sn[k];
+        }
+        if (h >= nh) continue;
+        if (is_q) {
+          u32x4_t o;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            o[k] = ok ? pack_f16x2(y[2 * k] * qs, y[2 * k + 1] * qs) : 0x7E007E00u;
+          st16(e.q_out + (t * e.nq + h) * HD + d0, o);
+        } else if (ok) {
+          u32x4_t kb, kh;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            kb[k] = pack_bf16x2(y[2 * k], y[2 * k + 1]);
+            kh[k] = pack_f16x2(y[2 * k], y[2 * k + 1]);
+          }
+          st16(e.k_cache + (((int64_t)b * e.nkv + h) * e.cap + pos) * HD + d0, kb);
+          if (e.k_fresh)
+            st16(e.k_fresh + (((int64_t)b * e.nkv + h) * e.fresh_w + (pos - e.fresh_base)) * HD +
+                     d0, kh);
+        }
+      }
+    }
+    return;
+  }
+  // v heads: item = (column c, group of 8 rows); consecutive lanes take consecutive groups
+  // so that a wave's stores run along positions
+  const int head0 = (n0 - p.seg2) / HD;
+  constexpr int RG = T::BM / 8;
+  for (int item = tid; item < T::BN * RG; item += T::THREADS) {
+    const int c = item / RG, r0 = (item % RG) * 8;
+    const int h = head0 + c / HD, d = c % HD;
+    if (h >= e.nkv || r0 >= rows_valid) continue;
+    const int64_t t0 = out_row0 + r0;
+    const int b = (int)(t0 / e.S), s0 = (int)(t0 % e.S);
+    const int pos = e.pos0 + s0;
+    const int n = min(8, rows_valid - r0);
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = h2f(st[(r0 + (k < n ? k : 0)) * LDT + c]);
+    bf16_t* vb = e.vt_cache + (((int64_t)b * e.nkv + h) * HD + d) * e.cap + pos;
+    f16_t* vf = e.vt_fresh ? e.vt_fresh + (((int64_t)b * e.nkv + h) * HD + d) * e.fresh_w +
+                                 (pos - e.fresh_base)
+                           : nullptr;
+    if (n == 8 && s0 + 8 <= e.S && (pos & 7) == 0 && pos + 8 <= e.cap &&
+        (!vf || ((pos - e.fresh_base) & 7) == 0)) {
+      u32x4_t ob, oh;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        ob[k] = pack_bf16x2(v[2 * k], v[2 * k + 1]);
+        oh[k] = pack_f16x2(v[2 * k], v[2 * k + 1]);
+      }
+      st16(vb, ob);
+      if (vf) st16(vf, oh);
+    } else {
+      // rows may cross into the next sequence: place each token by its own (b, s)
+      for (int k = 0; k < n; ++k) {
+        const int64_t t = t0 + k;
+        const int bk = (int)(t / e.S), sk = (int)(t % e.S), pk = e.pos0 + sk;
+        if (pk < 0 || pk >= e.cap || pk >= e.max_pos) continue;
+        const int64_t base = ((int64_t)bk * e.nkv + h) * HD + d;
+        e.vt_cache[base * e.cap + pk] = f2bf(v[k]);
+        if (e.vt_fresh) e.vt_fresh[base * e.fresh_w + (pk - e.fresh_base)] = f2h(v[k]);
+      }
+    }
+  }
+}
+
 template <class T, bool F16, int BMODE, int EPI, bool GROUPED>
 __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[T::STAGES][T::BM * T::BK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[T::STAGES][T::BN * T::BK];
+  // operand ring; the E_QKROPE epilogue reuses it (and more) for the fp16 output tile
+  constexpr int kRing = T::STAGES * (T::BM + T::BN) * T::BK * 2;
+  constexpr int kEpiLds = EPI == E_QKROPE ? T::BM * (T::BN + 8) * 2 : 0;
+  __shared__ __attribute__((aligned(16))) char smem[kRing > kEpiLds ? kRing : kEpiLds];
+  bf16_t* const sA = (bf16_t*)smem;                            // [STAGES][BM * BK]
+  bf16_t* const sB = sA + T::STAGES * T::BM * T::BK;           // [STAGES][BN * BK]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -211,10 +416,10 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
     const int koff = kt * T::BK;
 #pragma unroll
     for (int i = 0; i < A_INSTS; ++i)
-      lds_dma16(aptr[i] + koff, &sA[st][(wave * A_INSTS + i) * 512]);
+      lds_dma16(aptr[i] + koff, sA + st * (T::BM * T::BK) + (wave * A_INSTS + i) * 512);
 #pragma unroll
     for (int i = 0; i < B_INSTS; ++i)
-      lds_dma16(bptr[i] + koff, &sB[st][(wave * B_INSTS + i) * 512]);
+      lds_dma16(bptr[i] + koff, sB + st * (T::BN * T::BK) + (wave * B_INSTS + i) * 512);
   };
 
   // prologue: the first STAGES - 1 k-steps in flight, then wait for the first one
@@ -234,10 +439,10 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
     const int c = 2 * kk + fhalf;
 #pragma unroll
     for (int i = 0; i < T::TM; ++i)
-      fa[slot][i] = ld16(&sA[s][lds_off<T::BK>(wm * T::WM + i * 32 + frow, c)]);
+      fa[slot][i] = ld16(sA + s * (T::BM * T::BK) + lds_off<T::BK>(wm * T::WM + i * 32 + frow, c));
 #pragma unroll
     for (int j = 0; j < T::TN; ++j) {
-      u32x4_t v = ld16(&sB[s][lds_off<T::BK>(wn * T::WN + j * 32 + frow, c)]);
+      u32x4_t v = ld16(sB + s * (T::BN * T::BK) + lds_off<T::BK>(wn * T::WN + j * 32 + frow, c));
       fb[slot][j] = F16 ? bf16x8_to_f16x8(v) : v;
     }
   };
@@ -281,6 +486,10 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
   // column l%32 of the MFMA tile.
   const int ccol = lane & 31;
   const int rsub = (lane >> 5) * 4;
+  if constexpr (EPI == E_QKROPE) {
+    qkrope_epilogue<T>(p, acc, (f16_t*)smem, out_row0, rows_valid, n0, wm, wn, lane, wave);
+    return;
+  }
   if (EPI == E_SWIGLU) {
     constexpr int HALF_TN = T::TN / 2;
 #pragma unroll

@@ -97,10 +97,6 @@ rope_table_kernel(float* __restrict__ rope, int max_pos, int half, double theta,
 constexpr int kRopeTile = 64;
 
 // rotate within 16-lane rows by n (n in 1..15)
-template <int N>
-DEV float ror16(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
-}
 
 // DECODE: the S new tokens of sequence b at positions pos[b] .. pos[b] + S - 1 (a sequence
 // whose last position falls outside the cache or the RoPE table writes nothing and gets NaN
@@ -420,6 +416,30 @@ hipError_t embed_gather(const int32_t* ids, const bf16_t* table, float* out, int
 hipError_t rope_table(float* rope, int max_pos, int hd, double theta, hipStream_t s) {
   hipLaunchKernelGGL(rope_table_kernel, dim3(blocks_for((int64_t)max_pos * hd / 2, 256)),
                      dim3(256), 0, s, rope, max_pos, hd / 2, theta, hd);
+  return hipGetLastError();
+}
+
+// The fp16 copies are read in whole 64-position tiles: zero each (sequence, kv head)'s tail
+// from the last new position to the padded width (the fused QKV epilogue writes only the
+// new positions).
+__global__ void __launch_bounds__(256) fresh_tail_zero_kernel(RopeCacheArgs a) {
+  const int HD = 128;
+  const int b = blockIdx.x, h = blockIdx.y;
+  const bool is_k = blockIdx.z == 0;
+  const int t0 = a.pos0 + a.S - a.fresh_base, nt = a.fresh_w - t0;
+  for (int i = threadIdx.x; i < nt * HD; i += 256) {
+    const int r = t0 + i / HD, d = i % HD;
+    if (is_k)
+      a.k_fresh[(((int64_t)b * a.nkv + h) * a.fresh_w + r) * HD + d] = 0;
+    else
+      a.vt_fresh[(((int64_t)b * a.nkv + h) * HD + d) * a.fresh_w + r] = 0;
+  }
+}
+
+hipError_t fresh_tail_zero(const RopeCacheArgs& a, hipStream_t s) {
+  if (a.B <= 0 || !a.k_fresh || !a.vt_fresh) return hipSuccess;
+  if (a.pos0 + a.S - a.fresh_base > a.fresh_w) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fresh_tail_zero_kernel, dim3(a.B, a.nkv, 2), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

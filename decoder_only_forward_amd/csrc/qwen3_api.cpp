@@ -432,8 +432,24 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
     CHECK_HIP(rmsnorm_bf16(io.x_bf16, 1, 0, (const bf16_t*)w->input_layernorm, xn, T, H, eps, s));
   }
 
-  // QKV projection (q, k, v weights stacked along N without a copy), fp16 out: one
-  // rounding 4x finer than the bf16 cache that the keys end in
+  // QKV projection (q, k, v weights stacked along N without a copy), rounded to fp16 (4x
+  // finer than the bf16 cache the keys end in), then q/k RMSNorm + RoPE and the K/V cache
+  // writes: fused into the projection's epilogue for prefill tiles, a separate pass for
+  // decode-size products
+  RopeCacheArgs r{};
+  r.qkv = qkv; r.rope = rope;
+  r.q_norm = (const bf16_t*)w->q_norm; r.k_norm = (const bf16_t*)w->k_norm;
+  r.q_out = q; r.k_cache = (bf16_t*)kv->k; r.vt_cache = (bf16_t*)kv->vt;
+  r.pos = io.pos; r.pos0 = io.pos0; r.B = io.B; r.S = io.S;
+  r.nq = nq; r.nkv = nkv; r.cap = kv->capacity; r.max_pos = c->max_position_embeddings;
+  r.qk_norm = c->qk_norm; r.eps = eps;
+  r.interleaved = c->rope_interleaved;
+  if (!io.pos) {
+    r.k_fresh = (f16_t*)(ws + L.kf);
+    r.vt_fresh = (f16_t*)(ws + L.vtf);
+    r.fresh_base = io.pos0 & ~63;
+    r.fresh_w = ((io.pos0 + io.S - r.fresh_base + 63) / 64) * 64;
+  }
   {
     Args a{};
     a.M = T; a.N = (nq + 2 * nkv) * hd; a.K = H;
@@ -443,27 +459,28 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
     a.seg1 = nq * hd; a.seg2 = (nq + nkv) * hd;
     a.C = qkv; a.ldc = a.N;
     GemmPlan p = gemm_plan(a.M, a.N, a.K, gemm::B_QKV, gemm::E_F16, false);
-    ProfScope ps("qkv_gemm", s);
-    CHECK_HIP(gemm_run(a, true, gemm::B_QKV, gemm::E_F16, false, p, s));
-  }
-  // q/k RMSNorm + RoPE, K/V into the cache
-  {
-    RopeCacheArgs r{};
-    r.qkv = qkv; r.rope = rope;
-    r.q_norm = (const bf16_t*)w->q_norm; r.k_norm = (const bf16_t*)w->k_norm;
-    r.q_out = q; r.k_cache = (bf16_t*)kv->k; r.vt_cache = (bf16_t*)kv->vt;
-    r.pos = io.pos; r.pos0 = io.pos0; r.B = io.B; r.S = io.S;
-    r.nq = nq; r.nkv = nkv; r.cap = kv->capacity; r.max_pos = c->max_position_embeddings;
-    r.qk_norm = c->qk_norm; r.eps = eps;
-    r.interleaved = c->rope_interleaved;
-    if (!io.pos) {
-      r.k_fresh = (f16_t*)(ws + L.kf);
-      r.vt_fresh = (f16_t*)(ws + L.vtf);
-      r.fresh_base = io.pos0 & ~63;
-      r.fresh_w = ((io.pos0 + io.S - r.fresh_base + 63) / 64) * 64;
+    const bool fused = !io.pos && p.tile != kDecode;
+    if (fused) {
+      gemm::RopeEpi& e = a.re;
+      e.table = rope; e.q_norm = r.q_norm; e.k_norm = r.k_norm;
+      e.q_out = q; e.k_cache = r.k_cache; e.vt_cache = r.vt_cache;
+      e.k_fresh = r.k_fresh; e.vt_fresh = r.vt_fresh;
+      e.fresh_base = r.fresh_base; e.fresh_w = r.fresh_w; e.pos0 = io.pos0; e.S = io.S;
+      e.nq = nq; e.nkv = nkv; e.cap = kv->capacity; e.max_pos = c->max_position_embeddings;
+      e.qk_norm = c->qk_norm; e.interleaved = c->rope_interleaved; e.eps = eps;
+      {
+        ProfScope ps("qkv_gemm", s);
+        CHECK_HIP(gemm_run(a, true, gemm::B_QKV, gemm::E_QKROPE, false, p, s));
+      }
+      CHECK_HIP(fresh_tail_zero(r, s));
+    } else {
+      {
+        ProfScope ps("qkv_gemm", s);
+        CHECK_HIP(gemm_run(a, true, gemm::B_QKV, gemm::E_F16, false, p, s));
+      }
+      ProfScope ps("qk_norm_rope_cache", s);
+      CHECK_HIP(qkv_rope_cache(r, s));
     }
-    ProfScope ps("qk_norm_rope_cache", s);
-    CHECK_HIP(qkv_rope_cache(r, s));
   }
   // attention
   if (io.pos) {
