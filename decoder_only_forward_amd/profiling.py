@@ -43,7 +43,7 @@ KERNELS = {
 # Template signatures that single out one GEMM use (fp16 A, B mode, epilogue, grouped).
 # o_proj and down share one instantiation and are not told apart here.
 GEMM_SIGNATURE = {
-    "qkv_gemm": "true, 1, 6, false>",
+    "qkv_gemm": "true, 1, 7, false>",  # prefill: q/k-norm + RoPE + cache writes fused
     "gate_up_gemm": "true, 2, 5, false>",
     "lm_head_gemm": "true, 0, 1, false>",
     "moe_gate_up_gemm": ", 2, 5, true>",
