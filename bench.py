@@ -473,8 +473,8 @@ def main():
                          "HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU design is described in DESIGN.md", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); "
+              "each GPU would run these kernels on its own sequences", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -647,9 +647,11 @@ hipError_t attn_prefill(const AttnPrefillArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.S <= 0) return hipSuccess;
   const int nmb = (a.S + BQ - 1) / BQ;
   if (a.pos0 > 0)
-    hipLaunchKernelGGL(attn_prefill_kernel<true>, dim3(nmb * a.B * a.nq), dim3(PF_THREADS), 0, s, a);
+    hipLaunchKernelGGL(attn_prefill_kernel<true>, dim3(nmb * a.B * a.nq), dim3(PF_THREADS), 0, s,
+                       a);
   else
-    hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3(nmb * a.B * a.nq), dim3(PF_THREADS), 0, s, a);
+    hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3(nmb * a.B * a.nq), dim3(PF_THREADS), 0, s,
+                       a);
   return hipGetLastError();
 }
 

@@ -111,7 +111,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 // x from the lane N places round the same 16-lane row (DPP row_ror)
 template <int N>
 DEV float ror16(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
 }
 
 // Asynchronous 16-byte global -> LDS copy (global_load_lds_dwordx4): the 64 lanes of the

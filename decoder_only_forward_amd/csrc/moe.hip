@@ -234,7 +234,8 @@ combine_kernel(const float* __restrict__ y_rows, const int32_t* __restrict__ inv
     }
     const int64_t off = (int64_t)t * H + c * 8;
     if (residual) {  // out = residual + sum (in place allowed: read before written)
-      const f32x4_t r0 = *(const f32x4_t*)(residual + off), r1 = *(const f32x4_t*)(residual + off + 4);
+      const f32x4_t r0 = *(const f32x4_t*)(residual + off);
+      const f32x4_t r1 = *(const f32x4_t*)(residual + off + 4);
       for (int e = 0; e < 4; ++e) {
         acc[e] = r0[e] + acc[e];
         acc[4 + e] = r1[e] + acc[4 + e];
