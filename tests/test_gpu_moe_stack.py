@@ -180,3 +180,56 @@ def test_routed_stack_without_sparse_step_is_dense(gpu):
         torch.cuda.synchronize()
         outs.append(lg.cpu().numpy())
     np.testing.assert_array_equal(outs[0], outs[1])
+
+
+def test_routed_stack_multi_token_decode_and_generation(gpu):
+    # routed layers under the other entry points: a prefill of S tokens, then 4 new tokens
+    # per sequence decoded together at position S (compared with the oracle's prefill over
+    # the S + 4 tokens, rows clear of routing near-ties), and greedy generation whose first
+    # token is the argmax of the prefill's last row
+    import torch
+    cfg = _cfg("e2_k1_bf16_step1")
+    L, V = cfg["num_hidden_layers"], cfg["vocab_size"]
+    B, S, n, cap = 2, 21, 4, 64
+    log(f"case routed stack/multi-token decode + generation: B={B} S={S} n={n}")
+    model = _model(43, cfg)
+    mw, keep = _model_dev(model, gpu)
+    rope = _rope(cfg, gpu)
+    ids = synth.uniform_i32(43, "input.ids", (B, S + n), 0, V)
+    caches = [new_cache(B, cfg["num_key_value_heads"], cap, gpu) for _ in range(L)]
+    kvs = [q3.make_kv_layer(k, vt, cap) for k, vt in caches]
+    ws = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_STACK_PREFILL, B, S),
+                     dtype=torch.uint8, device=gpu)
+    last = torch.empty((B, V), dtype=torch.float32, device=gpu)
+    q3.qwen3_stack_forward(cfg, mw, rope, torch.from_numpy(np.ascontiguousarray(ids[:, :S]))
+                           .to(gpu), B, S, 0, None, kvs, last, q3.QWEN3_LOGITS_LAST, None, ws)
+    dec = torch.empty((B * n, V), dtype=torch.float32, device=gpu)
+    wsd = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_STACK_DECODE, B, n),
+                      dtype=torch.uint8, device=gpu)
+    pos = torch.full((B,), S, dtype=torch.int32, device=gpu)
+    q3.qwen3_stack_forward(cfg, mw, rope, torch.from_numpy(np.ascontiguousarray(ids[:, S:]))
+                           .to(gpu), B, n, 0, pos, kvs, dec, q3.QWEN3_LOGITS_ALL, None, wsd)
+    torch.cuda.synchronize()
+    got_last, got_dec = last.cpu().numpy(), dec.cpu().numpy().reshape(B, n, V)
+    first = []
+    for b in range(B):
+        ref, rl = oracle.stack_prefill(cfg, model, ids[b], want_router=True)
+        ok = _comparable(cfg, rl)
+        log(f"  b={b}: {ok.sum()}/{S + n} rows clear of routing near-ties")
+        assert ok.sum() >= (S + n) // 2
+        if ok[S - 1]:
+            parity(got_last[b], ref[S - 1], f"prefill last row[b={b}]")
+        if ok[S:].any():
+            parity(got_dec[b][ok[S:]], ref[S:][ok[S:]], f"multi-token decode[b={b}]")
+        first.append(int(oracle.argmax(got_last[b])[0]))
+    # generation: token 0 is the argmax of the prefill's last row (same kernels, same logits)
+    caches2 = [new_cache(B, cfg["num_key_value_heads"], cap, gpu) for _ in range(L)]
+    out = torch.full((B, 3), -1, dtype=torch.int32, device=gpu)
+    wsg = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_GENERATE, B, S),
+                      dtype=torch.uint8, device=gpu)
+    q3.qwen3_generate(cfg, mw, rope, torch.from_numpy(np.ascontiguousarray(ids[:, :S])).to(gpu),
+                      B, S, 3, [q3.make_kv_layer(k, vt, cap) for k, vt in caches2], out, wsg)
+    torch.cuda.synchronize()
+    gen = out.cpu().numpy()
+    np.testing.assert_array_equal(gen[:, 0], first)
+    assert ((gen >= 0) & (gen < V)).all()
