@@ -29,6 +29,11 @@ PREFILL_CASES = {
     "interleaved_rope": (dict(rope_interleaved=1), 2, 150, 0),
     "interleaved_rope_chunked": (dict(rope_interleaved=1), 1, 70, 60),
     "cfg1_0p6b": (None, 1, 128, 0),
+    # above 256 rows the projections are tiled and the QKV epilogue does q/k-norm, RoPE and
+    # the cache writes; 128-row tiles then straddle sequences when S is not a multiple of 128
+    "tiled_chunked": (dict(), 3, 130, 70),
+    "tiled_group7": (dict(nq=7, nkv=1), 3, 100, 0),
+    "tiled_no_qk_norm": (dict(qk_norm=0), 2, 160, 0),
 }
 
 
