@@ -206,6 +206,8 @@ def kernel_breakdown(timer, step, units, steps):
     res = {}
     for tag, (bound, amount, per_step) in units.items():
         _, k = timer.run(step, steps, 1, tag=tag, launches_per_step=per_step)
+        if not k["launches"]:
+            continue  # this configuration does not launch that kernel
         e = {"avg_ms": round(k["avg_ms"], 4), "launches_per_step": per_step,
              "ms_per_step": round(k["avg_ms"] * per_step, 4), "bound": bound}
         if amount:
@@ -267,7 +269,7 @@ def wl_decode(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, S
     kv_bytes = 2.0 * B * nkv * (ctx + S) * hd * 2
     g = nq // nkv
     nqg = -(-(S * g) // 8)
-    nsplit = min(-(-cap // 256), max(-(-cap // 4096), -(-1024 // (B * nqg * nkv))))
+    nsplit = min(-(-cap // 256), max(-(-cap // 8192), -(-512 // (B * nqg * nkv))))
     part_bytes = 4.0 * T * nq * nsplit * (hd + 2)  # split partials: design bytes, not algorithmic
     units = {
         # weights dominate the skinny GEMMs; activations in/out are counted too

@@ -592,7 +592,9 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDecodeArgs a) {
     }
   }
   __syncthreads();
-  // merge the block's four waves into one (max, sum, output) partial per query
+  // merge the block's four waves into one (max, sum, output) partial per query; with a
+  // single split that is the result: normalise and store it (NaN rows for a sequence
+  // outside the cache, as the combine kernel does)
   for (int i = tid; i < ncols * HD; i += 256) {
     const int h = i / HD, d = i % HD;
     const int qh = qg * kMaxGroup + h;
@@ -610,6 +612,12 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDecodeArgs a) {
         O += so[v][h][d] * f;
         L += sl[v][h] * f;
       }
+    }
+    if (a.splits == 1) {
+      const int64_t row = (int64_t)b * a.S + qh / g;
+      a.out[(row * a.nq + kvh * g + qh % g) * HD + d] =
+          f2h(ok ? O / L : __int_as_float(0x7FC00000));
+      continue;
     }
     part[d] = O;
     if (d == 0) {
@@ -656,10 +664,11 @@ hipError_t attn_prefill(const AttnPrefillArgs& a, hipStream_t s) {
 }
 
 void attn_decode_plan(int cap, int B, int nkv, int& splits, int& chunk) {
-  // about 4096 positions per block (1024 per wave), more blocks when the batch is too
-  // small for two rounds of resident waves, never fewer than 64 positions per wave
-  const int by_len = (cap + 4095) / 4096;
-  const int fill = (1024 + B * nkv - 1) / (B * nkv);
+  // up to 8192 positions per block (2048 per wave), more blocks when the batch is too
+  // small for one round of resident blocks (two per CU), never fewer than 64 positions per
+  // wave.  With one split the kernel normalises and stores the output itself.
+  const int by_len = (cap + 8191) / 8192;
+  const int fill = (512 + B * nkv - 1) / (B * nkv);
   splits = std::min((cap + 255) / 256, std::max(by_len, fill));
   chunk = (cap + splits - 1) / splits;
 }

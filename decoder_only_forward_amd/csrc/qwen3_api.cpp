@@ -495,8 +495,10 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
       ProfScope ps("attn_decode", s);
       CHECK_HIP(attn_decode(d, s));
     }
-    ProfScope ps("attn_decode_combine", s);
-    CHECK_HIP(attn_decode_combine(d, s));
+    if (d.splits > 1) {
+      ProfScope ps("attn_decode_combine", s);
+      CHECK_HIP(attn_decode_combine(d, s));
+    }
   } else {
     AttnPrefillArgs p{};
     p.q = q; p.k_cache = (const bf16_t*)kv->k; p.vt_cache = (const bf16_t*)kv->vt;

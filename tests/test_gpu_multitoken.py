@@ -132,3 +132,21 @@ def test_single_token_rows_equal_multi_token_first_row(gpu):
     for b, p in enumerate(positions):
         one = _oracle(cfg, model, 53, ids[b, 0], b, p, cap)
         parity(got[b, 0], one, f"first row[b={b}]")
+
+
+def test_decode_single_split_many_sequences(gpu):
+    # 256 sequences x 2 kv heads fill the GPU with one block per (sequence, kv head): the
+    # decode attention then normalises in the kernel with no combine pass; sampled sequences
+    # (ragged positions, one token and two tokens per sequence) against the oracle
+    cap = 128
+    B = 256
+    rng = np.random.default_rng(5)
+    positions = [int(p) for p in rng.integers(0, cap - 2, B)]
+    cfg = small_cfg(L=2, V=300)
+    for S in (1, 2):
+        log(f"case single-split decode: B={B} S={S}")
+        model, ids, got, nxt, _, _ = _run(gpu, cfg, 54, positions, S, cap, q3.QWEN3_LOGITS_ALL)
+        got = got.reshape(B, S, -1)
+        for b in (0, 1, 77, 128, 255):
+            ref = _oracle(cfg, model, 54, ids[b], b, positions[b], cap)
+            parity(got[b], ref, f"logits[b={b}, pos={positions[b]}, S={S}]")
