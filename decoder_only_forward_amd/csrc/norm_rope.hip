@@ -23,6 +23,42 @@ rmsnorm_kernel(const InT* __restrict__ in, int64_t in_row_stride, int64_t in_row
   if (row >= rows) return;
   const InT* x = in + ((int64_t)row * in_row_stride + in_row_offset) * H;
   const int nchunk = H / 8;
+  constexpr int kKeep = 4;  // chunks of 8 a lane keeps in registers (rows up to 2048 wide)
+  if (nchunk <= 64 * kKeep) {
+    // one pass over the row: every load is issued before the reduction
+    float f[kKeep][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < kKeep; ++k) {
+      const int c = lane + 64 * k;
+      if (c < nchunk) {
+        load8(x + c * 8, f[k]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[k][i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kKeep; ++k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss += f[k][i] * f[k][i];
+    ss = warp_sum(ss);
+    const float inv = rsqrtf(ss / (float)H + eps);
+    f16_t* y = out + (int64_t)row * H;
+#pragma unroll
+    for (int k = 0; k < kKeep; ++k) {
+      const int c = lane + 64 * k;
+      if (c >= nchunk) break;
+      float g[8];
+      unpack8(ld16(w + c * 8), g);
+      u32x4_t o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = pack_f16x2(f[k][2 * i] * inv * g[2 * i], f[k][2 * i + 1] * inv * g[2 * i + 1]);
+      st16(y + c * 8, o);
+    }
+    return;
+  }
   float ss = 0.f;
   for (int c = lane; c < nchunk; c += 64) {
     float f[8];
