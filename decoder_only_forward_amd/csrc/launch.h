@@ -113,8 +113,14 @@ hipError_t gen_feed(const int32_t* ids, int32_t* out_ids, int n_new, int col, in
 
 // ---- MoE (moe.hip)
 struct MoeRouteArgs {
-  const float* logits;  // [T][E]
+  float* logits;  // [T][E]: read, or written when x is set
   int T, E, k, norm_topk;
+  // few experts (E <= kRouteSmallE): the routing kernel forms the logits itself,
+  // logits[t][e] = x[t] . router[e] (fp32 accumulation), instead of reading a GEMM's
+  const void* x;           // [T][H] fp16 (x_f16) or bf16 rows; nullptr: read logits
+  bool x_f16;
+  const bf16_t* router;    // [E][H]
+  int H;
   int router_bf16;  // select on (and weight by) bf16-rounded softmax probabilities
   int32_t* idx;   // [T][k]
   float* w;       // [T][k]
@@ -128,6 +134,7 @@ struct MoeRouteArgs {
   int32_t* tile_count;    // [1] number of tiles in use (the first entries of the table)
   int max_tiles, tile_m;
 };
+constexpr int kRouteSmallE = 16;
 int moe_route_chunks(int T);
 hipError_t moe_route(const MoeRouteArgs& a, hipStream_t s);
 // out[t] = (residual[t] +) sum_j w[t][j] y_rows[inv_row[t][j]]; out fp32 or bf16

@@ -28,14 +28,47 @@ __global__ void __launch_bounds__(256) topk_kernel(MoeRouteArgs a) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
-  const float* r = a.logits + (int64_t)t * a.E;
   float v[4];
   int e_of[4];
+  if (a.x) {
+    // few experts: each logit is one wave-wide dot product (lanes take 8-element chunks)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int e = lane + 64 * i;
-    e_of[i] = e;
-    v[i] = e < a.E ? r[e] : -INFINITY;
+    for (int i = 0; i < 4; ++i) {
+      e_of[i] = lane + 64 * i;
+      v[i] = -INFINITY;
+    }
+    float acc[kRouteSmallE];
+#pragma unroll
+    for (int e = 0; e < kRouteSmallE; ++e) acc[e] = 0.f;
+    for (int c = lane; c < a.H / 8; c += 64) {
+      float xf[8];
+      const int64_t xo = (int64_t)t * a.H + c * 8;
+      if (a.x_f16) unpack8_f16(ld16((const f16_t*)a.x + xo), xf);
+      else unpack8(ld16((const bf16_t*)a.x + xo), xf);
+#pragma unroll
+      for (int e = 0; e < kRouteSmallE; ++e) {
+        if (e >= a.E) break;
+        float wf[8];
+        unpack8(ld16(a.router + (int64_t)e * a.H + c * 8), wf);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[e] = fmaf(xf[i], wf[i], acc[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kRouteSmallE; ++e) {
+      if (e >= a.E) break;
+      const float lg = warp_sum(acc[e]);
+      if (lane == 0) a.logits[(int64_t)t * a.E + e] = lg;
+      if (lane == e) v[0] = lg;
+    }
+  } else {
+    const float* r = a.logits + (int64_t)t * a.E;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int e = lane + 64 * i;
+      e_of[i] = e;
+      v[i] = e < a.E ? r[e] : -INFINITY;
+    }
   }
   if (a.router_bf16) {
     // selection keys: the bf16-rounded fp32 softmax probabilities

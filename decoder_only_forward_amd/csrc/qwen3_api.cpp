@@ -341,8 +341,9 @@ int moe_run(const qwen3_config* c, const void* router, const void* gate_up, cons
   f16_t* act = (f16_t*)(ws + L.act);
   float* yrows = (float*)(ws + L.yrows);
 
-  // router logits (fp32)
-  {
+  // router logits (fp32); with few experts the routing kernel forms them itself
+  const bool small_router = E <= kRouteSmallE;
+  if (!small_router) {
     Args a{};
     a.M = T; a.N = E; a.K = H;
     a.A = (const uint16_t*)io.x; a.lda = H;
@@ -357,6 +358,9 @@ int moe_run(const qwen3_config* c, const void* router, const void* gate_up, cons
     MoeRouteArgs r{};
     r.logits = lg; r.T = T; r.E = E; r.k = k; r.norm_topk = c->norm_topk_prob;
     r.router_bf16 = c->router_weights_bf16;
+    if (small_router) {
+      r.x = io.x; r.x_f16 = io.x_f16; r.router = (const bf16_t*)router; r.H = H;
+    }
     r.idx = idx; r.w = wt;
     r.chunk_counts = (int32_t*)(ws + L.chunk_counts);
     r.counts = (int32_t*)(ws + L.counts);
