@@ -179,24 +179,23 @@ DEV void qkrope_epilogue(const Args& p, const f32x16_t (&acc)[T::TM][T::TN], f16
 #pragma unroll
       for (int k = 0; k < 8; ++k) w[k] = 1.f;
     }
-    // NB items per lane at a time: all their LDS reads and RoPE table loads are issued
-    // before any is used, so one table latency covers the batch
-    constexpr int NB = 8, STEP = T::NWAVES * 4;
-    const int n_items = rows_valid * HEADS;
-    for (int base = wave * 4 + sub; base < n_items; base += NB * STEP) {
-      u32x4_t raw[NB];
+    // 16 lanes per token row handle all HEADS heads of the row with one RoPE-table load; NB
+    // rows per lane at a time, all their LDS reads and table loads issued before any is used
+    constexpr int NB = 4, STEP = T::NWAVES * 4;
+    for (int base = wave * 4 + sub; base < rows_valid; base += NB * STEP) {
+      u32x4_t raw[NB][HEADS];
       f32x4_t tc[NB][2], ts[NB][2];
       int pos_k[NB];
       bool ok_k[NB];
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
-        const int item = min(base + u * STEP, n_items - 1);
-        const int lr = item / HEADS, hl = item % HEADS;
+        const int lr = min(base + u * STEP, rows_valid - 1);
         const int64_t t = out_row0 + lr;
         const int pos = e.pos0 + (int)(t % e.S);
         pos_k[u] = pos;
         ok_k[u] = pos >= 0 && pos < e.cap && pos < e.max_pos;
-        raw[u] = ld16(st + lr * LDT + hl * HD + d0);
+#pragma unroll
+        for (int hl = 0; hl < HEADS; ++hl) raw[u][hl] = ld16(st + lr * LDT + hl * HD + d0);
         const int pc = ok_k[u] ? pos : 0;
         const float* cp = e.table + (int64_t)pc * half + i0;
         const float* sp = e.table + ((int64_t)e.max_pos + pc) * half + i0;
@@ -209,38 +208,20 @@ DEV void qkrope_epilogue(const Args& p, const f32x16_t (&acc)[T::TM][T::TN], f16
       }
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
-        const int item = base + u * STEP;
-        if (item >= n_items) break;
-        const int lr = item / HEADS, hl = item % HEADS;
-        const int h = head0 + hl;
+        const int lr = base + u * STEP;
+        if (lr >= rows_valid) break;
         const int64_t t = out_row0 + lr;
         const int b = (int)(t / e.S);
         const int pos = pos_k[u];
         const bool ok = ok_k[u];
-        float x[8];
-        unpack8_f16(raw[u], x);
-        if (e.qk_norm) {
-          float ss = 0.f;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) ss += x[k] * x[k];
-          ss += ror16<8>(ss);
-          ss += ror16<4>(ss);
-          ss += ror16<2>(ss);
-          ss += ror16<1>(ss);
-          const float inv = rsqrtf(ss / (float)HD + e.eps);
-#pragma unroll
-          for (int k = 0; k < 8; ++k) x[k] = x[k] * inv * w[k];
-        }
-        float y[8];
+        float c[8], sn[8];
         if (e.interleaved) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            const float c = ok ? tc[u][0][k] : 0.f, sn = ok ? ts[u][0][k] : 0.f;
-            y[2 * k] = x[2 * k] * c - x[2 * k + 1] * sn;
-            y[2 * k + 1] = x[2 * k] * sn + x[2 * k + 1] * c;
+            c[k] = ok ? tc[u][0][k] : 0.f;
+            sn[k] = ok ? ts[u][0][k] : 0.f;
           }
         } else {
-          float c[8], sn[8];
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             c[k] = ok ? tc[u][0][k] : 0.f;
@@ -248,27 +229,54 @@ DEV void qkrope_epilogue(const Args& p, const f32x16_t (&acc)[T::TM][T::TN], f16
             sn[k] = ok ? ts[u][0][k] : 0.f;
             sn[k + 4] = ok ? ts[u][1][k] : 0.f;
           }
-#pragma unroll
-          for (int k = 0; k < 8; ++k) y[k] = x[k] * c[k] + sgn * ror16<8>(x[k]) * sn[k];
         }
-        if (h >= nh) continue;
-        if (is_q) {
-          u32x4_t o;
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-            o[k] = ok ? pack_f16x2(y[2 * k] * qs, y[2 * k + 1] * qs) : 0x7E007E00u;
-          st16(e.q_out + (t * e.nq + h) * HD + d0, o);
-        } else if (ok) {
-          u32x4_t kb, kh;
+        for (int hl = 0; hl < HEADS; ++hl) {
+          const int h = head0 + hl;
+          float x[8];
+          unpack8_f16(raw[u][hl], x);
+          if (e.qk_norm) {
+            float ss = 0.f;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            kb[k] = pack_bf16x2(y[2 * k], y[2 * k + 1]);
-            kh[k] = pack_f16x2(y[2 * k], y[2 * k + 1]);
+            for (int k = 0; k < 8; ++k) ss += x[k] * x[k];
+            ss += ror16<8>(ss);
+            ss += ror16<4>(ss);
+            ss += ror16<2>(ss);
+            ss += ror16<1>(ss);
+            const float inv = rsqrtf(ss / (float)HD + e.eps);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) x[k] = x[k] * inv * w[k];
           }
-          st16(e.k_cache + (((int64_t)b * e.nkv + h) * e.cap + pos) * HD + d0, kb);
-          if (e.k_fresh)
-            st16(e.k_fresh + (((int64_t)b * e.nkv + h) * e.fresh_w + (pos - e.fresh_base)) * HD +
-                     d0, kh);
+          float y[8];
+          if (e.interleaved) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              y[2 * k] = x[2 * k] * c[k] - x[2 * k + 1] * sn[k];
+              y[2 * k + 1] = x[2 * k] * sn[k] + x[2 * k + 1] * c[k];
+            }
+          } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) y[k] = x[k] * c[k] + sgn * ror16<8>(x[k]) * sn[k];
+          }
+          if (h >= nh) continue;
+          if (is_q) {
+            u32x4_t o;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              o[k] = ok ? pack_f16x2(y[2 * k] * qs, y[2 * k + 1] * qs) : 0x7E007E00u;
+            st16(e.q_out + (t * e.nq + h) * HD + d0, o);
+          } else if (ok) {
+            u32x4_t kb, kh;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              kb[k] = pack_bf16x2(y[2 * k], y[2 * k + 1]);
+              kh[k] = pack_f16x2(y[2 * k], y[2 * k + 1]);
+            }
+            st16(e.k_cache + (((int64_t)b * e.nkv + h) * e.cap + pos) * HD + d0, kb);
+            if (e.k_fresh)
+              st16(e.k_fresh + (((int64_t)b * e.nkv + h) * e.fresh_w + (pos - e.fresh_base)) *
+                                   HD + d0, kh);
+          }
         }
       }
     }
