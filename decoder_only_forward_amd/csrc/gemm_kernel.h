@@ -24,7 +24,8 @@
 //   E_QKROPE    QKV projections of a prefill: the tile is rounded to fp16 and staged in
 //               LDS, then per (token, head): q/k RMSNorm, RoPE, q to q_out (pre-scaled
 //               fp16), k to the bf16 cache and its fp16 copy, v transposed to the V^T
-//               cache and its fp16 copy (see RopeEpi)
+//               cache and its fp16 copy; the copies' tails past the last position are
+//               zeroed (see RopeEpi)
 // B row sources:
 //   B_DENSE   one matrix;  B_QKV  q/k/v weights stacked along N without a copy;
 //   B_SWIGLU  gate and up rows interleaved per wave so that a lane holds the gate and
@@ -144,6 +145,29 @@ DEV void wait_vm() {
 //     by lane j ^ 8; interleaved: planes (2i, 2i + 1) inside a lane), 16-byte stores;
 //   v heads: one lane per (dim, 8 consecutive tokens), transposed 16-byte stores where the
 //     8 tokens are one sequence's aligned positions, element stores otherwise.
+// The attention reads the fp16 copies in whole 64-position tiles: zero each sequence's
+// tail, from its last new position to the padded width, for the tile whose rows hold the
+// sequence's last token (k heads: rows of k_fresh; v heads: columns of vt_fresh).
+template <int THREADS>
+DEV void zero_fresh_tail(const RopeEpi& e, int out_row0, int rows_valid, int head0, int heads,
+                         bool is_k) {
+  const int HD = 128;
+  const int t0 = e.pos0 + e.S - e.fresh_base, nt = e.fresh_w - t0;
+  if (!e.k_fresh || nt <= 0) return;
+  const int b_lo = out_row0 / e.S, b_hi = (out_row0 + rows_valid) / e.S - 1;
+  const int nh = min(heads, e.nkv - head0);
+  if (b_hi < b_lo || nh <= 0) return;
+  const int per_seq = nh * nt * HD;
+  for (int i = threadIdx.x; i < (b_hi - b_lo + 1) * per_seq; i += THREADS) {
+    const int b = b_lo + i / per_seq, j = i % per_seq;
+    const int h = head0 + j / (nt * HD), r = t0 + (j / HD) % nt, d = j % HD;
+    if (is_k)
+      e.k_fresh[(((int64_t)b * e.nkv + h) * e.fresh_w + r) * HD + d] = 0;
+    else
+      e.vt_fresh[(((int64_t)b * e.nkv + h) * HD + d) * e.fresh_w + r] = 0;
+  }
+}
+
 template <class T>
 DEV void qkrope_epilogue(const Args& p, const f32x16_t (&acc)[T::TM][T::TN], f16_t* st,
                          int out_row0, int rows_valid, int n0, int wm, int wn, int lane,
@@ -280,6 +304,7 @@ DEV void qkrope_epilogue(const Args& p, const f32x16_t (&acc)[T::TM][T::TN], f16
         }
       }
     }
+    if (!is_q) zero_fresh_tail<T::THREADS>(e, out_row0, rows_valid, head0, HEADS, true);
     return;
   }
   // v heads: item = (column c, group of 8 rows); consecutive lanes take consecutive groups
@@ -323,6 +348,7 @@ DEV void qkrope_epilogue(const Args& p, const f32x16_t (&acc)[T::TM][T::TN], f16
       }
     }
   }
+  zero_fresh_tail<T::THREADS>(e, out_row0, rows_valid, head0, T::BN / HD, false);
 }
 
 template <class T, bool F16, int BMODE, int EPI, bool GROUPED>

@@ -65,8 +65,6 @@ struct RopeCacheArgs {
   float eps;
 };
 hipError_t qkv_rope_cache(const RopeCacheArgs& a, hipStream_t s);
-// zero the fp16 copies past the last new position (for the fused QKV epilogue)
-hipError_t fresh_tail_zero(const RopeCacheArgs& a, hipStream_t s);
 
 // ---- attention (attention.hip)
 struct AttnPrefillArgs {

@@ -455,30 +455,6 @@ hipError_t rope_table(float* rope, int max_pos, int hd, double theta, hipStream_
   return hipGetLastError();
 }
 
-// The fp16 copies are read in whole 64-position tiles: zero each (sequence, kv head)'s tail
-// from the last new position to the padded width (the fused QKV epilogue writes only the
-// new positions).
-__global__ void __launch_bounds__(256) fresh_tail_zero_kernel(RopeCacheArgs a) {
-  const int HD = 128;
-  const int b = blockIdx.x, h = blockIdx.y;
-  const bool is_k = blockIdx.z == 0;
-  const int t0 = a.pos0 + a.S - a.fresh_base, nt = a.fresh_w - t0;
-  for (int i = threadIdx.x; i < nt * HD; i += 256) {
-    const int r = t0 + i / HD, d = i % HD;
-    if (is_k)
-      a.k_fresh[(((int64_t)b * a.nkv + h) * a.fresh_w + r) * HD + d] = 0;
-    else
-      a.vt_fresh[(((int64_t)b * a.nkv + h) * HD + d) * a.fresh_w + r] = 0;
-  }
-}
-
-hipError_t fresh_tail_zero(const RopeCacheArgs& a, hipStream_t s) {
-  if (a.B <= 0 || !a.k_fresh || !a.vt_fresh) return hipSuccess;
-  if (a.pos0 + a.S - a.fresh_base > a.fresh_w) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(fresh_tail_zero_kernel, dim3(a.B, a.nkv, 2), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
 hipError_t qkv_rope_cache(const RopeCacheArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.S <= 0) return hipSuccess;
   dim3 grid((a.S + kRopeTile - 1) / kRopeTile, a.B, a.nq + 2 * a.nkv);

@@ -472,11 +472,8 @@ int run_layer(const qwen3_config* c, const qwen3_layer_weights* w, const float* 
       e.fresh_base = r.fresh_base; e.fresh_w = r.fresh_w; e.pos0 = io.pos0; e.S = io.S;
       e.nq = nq; e.nkv = nkv; e.cap = kv->capacity; e.max_pos = c->max_position_embeddings;
       e.qk_norm = c->qk_norm; e.interleaved = c->rope_interleaved; e.eps = eps;
-      {
-        ProfScope ps("qkv_gemm", s);
-        CHECK_HIP(gemm_run(a, true, gemm::B_QKV, gemm::E_QKROPE, false, p, s));
-      }
-      CHECK_HIP(fresh_tail_zero(r, s));
+      ProfScope ps("qkv_gemm", s);
+      CHECK_HIP(gemm_run(a, true, gemm::B_QKV, gemm::E_QKROPE, false, p, s));
     } else {
       {
         ProfScope ps("qkv_gemm", s);
