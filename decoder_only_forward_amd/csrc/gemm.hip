@@ -10,6 +10,7 @@ using namespace gemm;
 
 using TBig = Tile<256, 256, 2, 4>;   // 8 waves (2 per SIMD), 128x64 per wave, 128 KB LDS
 using TMid = Tile<128, 128, 2, 2>;   // 4 waves, 64x64 per wave, 64 KB LDS
+using TTall = Tile<256, 128, 4, 2>;  // 8 waves, 64x64 per wave, 96 KB LDS: narrow outputs
 using TSkin = Tile<64, 128, 2, 2>;   // 4 waves, 32x64 per wave: decode (M <= 64)
 
 template <class T>
@@ -178,8 +179,11 @@ GemmPlan gemm_plan(int M, int N, int K, int bmode, int epi, bool grouped) {
     }
     return p;
   }
-  int big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  p.tile = big_tiles >= 512 ? kBig : kMid;
+  // the largest tile that still gives every CU a block: 256x256 moves the fewest bytes per
+  // flop through the copy path, 256x128 a third more, 128x128 twice as many
+  const int big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const int tall_tiles = ((M + 255) / 256) * ((N + 127) / 128);
+  p.tile = big_tiles >= 512 ? kBig : tall_tiles >= 256 ? kTall : kMid;
   return p;
 }
 
@@ -213,6 +217,13 @@ hipError_t gemm_run(const Args& a_in, bool f16, int bmode, int epi, bool grouped
   GEMM_CASE(kBig, TBig, true, B_DENSE, E_RESF_B16, false)
   GEMM_CASE(kBig, TBig, true, B_SWIGLU, E_SWIGLU, false)
   GEMM_CASE(kBig, TBig, true, B_DENSE, E_F32, false)
+  GEMM_CASE(kTall, TTall, true, B_QKV, E_F16, false)
+  GEMM_CASE(kTall, TTall, true, B_QKV, E_QKROPE, false)
+  GEMM_CASE(kTall, TTall, true, B_DENSE, E_RES_F32, false)
+  GEMM_CASE(kTall, TTall, true, B_DENSE, E_RESB_F32, false)
+  GEMM_CASE(kTall, TTall, true, B_DENSE, E_RESF_B16, false)
+  GEMM_CASE(kTall, TTall, true, B_SWIGLU, E_SWIGLU, false)
+  GEMM_CASE(kTall, TTall, true, B_DENSE, E_F32, false)
   GEMM_CASE(kMid, TMid, true, B_QKV, E_F16, false)
   GEMM_CASE(kMid, TMid, true, B_DENSE, E_RES_F32, false)
   GEMM_CASE(kMid, TMid, true, B_DENSE, E_RESB_F32, false)

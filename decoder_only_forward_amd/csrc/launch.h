@@ -11,7 +11,7 @@ namespace q3 {
 
 // ---- GEMM (gemm.hip)
 // Tile families; kAuto picks by problem size.
-enum GemmTile { kAuto = 0, kBig = 1, kMid = 2, kSkinny = 3, kDecode = 4 };
+enum GemmTile { kAuto = 0, kBig = 1, kMid = 2, kSkinny = 3, kDecode = 4, kTall = 5 };
 
 struct GemmPlan {
   int tile;      // GemmTile actually used
