@@ -125,3 +125,43 @@ def test_stack_rejects_bad_arguments():
     _expect(lambda: call(cs=[caches[0], q3.make_kv_layer(0x10000, 0x20000, 192)]),
             q3.QWEN3_EINVAL, "capacity")
     _expect(lambda: call(), q3.QWEN3_EWORKSPACE, "workspace")
+
+
+def test_routed_stack_multi_token_and_generation_reject_bad_arguments():
+    # validation happens on the host before anything is enqueued (no GPU needed)
+    cfg = dict(recipes.QWEN3_0P6B, num_hidden_layers=2, num_experts=2, num_experts_per_tok=1,
+               moe_intermediate_size=3072, norm_topk_prob=0, decoder_sparse_step=1,
+               router_weights_bf16=1)
+    full = _fake_layer()
+    no_router = dict(full, router=0)
+    caches = [q3.make_kv_layer(0x10000, 0x20000, 128)] * 2
+
+    def stack(c=cfg, layers=(full, full), seq_len=16, pos=None):
+        mw, keep = q3.make_model_weights(0x7000, 0x8000, list(layers))
+        q3.qwen3_stack_forward(c, mw, 0x3000, 0x6000, 1, seq_len, 0, pos, caches, 0x9000,
+                               q3.QWEN3_LOGITS_ALL, None, None, stream=0)
+
+    _expect(lambda: stack(layers=(full, no_router)), q3.QWEN3_EINVAL, "router")
+    _expect(lambda: stack(c=dict(cfg, decoder_sparse_step=-1)), q3.QWEN3_EINVAL,
+            "decoder_sparse_step")
+    _expect(lambda: stack(c=dict(cfg, router_weights_bf16=2)), q3.QWEN3_EINVAL,
+            "router_weights_bf16")
+    # the routed layers need no dense FFN weights; a dense stack needs them
+    dense_only = dict(cfg, num_experts=0)
+    _expect(lambda: stack(c=dense_only, layers=(dict(full, gate_proj=0), full)),
+            q3.QWEN3_EINVAL, "gate_proj")
+    _expect(lambda: stack(layers=(dict(full, gate_proj=0), full)), q3.QWEN3_EWORKSPACE,
+            "workspace")
+    # decode of several tokens per sequence: seq_len must fit the cache
+    _expect(lambda: stack(seq_len=200, pos=0x4000), q3.QWEN3_ERANGE, "capacity")
+    _expect(lambda: stack(seq_len=8, pos=0x4000), q3.QWEN3_EWORKSPACE, "workspace")
+
+    def gen(temperature=0.5, top_p=0.9, uniforms=0x5000, n_new=4):
+        mw, keep = q3.make_model_weights(0x7000, 0x8000, [full, full])
+        q3.qwen3_generate(cfg, mw, 0x3000, 0x6000, 1, 16, n_new, caches, 0x9000, None,
+                          temperature=temperature, top_p=top_p, uniforms=uniforms, stream=0)
+
+    _expect(lambda: gen(temperature=-1.0), q3.QWEN3_EINVAL, "temperature")
+    _expect(lambda: gen(top_p=1.5), q3.QWEN3_EINVAL, "top_p")
+    _expect(lambda: gen(uniforms=None), q3.QWEN3_EINVAL, "uniforms")
+    _expect(lambda: gen(n_new=200), q3.QWEN3_ERANGE, "capacity")
