@@ -150,3 +150,16 @@ def test_decode_single_split_many_sequences(gpu):
         for b in (0, 1, 77, 128, 255):
             ref = _oracle(cfg, model, 54, ids[b], b, positions[b], cap)
             parity(got[b], ref, f"logits[b={b}, pos={positions[b]}, S={S}]")
+
+
+def test_decode_at_the_last_positions_of_cache_and_rope_table(gpu):
+    # capacity == max_position_embeddings: the new tokens take the very last cache slots and
+    # RoPE table rows (one token at position 255, three tokens at 253..255)
+    cap = 256
+    cfg = small_cfg(L=2, V=300, max_pos=cap)
+    for S, positions in ((1, [cap - 1, 100]), (3, [cap - 3, 0])):
+        log(f"case decode at the table end: S={S} pos={positions}")
+        model, ids, got, nxt, _, _ = _run(gpu, cfg, 55, positions, S, cap, q3.QWEN3_LOGITS_ALL)
+        got = got.reshape(len(positions), S, -1)
+        for b, p in enumerate(positions):
+            parity(got[b], _oracle(cfg, model, 55, ids[b], b, p, cap), f"logits[b={b}, pos={p}]")
