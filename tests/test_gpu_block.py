@@ -34,6 +34,9 @@ PREFILL_CASES = {
     "tiled_chunked": (dict(), 3, 130, 70),
     "tiled_group7": (dict(nq=7, nkv=1), 3, 100, 0),
     "tiled_no_qk_norm": (dict(qk_norm=0), 2, 160, 0),
+    # longer sequences: several causal row blocks of very different lengths
+    "long_sequence": (dict(), 1, 1000, 0),
+    "long_group7": (dict(nq=7, nkv=1), 2, 450, 0),
 }
 
 
