@@ -134,11 +134,8 @@ constexpr int kRopeTile = 64;
 
 // rotate within 16-lane rows by n (n in 1..15)
 
-// DECODE: the S new tokens of sequence b at positions pos[b] .. pos[b] + S - 1 (a sequence
-// whose last position falls outside the cache or the RoPE table writes nothing and gets NaN
-// q rows); the kernel is compiled separately for it so the prefill path keeps all of its
-// loads unconditional.
-template <bool DECODE>
+// Prefill: tokens of sequence b at positions pos0 .. pos0 + S - 1 (decode steps use
+// qkv_rope_decode_kernel below).
 __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
   const int HD = 128;
   const int tile = blockIdx.x, b = blockIdx.y, slot = blockIdx.z;
@@ -190,19 +187,10 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
       live_r[k] = s < a.S;
       const int sc = live_r[k] ? s : a.S - 1;
       const int64_t t = (int64_t)b * a.S + sc;
-      int pos;
-      if (DECODE) {
-        const int p0 = a.pos[b];
-        pos = p0 + sc;
-        ok_r[k] = p0 >= 0 && p0 + a.S <= a.cap && p0 + a.S <= a.max_pos;
-      } else {
-        pos = a.pos0 + sc;
-        ok_r[k] = pos >= 0 && pos < a.cap && pos < a.max_pos;
-      }
+      const int pos = a.pos0 + sc;
+      ok_r[k] = pos >= 0 && pos < a.cap && pos < a.max_pos;
       pos_r[k] = pos;
-      // decode: rows other than the one token load nothing; prefill rows past the end
-      // load a clamped row so that every load is unconditional
-      if (DECODE && !live_r[k]) continue;
+      // rows past the end load a clamped row so that every load is unconditional
       raw[k] = ld16(a.qkv + t * row_elems + slot * HD + d0);
       const int pc = ok_r[k] ? pos : 0;
       const float* cp = a.rope + (int64_t)pc * half + i0;
@@ -305,18 +293,7 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
     }
   }
   __syncthreads();
-  if (DECODE) {
-    // decode: this tile's tokens of the sequence, from its own position on
-    const int p0 = a.pos[b];
-    if (p0 < 0 || p0 + a.S > a.cap || p0 + a.S > a.max_pos) return;
-    const int n = min(kRopeTile, a.S - s0);
-    for (int i = tid; i < HD * n; i += 256) {
-      const int d = i / n, r = i % n;
-      a.vt_cache[(((int64_t)b * a.nkv + h) * HD + d) * a.cap + p0 + s0 + r] = f2bf(sv[r][d]);
-    }
-    return;
-  }
-  // prefill: positions pos0 + s0 .. contiguous
+  // positions pos0 + s0 .. contiguous
   for (int i = tid; i < HD * (kRopeTile / 8); i += 256) {
     const int d = i / (kRopeTile / 8), r0 = (i % (kRopeTile / 8)) * 8;
     const int s = s0 + r0;
@@ -455,13 +432,102 @@ hipError_t rope_table(float* rope, int max_pos, int hd, double theta, hipStream_
   return hipGetLastError();
 }
 
+// Decode: 16 lanes per (token row, head slot), 16 such items per block, so a step of a few
+// tokens per sequence launches as many blocks as it has work (one (64-token tile, sequence,
+// head) block each would leave 15 of 16 lane groups idle).  q/k heads: RMSNorm and RoPE as
+// above; v heads: 8 dims per lane written into their V^T rows at the token's position.
+__global__ void __launch_bounds__(256) qkv_rope_decode_kernel(RopeCacheArgs a) {
+  const int HD = 128, half = HD / 2;
+  const int slots = a.nq + 2 * a.nkv;
+  const int item = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int T = a.B * a.S;
+  if (item >= T * slots) return;  // whole 16-lane groups leave together
+  const int t = item / slots, slot = item % slots;
+  const int b = t / a.S, sq = t % a.S;
+  const int p0 = a.pos[b];
+  const bool ok = p0 >= 0 && p0 + a.S <= a.cap && p0 + a.S <= a.max_pos;
+  const int pos = p0 + sq;
+  const int j = threadIdx.x & 15, d0 = 8 * j;
+  const int row_elems = slots * HD;
+  float x[8];
+  unpack8_f16(ld16(a.qkv + (int64_t)t * row_elems + slot * HD + d0), x);
+  if (slot >= a.nq + a.nkv) {  // v head
+    if (!ok) return;
+    const int h = slot - a.nq - a.nkv;
+    bf16_t* vb = a.vt_cache + (((int64_t)b * a.nkv + h) * HD + d0) * a.cap + pos;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vb[(int64_t)e * a.cap] = f2bf(x[e]);
+    return;
+  }
+  const bool is_q = slot < a.nq;
+  const int h = is_q ? slot : slot - a.nq;
+  if (a.qk_norm) {
+    float w[8];
+    unpack8(ld16((is_q ? a.q_norm : a.k_norm) + d0), w);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+    ss += ror16<8>(ss);
+    ss += ror16<4>(ss);
+    ss += ror16<2>(ss);
+    ss += ror16<1>(ss);
+    const float inv = rsqrtf(ss / (float)HD + a.eps);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = x[e] * inv * w[e];
+  }
+  const int pc = ok ? pos : 0;
+  const int i0 = a.interleaved ? d0 / 2 : d0 & (half - 1);
+  const float* cp = a.rope + (int64_t)pc * half + i0;
+  const float* sp = a.rope + ((int64_t)a.max_pos + pc) * half + i0;
+  float y[8];
+  if (a.interleaved) {
+    const f32x4_t c4 = *(const f32x4_t*)cp, s4 = *(const f32x4_t*)sp;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float c = ok ? c4[e] : 0.f, sn = ok ? s4[e] : 0.f;
+      y[2 * e] = x[2 * e] * c - x[2 * e + 1] * sn;
+      y[2 * e + 1] = x[2 * e] * sn + x[2 * e + 1] * c;
+    }
+  } else {
+    const float sgn = d0 < half ? -1.f : 1.f;
+    const f32x4_t c0 = *(const f32x4_t*)cp, c1 = *(const f32x4_t*)(cp + 4);
+    const f32x4_t s0 = *(const f32x4_t*)sp, s1 = *(const f32x4_t*)(sp + 4);
+    float c[8], sn[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      c[e] = ok ? c0[e] : 0.f;
+      c[e + 4] = ok ? c1[e] : 0.f;
+      sn[e] = ok ? s0[e] : 0.f;
+      sn[e + 4] = ok ? s1[e] : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = x[e] * c[e] + sgn * ror16<8>(x[e]) * sn[e];
+  }
+  if (is_q) {
+    const float qs = 0.08838834764831845f * kLog2e;
+    u32x4_t o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = ok ? pack_f16x2(y[2 * e] * qs, y[2 * e + 1] * qs) : 0x7E007E00u;
+    st16(a.q_out + ((int64_t)t * a.nq + h) * HD + d0, o);
+  } else if (ok) {
+    u32x4_t kb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kb[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
+    st16(a.k_cache + (((int64_t)b * a.nkv + h) * a.cap + pos) * HD + d0, kb);
+  }
+}
+
 hipError_t qkv_rope_cache(const RopeCacheArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.S <= 0) return hipSuccess;
+  if (a.pos) {
+    const int64_t items = (int64_t)a.B * a.S * (a.nq + 2 * a.nkv);
+    hipLaunchKernelGGL(qkv_rope_decode_kernel, dim3((unsigned)((items + 15) / 16)), dim3(256), 0,
+                       s, a);
+    return hipGetLastError();
+  }
   dim3 grid((a.S + kRopeTile - 1) / kRopeTile, a.B, a.nq + 2 * a.nkv);
-  if (a.pos)
-    hipLaunchKernelGGL(qkv_rope_cache_kernel<true>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(qkv_rope_cache_kernel<false>, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(qkv_rope_cache_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

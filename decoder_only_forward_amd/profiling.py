@@ -31,7 +31,7 @@ CSRC = os.path.join(HERE, "csrc")
 _GEMM = ["gemm_kernel.h", "gemm.hip", "common.h"]
 KERNELS = {
     "qkv_gemm": ("gemm_kernel<", _GEMM),
-    "qk_norm_rope_cache": ("qkv_rope_cache_kernel", ["norm_rope.hip", "common.h"]),
+    "qk_norm_rope_cache": ("qkv_rope_", ["norm_rope.hip", "common.h"]),
     "attn_prefill": ("attn_prefill_kernel", ["attention.hip", "common.h"]),
     "attn_decode": ("attn_decode_kernel", ["attention.hip", "common.h"]),
     "gate_up_gemm": ("gemm_kernel<", _GEMM),
