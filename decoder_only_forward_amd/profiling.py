@@ -7,7 +7,10 @@ Two kinds of run are summarised (both write CSV with ``--output-format csv``):
 * hardware counters (``--pmc FETCH_SIZE`` and, in a second run, ``--pmc WRITE_SIZE``):
   HBM kilobytes read / written per dispatch.  The raw counter is scaled by what it reads
   for a plain elementwise copy of known size, run first in the same process
-  (``bench.py --copy-gib``), so the figure is in real bytes.
+  (``bench.py --copy-gib``), so the figure is in real bytes;
+* matrix-core counters (``--pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F16
+  SQ_BUSY_CYCLES GRBM_GUI_ACTIVE``): per kernel class, the fp16 MFMA work executed (each
+  MOPS unit is 512 flops) and the share of SIMD cycles the matrix cores were busy.
 
 The traffic table is keyed by profile tag and stamped with a hash of the sources the
 kernel is built from; ``bench.py`` reports it only while those sources are unchanged.
@@ -16,6 +19,7 @@ Usage (after the rocprofv3 runs):
   python -m decoder_only_forward_amd.profiling stats <dir> <workload> <command> <out.md>
   python -m decoder_only_forward_amd.profiling traffic <fetch_dir> <write_dir> <workload>
          <copy_gib> <command_fetch> <command_write> <traffic.json>
+  python -m decoder_only_forward_amd.profiling mfma <out.md> <command> <workload>=<dir> ...
 """
 import csv
 import glob
@@ -180,6 +184,78 @@ def traffic_markdown(table):
     return "\n".join(out) + "\n"
 
 
+MFMA_PEAK_F16 = 2.5e15  # dense fp16/bf16 MFMA flops per second at the 2.4 GHz peak clock
+
+
+def _gpu_agent(rocprof_dir):
+    for r in _csv_rows(os.path.join(rocprof_dir, "**", "*agent_info.csv")):
+        if r["Agent_Type"] == "GPU":
+            return int(r["Simd_Count"]), int(r["Num_Xcc"])
+    raise SystemExit(f"no GPU agent in {rocprof_dir}")
+
+
+def mfma_rows(rocprof_dir):
+    """Per kernel class: dispatches, mean duration, executed fp16 MFMA flops per dispatch,
+    MFMA busy share and the shader clock implied by the active-cycle count.
+
+    GRBM_GUI_ACTIVE comes back summed over the XCDs, so one XCD's active cycles are the sum
+    over Num_Xcc; SQ_VALU_MFMA_BUSY_CYCLES is summed over every SIMD of the chip."""
+    simds, xcc = _gpu_agent(rocprof_dir)
+    per, meta = {}, {}
+    for r in _csv_rows(os.path.join(rocprof_dir, "**", "*counter_collection.csv")):
+        d = per.setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        meta[r["Dispatch_Id"]] = (r["Kernel_Name"],
+                                  int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    groups = {}
+    for k, c in per.items():
+        name, dur = meta[k]
+        g = groups.setdefault(name, [0, 0.0, 0.0, 0.0, 0.0])
+        g[0] += 1
+        g[1] += dur
+        g[2] += c.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) * 512.0
+        g[3] += c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        g[4] += c.get("GRBM_GUI_ACTIVE", 0.0) / xcc
+    out = []
+    for name, (n, dur, flops, busy, active) in groups.items():
+        if flops == 0.0:
+            continue
+        label = short_name(name)
+        for tag, sig in GEMM_SIGNATURE.items():
+            if "gemm_kernel<" in name and sig in name:
+                label += f" ({tag})"
+        out.append({"kernel": label, "dispatches": n, "avg_us": dur / n / 1e3,
+                    "gflop": flops / n / 1e9, "tflops": flops / dur / 1e3,
+                    "busy_pct": 100.0 * busy / (active * simds),
+                    "clock_ghz": active / dur, "total_us": dur / 1e3})
+    out.sort(key=lambda e: -e["total_us"])
+    return out
+
+
+def mfma_markdown(runs, command):
+    out = ["# MFMA utilisation per kernel (rocprofv3 matrix-core counters)", "",
+           "Command (run from the repository root, once per workload):", "", "```",
+           command, "```", "",
+           "Executed flops are SQ_INSTS_VALU_MFMA_MOPS_F16 x 512 per dispatch; the rate is "
+           "that over the dispatch's own duration; the fraction is of the 2.5 PFLOP/s dense "
+           "fp16/bf16 peak (2.4 GHz).  MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES over (one XCD's "
+           "GRBM_GUI_ACTIVE x 1024 SIMDs): the share of SIMD cycles the matrix cores were "
+           "busy at the clock the chip actually ran, which is given beside it "
+           "(active cycles of one XCD / duration).  Counter runs serialise dispatches, so "
+           "durations are a little longer than in the timed benchmark.", ""]
+    for workload, rows in runs:
+        out += [f"## {workload}", "",
+                "| kernel | dispatches | avg us | GFLOP / dispatch | TFLOP/s | of peak | "
+                "MFMA busy % | clock GHz |", "|---|---:|---:|---:|---:|---:|---:|---:|"]
+        for e in rows:
+            out.append(f"| `{e['kernel']}` | {e['dispatches']} | {e['avg_us']:.1f} | "
+                       f"{e['gflop']:.2f} | {e['tflops']:.0f} | "
+                       f"{1e12 * e['tflops'] / MFMA_PEAK_F16:.3f} | {e['busy_pct']:.1f} | "
+                       f"{e['clock_ghz']:.2f} |")
+        out.append("")
+    return "\n".join(out)
+
+
 def main(argv):
     if argv[0] == "stats":
         d, workload, cmd, out = argv[1:5]
@@ -197,6 +273,11 @@ def main(argv):
             json.dump(table, fh, indent=1, sort_keys=True)
         with open(os.path.splitext(out)[0] + ".md", "w") as fh:
             fh.write(traffic_markdown(table))
+    elif argv[0] == "mfma":
+        out, cmd = argv[1:3]
+        runs = [(a.split("=", 1)[0], mfma_rows(a.split("=", 1)[1])) for a in argv[3:]]
+        with open(out, "w") as fh:
+            fh.write(mfma_markdown(runs, cmd))
     else:
         raise SystemExit(__doc__)
 
