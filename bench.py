@@ -89,9 +89,7 @@ def setup_stack(torch, q3, recipes, dev, cfg, B, S, cap, seed_model, seed_in):
     L, nkv = cfg["num_hidden_layers"], cfg["num_key_value_heads"]
     caches = []
     for _ in range(L):
-        k = torch.empty((B, nkv, cap, 128), dtype=torch.bfloat16, device=dev)
-        vt = torch.empty((B, nkv, 128, cap), dtype=torch.bfloat16, device=dev)
-        caches.append((k, vt))
+        caches.append(q3.kv_cache_empty(B, nkv, cap, dev))
     return model, mw, keep, rope, caches
 
 
@@ -244,8 +242,15 @@ def wl_decode(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, S
     model, mw, keep, rope, caches = setup_stack(torch, q3, recipes, dev, cfg, B, 1, cap,
                                                 recipes.MODEL_SEED_0P6B, 3)
     t0 = time.time()
+    # the generator fills logical [B, nkv, cap, 128] tensors; copy them into the tiled cache
+    k_log = torch.empty((B, cfg["num_key_value_heads"], cap, 128), dtype=torch.bfloat16,
+                        device=dev)
+    v_log = torch.empty_like(k_log)
     for l, (k, vt) in enumerate(caches):
-        recipes.kv_fill_device(k, vt, 3, l, ctx, ctx)
+        recipes.kv_fill_device(k_log, v_log, 3, l, ctx, ctx)
+        q3.k_cache_from_logical(k_log, out=k)
+        q3.v_cache_from_logical(v_log, out=vt)
+    del k_log, v_log
     torch.cuda.synchronize()
     log(f"  decode: KV cache {len(caches)} x 2 x {tuple(caches[0][0].shape)} filled in "
         f"{time.time() - t0:.1f}s")
@@ -399,8 +404,7 @@ def wl_block(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, bi
     q3.qwen3_rope_table_init(cfg, rope)
     nkv = cfg["num_key_value_heads"]
     cap = ((S + 63) // 64) * 64
-    k = torch.empty((B, nkv, cap, 128), dtype=torch.bfloat16, device=dev)
-    vt = torch.empty((B, nkv, 128, cap), dtype=torch.bfloat16, device=dev)
+    k, vt = q3.kv_cache_empty(B, nkv, cap, dev)
     kv = q3.make_kv_layer(k, vt, cap)
     H = cfg["hidden_size"]
     x = torch.empty((B, S, H), dtype=torch.bfloat16, device=dev)

@@ -147,6 +147,65 @@ def make_kv_layer(k, vt, capacity):
     return KVLayer(_ptr(k), _ptr(vt), int(capacity))
 
 
+# ---- KV-cache layout (data movement only: conversions for setting up or inspecting a cache)
+# Per layer and (sequence, kv head), positions are grouped in tiles of KV_TILE:
+#   K: [cap / 32][4][32][32]   tile, 32-dim chunk, position in the tile, dim in the chunk
+#   V: [cap / 32][128][32]     tile, dim, position in the tile
+KV_TILE = 32
+
+
+def kv_cache_empty(batch, nkv, capacity, device, head_dim=128):
+    """Uninitialised K and V caches of one layer in the library's tiled layout."""
+    import torch
+    if capacity % 64 or head_dim != 128:
+        raise ValueError("capacity must be a multiple of 64 and head_dim 128")
+    nt = capacity // KV_TILE
+    k = torch.empty((batch, nkv, nt, 4, KV_TILE, 32), dtype=torch.bfloat16, device=device)
+    vt = torch.empty((batch, nkv, nt, head_dim, KV_TILE), dtype=torch.bfloat16, device=device)
+    return k, vt
+
+
+def k_cache_from_logical(k_log, out=None):
+    """Tiled K cache from a logical [B, nkv, cap, 128] tensor (a copy, into ``out`` if given)."""
+    B, nkv, cap, _ = k_log.shape
+    nt = cap // KV_TILE
+    src = k_log.reshape(B, nkv, nt, KV_TILE, 4, 32).permute(0, 1, 2, 4, 3, 5)
+    if out is None:
+        return src.contiguous()
+    return out.view(B, nkv, nt, 4, KV_TILE, 32).copy_(src)
+
+
+def v_cache_from_logical(v_log, out=None):
+    """Tiled V cache from a logical [B, nkv, cap, 128] tensor (a copy, into ``out`` if given)."""
+    B, nkv, cap, hd = v_log.shape
+    nt = cap // KV_TILE
+    src = v_log.reshape(B, nkv, nt, KV_TILE, hd).permute(0, 1, 2, 4, 3)
+    if out is None:
+        return src.contiguous()
+    return out.view(B, nkv, nt, hd, KV_TILE).copy_(src)
+
+
+def k_cache_to_logical(k):
+    """Logical [B, nkv, cap, 128] view-copy of a tiled K cache."""
+    B, nkv, nt = k.shape[:3]
+    return (k.reshape(B, nkv, nt, 4, KV_TILE, 32).permute(0, 1, 2, 4, 3, 5)
+            .reshape(B, nkv, nt * KV_TILE, 128))
+
+
+def v_cache_to_logical(vt):
+    """Logical [B, nkv, cap, 128] view-copy of a tiled V cache."""
+    B, nkv, nt = vt.shape[:3]
+    return vt.reshape(B, nkv, nt, 128, KV_TILE).permute(0, 1, 2, 4, 3).reshape(B, nkv, nt * KV_TILE, 128)
+
+
+def kv_cache_from_logical(k_log, v_log):
+    return k_cache_from_logical(k_log), v_cache_from_logical(v_log)
+
+
+def kv_cache_to_logical(k, vt):
+    return k_cache_to_logical(k), v_cache_to_logical(vt)
+
+
 def make_model_weights(embed_tokens, norm, layers, lm_head=None):
     """layers: list of dicts (or LayerWeights).  Returns (ModelWeights, keepalive)."""
     structs = [x if isinstance(x, LayerWeights) else make_layer_weights(x) for x in layers]

@@ -108,6 +108,17 @@ DEV void st16(void* p, u32x4_t v) { *(u32x4_t*)p = v; }
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// KV-cache layout (bf16, per layer).  Each (sequence, kv head) owns a region of cap * 128
+// elements; positions are grouped in tiles of 32 (cap is a multiple of 64):
+//   K: [cap / 32][4][32][32]  tile, 32-dim chunk, position in the tile, dim in the chunk
+//   V: [cap / 32][128][32]    tile, dim, position in the tile
+// so one 32-position tile is 8 KB of K and 8 KB of V, and every 128-byte line a decode
+// fragment load touches is read whole by that load.  Element offsets inside a region:
+DEV int kcache_idx(int pos, int d) {
+  return ((((pos >> 5) << 2) + (d >> 5)) << 10) + ((pos & 31) << 5) + (d & 31);
+}
+DEV int vcache_idx(int pos, int d) { return ((((pos >> 5) << 7) + d) << 5) + (pos & 31); }
+
 // x from the lane N places round the same 16-lane row (DPP row_ror)
 template <int N>
 DEV float ror16(float x) {

@@ -48,8 +48,8 @@ struct RopeEpi {
   const bf16_t* q_norm;
   const bf16_t* k_norm;
   f16_t* q_out;      // [T][nq][hd], pre-scaled by log2(e) / sqrt(hd)
-  bf16_t* k_cache;   // [B][nkv][cap][hd]
-  bf16_t* vt_cache;  // [B][nkv][hd][cap]
+  bf16_t* k_cache;   // [B][nkv] regions, 32-position tiles (kcache_idx)
+  bf16_t* vt_cache;  // [B][nkv] regions, 32-position tiles (vcache_idx)
   f16_t* k_fresh;    // [B][nkv][fresh_w][hd], position - fresh_base
   f16_t* vt_fresh;   // [B][nkv][hd][fresh_w]
   int fresh_base, fresh_w, pos0, S, nq, nkv, cap, max_pos, qk_norm, interleaved;
@@ -296,7 +296,7 @@ DEV void qkrope_epilogue(const Args& p, const f32x16_t (&acc)[T::TM][T::TN], f16
               kb[k] = pack_bf16x2(y[2 * k], y[2 * k + 1]);
               kh[k] = pack_f16x2(y[2 * k], y[2 * k + 1]);
             }
-            st16(e.k_cache + (((int64_t)b * e.nkv + h) * e.cap + pos) * HD + d0, kb);
+            st16(e.k_cache + ((int64_t)b * e.nkv + h) * e.cap * HD + kcache_idx(pos, d0), kb);
             if (e.k_fresh)
               st16(e.k_fresh + (((int64_t)b * e.nkv + h) * e.fresh_w + (pos - e.fresh_base)) *
                                    HD + d0, kh);
@@ -307,12 +307,12 @@ DEV void qkrope_epilogue(const Args& p, const f32x16_t (&acc)[T::TM][T::TN], f16
     if (!is_q) zero_fresh_tail<T::THREADS>(e, out_row0, rows_valid, head0, HEADS, true);
     return;
   }
-  // v heads: item = (column c, group of 8 rows); consecutive lanes take consecutive groups
-  // so that a wave's stores run along positions
+  // v heads: item = (32-row group, column c, group of 8 rows); four consecutive lanes take
+  // the four 8-row groups of one column, the next lanes the next columns, so that with
+  // tile-aligned positions a wave's 16-byte stores cover 16 whole dims of a cache tile
   const int head0 = (n0 - p.seg2) / HD;
-  constexpr int RG = T::BM / 8;
-  for (int item = tid; item < T::BN * RG; item += T::THREADS) {
-    const int c = item / RG, r0 = (item % RG) * 8;
+  for (int item = tid; item < T::BN * (T::BM / 8); item += T::THREADS) {
+    const int c = (item >> 2) % T::BN, r0 = ((item >> 2) / T::BN) * 32 + (item & 3) * 8;
     const int h = head0 + c / HD, d = c % HD;
     if (h >= e.nkv || r0 >= rows_valid) continue;
     const int64_t t0 = out_row0 + r0;
@@ -322,7 +322,7 @@ DEV void qkrope_epilogue(const Args& p, const f32x16_t (&acc)[T::TM][T::TN], f16
     float v[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = h2f(st[(r0 + (k < n ? k : 0)) * LDT + c]);
-    bf16_t* vb = e.vt_cache + (((int64_t)b * e.nkv + h) * HD + d) * e.cap + pos;
+    bf16_t* const vreg = e.vt_cache + ((int64_t)b * e.nkv + h) * e.cap * HD;
     f16_t* vf = e.vt_fresh ? e.vt_fresh + (((int64_t)b * e.nkv + h) * HD + d) * e.fresh_w +
                                  (pos - e.fresh_base)
                            : nullptr;
@@ -334,7 +334,7 @@ DEV void qkrope_epilogue(const Args& p, const f32x16_t (&acc)[T::TM][T::TN], f16
         ob[k] = pack_bf16x2(v[2 * k], v[2 * k + 1]);
         oh[k] = pack_f16x2(v[2 * k], v[2 * k + 1]);
       }
-      st16(vb, ob);
+      st16(vreg + vcache_idx(pos, d), ob);
       if (vf) st16(vf, oh);
     } else {
       // rows may cross into the next sequence: place each token by its own (b, s)
@@ -342,9 +342,9 @@ DEV void qkrope_epilogue(const Args& p, const f32x16_t (&acc)[T::TM][T::TN], f16
         const int64_t t = t0 + k;
         const int bk = (int)(t / e.S), sk = (int)(t % e.S), pk = e.pos0 + sk;
         if (pk < 0 || pk >= e.cap || pk >= e.max_pos) continue;
-        const int64_t base = ((int64_t)bk * e.nkv + h) * HD + d;
-        e.vt_cache[base * e.cap + pk] = f2bf(v[k]);
-        if (e.vt_fresh) e.vt_fresh[base * e.fresh_w + (pk - e.fresh_base)] = f2h(v[k]);
+        const int64_t bh = (int64_t)bk * e.nkv + h;
+        e.vt_cache[bh * e.cap * HD + vcache_idx(pk, d)] = f2bf(v[k]);
+        if (e.vt_fresh) e.vt_fresh[(bh * HD + d) * e.fresh_w + (pk - e.fresh_base)] = f2h(v[k]);
       }
     }
   }

@@ -51,8 +51,8 @@ struct RopeCacheArgs {
   const bf16_t* q_norm;
   const bf16_t* k_norm;
   f16_t* q_out;  // [T][nq][hd] fp16, pre-scaled by log2(e) / sqrt(hd)
-  bf16_t* k_cache;  // [B][nkv][cap][hd]
-  bf16_t* vt_cache; // [B][nkv][hd][cap]
+  bf16_t* k_cache;  // [B][nkv] regions of cap * hd, 32-position tiles (kcache_idx)
+  bf16_t* vt_cache; // [B][nkv] regions of cap * hd, 32-position tiles (vcache_idx)
   const int32_t* pos;  // decode: device [B], token s at pos[b] + s; prefill: nullptr
   // prefill only: fp16 copies of the new keys / values (not rounded to bf16) for the attention,
   // indexed by absolute position - fresh_base; k_fresh [B][nkv][fresh_w][hd],
@@ -69,8 +69,8 @@ hipError_t qkv_rope_cache(const RopeCacheArgs& a, hipStream_t s);
 // ---- attention (attention.hip)
 struct AttnPrefillArgs {
   const f16_t* q;        // [B][S][nq][hd] fp16
-  const bf16_t* k_cache; // [B][nkv][cap][hd]
-  const bf16_t* vt_cache;// [B][nkv][hd][cap]
+  const bf16_t* k_cache; // [B][nkv] regions of cap * hd, 32-position tiles
+  const bf16_t* vt_cache;// [B][nkv] regions of cap * hd, 32-position tiles
   f16_t* out;            // [B][S][nq][hd] fp16
   // keys / values at positions >= pos0 come from these fp16 copies (see RopeCacheArgs)
   const f16_t* k_fresh;

@@ -121,8 +121,9 @@ rope_table_kernel(float* __restrict__ rope, int max_pos, int half, double theta,
 
 // Per (64-token tile, sequence, head slot):
 //   q heads:  q = rope(rmsnorm_hd(q)) * log2(e)/sqrt(hd) -> q_out [T][nq][hd] (fp16)
-//   k heads:  k = rope(rmsnorm_hd(k)) -> k_cache[b][h][pos][:]
-//   v heads:  v -> vt_cache[b][h][:][pos]  (transposed through LDS)
+//   k heads:  k = rope(rmsnorm_hd(k)) -> K cache of (b, h) at pos
+//   v heads:  v -> V cache of (b, h) at pos  (dim-major inside each 32-position tile,
+//             transposed through LDS)
 // ([P3] "GQA 注意力": per-head q/k RMSNorm before RoPE, offset = cached length;
 // "RoPE": pairs (i, i + hd/2) rotated by pos * theta_i; with a.interleaved the planes are
 // (2i, 2i + 1) instead, the complex-number form of [P1] section 8.)
@@ -258,7 +259,7 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
           kb[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
           kh[e] = pack_f16x2(y[2 * e], y[2 * e + 1]);
         }
-        st16(a.k_cache + (((int64_t)b * a.nkv + h) * a.cap + pos) * HD + d0, kb);
+        st16(a.k_cache + ((int64_t)b * a.nkv + h) * a.cap * HD + kcache_idx(pos, d0), kb);
         if (a.k_fresh)
           st16(a.k_fresh + (((int64_t)b * a.nkv + h) * a.fresh_w + (pos - a.fresh_base)) * HD + d0,
                kh);
@@ -300,7 +301,7 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
     if (s >= a.S) continue;
     const int pos = a.pos0 + s;
     const int n = min(8, a.S - s);  // valid tokens in this group
-    bf16_t* vb = a.vt_cache + (((int64_t)b * a.nkv + h) * HD + d) * a.cap + pos;
+    bf16_t* const vreg = a.vt_cache + ((int64_t)b * a.nkv + h) * a.cap * HD;
     f16_t* vf = a.vt_fresh ? a.vt_fresh + (((int64_t)b * a.nkv + h) * HD + d) * a.fresh_w +
                                  (pos - a.fresh_base)
                            : nullptr;
@@ -311,11 +312,11 @@ __global__ void __launch_bounds__(256) qkv_rope_cache_kernel(RopeCacheArgs a) {
         ob[e] = pack_bf16x2(sv[r0 + 2 * e][d], sv[r0 + 2 * e + 1][d]);
         oh[e] = pack_f16x2(sv[r0 + 2 * e][d], sv[r0 + 2 * e + 1][d]);
       }
-      st16(vb, ob);
+      st16(vreg + vcache_idx(pos, d), ob);
       if (vf) st16(vf, oh);
     } else {
       for (int e = 0; e < n; ++e) {
-        vb[e] = f2bf(sv[r0 + e][d]);
+        vreg[vcache_idx(pos + e, d)] = f2bf(sv[r0 + e][d]);
         if (vf) vf[e] = f2h(sv[r0 + e][d]);
       }
     }
@@ -454,9 +455,9 @@ __global__ void __launch_bounds__(256) qkv_rope_decode_kernel(RopeCacheArgs a) {
   if (slot >= a.nq + a.nkv) {  // v head
     if (!ok) return;
     const int h = slot - a.nq - a.nkv;
-    bf16_t* vb = a.vt_cache + (((int64_t)b * a.nkv + h) * HD + d0) * a.cap + pos;
+    bf16_t* const vreg = a.vt_cache + ((int64_t)b * a.nkv + h) * a.cap * HD;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) vb[(int64_t)e * a.cap] = f2bf(x[e]);
+    for (int e = 0; e < 8; ++e) vreg[vcache_idx(pos, d0 + e)] = f2bf(x[e]);
     return;
   }
   const bool is_q = slot < a.nq;
@@ -514,7 +515,7 @@ __global__ void __launch_bounds__(256) qkv_rope_decode_kernel(RopeCacheArgs a) {
     u32x4_t kb;
 #pragma unroll
     for (int e = 0; e < 4; ++e) kb[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
-    st16(a.k_cache + (((int64_t)b * a.nkv + h) * a.cap + pos) * HD + d0, kb);
+    st16(a.k_cache + ((int64_t)b * a.nkv + h) * a.cap * HD + kcache_idx(pos, d0), kb);
   }
 }
 

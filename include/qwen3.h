@@ -28,12 +28,18 @@
  *     multiples of 64; num_attention_heads a multiple of num_key_value_heads with a
  *     group size of at most 8; MoE: at most 256 experts and 8 experts per token.
  *
- * KV cache (per layer, caller-owned, bf16):
- *   k  [batch][num_key_value_heads][capacity][head_dim]   key rows by position
- *   vt [batch][num_key_value_heads][head_dim][capacity]   values, position-minor
+ * KV cache (per layer, caller-owned, bf16), tiled by 32 positions (head_dim = 128):
+ *   k  [batch][num_key_value_heads][capacity/32][4][32][32]
+ *        tile, 32-dim chunk, position in the tile, dim in the chunk:
+ *        K(b, h, pos, d) at (((b*nkv + h)*(capacity/32) + pos/32)*4 + d/32)*1024
+ *                           + (pos%32)*32 + d%32
+ *   vt [batch][num_key_value_heads][capacity/32][128][32]
+ *        tile, dim, position in the tile:
+ *        V(b, h, pos, d) at (((b*nkv + h)*(capacity/32) + pos/32)*128 + d)*32 + pos%32
  *   Keys are stored after q/k-norm and RoPE, values as projected ([P3] "GQA 注意力":
- *   the cache keeps normalised, rotated K).  The value half is kept transposed so the
- *   attention kernels read it in the operand order of the matrix cores.
+ *   the cache keeps normalised, rotated K).  A 32-position tile is 8 KB of K and 8 KB of
+ *   V in the operand order of the decode attention's matrix-core loads, so each of its
+ *   loads reads whole 128-byte lines.
  *   capacity must be a multiple of 64 and at most max_position_embeddings rounded
  *   up to 64.
  */
@@ -127,8 +133,8 @@ typedef struct qwen3_moe_weights {
 
 /* One layer's KV cache (see layout above). */
 typedef struct qwen3_kv_layer {
-  void *k;          /* [B][nkv][capacity][hd] bf16 */
-  void *vt;         /* [B][nkv][hd][capacity] bf16 */
+  void *k;          /* [B][nkv][capacity/32][4][32][32] bf16 (tiled, see above) */
+  void *vt;         /* [B][nkv][capacity/32][hd][32] bf16 (tiled, see above) */
   int32_t capacity; /* positions per sequence, multiple of 64 */
 } qwen3_kv_layer;
 

@@ -242,25 +242,23 @@ def model_device(seed, cfg, device, n_layers=None):
     return d
 
 
-def kv_fill_device(k, vt, seed, l, n_pos, ctx):
-    """Fill cache slots [0, n_pos) of every (sequence, kv head) of one layer with the
-    logical tensor [B, nkv, ctx, hd] named kv.{l}.k / kv.{l}.v.
-    k: [B, nkv, cap, hd]; vt: [B, nkv, hd, cap]."""
+def kv_fill_device(k_log, v_log, seed, l, n_pos, ctx):
+    """Fill positions [0, n_pos) of every (sequence, kv head) of one layer's logical K and V
+    tensors, both [B, nkv, cap, hd], with the logical tensor [B, nkv, ctx, hd] named
+    kv.{l}.k / kv.{l}.v."""
     from . import normal_bf16_device
-    B, nkv, cap, hd = k.shape
+    B, nkv, cap, hd = k_log.shape
     kn, vn = kv_names(l)
     if n_pos == ctx:
-        normal_bf16_device(k, seed, kn, 0.0, 1.0, logical=(B * nkv, n_pos, hd),
-                           strides=(cap * hd, hd, 1))
-        normal_bf16_device(vt, seed, vn, 0.0, 1.0, logical=(B * nkv, n_pos, hd),
-                           strides=(hd * cap, 1, cap))
+        for t, name in ((k_log, kn), (v_log, vn)):
+            normal_bf16_device(t, seed, name, 0.0, 1.0, logical=(B * nkv, n_pos, hd),
+                               strides=(cap * hd, hd, 1))
         return
     for i in range(B * nkv):
         b, h = divmod(i, nkv)
-        normal_bf16_device(k[b, h], seed, kn, 0.0, 1.0, offset=i * ctx * hd,
-                           logical=(1, n_pos, hd), strides=(0, hd, 1))
-        normal_bf16_device(vt[b, h], seed, vn, 0.0, 1.0, offset=i * ctx * hd,
-                           logical=(1, n_pos, hd), strides=(0, 1, cap))
+        for t, name in ((k_log, kn), (v_log, vn)):
+            normal_bf16_device(t[b, h], seed, name, 0.0, 1.0, offset=i * ctx * hd,
+                               logical=(1, n_pos, hd), strides=(0, hd, 1))
 
 
 def moe_device(seed, cfg, device, skew=True, l=0):

@@ -9,6 +9,7 @@ import sys
 
 import numpy as np
 
+import decoder_only_forward_amd as q3
 import synth
 from synth import recipes
 
@@ -61,37 +62,50 @@ def layer_to_dev(layer_host, device):
     return {m[k]: to_dev_bf16(v, device) for k, v in layer_host.items()}
 
 
-def new_cache(B, nkv, cap, device, hd=128, fill=None):
-    import torch
-    k = torch.empty((B, nkv, cap, hd), dtype=torch.bfloat16, device=device)
-    vt = torch.empty((B, nkv, hd, cap), dtype=torch.bfloat16, device=device)
-    if fill is None:
-        k.fill_(float("nan"))  # untouched slots must never be read
-        vt.fill_(float("nan"))
+def new_cache(B, nkv, cap, device):
+    """One layer's K and V caches in the library's tiled layout, every slot NaN (untouched
+    slots must never be read)."""
+    k, vt = q3.kv_cache_empty(B, nkv, cap, device)
+    k.fill_(float("nan"))
+    vt.fill_(float("nan"))
     return k, vt
 
 
-def fill_cache_synthetic(k, vt, seed, l, n_pos, ctx):
+def fill_cache_synthetic(k, vt, seed, l, n_pos, ctx, rows=None):
     """Positions [0, n_pos) of every (sequence, kv head) from the generator, logical tensor
-    [B, nkv, ctx, hd] named kv.{l}.k / kv.{l}.v."""
-    B, nkv, cap, hd = k.shape
+    [B, nkv, ctx, hd] named kv.{l}.k / kv.{l}.v; other slots keep their contents.  With
+    ``rows`` = {b: n_pos_b} only those sequences are filled, each to its own length."""
+    k_log, v_log = q3.kv_cache_to_logical(k, vt)
+    B, nkv = k_log.shape[:2]
     kn, vn = recipes.kv_names(l)
     for b in range(B):
+        n = n_pos if rows is None else rows.get(b, 0)
+        if n <= 0:
+            continue
         for h in range(nkv):
-            off = ((b * nkv + h) * ctx) * hd
-            synth.normal_bf16_device(k[b, h], seed, kn, 0.0, 1.0, offset=off,
-                                     logical=(1, n_pos, hd), strides=(0, hd, 1))
-            synth.normal_bf16_device(vt[b, h], seed, vn, 0.0, 1.0, offset=off,
-                                     logical=(1, n_pos, hd), strides=(0, 1, cap))
+            off = ((b * nkv + h) * ctx) * 128
+            for t, name in ((k_log, kn), (v_log, vn)):
+                synth.normal_bf16_device(t[b, h], seed, name, 0.0, 1.0, offset=off,
+                                         logical=(1, n, 128), strides=(0, 128, 1))
+    kt, vtt = q3.kv_cache_from_logical(k_log, v_log)
+    k.copy_(kt)
+    vt.copy_(vtt)
+
+
+def cache_logical_host(k, vt):
+    """(K, V) of a device cache as logical [B, nkv, cap, hd] bf16 bit arrays."""
+    k_log, v_log = q3.kv_cache_to_logical(k, vt)
+    return bf16_host(k_log), bf16_host(v_log)
 
 
 def cache_k_logical(k, b, n_pos):
     """[nkv, n_pos, hd] float64 from the device K cache."""
-    return f64(bf16_host(k[b, :, :n_pos, :]))
+    return f64(bf16_host(q3.k_cache_to_logical(k)[b, :, :n_pos, :]))
 
 
 def cache_v_logical(vt, b, n_pos):
-    return f64(bf16_host(vt[b, :, :, :n_pos])).transpose(0, 2, 1)
+    """[nkv, n_pos, hd] float64 from the device V cache."""
+    return f64(bf16_host(q3.v_cache_to_logical(vt)[b, :, :n_pos, :]))
 
 
 def small_cfg(H=256, nq=4, nkv=2, I=512, L=2, V=512, qk_norm=1, max_pos=4096,

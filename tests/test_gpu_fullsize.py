@@ -44,8 +44,7 @@ def test_stack_prefill_4x2048(gpu):
     log("case full/stack_prefill 4x2048, 28 layers, all-position logits")
     model = recipes.model_device(recipes.MODEL_SEED_0P6B, cfg, gpu)
     mw, keep = q3.make_model_weights(model["embed"], model["norm"], model["layers"], None)
-    caches = [(torch.empty((B, 8, S, 128), dtype=torch.bfloat16, device=gpu),
-               torch.empty((B, 8, 128, S), dtype=torch.bfloat16, device=gpu)) for _ in range(L)]
+    caches = [q3.kv_cache_empty(B, 8, S, gpu) for _ in range(L)]
     kvs = [q3.make_kv_layer(k, vt, S) for k, vt in caches]
     ids = torch.empty((B, S), dtype=torch.int32, device=gpu)
     synth.uniform_i32_device(ids, 2, "input.ids", 0, V)
@@ -70,13 +69,13 @@ def test_stack_prefill_4x2048(gpu):
     # layer-0 keys / values at late positions depend only on that position's token
     lay0 = host["layers"][0]
     emb = f64(host["embed"])
-    k0, vt0 = caches[0]
+    k0, v0 = q3.kv_cache_to_logical(*caches[0])
     for b, p in ((1, 2047), (2, 1500), (0, 777)):
         x = emb[ids_h[b, p]][None]
         z = np.zeros((8, p, 128))
         _, nk, nv = oracle.block(cfg, lay0, x, p, z, z)
         gk = f64(bf16_host(k0[b, :, p, :]))
-        gv = f64(bf16_host(vt0[b, :, :, p]))
+        gv = f64(bf16_host(v0[b, :, p, :]))
         parity(gk, nk[:, 0, :], f"layer0 k[b={b}, pos={p}]")
         parity(gv, nv[:, 0, :], f"layer0 v[b={b}, pos={p}]")
 
@@ -91,10 +90,11 @@ def test_stack_decode_64_ctx4096(gpu):
     mw, keep = q3.make_model_weights(model["embed"], model["norm"], model["layers"], None)
     caches = []
     for l in range(L):
-        k = torch.empty((B, 8, cap, 128), dtype=torch.bfloat16, device=gpu)
-        vt = torch.empty((B, 8, 128, cap), dtype=torch.bfloat16, device=gpu)
-        recipes.kv_fill_device(k, vt, 3, l, ctx, ctx)
-        caches.append((k, vt))
+        k_log = torch.empty((B, 8, cap, 128), dtype=torch.bfloat16, device=gpu)
+        v_log = torch.empty_like(k_log)
+        recipes.kv_fill_device(k_log, v_log, 3, l, ctx, ctx)
+        caches.append(q3.kv_cache_from_logical(k_log, v_log))
+        del k_log, v_log
     kvs = [q3.make_kv_layer(k, vt, cap) for k, vt in caches]
     ids = torch.empty((B,), dtype=torch.int32, device=gpu)
     synth.uniform_i32_device(ids, 3, "input.ids", 0, V)
@@ -183,8 +183,7 @@ def test_block_7b_32768(gpu):
     B, S, H, nkv = 1, 32768, cfg["hidden_size"], cfg["num_key_value_heads"]
     log("case full/block_7b 1 x 32768")
     w = recipes.layer_device(5, cfg, 0, gpu)
-    k = torch.empty((B, nkv, S, 128), dtype=torch.bfloat16, device=gpu)
-    vt = torch.empty((B, nkv, 128, S), dtype=torch.bfloat16, device=gpu)
+    k, vt = q3.kv_cache_empty(B, nkv, S, gpu)
     x = torch.empty((B, S, H), dtype=torch.bfloat16, device=gpu)
     synth.normal_bf16_device(x, 5, recipes.activations_name(), 0.0, 1.0)
     xo = torch.empty_like(x)
@@ -200,5 +199,6 @@ def test_block_7b_32768(gpu):
     ref, nk, nv = oracle.block(cfg, layer, xh, 0, None, None, rows=rows)
     parity(got, ref, f"x_out rows {rows.tolist()}")
     kp = [0, 777, 32767]
-    parity(f64(bf16_host(k[0, :, kp, :])), nk[:, kp, :], "cache k rows")
-    parity(f64(bf16_host(vt[0, :, :, kp])).transpose(0, 2, 1), nv[:, kp, :], "cache v rows")
+    k_log, v_log = q3.kv_cache_to_logical(k, vt)
+    parity(f64(bf16_host(k_log[0, :, kp, :])), nk[:, kp, :], "cache k rows")
+    parity(f64(bf16_host(v_log[0, :, kp, :])), nv[:, kp, :], "cache v rows")

@@ -10,24 +10,10 @@ import decoder_only_forward_amd as q3
 import oracle
 import synth
 from synth import recipes
-from q3_testutil import bf16_host, layer_to_dev, log, new_cache, parity, small_cfg, to_dev_bf16
+from q3_testutil import (cache_logical_host, fill_cache_synthetic, layer_to_dev, log, new_cache,
+                         parity, small_cfg, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
-
-
-def _fill(k, vt, seed, l, b, n_pos, ctx):
-    """Cache positions [0, n_pos) of sequence b from the generator (logical tensor
-    [B, nkv, ctx, hd] named kv.{l}.k / kv.{l}.v); other slots keep their NaN fill."""
-    _, nkv, cap, hd = k.shape
-    kn, vn = recipes.kv_names(l)
-    if n_pos == 0:
-        return
-    for h in range(nkv):
-        off = ((b * nkv + h) * ctx) * hd
-        synth.normal_bf16_device(k[b, h], seed, kn, 0.0, 1.0, offset=off,
-                                 logical=(1, n_pos, hd), strides=(0, hd, 1))
-        synth.normal_bf16_device(vt[b, h], seed, vn, 0.0, 1.0, offset=off,
-                                 logical=(1, n_pos, hd), strides=(0, 1, cap))
 
 
 def _run(gpu, cfg, seed, positions, S, cap, mode):
@@ -45,10 +31,10 @@ def _run(gpu, cfg, seed, positions, S, cap, mode):
     caches = []
     for l in range(L):
         k, vt = new_cache(B, nkv, cap, gpu)
-        for b, p in enumerate(positions):
-            _fill(k, vt, seed, l, b, min(max(p, 0), cap), ctx)
+        fill_cache_synthetic(k, vt, seed, l, 0, ctx,
+                             rows={b: min(max(p, 0), cap) for b, p in enumerate(positions)})
         caches.append((k, vt))
-    before = [(bf16_host(k), bf16_host(vt)) for k, vt in caches]
+    before = [cache_logical_host(k, vt) for k, vt in caches]
     ids = synth.uniform_i32(seed, "input.ids", (B, S), 0, V)
     rows = B * S if mode == q3.QWEN3_LOGITS_ALL else B
     logits = torch.empty((rows, V), dtype=torch.float32, device=gpu)
@@ -61,7 +47,7 @@ def _run(gpu, cfg, seed, positions, S, cap, mode):
                            nxt, ws)
     torch.cuda.synchronize()
     got = logits.cpu().numpy()
-    after = [(bf16_host(k), bf16_host(vt)) for k, vt in caches]
+    after = [cache_logical_host(k, vt) for k, vt in caches]
     return model, ids, got, nxt.cpu().numpy(), before, after
 
 

@@ -1,0 +1,46 @@
+"""The tiled KV-cache layout helpers of the Python binding against the element offsets the
+C header states for K(b, h, pos, d) and V(b, h, pos, d) (CPU only)."""
+import numpy as np
+import torch
+
+import decoder_only_forward_amd as q3
+
+
+def _k_off(b, h, pos, d, nkv, cap):
+    return (((b * nkv + h) * (cap // 32) + pos // 32) * 4 + d // 32) * 1024 + (pos % 32) * 32 + d % 32
+
+
+def _v_off(b, h, pos, d, nkv, cap):
+    return (((b * nkv + h) * (cap // 32) + pos // 32) * 128 + d) * 32 + pos % 32
+
+
+def test_tiled_cache_offsets_and_round_trip():
+    B, nkv, cap = 2, 3, 128
+    g = torch.Generator().manual_seed(0)
+    k_log = torch.randn((B, nkv, cap, 128), generator=g).to(torch.bfloat16)
+    v_log = torch.randn((B, nkv, cap, 128), generator=g).to(torch.bfloat16)
+    k, vt = q3.kv_cache_from_logical(k_log, v_log)
+    assert k.shape == (B, nkv, cap // 32, 4, 32, 32) and vt.shape == (B, nkv, cap // 32, 128, 32)
+    kf = k.reshape(-1).view(torch.int16).numpy()
+    vf = vt.reshape(-1).view(torch.int16).numpy()
+    kl = k_log.view(torch.int16).numpy()
+    vl = v_log.view(torch.int16).numpy()
+    rng = np.random.default_rng(1)
+    for _ in range(2000):
+        b, h = int(rng.integers(B)), int(rng.integers(nkv))
+        pos, d = int(rng.integers(cap)), int(rng.integers(128))
+        assert kf[_k_off(b, h, pos, d, nkv, cap)] == kl[b, h, pos, d]
+        assert vf[_v_off(b, h, pos, d, nkv, cap)] == vl[b, h, pos, d]
+    k2, v2 = q3.kv_cache_to_logical(k, vt)
+    assert torch.equal(k2, k_log) and torch.equal(v2, v_log)
+    # in-place variant writes the same bytes into a preallocated cache
+    ko, vo = q3.kv_cache_empty(B, nkv, cap, "cpu")
+    q3.k_cache_from_logical(k_log, out=ko)
+    q3.v_cache_from_logical(v_log, out=vo)
+    assert torch.equal(ko, k) and torch.equal(vo, vt)
+
+
+def test_tiled_cache_rejects_bad_capacity():
+    import pytest
+    with pytest.raises(ValueError):
+        q3.kv_cache_empty(1, 1, 96, "cpu")
