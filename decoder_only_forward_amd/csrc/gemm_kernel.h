@@ -15,7 +15,7 @@
 // Every wave owns a WM x WN sub-tile made of 32x32 MFMA tiles.
 //
 // Fused epilogues (one per projection of the decoder block):
-//   E_F32       fp32 store                               (LM head, router, MoE down)
+//   E_F32       fp32 streaming store                     (LM head, router, MoE down)
 //   E_F16       fp16 store                               (QKV projections)
 //   E_RES_F32   out_f32 = res_f32 + acc (in place ok)    (o_proj / down in the stack)
 //   E_RESB_F32  out_f32 = float(res_bf16) + acc          (o_proj in the block API)
@@ -587,7 +587,10 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
       const int64_t row = out_row0 + lr;
       const float v = acc[i][j][r];
       if (EPI == E_F32) {
-        ((float*)p.C)[row * p.ldc + col] = v;
+        // fp32 outputs (logits, MoE slot rows) are far larger than the caches and read
+        // once by a later pass: streaming stores (measured: LM head -1%, MoE down -5%,
+        // and the combine that reads the slot rows -17%)
+        __builtin_nontemporal_store(v, (float*)p.C + row * p.ldc + col);
       } else if (EPI == E_F16) {
         ((f16_t*)p.C)[row * p.ldc + col] = f2h(v);
       } else if (EPI == E_RES_F32 || EPI == E_RESB_F32) {
