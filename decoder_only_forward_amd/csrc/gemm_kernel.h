@@ -524,23 +524,29 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
     qkrope_epilogue<T>(p, acc, (f16_t*)smem, out_row0, rows_valid, n0, wm, wn, lane, wave);
     return;
   }
-  if (EPI == E_SWIGLU) {
-    constexpr int HALF_TN = T::TN / 2;
+  if constexpr (EPI == E_SWIGLU) {
+    // silu(gate) * up rounded to fp16, staged in LDS ([BM][BN / 2 + 8]) so that the global
+    // stores go out as 16-byte chunks of whole rows instead of 2-byte scatters
+    constexpr int HALF_TN = T::TN / 2, OBN = T::BN / 2, LDO = OBN + 8, CPR = OBN / 8;
+    static_assert(T::BM * LDO * 2 <= (int)sizeof(smem), "SwiGLU staging exceeds the ring");
+    f16_t* const so = (f16_t*)smem;
+    __syncthreads();  // every wave is done with the operand ring
 #pragma unroll
     for (int i = 0; i < T::TM; ++i)
 #pragma unroll
-      for (int j = 0; j < HALF_TN; ++j) {
-        int col = tn * (T::BN / 2) + wn * (T::WN / 2) + j * 32 + ccol;
-        if (col >= p.N / 2) continue;
+      for (int j = 0; j < HALF_TN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          int lr = wm * T::WM + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
-          if (lr >= rows_valid) continue;
-          float g = acc[i][j][r], u = acc[i][j + HALF_TN][r];
-          f16_t* out = (f16_t*)p.C + (int64_t)(out_row0 + lr) * p.ldc + col;
-          *out = f2h(silu(g) * u);
+          const int lr = wm * T::WM + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
+          const float g = acc[i][j][r], u = acc[i][j + HALF_TN][r];
+          so[lr * LDO + wn * (T::WN / 2) + j * 32 + ccol] = f2h(silu(g) * u);
         }
-      }
+    __syncthreads();
+    for (int c = threadIdx.x; c < T::BM * CPR; c += T::THREADS) {
+      const int lr = c / CPR, col = tn * OBN + (c % CPR) * 8;
+      if (lr >= rows_valid || col >= p.N / 2) continue;
+      st16((f16_t*)p.C + (int64_t)(out_row0 + lr) * p.ldc + col, ld16(so + lr * LDO + (c % CPR) * 8));
+    }
     return;
   }
   // Residual modes walk the accumulator groups (i, j) as a pipeline: the residual values
