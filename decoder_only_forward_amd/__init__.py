@@ -144,6 +144,12 @@ def make_layer_weights(w):
 
 
 def make_kv_layer(k, vt, capacity):
+    """qwen3_kv_layer for one layer's tiled K and V caches (see kv_cache_empty)."""
+    for name, t in (("k", k), ("vt", vt)):
+        n = getattr(t, "numel", None)
+        if n is not None and (n() == 0 or n() % (int(capacity) * 128)):
+            raise ValueError(f"{name}: {n()} elements is not a whole number of "
+                             f"capacity x 128 = {int(capacity) * 128} regions")
     return KVLayer(_ptr(k), _ptr(vt), int(capacity))
 
 

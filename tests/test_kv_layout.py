@@ -44,3 +44,11 @@ def test_tiled_cache_rejects_bad_capacity():
     import pytest
     with pytest.raises(ValueError):
         q3.kv_cache_empty(1, 1, 96, "cpu")
+
+
+def test_make_kv_layer_checks_region_sizes():
+    import pytest
+    k, vt = q3.kv_cache_empty(2, 1, 64, "cpu")
+    q3.make_kv_layer(k, vt, 64)  # whole regions: accepted
+    with pytest.raises(ValueError):
+        q3.make_kv_layer(k, vt, 192)  # 2 x 64 positions is not a multiple of 192
