@@ -201,7 +201,8 @@ def k_cache_to_logical(k):
 def v_cache_to_logical(vt):
     """Logical [B, nkv, cap, 128] view-copy of a tiled V cache."""
     B, nkv, nt = vt.shape[:3]
-    return vt.reshape(B, nkv, nt, 128, KV_TILE).permute(0, 1, 2, 4, 3).reshape(B, nkv, nt * KV_TILE, 128)
+    return (vt.reshape(B, nkv, nt, 128, KV_TILE).permute(0, 1, 2, 4, 3)
+            .reshape(B, nkv, nt * KV_TILE, 128))
 
 
 def kv_cache_from_logical(k_log, v_log):

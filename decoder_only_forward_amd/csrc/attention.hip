@@ -379,7 +379,7 @@ struct DecTile {
 // load 16 dims x 64 bytes (1 KB in one piece).
 struct DecSrc {
   __amdgpu_buffer_rsrc_t k, v;
-  uint32_t k_lane;  // bytes: K position 8 (r / 4) + r % 4 of the tile, dims 8 grp .. of chunk 0
+  uint32_t k_lane;  // bytes: K position 8 (r / 4) + r % 4 of the tile, chunk 0 dims 8 grp ..
   uint32_t v_lane;  // bytes: V dim r of the tile, positions 8 grp ..
 };
 
@@ -395,11 +395,12 @@ DEV void dec_load(DecTile& t, const DecSrc& src, int key0) {
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      t.k[s * 4 + c] = __builtin_amdgcn_raw_buffer_load_b128(src.k, tb + src.k_lane + s * 256 + c * 2048,
-                                                             0, kStreamPolicy);
+      t.k[s * 4 + c] = __builtin_amdgcn_raw_buffer_load_b128(
+          src.k, tb + src.k_lane + s * 256 + c * 2048, 0, kStreamPolicy);
 #pragma unroll
   for (int rt = 0; rt < 8; ++rt)
-    t.v[rt] = __builtin_amdgcn_raw_buffer_load_b128(src.v, tb + src.v_lane + rt * 1024, 0, kStreamPolicy);
+    t.v[rt] = __builtin_amdgcn_raw_buffer_load_b128(src.v, tb + src.v_lane + rt * 1024, 0,
+                                                    kStreamPolicy);
 }
 
 DEV f32x4_t mfma16_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
@@ -545,7 +546,8 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDecodeArgs a) {
     src.k = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.k_cache + ((int64_t)b * a.nkv + kvh) * region), 0, (int)(region * 2), 0x00020000);
     src.v = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.vt_cache + ((int64_t)b * a.nkv + kvh) * region), 0, (int)(region * 2), 0x00020000);
+        (void*)(a.vt_cache + ((int64_t)b * a.nkv + kvh) * region), 0, (int)(region * 2),
+        0x00020000);
     src.k_lane = (uint32_t)(8 * (r >> 2) + (r & 3)) * 64 + grp * 16;
     src.v_lane = (uint32_t)r * 64 + grp * 16;
     // two register buffers: the wave's next tile is in flight while one is consumed.

@@ -545,7 +545,8 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
     for (int c = threadIdx.x; c < T::BM * CPR; c += T::THREADS) {
       const int lr = c / CPR, col = tn * OBN + (c % CPR) * 8;
       if (lr >= rows_valid || col >= p.N / 2) continue;
-      st16((f16_t*)p.C + (int64_t)(out_row0 + lr) * p.ldc + col, ld16(so + lr * LDO + (c % CPR) * 8));
+      st16((f16_t*)p.C + (int64_t)(out_row0 + lr) * p.ldc + col,
+           ld16(so + lr * LDO + (c % CPR) * 8));
     }
     return;
   }

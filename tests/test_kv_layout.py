@@ -7,7 +7,8 @@ import decoder_only_forward_amd as q3
 
 
 def _k_off(b, h, pos, d, nkv, cap):
-    return (((b * nkv + h) * (cap // 32) + pos // 32) * 4 + d // 32) * 1024 + (pos % 32) * 32 + d % 32
+    tile = (b * nkv + h) * (cap // 32) + pos // 32
+    return (tile * 4 + d // 32) * 1024 + (pos % 32) * 32 + d % 32
 
 
 def _v_off(b, h, pos, d, nkv, cap):
