@@ -102,6 +102,8 @@ DECODE_CASES = {
     "group7": (dict(nq=7, nkv=1), [300, 5], 320),
     "interleaved_rope": (dict(rope_interleaved=1), [0, 77, 200], 256),
     "cfg_0p6b": (None, [4096, 1000], 4160),
+    # the 7B-shaped block: K = 3584 and 18944 decode products, 7 q heads per kv head
+    "cfg_7b": ("7b", [2000, 37], 2048),
 }
 
 
@@ -109,7 +111,12 @@ DECODE_CASES = {
 def test_block_decode_parity(gpu, name):
     import torch
     kw, positions, cap = DECODE_CASES[name]
-    cfg = dict(recipes.QWEN3_0P6B) if kw is None else small_cfg(**kw)
+    if kw is None:
+        cfg = dict(recipes.QWEN3_0P6B)
+    elif kw == "7b":
+        cfg = dict(recipes.QWEN_7B_BLOCK)
+    else:
+        cfg = small_cfg(**kw)
     log(f"case block_decode/{name}: pos={positions} cap={cap}")
     seed = 12
     B = len(positions)
