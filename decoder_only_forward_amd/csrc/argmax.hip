@@ -19,7 +19,17 @@ argmax_chunk_kernel(const float* __restrict__ logits, int64_t row_stride, int V,
   const float* x = logits + (int64_t)row * row_stride;
   float bv = -INFINITY;
   int bi = 0x7FFFFFFF;
-  for (int v = v0 + threadIdx.x; v < v1; v += 256) better(x[v], v, bv, bi);
+  // 16-byte loads over the aligned middle of the chunk, single elements at its ends (the
+  // result does not depend on the visiting order: larger value, then lower index, wins)
+  const int a0 = min(v1, v0 + (int)(((16 - ((uintptr_t)(x + v0) & 15)) & 15) >> 2));
+  const int a1 = a0 + ((v1 - a0) & ~3);
+  for (int v = v0 + threadIdx.x; v < a0; v += 256) better(x[v], v, bv, bi);
+  for (int v = a0 + 4 * threadIdx.x; v < a1; v += 4 * 256) {
+    const f32x4_t q = *(const f32x4_t*)(x + v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) better(q[e], v + e, bv, bi);
+  }
+  for (int v = a1 + threadIdx.x; v < v1; v += 256) better(x[v], v, bv, bi);
   for (int o = 32; o > 0; o >>= 1) {
     float ov = __shfl_xor(bv, o, 64);
     int oi = __shfl_xor(bi, o, 64);
