@@ -183,6 +183,12 @@ def _layers(model):
     return arr, keep
 
 
+def _check_ids(ids, cfg):
+    """Token ids index the embedding rows: each must lie in [0, vocab_size)."""
+    if ids.size and (ids.min() < 0 or ids.max() >= cfg["vocab_size"]):
+        raise ValueError(f"token id outside [0, {cfg['vocab_size']})")
+
+
 def stack_prefill(cfg, model, ids, rows=None, want_kv=False, want_router=False):
     """Whole model on one sequence from position 0.  model: dict(embed, norm, lm_head or None,
     layers=[layer dicts]).  Returns logits [len(rows), V] (and per-layer k, v when asked;
@@ -190,6 +196,7 @@ def stack_prefill(cfg, model, ids, rows=None, want_kv=False, want_router=False):
     c = make_cfg(cfg)
     arr, keep = _layers(model)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
+    _check_ids(ids, cfg)
     S = ids.shape[0]
     rows = np.arange(S, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
     embed, norm = _u16(model["embed"]), _u16(model["norm"])
@@ -222,6 +229,7 @@ def stack_decode(cfg, model, token_id, pos, cache_k, cache_v, want_router=False)
     L = c.n_layers
     single = np.ndim(token_id) == 0
     ids = np.ascontiguousarray(np.atleast_1d(token_id), dtype=np.int32)
+    _check_ids(ids, cfg)
     n = ids.shape[0]
     f64 = cache_k[0].dtype == np.float64
     ck = [(_f64(a) if f64 else _u16(a)) for a in cache_k]
