@@ -265,6 +265,25 @@ def moe_ffn(cfg, router, gate_up, down, x):
     return y, idx, w, lg
 
 
+def moe_ffn_at(cfg, gate_up, down, x, idx, w):
+    """Routed MoE FFN at a given selection: y[t] = sum_j w[t, j] expert_{idx[t, j]}(x[t]).
+    x [T, H] float; idx [T, k] int; w [T, k] float.  Returns y [T, H]."""
+    c = make_cfg(cfg)
+    x = _f64(x)
+    T, H = x.shape
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    w = _f64(w)
+    if idx.shape != (T, c.top_k) or w.shape != (T, c.top_k):
+        raise ValueError("idx and w must be [T, num_experts_per_tok]")
+    if idx.size and (idx.min() < 0 or idx.max() >= c.n_experts):
+        raise ValueError("expert index outside [0, num_experts)")
+    gate_up, down = _u16(gate_up), _u16(down)
+    y = np.empty((T, H), dtype=np.float64)
+    lib().oracle_moe_ffn_at(ctypes.byref(c), _p(gate_up), _p(down), _p(x), ctypes.c_int64(T),
+                            _p(idx), _p(w), _p(y))
+    return y
+
+
 def topk(logits, k):
     lg = np.ascontiguousarray(logits, dtype=np.float32)
     T, E = lg.shape

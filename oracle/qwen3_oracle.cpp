@@ -434,6 +434,25 @@ void oracle_route_bf16(const double *logits, int64_t T, int E, int k, int norm_t
   }
 }
 
+// The selected experts of one token, mixed: y = sum_j w_j down_e(silu(gate_e x) * up_e x) with
+// e = idx[j]; each expert is a SwiGLU whose fused gate_up_proj [2I, H] splits into gate =
+// rows [0, I) and up = rows [I, 2I) ([P3] "MoE": chunk(2) of gate_up_proj, the expert
+// outputs weighted and summed per token).
+static void expert_mix(int H, int I, int k, const uint16_t *gate_up, const uint16_t *down,
+                       const double *xt, const int32_t *idx, const double *w, double *y) {
+  std::vector<double> g(I), u(I), o(H);
+  for (int i = 0; i < H; ++i) y[i] = 0.0;
+  for (int j = 0; j < k; ++j) {
+    int e = idx[j];
+    const uint16_t *gu = gate_up + (int64_t)e * 2 * I * H;
+    linear_row(xt, gu, I, H, g.data());
+    linear_row(xt, gu + (int64_t)I * H, I, H, u.data());
+    for (int i = 0; i < I; ++i) g[i] = silu(g[i]) * u[i];
+    linear_row(g.data(), down + (int64_t)e * H * I, H, I, o.data());
+    for (int i = 0; i < H; ++i) y[i] += w[j] * o[i];
+  }
+}
+
 // Routed MoE FFN of one token ([P3] "MoE": router linear, fp32 softmax, top-k, optional
 // renormalisation; each selected expert is a SwiGLU whose fused gate_up_proj [2I, H]
 // splits into gate = rows [0, I) and up = rows [I, 2I) (chunk(2)); outputs are summed with
@@ -455,17 +474,7 @@ static void moe_row(const oracle_cfg *c, const uint16_t *router, const uint16_t 
     for (int j = 0; j < k; ++j) idx[j] = order[j];
     oracle_route_weights(r, idx, 1, E, k, c->norm_topk, w);
   }
-  std::vector<double> g(I), u(I), o(H);
-  for (int i = 0; i < H; ++i) y[i] = 0.0;
-  for (int j = 0; j < k; ++j) {
-    int e = idx[j];
-    const uint16_t *gu = gate_up + (int64_t)e * 2 * I * H;
-    linear_row(xt, gu, I, H, g.data());
-    linear_row(xt, gu + (int64_t)I * H, I, H, u.data());
-    for (int i = 0; i < I; ++i) g[i] = silu(g[i]) * u[i];
-    linear_row(g.data(), down + (int64_t)e * H * I, H, I, o.data());
-    for (int i = 0; i < H; ++i) y[i] += w[j] * o[i];
-  }
+  expert_mix(H, I, k, gate_up, down, xt, idx, w, y);
 }
 
 // Routed MoE FFN over T tokens, token by token (see moe_row).
@@ -476,6 +485,19 @@ void oracle_moe_ffn(const oracle_cfg *c, const uint16_t *router, const uint16_t 
   parallel_for(T, [&](int64_t t) {
     moe_row(c, router, gate_up, down, x + t * H, y + t * H, idx + t * k, w + t * k,
             logits + t * E);
+  });
+}
+
+// Routed MoE FFN evaluated at a given selection: token t mixes experts idx[t][0..k) with
+// weights w[t][0..k) (see expert_mix).  This is the token-wise reference of [P3] "MoE" with
+// the routing taken as an input, so that a device's output can be checked at the device's
+// own expert choice for tokens whose top-k sits on a near-tie of router logits.
+void oracle_moe_ffn_at(const oracle_cfg *c, const uint16_t *gate_up, const uint16_t *down,
+                       const double *x, int64_t T, const int32_t *idx, const double *w,
+                       double *y) {
+  const int H = c->hidden, k = c->top_k, I = c->moe_inter;
+  parallel_for(T, [&](int64_t t) {
+    expert_mix(H, I, k, gate_up, down, x + t * H, idx + t * k, w + t * k, y + t * H);
   });
 }
 

@@ -76,6 +76,9 @@ void oracle_stack_decode(const oracle_cfg *c, const uint16_t *embed, const uint1
 void oracle_moe_ffn(const oracle_cfg *c, const uint16_t *router, const uint16_t *gate_up,
                     const uint16_t *down, const double *x, int64_t T, double *y, int32_t *idx,
                     double *w, double *logits);
+void oracle_moe_ffn_at(const oracle_cfg *c, const uint16_t *gate_up, const uint16_t *down,
+                       const double *x, int64_t T, const int32_t *idx, const double *w,
+                       double *y);
 void oracle_topk(const float *logits, int64_t T, int E, int k, int32_t *idx);
 void oracle_route_weights(const double *logits, const int32_t *idx, int64_t T, int E, int k,
                           int norm_topk, double *w);

@@ -655,3 +655,105 @@ def test_route_bf16_closed_form():
     idx, w = oracle.route_bf16(np.array([[0.0, 0.0, -100.0]]), 2)
     np.testing.assert_array_equal(idx[0], [0, 1])
     np.testing.assert_array_equal(w[0], [0.5, 0.5])
+
+
+# ---------------------------------------------------------------- MoE at a given selection
+
+def test_moe_at_selection_equals_moe_ffn_and_single_expert_swiglu():
+    # moe_ffn_at with moe_ffn's own selection and weights reproduces moe_ffn's y; one
+    # selected expert at weight 1 is that expert's SwiGLU (gate = rows [0, I), up = the rest);
+    # the output is linear in the weights (a dropped or doubled slot fails this)
+    cfg = _moe_cfg(E=8, k=3)
+    H, I = cfg["hidden_size"], cfg["moe_intermediate_size"]
+    r, gu, dn = _moe_weights(cfg)
+    x = rng.standard_normal((21, H))
+    y, idx, w, _ = oracle.moe_ffn(cfg, r, gu, dn, x)
+    np.testing.assert_allclose(oracle.moe_ffn_at(cfg, gu, dn, x, idx, w), y, atol=1e-14)
+    e = 5
+    one = dict(cfg, num_experts_per_tok=1)
+    y1 = oracle.moe_ffn_at(one, gu, dn, x, np.full((21, 1), e), np.ones((21, 1)))
+    np.testing.assert_allclose(y1, oracle.swiglu_ffn(x, gu[e][:I], gu[e][I:], dn[e]),
+                               atol=1e-14)
+    # another selection: each slot's expert output scaled by its own weight
+    idx2 = np.stack([rng.permutation(8)[:3] for _ in range(21)]).astype(np.int32)
+    w2 = rng.random((21, 3))
+    want = np.zeros_like(x)
+    for j in range(3):
+        for t in range(21):
+            ee = idx2[t, j]
+            want[t] += w2[t, j] * oracle.swiglu_ffn(x[t:t + 1], gu[ee][:I], gu[ee][I:],
+                                                     dn[ee])[0]
+    np.testing.assert_allclose(oracle.moe_ffn_at(cfg, gu, dn, x, idx2, w2), want, atol=1e-13)
+
+
+# ---------------------------------------------------------------- untied head, generation
+
+def _untied(model, perm):
+    """The same model with an untied head whose row v is embedding row perm[v]."""
+    m = dict(model)
+    m["lm_head"] = np.ascontiguousarray(model["embed"][perm])
+    return m
+
+
+def test_untied_head_reads_lm_head_rows():
+    # lm_head = embedding rows permuted: logits column v must equal the tied model's column
+    # perm[v] at every position, in prefill and decode (reading embed instead of lm_head for
+    # the head, or lm_head instead of embed for the input lookup, breaks the identity)
+    cfg = _small_cfg()
+    V = cfg["vocab_size"]
+    model = recipes.model_host(8, cfg)
+    perm = rng.permutation(V)
+    mu = _untied(model, perm)
+    cu = dict(cfg, tie_word_embeddings=0)
+    ids = np.array([4, 250, 31, 31, 7, 190], np.int32)
+    tied, ko, vo = oracle.stack_prefill(cfg, model, ids, want_kv=True)
+    unt = oracle.stack_prefill(cu, mu, ids)
+    np.testing.assert_allclose(unt, tied[:, perm], rtol=0, atol=1e-13)
+    p = 5
+    dt = oracle.stack_decode(cfg, model, ids[p], p, [k[:, :p] for k in ko],
+                             [v[:, :p] for v in vo])
+    du = oracle.stack_decode(cu, mu, ids[p], p, [k[:, :p] for k in ko], [v[:, :p] for v in vo])
+    np.testing.assert_allclose(du, dt[perm], rtol=0, atol=1e-13)
+    # the permutation is not the identity on the argmax (the check has teeth)
+    assert oracle.argmax(unt[-1])[0] != oracle.argmax(tied[-1])[0]
+
+
+def _zero_layer_model(cfg, V, seed=11):
+    """Every projection weight zero (each block is then the identity on the residual); the
+    embedding rows are +-1/4 signs, so rmsnorm(E[t]) . E[u] is largest at u = t."""
+    H = cfg["hidden_size"]
+    g = np.random.default_rng(seed)
+    model = recipes.model_host(seed, cfg)
+    for lw in model["layers"]:
+        for f in ("q", "k", "v", "o", "gate", "up", "down"):
+            lw[f] = np.zeros_like(lw[f])
+    model["embed"] = bf16(np.where(g.random((V, H)) < 0.5, -0.25, 0.25))
+    return model
+
+
+def test_generate_greedy_follows_the_head_permutation_with_zero_layers():
+    # With zero projections every block returns its input, so the last hidden state is the
+    # embedding row of the last token; with lm_head row v = E[perm[v]] the greedy next token
+    # after t is the v with perm[v] = t.  Generation must therefore walk the inverse
+    # permutation's cycle from the prompt's last token: a wrong feed-back (not the previous
+    # token, or not at the end of the sequence) leaves that cycle.
+    cfg = dict(_small_cfg(), tie_word_embeddings=0)
+    V, H = cfg["vocab_size"], cfg["hidden_size"]
+    model = _zero_layer_model(cfg, V)
+    perm = rng.permutation(V)
+    inv = np.argsort(perm)
+    model = _untied(model, perm)
+    # the next-token map from embed, norm and lm_head alone (numpy), against the closed form
+    E = _f(model["embed"])
+    wf = _f(model["norm"])
+    hn = E / np.sqrt((E * E).mean(axis=1, keepdims=True) + cfg["rms_norm_eps"]) * wf
+    nxt = np.argmax(hn @ _f(model["lm_head"]).T, axis=1)
+    np.testing.assert_array_equal(nxt, inv)
+    prompt = [17, 3, 250, 99]
+    got = oracle.generate(cfg, model, prompt, 6)
+    want, t = [], prompt[-1]
+    for _ in range(6):
+        t = int(inv[t])
+        want.append(t)
+    np.testing.assert_array_equal(got, want)
+    assert len(set(want)) > 1
