@@ -56,26 +56,53 @@ class Timer:
     def __init__(self, torch, q3):
         self.torch, self.q3 = torch, q3
 
-    def run(self, fn, steps, warmup, tag=None, launches_per_step=1):
+    def run(self, fn, steps, warmup, tag=None, launches_per_step=1, per_step=None):
+        """Mean ms per step over `steps` back-to-back calls (events before the first and
+        after the last); with a dict `per_step`, also the median and minimum of the
+        per-call durations (an event between consecutive calls)."""
         torch, q3 = self.torch, self.q3
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
         if tag:
             q3.qwen3_profile_begin(tag, steps * launches_per_step)
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
+        for i in range(steps):
             fn()
-        t1.record()
+            ev[i + 1].record()
         torch.cuda.synchronize()
-        total = t0.elapsed_time(t1)
+        total = ev[0].elapsed_time(ev[-1])
+        if per_step is not None:
+            d = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+            per_step["ms_per_step_median"] = d[len(d) // 2] if len(d) % 2 else \
+                0.5 * (d[len(d) // 2 - 1] + d[len(d) // 2])
+            per_step["ms_per_step_min"] = d[0]
         kernel = None
         if tag:
             kms, n = q3.qwen3_profile_end()
             kernel = {"tag": tag, "launches": n, "avg_ms": kms / max(n, 1)}
         return total / steps, kernel
+
+    def run_cold(self, fn, steps, flush_bytes):
+        """Per-call durations with the caches flushed before each call: a buffer of
+        flush_bytes (larger than the 256 MB last-level cache) is written between calls,
+        outside the timed events.  Returns (median, min) ms."""
+        torch = self.torch
+        buf = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+        d = []
+        for i in range(steps):
+            buf.fill_(float(i))
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            d.append(e0.elapsed_time(e1))
+        del buf
+        d.sort()
+        return d[len(d) // 2], d[0]
 
 
 # ------------------------------------------------------------------------- workloads
@@ -126,7 +153,7 @@ def wl_prefill(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, 
         for tag in ("gate_up_gemm", "down_gemm"):
             del units[tag]
         units.update(moe_units(cfg, T, L))
-    ms, dom, rf, kernels = measure(timer, step, steps, warmup, name, units, "attn_prefill",
+    ms, dom, rf, kernels, stats = measure(timer, step, steps, warmup, name, units, "attn_prefill",
                                    breakdown)
     out = {"name": name, "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms,
            "config": {"workload": name, "batch": B, "seq_len": S, "layers": L,
@@ -142,6 +169,7 @@ def wl_prefill(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, 
     total_flops = stack_prefill_flops(cfg, B, S)
     out["whole_step_mfma_frac"] = round(total_flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)
     out["algorithmic_tflop_per_step"] = round(total_flops / 1e12, 3)
+    out.update({k: round(v, 4) for k, v in stats.items()})
     if kernels:
         out["kernels"] = kernels
     del logits, caches, kvs, model, ws
@@ -223,13 +251,15 @@ def measure(timer, step, steps, warmup, workload, units, default_tag, breakdown)
     if kernels:
         tag = max(kernels, key=lambda t: kernels[t]["ms_per_step"])
     bound, amount, per_step = units[tag]
-    ms, kern = timer.run(step, steps, warmup, tag=tag, launches_per_step=per_step)
+    stats = {}
+    ms, kern = timer.run(step, steps, warmup, tag=tag, launches_per_step=per_step,
+                         per_step=stats)
     from decoder_only_forward_amd import profiling
     traffic = profiling.traffic_for(workload, tag)
     rf = (roofline_mfma if bound == "mfma" else roofline_hbm)(amount, kern["avg_ms"], traffic)
     dom = dict(kern, **({"flops_per_launch": amount} if bound == "mfma"
                         else {"bytes_per_launch": amount}))
-    return ms, dom, rf, kernels
+    return ms, dom, rf, kernels, stats
 
 
 def wl_decode(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, S=1):
@@ -290,7 +320,7 @@ def wl_decode(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, S
         "lm_head_gemm": ("hbm", 2.0 * V * H + 4.0 * T * V, 1),
         "argmax": ("hbm", 4.0 * B * V, 1),
     }
-    ms, dom, rf, kernels = measure(timer, step, steps, warmup, name, units, "attn_decode",
+    ms, dom, rf, kernels, stats = measure(timer, step, steps, warmup, name, units, "attn_decode",
                                    breakdown)
     step_bytes = decode_step_bytes(cfg, B, ctx, S)
     out = {"name": name, "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms,
@@ -299,6 +329,7 @@ def wl_decode(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, S
            "dominant_kernel": dom, "roofline": rf,
            "whole_step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
            "algorithmic_gb_per_step": round(step_bytes / 1e9, 3)}
+    out.update({k: round(v, 4) for k, v in stats.items()})
     if kernels:
         out["kernels"] = kernels
     del caches, kvs, model, ws, logits
@@ -375,17 +406,21 @@ def wl_moe(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown):
 
     H, I = cfg["hidden_size"], cfg["moe_intermediate_size"]
     units = moe_units(cfg, T, 1)
-    ms, dom, rf, kernels = measure(timer, step, steps, warmup, "moe_ffn", units,
+    ms, dom, rf, kernels, stats = measure(timer, step, steps, warmup, "moe_ffn", units,
                                    "moe_gate_up_gemm", breakdown)
     counts = (offsets[1:] - offsets[:-1]).cpu().numpy()
+    tile_rows = int(((counts + 255) // 256 * 256).sum())
     total = 2.0 * T * E * H + 2.0 * T * k * 2 * I * H + 2.0 * T * k * I * H
     out = {"name": "moe_ffn", "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms,
            "config": {"workload": "moe_ffn_2048x128e_top8", "tokens": T, "hidden": H,
                       "experts": E, "top_k": k, "expert_intermediate": I,
                       "load_max_over_mean": round(float(counts.max() / counts.mean()), 2),
-                      "load_min": int(counts.min()), "load_max": int(counts.max())},
+                      "load_min": int(counts.min()), "load_max": int(counts.max()),
+                      "experts_below_256_rows": int((counts < 256).sum()),
+                      "grouped_tile_row_use": round(float(counts.sum()) / tile_rows, 4)},
            "dominant_kernel": dom, "roofline": rf,
            "whole_step_mfma_frac": round(total / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)}
+    out.update({k: round(v, 4) for k, v in stats.items()})
     if kernels:
         out["kernels"] = kernels
     del router, gu, dn, ws
@@ -421,7 +456,7 @@ def wl_block(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, bi
     nq = cfg["num_attention_heads"]
     name = ("block_7b" if big else "block_0p6b") + ("_rope_interleaved" if rope_interleaved else "")
     units = dense_units(cfg, B, S, 1)
-    ms, dom, rf, kernels = measure(timer, step, steps, warmup, name, units, "attn_prefill",
+    ms, dom, rf, kernels, stats = measure(timer, step, steps, warmup, name, units, "attn_prefill",
                                    breakdown)
     out = {"name": name, "tokens_per_s": B * S / (ms * 1e-3), "ms_per_step": ms,
            "config": {"workload": name, "batch": B, "seq_len": S, "hidden": H,
@@ -430,6 +465,13 @@ def wl_block(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, bi
            "dominant_kernel": dom, "roofline": rf,
            "whole_step_mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
            "algorithmic_tflop_per_step": round(flops / 1e12, 3)}
+    out.update({k: round(v, 4) for k, v in stats.items()})
+    if not big:
+        # the same call with every cache level cold: a 512 MB buffer (twice the 256 MB
+        # last-level cache) is written before each call, outside the timed events
+        med, mn = timer.run_cold(step, 10 * steps, 512 << 20)
+        out["cold_cache_ms_median"] = round(med, 4)
+        out["cold_cache_ms_min"] = round(mn, 4)
     if kernels:
         out["kernels"] = kernels
     del w, k, vt, x, xo, ws
@@ -439,14 +481,26 @@ def wl_block(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, bi
 
 # ------------------------------------------------------------------------- CPU baseline
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(n_tokens):
     """The oracle (as it stands) on a bounded sample of the prefill workload: the first
-    n_tokens of sequence 0, all 28 layers, final norm and tied LM head on every row."""
+    n_tokens of sequence 0, all 28 layers, final norm and tied LM head on every row, with one
+    thread per host core this process may run on."""
     import numpy as np
     import oracle
     import synth
     from synth import recipes
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
+    threads = len(os.sched_getaffinity(0))
     oracle.set_threads(threads)
     cfg = dict(recipes.QWEN3_0P6B)
     model = recipes.model_host(recipes.MODEL_SEED_0P6B, cfg)
@@ -455,13 +509,38 @@ def cpu_baseline(n_tokens):
     oracle.stack_prefill(cfg, model, np.ascontiguousarray(ids))
     dt = time.time() - t0
     return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": oracle.get_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
             "sample": f"sequence 0, first {n_tokens} tokens of the 4x2048 prefill workload; 28 "
                       f"layers + final norm + tied LM head on all {n_tokens} rows; fp64 C++ "
                       f"oracle, {dt:.1f}s wall"}
 
 
 # ------------------------------------------------------------------------- main
+
+def device_info():
+    """Compute units and engine clock of GPU agent 0 as rocminfo reports them (run before
+    this process touches the GPU)."""
+    import subprocess
+    info = {}
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return info
+    agent = None
+    for ln in out.splitlines():
+        t = ln.strip()
+        if t.startswith("Name:") and "gfx" in t:
+            agent = t.split(":", 1)[1].strip()
+            info["agent"] = agent
+        elif agent and t.startswith("Max Clock Freq. (MHz):") and "max_clock_mhz" not in info:
+            info["max_clock_mhz"] = int(t.split(":", 1)[1].split()[0])
+        elif agent and t.startswith("Compute Unit:") and "compute_units" not in info:
+            info["compute_units"] = int(t.split(":", 1)[1].split()[0])
+        if len(info) == 3:
+            break
+    return info
+
 
 def main():
     ap = argparse.ArgumentParser()
@@ -483,6 +562,7 @@ def main():
               "each GPU would run these kernels on its own sequences", file=sys.stderr)
         sys.exit(2)
 
+    dinfo = device_info()
     import torch
     import decoder_only_forward_amd as q3
     import synth
@@ -535,6 +615,11 @@ def main():
             "scaling": "weak", "vs_baseline": None, "dtype": "f16",
             "data": "synthetic (seeded counter-based generator, random-init weights)",
             "config": m["config"], "roofline": m.get("roofline")}
+    for k in ("ms_per_step_median", "ms_per_step_min"):
+        if k in m:
+            line[k] = round(m[k], 4)
+    line["device"] = dict(dinfo, peaks={"mfma_f16_bf16_tflops": PEAK_MFMA_TFLOPS,
+                                        "hbm_gbs": PEAK_HBM_GBS})
     if "decode" in results:
         line["decode_tokens_per_s"] = round(results["decode"]["tokens_per_s"], 1)
     if args.cpu_tokens > 0 and main_wl == "prefill":

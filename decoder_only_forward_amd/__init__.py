@@ -71,7 +71,8 @@ class MoeWeights(ctypes.Structure):
 
 
 class KVLayer(ctypes.Structure):
-    _fields_ = [("k", ctypes.c_void_p), ("vt", ctypes.c_void_p), ("capacity", ctypes.c_int32)]
+    _fields_ = [("k", ctypes.c_void_p), ("vt", ctypes.c_void_p), ("capacity", ctypes.c_int32),
+                ("regions", ctypes.c_int32)]
 
 
 _lib = None
@@ -143,14 +144,26 @@ def make_layer_weights(w):
     return LayerWeights(**{k: _ptr(w.get(k)) for k in LAYER_FIELDS})
 
 
-def make_kv_layer(k, vt, capacity):
-    """qwen3_kv_layer for one layer's tiled K and V caches (see kv_cache_empty)."""
+def make_kv_layer(k, vt, capacity, regions=None):
+    """qwen3_kv_layer for one layer's tiled K and V caches (see kv_cache_empty).  For
+    tensors the region count (sequence x kv head regions of capacity x 128 elements) is
+    taken from their sizes; raw pointers must state it."""
+    counts = []
     for name, t in (("k", k), ("vt", vt)):
         n = getattr(t, "numel", None)
-        if n is not None and (n() == 0 or n() % (int(capacity) * 128)):
+        if n is None:
+            continue
+        if n() == 0 or n() % (int(capacity) * 128):
             raise ValueError(f"{name}: {n()} elements is not a whole number of "
                              f"capacity x 128 = {int(capacity) * 128} regions")
-    return KVLayer(_ptr(k), _ptr(vt), int(capacity))
+        counts.append(n() // (int(capacity) * 128))
+    if regions is None:
+        if len(counts) != 2:
+            raise ValueError("regions must be given for raw cache pointers")
+        regions = min(counts)
+    elif counts and regions > min(counts):
+        raise ValueError(f"regions={regions} exceeds what the tensors hold ({min(counts)})")
+    return KVLayer(_ptr(k), _ptr(vt), int(capacity), int(regions))
 
 
 # ---- KV-cache layout (data movement only: conversions for setting up or inspecting a cache)

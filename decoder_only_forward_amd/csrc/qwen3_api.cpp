@@ -264,8 +264,13 @@ int check_moe_cfg(const qwen3_config* c) {
   return QWEN3_OK;
 }
 
-int check_cache(const qwen3_config* c, const qwen3_kv_layer* kv, const char* what) {
+int check_cache(const qwen3_config* c, const qwen3_kv_layer* kv, const char* what, int batch) {
   if (!kv) return fail(QWEN3_EINVAL, "%s: cache is NULL", what);
+  if ((int64_t)batch * c->num_key_value_heads > kv->regions)
+    return fail(QWEN3_EINVAL,
+                "%s: regions=%d is fewer than batch x num_key_value_heads = %lld "
+                "(sequence, kv head) regions", what, kv->regions,
+                (long long)batch * c->num_key_value_heads);
   if (!aligned16(kv->k) || !aligned16(kv->vt))
     return fail(QWEN3_EINVAL, "%s: cache k/vt NULL or not 16-byte aligned", what);
   if (kv->capacity <= 0 || kv->capacity % 64)
@@ -709,7 +714,7 @@ int qwen3_block_prefill(const qwen3_config* c, const qwen3_layer_weights* w, con
   REQ_PTR(x_in, "x_in");
   REQ_PTR(x_out, "x_out");
   if (x_in == x_out) return fail(QWEN3_EINVAL, "x_in and x_out may not alias");
-  TRY(check_cache(c, cache, "cache"));
+  TRY(check_cache(c, cache, "cache", batch));
   TRY(check_range(c, cache, pos0, seq_len));
   if ((int64_t)batch * seq_len > (1 << 30)) return fail(QWEN3_EINVAL, "too many tokens");
   DenseLayout L = dense_layout(c, QWEN3_OP_BLOCK_PREFILL, batch, seq_len, cache->capacity);
@@ -735,7 +740,7 @@ int qwen3_block_decode(const qwen3_config* c, const qwen3_layer_weights* w, cons
   REQ_PTR(x_out, "x_out");
   if (!pos) return fail(QWEN3_EINVAL, "pos is NULL");
   if (x_in == x_out) return fail(QWEN3_EINVAL, "x_in and x_out may not alias");
-  TRY(check_cache(c, cache, "cache"));
+  TRY(check_cache(c, cache, "cache", batch));
   DenseLayout L = dense_layout(c, QWEN3_OP_BLOCK_DECODE, batch, 1, cache->capacity);
   if (!aligned16(workspace) || workspace_bytes < L.total)
     return fail(QWEN3_EWORKSPACE, "workspace needs %zu bytes (got %zu)", L.total,
@@ -752,7 +757,7 @@ namespace {
 
 // Model-level argument checks shared by the stack forward and generation.
 int check_stack(const qwen3_config* c, const qwen3_model_weights* w, const float* rope,
-                const qwen3_kv_layer* caches) {
+                const qwen3_kv_layer* caches, int batch) {
   TRY(check_dense_cfg(c));
   if (!w) return fail(QWEN3_EINVAL, "model weights are NULL");
   if (c->num_hidden_layers <= 0 || !w->layers)
@@ -772,7 +777,7 @@ int check_stack(const qwen3_config* c, const qwen3_model_weights* w, const float
   REQ_PTR(rope, "rope");
   if (!caches) return fail(QWEN3_EINVAL, "caches is NULL");
   for (int l = 0; l < c->num_hidden_layers; ++l) {
-    TRY(check_cache(c, &caches[l], "caches[l]"));
+    TRY(check_cache(c, &caches[l], "caches[l]", batch));
     if (caches[l].capacity != caches[0].capacity)
       return fail(QWEN3_EINVAL, "all layers' caches must share one capacity");
   }
@@ -851,10 +856,10 @@ int qwen3_stack_forward(const qwen3_config* c, const qwen3_model_weights* w, con
                         int32_t logits_mode, int32_t* next_ids, void* workspace,
                         size_t workspace_bytes, void* stream) {
   g_err.clear();
-  TRY(check_stack(c, w, rope, caches));
-  if (!ids) return fail(QWEN3_EINVAL, "ids is NULL");
   if (batch <= 0 || seq_len <= 0)
     return fail(QWEN3_EINVAL, "batch=%d seq_len=%d must be positive", batch, seq_len);
+  TRY(check_stack(c, w, rope, caches, batch));
+  if (!ids) return fail(QWEN3_EINVAL, "ids is NULL");
   if (logits_mode != QWEN3_LOGITS_NONE && logits_mode != QWEN3_LOGITS_ALL &&
       logits_mode != QWEN3_LOGITS_LAST)
     return fail(QWEN3_EINVAL, "logits_mode=%d", logits_mode);
@@ -883,12 +888,12 @@ int qwen3_generate(const qwen3_config* c, const qwen3_model_weights* w, const fl
                    const float* uniforms, int32_t* out_ids, void* workspace,
                    size_t workspace_bytes, void* stream) {
   g_err.clear();
-  TRY(check_stack(c, w, rope, caches));
-  if (!prompt_ids) return fail(QWEN3_EINVAL, "prompt_ids is NULL");
-  if (!out_ids) return fail(QWEN3_EINVAL, "out_ids is NULL");
   if (batch <= 0 || prompt_len <= 0 || n_new <= 0)
     return fail(QWEN3_EINVAL, "batch=%d prompt_len=%d n_new=%d must be positive", batch,
                 prompt_len, n_new);
+  TRY(check_stack(c, w, rope, caches, batch));
+  if (!prompt_ids) return fail(QWEN3_EINVAL, "prompt_ids is NULL");
+  if (!out_ids) return fail(QWEN3_EINVAL, "out_ids is NULL");
   const bool sampling = temperature != 0.f;
   if (sampling) {
     if (!(temperature > 0.f)) return fail(QWEN3_EINVAL, "temperature must be >= 0");

@@ -24,6 +24,18 @@
  *     qwen3_last_error() names the offending field.  A failed kernel launch returns
  *     QWEN3_EHIP.  Device faults surface at the caller's next synchronisation.
  *   - Alignment: every pointer must be 16-byte aligned.
+ *   - Precision: weights, the embedding and the KV cache are bf16 in memory; matrix-core
+ *     products accumulate in fp32; norms, softmax and RoPE run in fp32; inside
+ *     qwen3_stack_forward the residual stream is fp32, and logits are fp32.  The activations
+ *     passed between kernels (normalised rows, q/k/v projections, attention output, SwiGLU
+ *     output) are IEEE fp16: 11-bit significand (8x finer than bf16), largest finite
+ *     magnitude 65504.  A value whose magnitude rounds past 65504 becomes an infinity, and
+ *     every output computed from it is non-finite: in the block entry points that token's
+ *     output row; in the stack also later layers' rows of that sequence that attend to it.
+ *     Rows that stay inside the range are unaffected.  On the fp16 path bf16 weights are
+ *     converted to fp16 after loading: exact for magnitudes in [2^-14, 65504]; smaller ones
+ *     keep fp16-subnormal precision (absolute error at most 2^-25); larger ones are not
+ *     supported.  qwen3_moe_ffn reads its bf16 input x as bf16 matrix-core operands.
  *   - Supported shapes: head_dim == 128; hidden_size and the intermediate sizes
  *     multiples of 64; num_attention_heads a multiple of num_key_value_heads with a
  *     group size of at most 8; MoE: at most 256 experts and 8 experts per token.
@@ -136,6 +148,9 @@ typedef struct qwen3_kv_layer {
   void *k;          /* [B][nkv][capacity/32][4][32][32] bf16 (tiled, see above) */
   void *vt;         /* [B][nkv][capacity/32][hd][32] bf16 (tiled, see above) */
   int32_t capacity; /* positions per sequence, multiple of 64 */
+  int32_t regions;  /* (sequence, kv head) regions of capacity * hd elements that k and vt
+                       each hold; a call on `batch` sequences needs batch * num_key_value_heads
+                       of them (else QWEN3_EINVAL, nothing enqueued) */
 } qwen3_kv_layer;
 
 /* Operation selector for qwen3_workspace_bytes. */

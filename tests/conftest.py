@@ -19,3 +19,19 @@ def gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     return torch.device("cuda:0")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """With Q3_PARITY_LOG set, write every parity comparison of the run (test, tensor,
+    element count, max-abs and mean-relative error with their bars) to that JSON file."""
+    path = os.environ.get("Q3_PARITY_LOG")
+    if not path:
+        return
+    try:
+        import q3_testutil
+    except ImportError:
+        return
+    import json
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(q3_testutil.RECORDS, f, indent=1)

@@ -22,7 +22,22 @@ def log(msg):
     sys.stdout.flush()
 
 
-def parity(got, ref, what="", max_abs_rel=MAX_ABS_REL_RMS, mean_rel=MEAN_REL):
+# Every comparison made by parity() in this process: the test that made it, what was
+# compared, the element count and both error measures against their bars.  The session
+# hook in conftest.py writes them to the JSON file named by Q3_PARITY_LOG.
+RECORDS = []
+
+
+def _current_test():
+    import os
+    return os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+
+
+def parity(got, ref, what="", max_abs_rel=MAX_ABS_REL_RMS, mean_rel=MEAN_REL, stored_bf16=False):
+    """Compare a GPU tensor with the oracle's: max |got - ref| <= max_abs_rel * rms(ref) and
+    sum |got - ref| / sum |ref| <= mean_rel.  With stored_bf16 (the GPU output is bf16) the
+    error against the oracle rounded to bf16 is reported too: it separates the output
+    rounding from the computation's own error."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
@@ -31,11 +46,56 @@ def parity(got, ref, what="", max_abs_rel=MAX_ABS_REL_RMS, mean_rel=MEAN_REL):
     rms = float(np.sqrt(np.mean(ref * ref)))
     max_abs = float(err.max()) if err.size else 0.0
     l1 = float(err.sum() / max(np.abs(ref).sum(), 1e-300))
-    log(f"  parity {what}: max_abs={max_abs:.3e} (bar {max_abs_rel * rms:.3e}) "
-        f"mean_rel={l1:.3e} (bar {mean_rel:.1e})")
+    rec = dict(test=_current_test(), what=what, n=int(ref.size), rms=rms, max_abs=max_abs,
+               max_abs_bar=max_abs_rel * rms, mean_rel=l1, mean_rel_bar=mean_rel)
+    extra = ""
+    if stored_bf16 and err.size:
+        rb = synth.bf16_to_f32(synth.f32_to_bf16(ref.astype(np.float32))).astype(np.float64)
+        rec["max_abs_vs_bf16_ref"] = float(np.abs(got - rb).max())
+        extra = f" [vs bf16(oracle) {rec['max_abs_vs_bf16_ref']:.3e}]"
+    RECORDS.append(rec)
+    log(f"  parity {what}: max_abs={max_abs:.3e} (bar {max_abs_rel * rms:.3e}, "
+        f"{max_abs / max(max_abs_rel * rms, 1e-300):.2f} of it) mean_rel={l1:.3e} "
+        f"(bar {mean_rel:.1e}, {l1 / mean_rel:.2f}){extra}")
     assert max_abs <= max_abs_rel * rms, f"{what}: max_abs {max_abs} > {max_abs_rel} * rms {rms}"
     assert l1 <= mean_rel, f"{what}: mean relative error {l1} > {mean_rel}"
     return max_abs, l1
+
+
+class ParityAccumulator:
+    """parity() over a tensor compared in pieces: the error sums and maxima of each piece
+    are accumulated and the bar is applied once to the whole tensor (rms and L1 norm of the
+    whole oracle tensor), exactly as one parity() call on the concatenation would."""
+
+    def __init__(self, what, max_abs_rel=MAX_ABS_REL_RMS, mean_rel=MEAN_REL):
+        self.what, self.max_abs_rel, self.mean_rel = what, max_abs_rel, mean_rel
+        self.n = 0
+        self.sq = self.abs_ref = self.abs_err = self.max_err = 0.0
+
+    def add(self, got, ref):
+        got = np.asarray(got, np.float64)
+        ref = np.asarray(ref, np.float64)
+        assert got.shape == ref.shape, (self.what, got.shape, ref.shape)
+        assert np.all(np.isfinite(got)), f"{self.what}: non-finite GPU output"
+        err = np.abs(got - ref)
+        self.n += ref.size
+        self.sq += float(np.sum(ref * ref))
+        self.abs_ref += float(np.abs(ref).sum())
+        self.abs_err += float(err.sum())
+        self.max_err = max(self.max_err, float(err.max()) if err.size else 0.0)
+
+    def check(self):
+        rms = float(np.sqrt(self.sq / max(self.n, 1)))
+        l1 = self.abs_err / max(self.abs_ref, 1e-300)
+        bar = self.max_abs_rel * rms
+        RECORDS.append(dict(test=_current_test(), what=self.what, n=self.n, rms=rms,
+                            max_abs=self.max_err, max_abs_bar=bar, mean_rel=l1,
+                            mean_rel_bar=self.mean_rel))
+        log(f"  parity {self.what}: max_abs={self.max_err:.3e} (bar {bar:.3e}, "
+            f"{self.max_err / max(bar, 1e-300):.2f} of it) mean_rel={l1:.3e} "
+            f"(bar {self.mean_rel:.1e}, {l1 / self.mean_rel:.2f}) over {self.n} elements")
+        assert self.max_err <= bar, f"{self.what}: max_abs {self.max_err} > {bar}"
+        assert l1 <= self.mean_rel, f"{self.what}: mean relative error {l1} > {self.mean_rel}"
 
 
 def f64(u16):

@@ -64,7 +64,7 @@ def test_workspace_bytes_scale_with_tokens():
 def test_block_prefill_rejects_bad_arguments():
     cfg = dict(recipes.QWEN3_0P6B)
     lw = _fake_layer()
-    cache = q3.make_kv_layer(0x10000, 0x20000, 128)
+    cache = q3.make_kv_layer(0x10000, 0x20000, 128, regions=64)
     args = dict(rope=0x3000, x_in=0x4000, x_out=0x5000, batch=1, seq_len=64, pos0=0,
                 cache=cache, workspace=None)
 
@@ -85,11 +85,16 @@ def test_block_prefill_rejects_bad_arguments():
     _expect(lambda: call(x_out=0x4000), q3.QWEN3_EINVAL, "alias")
     _expect(lambda: call(seq_len=129), q3.QWEN3_ERANGE, "capacity")
     _expect(lambda: call(pos0=-1), q3.QWEN3_ERANGE, "pos0")
-    _expect(lambda: call(cache=q3.make_kv_layer(0x10000, 0x20000, 100)), q3.QWEN3_EINVAL,
+    _expect(lambda: call(cache=q3.make_kv_layer(0x10000, 0x20000, 100, regions=64)), q3.QWEN3_EINVAL,
             "capacity")
     big = dict(cfg, max_position_embeddings=100)
-    _expect(lambda: call(c=big, seq_len=101, cache=q3.make_kv_layer(0x10000, 0x20000, 128)),
+    _expect(lambda: call(c=big, seq_len=101, cache=q3.make_kv_layer(0x10000, 0x20000, 128, regions=64)),
             q3.QWEN3_ERANGE, "max_position_embeddings")
+    # a cache holding fewer (sequence, kv head) regions than batch x num_key_value_heads
+    _expect(lambda: call(cache=q3.make_kv_layer(0x10000, 0x20000, 128, regions=7)),
+            q3.QWEN3_EINVAL, "regions")
+    _expect(lambda: call(batch=2, cache=q3.make_kv_layer(0x10000, 0x20000, 128, regions=15)),
+            q3.QWEN3_EINVAL, "regions")
     _expect(lambda: call(), q3.QWEN3_EWORKSPACE, "workspace")
 
 
@@ -113,7 +118,7 @@ def test_stack_rejects_bad_arguments():
     cfg = dict(recipes.QWEN3_0P6B, num_hidden_layers=2)
     layers = [_fake_layer(), _fake_layer()]
     mw, keep = q3.make_model_weights(0x7000, 0x8000, layers)
-    caches = [q3.make_kv_layer(0x10000, 0x20000, 128)] * 2
+    caches = [q3.make_kv_layer(0x10000, 0x20000, 128, regions=64)] * 2
 
     def call(c=cfg, mode=q3.QWEN3_LOGITS_ALL, logits=0x9000, seq_len=16, cs=caches):
         q3.qwen3_stack_forward(c, mw, 0x3000, 0x6000, 1, seq_len, 0, None, cs, logits, mode,
@@ -122,8 +127,10 @@ def test_stack_rejects_bad_arguments():
     _expect(lambda: call(mode=7), q3.QWEN3_EINVAL, "logits_mode")
     _expect(lambda: call(logits=0), q3.QWEN3_EINVAL, "logits")
     _expect(lambda: call(seq_len=200), q3.QWEN3_ERANGE, "capacity")
-    _expect(lambda: call(cs=[caches[0], q3.make_kv_layer(0x10000, 0x20000, 192)]),
+    _expect(lambda: call(cs=[caches[0], q3.make_kv_layer(0x10000, 0x20000, 192, regions=64)]),
             q3.QWEN3_EINVAL, "capacity")
+    _expect(lambda: call(cs=[caches[0], q3.make_kv_layer(0x10000, 0x20000, 128, regions=4)]),
+            q3.QWEN3_EINVAL, "regions")
     _expect(lambda: call(), q3.QWEN3_EWORKSPACE, "workspace")
 
 
@@ -134,7 +141,7 @@ def test_routed_stack_multi_token_and_generation_reject_bad_arguments():
                router_weights_bf16=1)
     full = _fake_layer()
     no_router = dict(full, router=0)
-    caches = [q3.make_kv_layer(0x10000, 0x20000, 128)] * 2
+    caches = [q3.make_kv_layer(0x10000, 0x20000, 128, regions=64)] * 2
 
     def stack(c=cfg, layers=(full, full), seq_len=16, pos=None):
         mw, keep = q3.make_model_weights(0x7000, 0x8000, list(layers))

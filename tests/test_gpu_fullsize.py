@@ -1,17 +1,19 @@
-"""GPU parity at the benchmark's full sizes, in the launch configuration bench.py times.
-
-The oracle cannot recompute every output at these sizes, so each test checks outputs the
-oracle can compute one by one:
-  * prefill stack 4 x 2048: a causal model's first P rows depend only on the first P
-    tokens, so logits rows [0, P) of the full run equal an oracle prefill of the prefix;
-    layer-0 keys/values at any position depend only on that position's token;
-  * decode batch 64 at a 4096-token cache: sampled sequences, each recomputed by the
-    oracle from its own regenerated cache;
-  * MoE 8192 tokens: router logits, top-k and dispatch order for every token, expert
-    outputs for a sampled token subset;
-  * 7B block at 32768 tokens: a prefix of rows plus late rows (keys/values for every
-    position are recomputed), and sampled cache rows.
+"""GPU parity at the benchmark's full sizes, in the launch configuration bench.py times,
+over the whole compared tensors:
+  * prefill stack 4 x 2048: every logit of every position of every sequence, and every
+    layer's written K/V cache rows, against an oracle prefill of each whole sequence;
+  * decode batch 64 at a 4096-token cache: the logits of all 64 sequences, each recomputed
+    by the oracle from its own regenerated cache; greedy ids under the same-input rule;
+  * MoE 8192 tokens: router logits, top-k, weights and dispatch order of every token, and
+    y of every token against the oracle evaluated at the GPU's own expert selection (equal to
+    the oracle's own routing wherever the two selections agree);
+  * 7B block at 32768 tokens: the K/V cache rows of all 32768 positions, and x_out rows
+    covering every 128-row span of the sequence (the whole x_out in a separate opt-in test,
+    Q3_FULL_7B=1, about seven minutes of oracle time).
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 
@@ -19,7 +21,7 @@ import decoder_only_forward_amd as q3
 import oracle
 import synth
 from synth import recipes
-from q3_testutil import bf16_host, f64, log, parity
+from q3_testutil import ParityAccumulator, bf16_host, f64, log, parity
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
@@ -32,8 +34,9 @@ def _rope(cfg, dev):
 
 
 def _threads():
-    import os
-    oracle.set_threads(int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count()))
+    n = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count())
+    oracle.set_threads(n)
+    return n
 
 
 def test_stack_prefill_4x2048(gpu):
@@ -58,31 +61,31 @@ def test_stack_prefill_4x2048(gpu):
     ids_h = ids.cpu().numpy()
     np.testing.assert_array_equal(ids_h, synth.uniform_i32(2, "input.ids", (B, S), 0, V))
     last = logits[:, -1, :].cpu().numpy()
-    assert np.all(np.isfinite(last))
-    np.testing.assert_array_equal(nxt.cpu().numpy(), oracle.argmax(last))
-    del model, mw
+    np.testing.assert_array_equal(nxt.cpu().numpy(), oracle.argmax(last))  # same-input rule
+    del model, mw, ws
     host = recipes.model_host(recipes.MODEL_SEED_0P6B, cfg)
-    P = 40
-    for b in (0, 3):
-        ref = oracle.stack_prefill(cfg, host, ids_h[b, :P])
-        parity(logits[b, :P].cpu().numpy(), ref, f"logits[b={b}, rows 0..{P - 1}]")
-    # layer-0 keys / values at late positions depend only on that position's token
-    lay0 = host["layers"][0]
-    emb = f64(host["embed"])
-    k0, v0 = q3.kv_cache_to_logical(*caches[0])
-    for b, p in ((1, 2047), (2, 1500), (0, 777)):
-        x = emb[ids_h[b, p]][None]
-        z = np.zeros((8, p, 128))
-        _, nk, nv = oracle.block(cfg, lay0, x, p, z, z)
-        gk = f64(bf16_host(k0[b, :, p, :]))
-        gv = f64(bf16_host(v0[b, :, p, :]))
-        parity(gk, nk[:, 0, :], f"layer0 k[b={b}, pos={p}]")
-        parity(gv, nv[:, 0, :], f"layer0 v[b={b}, pos={p}]")
+    acc_lg = ParityAccumulator("logits[4, 2048, 151936] (all)")
+    acc_k = ParityAccumulator("cache K, 28 layers x 4 x 8 x 2048 x 128 (all)")
+    acc_v = ParityAccumulator("cache V, 28 layers x 4 x 8 x 2048 x 128 (all)")
+    for b in range(B):
+        log(f"  oracle prefill of sequence {b} (2048 tokens, 28 layers, all logits) ...")
+        ref, ko, vo = oracle.stack_prefill(cfg, host, ids_h[b], want_kv=True)
+        for r0 in range(0, S, 256):
+            acc_lg.add(logits[b, r0:r0 + 256].cpu().numpy(), ref[r0:r0 + 256])
+        del ref
+        for l in range(L):
+            k_log, v_log = q3.kv_cache_to_logical(*caches[l])
+            acc_k.add(f64(bf16_host(k_log[b])), ko[l])
+            acc_v.add(f64(bf16_host(v_log[b])), vo[l])
+        del ko, vo
+    acc_lg.check()
+    acc_k.check()
+    acc_v.check()
 
 
 def test_stack_decode_64_ctx4096(gpu):
     import torch
-    _threads()
+    nthr = _threads()
     cfg = dict(recipes.QWEN3_0P6B)
     B, ctx, cap, V, L = 64, 4096, 4160, cfg["vocab_size"], cfg["num_hidden_layers"]
     log("case full/stack_decode batch 64, cache 4096, 28 layers")
@@ -107,25 +110,32 @@ def test_stack_decode_64_ctx4096(gpu):
                            q3.QWEN3_LOGITS_LAST, nxt, ws)
     torch.cuda.synchronize()
     lg = logits.cpu().numpy()
-    assert np.all(np.isfinite(lg))
     ids_gpu = nxt.cpu().numpy()
     np.testing.assert_array_equal(ids_gpu, oracle.argmax(lg))  # same-input rule
     ids_h = ids.cpu().numpy()
-    del model, mw
+    del model, mw, caches, kvs, ws
+    torch.cuda.empty_cache()
     host = recipes.model_host(recipes.MODEL_SEED_0P6B, cfg)
-    near_ties = 0
-    for b in (0, 37, 63):
+
+    def one(b):
         ck, cv = zip(*[recipes.kv_host(3, cfg, l, b, ctx, (8, ctx)) for l in range(L)])
-        ref = oracle.stack_decode(cfg, host, ids_h[b], ctx, list(ck), list(cv))
-        _, err = parity(lg[b], ref, f"decode logits[b={b}]")
-        max_err = float(np.abs(lg[b] - ref).max())
-        top2 = np.sort(ref)[-2:]
+        return oracle.stack_decode(cfg, host, ids_h[b], ctx, list(ck), list(cv))
+
+    log(f"  oracle decode of all {B} sequences ({min(8, nthr)} at a time) ...")
+    with ThreadPoolExecutor(max_workers=min(8, nthr)) as ex:
+        ref = np.stack(list(ex.map(one, range(B))))
+    _, _ = parity(lg, ref, "decode logits[64, 151936] (all)")
+    max_err = float(np.abs(lg - ref).max())
+    near_ties = 0
+    for b in range(B):
+        top2 = np.sort(ref[b])[-2:]
         if top2[1] - top2[0] > 2 * max_err:
-            assert ids_gpu[b] == int(np.argmax(ref)), b
+            assert ids_gpu[b] == int(np.argmax(ref[b])), b
         else:
             near_ties += 1
-            assert ref[ids_gpu[b]] >= ref.max() - 2 * max_err
-    log(f"  near-tie rows: {near_ties}")
+            assert ref[b][ids_gpu[b]] >= ref[b].max() - 2 * max_err, b
+    log(f"  greedy ids equal the oracle's on {B - near_ties}/{B} rows; near-tie rows "
+        f"(top-2 gap within twice the max logit error): {near_ties}")
 
 
 def test_moe_8192_tokens_128_experts(gpu):
@@ -153,11 +163,12 @@ def test_moe_8192_tokens_128_experts(gpu):
     g = {kk: v.cpu().numpy() for kk, v in out.items()}
     gy = f64(bf16_host(y))
     rh, guh, dnh = recipes.moe_host(4, cfg)
-    xh = f64(synth.normal_bf16(4, recipes.activations_name(), (T, H)))
-    np.testing.assert_array_equal(bf16_host(x), synth.normal_bf16(4, recipes.activations_name(),
-                                                                  (T, H)))
+    xb = synth.normal_bf16(4, recipes.activations_name(), (T, H))
+    np.testing.assert_array_equal(bf16_host(x), xb)
+    xh = f64(xb)
     lg_ref = oracle.linear_rows(xh, rh)
-    parity(g["logits"], lg_ref, "router_logits[all tokens]")
+    parity(g["logits"], lg_ref, "router_logits[8192, 128] (all)")
+    # integer work on the GPU's own router logits: bit-exact
     np.testing.assert_array_equal(g["idx"], oracle.topk(g["logits"], k))
     counts, offsets, perm, inv = oracle.permute(g["idx"], E)
     np.testing.assert_array_equal(g["offsets"], offsets)
@@ -167,21 +178,31 @@ def test_moe_8192_tokens_128_experts(gpu):
                                                             g["idx"]), rtol=2e-6, atol=1e-7)
     log(f"  expert load: max {counts.max()}, min {counts.min()}, "
         f"max/mean {counts.max() / counts.mean():.2f}")
-    sample = np.random.default_rng(0).choice(T, 192, replace=False)
-    sample.sort()
-    y_ref, idx_ref, _, _ = oracle.moe_ffn(cfg, rh, guh, dnh, xh[sample])
-    agree = np.all(np.sort(g["idx"][sample], 1) == np.sort(idx_ref, 1), axis=1)
-    log(f"  routing agreement on the sample {agree.sum()}/{len(sample)}")
-    assert agree.mean() > 0.95
-    parity(gy[sample][agree], y_ref[agree], "y[sampled tokens]")
+    # the oracle's own routing; tokens it selects differently must be near-ties of the
+    # router logits (within twice the measured logit error)
+    idx_ref = oracle.topk(lg_ref.astype(np.float32), k)
+    agree = np.all(np.sort(g["idx"], 1) == np.sort(idx_ref, 1), axis=1)
+    lg_err = float(np.abs(g["logits"] - lg_ref).max())
+    kth = np.sort(lg_ref, axis=1)[:, -k]
+    chosen_min = np.take_along_axis(lg_ref, g["idx"], axis=1).min(axis=1)
+    assert np.all(chosen_min[~agree] >= kth[~agree] - 2 * lg_err)
+    log(f"  routing equals the oracle's own on {agree.sum()}/{T} tokens; the other "
+        f"{(~agree).sum()} select within a near-tie of router logits")
+    # y of every token against the oracle at the GPU's selection, weighted by the oracle's
+    # own (fp64) softmax over that selection
+    w_ref = oracle.route_weights(lg_ref, g["idx"])
+    log("  oracle experts at the GPU's selection for all 8192 tokens ...")
+    y_ref = oracle.moe_ffn_at(cfg, guh, dnh, xh, g["idx"], w_ref)
+    parity(gy, y_ref, "y[8192, 2048] (all, at the GPU's selection)", stored_bf16=True)
+    if agree.any():
+        parity(gy[agree], y_ref[agree], "y of tokens whose routing equals the oracle's",
+               stored_bf16=True)
 
 
-def test_block_7b_32768(gpu):
+def _block_7b(gpu):
     import torch
-    _threads()
     cfg = dict(recipes.QWEN_7B_BLOCK)
     B, S, H, nkv = 1, 32768, cfg["hidden_size"], cfg["num_key_value_heads"]
-    log("case full/block_7b 1 x 32768")
     w = recipes.layer_device(5, cfg, 0, gpu)
     k, vt = q3.kv_cache_empty(B, nkv, S, gpu)
     x = torch.empty((B, S, H), dtype=torch.bfloat16, device=gpu)
@@ -192,13 +213,39 @@ def test_block_7b_32768(gpu):
     q3.qwen3_block_prefill(cfg, w, _rope(cfg, gpu), x, xo, B, S, 0, q3.make_kv_layer(k, vt, S),
                            ws)
     torch.cuda.synchronize()
-    rows = np.array([0, 1, 63, 64, 127, 128, 4095, 16383, 20000, 32767])
-    got = f64(bf16_host(xo[0]))[rows]
+    got = f64(bf16_host(xo[0]))
+    k_log, v_log = q3.kv_cache_to_logical(k, vt)
+    gk, gv = f64(bf16_host(k_log[0])), f64(bf16_host(v_log[0]))
     layer = recipes.layer_host(5, cfg, 0)
     xh = f64(synth.normal_bf16(5, recipes.activations_name(), (S, H)))
+    return cfg, S, got, gk, gv, layer, xh
+
+
+def test_block_7b_32768(gpu):
+    _threads()
+    log("case full/block_7b 1 x 32768")
+    cfg, S, got, gk, gv, layer, xh = _block_7b(gpu)
+    # one row in every 128-row span (offsets varying inside the span) plus tile edges and
+    # the last row
+    span = np.arange(0, S, 128) + (np.arange(S // 128) * 37) % 128
+    edges = [0, 1, 31, 32, 63, 64, 127, 128, 191, 192, 255, 256, 4095, 16383, 32704, 32767]
+    rows = np.unique(np.concatenate([span, edges]))
+    log(f"  oracle block: K/V of all {S} positions, x_out of {len(rows)} rows ...")
     ref, nk, nv = oracle.block(cfg, layer, xh, 0, None, None, rows=rows)
-    parity(got, ref, f"x_out rows {rows.tolist()}")
-    kp = [0, 777, 32767]
-    k_log, v_log = q3.kv_cache_to_logical(k, vt)
-    parity(f64(bf16_host(k_log[0, :, kp, :])), nk[:, kp, :], "cache k rows")
-    parity(f64(bf16_host(v_log[0, :, kp, :])), nv[:, kp, :], "cache v rows")
+    parity(got[rows], ref, f"x_out, {len(rows)} rows covering every 128-row span",
+           stored_bf16=True)
+    parity(gk, nk, "cache K [4, 32768, 128] (all)", stored_bf16=True)
+    parity(gv, nv, "cache V [4, 32768, 128] (all)", stored_bf16=True)
+
+
+@pytest.mark.skipif(os.environ.get("Q3_FULL_7B") != "1",
+                    reason="whole 7B x_out: about seven minutes of oracle time; Q3_FULL_7B=1")
+@pytest.mark.timeout(1800)
+def test_block_7b_32768_full_x_out(gpu):
+    _threads()
+    log("case full/block_7b 1 x 32768, every x_out row")
+    cfg, S, got, gk, gv, layer, xh = _block_7b(gpu)
+    ref, nk, nv = oracle.block(cfg, layer, xh, 0, None, None)
+    parity(got, ref, "x_out [32768, 3584] (all)", stored_bf16=True)
+    parity(gk, nk, "cache K [4, 32768, 128] (all)", stored_bf16=True)
+    parity(gv, nv, "cache V [4, 32768, 128] (all)", stored_bf16=True)

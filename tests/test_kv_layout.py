@@ -53,3 +53,14 @@ def test_make_kv_layer_checks_region_sizes():
     q3.make_kv_layer(k, vt, 64)  # whole regions: accepted
     with pytest.raises(ValueError):
         q3.make_kv_layer(k, vt, 192)  # 2 x 64 positions is not a multiple of 192
+
+
+def test_make_kv_layer_records_regions():
+    import pytest
+    k, vt = q3.kv_cache_empty(3, 2, 64, "cpu")
+    assert q3.make_kv_layer(k, vt, 64).regions == 6
+    assert q3.make_kv_layer(k, vt, 64, regions=4).regions == 4
+    with pytest.raises(ValueError):
+        q3.make_kv_layer(k, vt, 64, regions=7)  # more than the tensors hold
+    with pytest.raises(ValueError):
+        q3.make_kv_layer(0x10000, 0x20000, 64)  # raw pointers must state it
