@@ -67,6 +67,58 @@ DEV f32x4_t mfma16_f16(f16x8_t a, f16x8_t b, f32x4_t c) {
 // the live state (Q^T 48, O^T 96, S^T 24, P^T 12 registers) small enough for two waves per
 // SIMD, so one wave's softmax overlaps the other's matrix work.  (32 rows per wave at three
 // waves per SIMD measured slower: less reuse of each K/V fragment, more per-wave overhead.)
+// Work placement of the prefill blocks.  A work item is (row level, sequence, q head);
+// heavy (late) row levels go first.  Workgroups reach the eight XCDs round-robin (block
+// id mod 8), and each XCD has its own L2, so the items are arranged for each XCD to keep
+// whole (sequence, kv head) groups: the q heads of a group read the same K/V, which then
+// stays in one L2.  With G = B * nkv groups:
+//   G a multiple of 8: XCD x owns groups x, x + 8, ...; its i-th block takes level
+//     i / n_x, then group and head in order (n_x = G / 8 * g items per level);
+//   G dividing 8: R = 8 / G XCDs share one group; XCD x serves group x / R and takes the
+//     group's items n = i R + x % R (n = level * g + head), so the levels stay balanced;
+//   otherwise: block id = level * (B * nq) + b * nq + h, every XCD receiving every eighth
+//     item of each level.
+// The block-id -> item map is a bijection onto the items plus idle ids (mode two pads
+// the grid to 8 P blocks), so results do not depend on the placement; only locality does.
+DEV bool prefill_item(int wid, int nmb, int B, int nq, int nkv, int& mb, int& b, int& h) {
+  const int g = nq / nkv, G = B * nkv;
+  int level, grpi, head;
+  if (G % 8 == 0) {
+    const int x = wid & 7, i = wid >> 3, nx = (G / 8) * g;
+    level = i / nx;
+    const int j = i % nx;
+    grpi = x + 8 * (j / g);
+    head = j % g;
+  } else if (8 % G == 0) {
+    const int R = 8 / G, x = wid & 7, i = wid >> 3;
+    const int n = i * R + x % R;
+    if (n >= nmb * g) return false;
+    grpi = x / R;
+    level = n / g;
+    head = n % g;
+  } else {
+    level = wid / (B * nq);
+    const int rem = wid % (B * nq);
+    grpi = (rem / nq) * nkv + (rem % nq) / g;
+    head = rem % g;
+  }
+  if (level >= nmb) return false;
+  mb = nmb - 1 - level;
+  b = grpi / nkv;
+  h = (grpi % nkv) * g + head;
+  return true;
+}
+
+int prefill_blocks(int nmb, int B, int nq, int nkv) {
+  const int g = nq / nkv, G = B * nkv;
+  if (G % 8 == 0) return nmb * B * nq;
+  if (8 % G == 0) {
+    const int R = 8 / G;
+    return 8 * ((nmb * g + R - 1) / R);
+  }
+  return nmb * B * nq;
+}
+
 template <bool HAS_PAST>
 __global__ void __launch_bounds__(PF_THREADS, HAS_PAST ? 1 : 2) attn_prefill_kernel(AttnPrefillArgs a) {
   __shared__ __attribute__((aligned(16))) f16_t sK[2][BKV * HD];
@@ -75,15 +127,8 @@ __global__ void __launch_bounds__(PF_THREADS, HAS_PAST ? 1 : 2) attn_prefill_ker
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, grp = lane >> 4;
   const int nmb = (a.S + BQ - 1) / BQ;
-  // Heavy (late) row blocks first.  Workgroups reach the eight XCDs round-robin, so with
-  // this order every XCD receives every eighth block of each causal row level: the XCDs
-  // get equal work, and when B * nq is a multiple of 8 each keeps the same heads (and
-  // their K/V) for all levels.  (Contiguous block ranges per XCD would hand one XCD all
-  // the longest rows.)
-  const int wid = blockIdx.x;
-  const int mb = nmb - 1 - wid / (a.B * a.nq);
-  const int rem = wid % (a.B * a.nq);
-  const int b = rem / a.nq, h = rem % a.nq;
+  int mb, b, h;
+  if (!prefill_item(blockIdx.x, nmb, a.B, a.nq, a.nkv, mb, b, h)) return;
   const int g = a.nq / a.nkv, kvh = h / g;
 
   const int row0 = mb * BQ;                          // first query row (token index)
@@ -665,12 +710,11 @@ __global__ void __launch_bounds__(128) attn_decode_combine_kernel(AttnDecodeArgs
 hipError_t attn_prefill(const AttnPrefillArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.S <= 0) return hipSuccess;
   const int nmb = (a.S + BQ - 1) / BQ;
+  const int blocks = prefill_blocks(nmb, a.B, a.nq, a.nkv);
   if (a.pos0 > 0)
-    hipLaunchKernelGGL(attn_prefill_kernel<true>, dim3(nmb * a.B * a.nq), dim3(PF_THREADS), 0, s,
-                       a);
+    hipLaunchKernelGGL(attn_prefill_kernel<true>, dim3(blocks), dim3(PF_THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3(nmb * a.B * a.nq), dim3(PF_THREADS), 0, s,
-                       a);
+    hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3(blocks), dim3(PF_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
