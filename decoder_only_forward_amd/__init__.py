@@ -33,9 +33,12 @@ QWEN3_LOGITS_ALL = 1
 QWEN3_LOGITS_LAST = 2
 
 EXPORTS = ("qwen3_workspace_bytes", "qwen3_rope_table_init", "qwen3_block_prefill",
-           "qwen3_block_decode", "qwen3_moe_ffn", "qwen3_stack_forward", "qwen3_generate",
-           "qwen3_status_string", "qwen3_last_error", "qwen3_profile_begin",
-           "qwen3_profile_end")
+           "qwen3_block_decode", "qwen3_block_decode_static", "qwen3_moe_ffn",
+           "qwen3_stack_forward", "qwen3_generate", "qwen3_status_string", "qwen3_last_error",
+           "qwen3_profile_begin", "qwen3_profile_end")
+
+# qwen3_block_decode_static's device scratch per GPU (QWEN3_STATIC_SCRATCH_BYTES)
+QWEN3_STATIC_SCRATCH_BYTES = 16 << 20
 
 
 class Config(ctypes.Structure):
@@ -94,6 +97,8 @@ def lib():
         L.qwen3_block_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
         L.qwen3_block_decode.restype = ctypes.c_int
         L.qwen3_block_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+        L.qwen3_block_decode_static.restype = ctypes.c_int
+        L.qwen3_block_decode_static.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp]
         L.qwen3_moe_ffn.restype = ctypes.c_int
         L.qwen3_moe_ffn.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.qwen3_stack_forward.restype = ctypes.c_int
@@ -292,6 +297,15 @@ def qwen3_block_decode(cfg, w, rope, x_in, x_out, batch, pos, cache, workspace, 
     _check(lib().qwen3_block_decode(ctypes.byref(_cfg(cfg)), ctypes.byref(lw), _ptr(rope),
                                     _ptr(x_in), _ptr(x_out), batch, _ptr(pos), _byref(cache),
                                     wp, wb, _stream(stream)))
+
+
+def qwen3_block_decode_static(cfg, w, rope, x_in, x_out, batch, pos, cache, stream=None):
+    """qwen3_block_decode with the library's static device scratch instead of a workspace
+    (no allocation; calls that may overlap on one GPU must be serialised by the caller)."""
+    lw = w if isinstance(w, LayerWeights) else make_layer_weights(w)
+    _check(lib().qwen3_block_decode_static(ctypes.byref(_cfg(cfg)), ctypes.byref(lw), _ptr(rope),
+                                           _ptr(x_in), _ptr(x_out), batch, _ptr(pos),
+                                           _byref(cache), _stream(stream)))
 
 
 def qwen3_moe_ffn(cfg, w, x, y, n_tokens, router_logits=None, topk_idx=None, topk_w=None,

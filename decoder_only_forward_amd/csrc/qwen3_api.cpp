@@ -4,6 +4,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "../../include/qwen3.h"
@@ -727,11 +728,14 @@ int qwen3_block_prefill(const qwen3_config* c, const qwen3_layer_weights* w, con
   return run_layer(c, w, rope, cache, io, (char*)workspace, L, (hipStream_t)stream);
 }
 
-int qwen3_block_decode(const qwen3_config* c, const qwen3_layer_weights* w, const float* rope,
-                       const void* x_in, void* x_out, int32_t batch, const int32_t* pos,
-                       const qwen3_kv_layer* cache, void* workspace, size_t workspace_bytes,
-                       void* stream) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the block decode entry points; *L receives the workspace layout.
+int check_block_decode(const qwen3_config* c, const qwen3_layer_weights* w, const float* rope,
+                       const void* x_in, const void* x_out, int32_t batch, const int32_t* pos,
+                       const qwen3_kv_layer* cache, DenseLayout* L) {
   TRY(check_dense_cfg(c));
   TRY(check_layer(c, w));
   if (batch <= 0) return fail(QWEN3_EINVAL, "batch=%d must be positive", batch);
@@ -741,14 +745,79 @@ int qwen3_block_decode(const qwen3_config* c, const qwen3_layer_weights* w, cons
   if (!pos) return fail(QWEN3_EINVAL, "pos is NULL");
   if (x_in == x_out) return fail(QWEN3_EINVAL, "x_in and x_out may not alias");
   TRY(check_cache(c, cache, "cache", batch));
-  DenseLayout L = dense_layout(c, QWEN3_OP_BLOCK_DECODE, batch, 1, cache->capacity);
-  if (!aligned16(workspace) || workspace_bytes < L.total)
-    return fail(QWEN3_EWORKSPACE, "workspace needs %zu bytes (got %zu)", L.total,
-                workspace_bytes);
+  *L = dense_layout(c, QWEN3_OP_BLOCK_DECODE, batch, 1, cache->capacity);
+  return QWEN3_OK;
+}
+
+int run_block_decode(const qwen3_config* c, const qwen3_layer_weights* w, const float* rope,
+                     const void* x_in, void* x_out, int32_t batch, const int32_t* pos,
+                     const qwen3_kv_layer* cache, char* ws, const DenseLayout& L,
+                     hipStream_t s) {
   LayerIO io{};
   io.T = batch; io.B = batch; io.S = 1; io.pos = pos;
   io.x_bf16 = (const bf16_t*)x_in; io.x_out = (bf16_t*)x_out;
-  return run_layer(c, w, rope, cache, io, (char*)workspace, L, (hipStream_t)stream);
+  return run_layer(c, w, rope, cache, io, ws, L, s);
+}
+
+// Scratch of the allocation-free decode entry point: one copy per GPU, resident while the
+// library is loaded.  Host code never passes `scratch` itself to a kernel (on the host it
+// is only a stand-in for the symbol); it uses the device address that hipGetSymbolAddress
+// returns, looked up once per device on the first call there.
+static __device__ __align__(256) char scratch[QWEN3_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(char** out) {
+  int dev = -1;
+  CHECK_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(QWEN3_EUNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    CHECK_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(QWEN3_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = (char*)g_scratch_ptr[dev];
+  return QWEN3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qwen3_block_decode(const qwen3_config* c, const qwen3_layer_weights* w, const float* rope,
+                       const void* x_in, void* x_out, int32_t batch, const int32_t* pos,
+                       const qwen3_kv_layer* cache, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  g_err.clear();
+  DenseLayout L;
+  TRY(check_block_decode(c, w, rope, x_in, x_out, batch, pos, cache, &L));
+  if (!aligned16(workspace) || workspace_bytes < L.total)
+    return fail(QWEN3_EWORKSPACE, "workspace needs %zu bytes (got %zu)", L.total,
+                workspace_bytes);
+  return run_block_decode(c, w, rope, x_in, x_out, batch, pos, cache, (char*)workspace, L,
+                          (hipStream_t)stream);
+}
+
+int qwen3_block_decode_static(const qwen3_config* c, const qwen3_layer_weights* w,
+                              const float* rope, const void* x_in, void* x_out, int32_t batch,
+                              const int32_t* pos, const qwen3_kv_layer* cache, void* stream) {
+  g_err.clear();
+  DenseLayout L;
+  TRY(check_block_decode(c, w, rope, x_in, x_out, batch, pos, cache, &L));
+  if (L.total > (size_t)QWEN3_STATIC_SCRATCH_BYTES)
+    return fail(QWEN3_EWORKSPACE,
+                "this call needs %zu bytes of scratch; the static scratch holds %zu (use "
+                "qwen3_block_decode with a workspace)", L.total,
+                (size_t)QWEN3_STATIC_SCRATCH_BYTES);
+  char* ws = nullptr;
+  TRY(static_scratch(&ws));
+  return run_block_decode(c, w, rope, x_in, x_out, batch, pos, cache, ws, L,
+                          (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -207,6 +207,22 @@ int qwen3_block_decode(const qwen3_config *cfg, const qwen3_layer_weights *w,
                        const int32_t *pos, const qwen3_kv_layer *cache, void *workspace,
                        size_t workspace_bytes, void *stream);
 
+/* Allocation-free block decode, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * operation, arguments and results as qwen3_block_decode, but its scratch memory is the
+ * library's static device buffer of QWEN3_STATIC_SCRATCH_BYTES per GPU instead of a caller
+ * workspace.  It calls no allocator.  A call whose scratch need (qwen3_workspace_bytes
+ * with QWEN3_OP_BLOCK_DECODE for this batch and cache capacity) exceeds the buffer returns
+ * QWEN3_EWORKSPACE with nothing enqueued.  The buffer is looked up on the current device
+ * on its first call there.  Every call on one GPU shares that GPU's buffer: calls that
+ * may overlap in time on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  The kernels write every scratch byte before reading it
+ * within a call, so nothing needs clearing between calls. */
+#define QWEN3_STATIC_SCRATCH_BYTES (16u << 20)
+int qwen3_block_decode_static(const qwen3_config *cfg, const qwen3_layer_weights *w,
+                              const float *rope, const void *x_in, void *x_out, int32_t batch,
+                              const int32_t *pos, const qwen3_kv_layer *cache, void *stream);
+
 /* Routed MoE FFN sub-layer on already-normalised inputs ([P3] "MoE"):
  *   r = x Wr^T (fp32); the k experts with the largest r are chosen (descending, ties to
  *   the lower index); w = their softmax probabilities, renormalised over the k when

@@ -172,3 +172,27 @@ def test_routed_stack_multi_token_and_generation_reject_bad_arguments():
     _expect(lambda: gen(top_p=1.5), q3.QWEN3_EINVAL, "top_p")
     _expect(lambda: gen(uniforms=None), q3.QWEN3_EINVAL, "uniforms")
     _expect(lambda: gen(n_new=200), q3.QWEN3_ERANGE, "capacity")
+
+
+def test_block_decode_static_rejects_calls_beyond_its_scratch():
+    # the allocation-free entry validates like qwen3_block_decode and refuses a call whose
+    # scratch need exceeds the static buffer before touching the device
+    with open(os.path.join(ROOT, "include", "qwen3.h")) as f:
+        m = re.search(r"#define QWEN3_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == q3.QWEN3_STATIC_SCRATCH_BYTES
+    cfg = dict(recipes.QWEN3_0P6B)
+    lw = _fake_layer()
+
+    def call(batch, cache):
+        q3.qwen3_block_decode_static(cfg, lw, 0x3000, 0x4000, 0x5000, batch, 0x6000, cache,
+                                     stream=0)
+
+    big = 4096
+    assert q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_BLOCK_DECODE, big) > \
+        q3.QWEN3_STATIC_SCRATCH_BYTES
+    _expect(lambda: call(big, q3.make_kv_layer(0x10000, 0x20000, 128, regions=big * 8)),
+            q3.QWEN3_EWORKSPACE, "static scratch")
+    _expect(lambda: call(2, q3.make_kv_layer(0x10000, 0x20000, 128, regions=8)),
+            q3.QWEN3_EINVAL, "regions")
+    _expect(lambda: call(1, q3.make_kv_layer(0x10000, 0x20000, 100, regions=8)),
+            q3.QWEN3_EINVAL, "capacity")
