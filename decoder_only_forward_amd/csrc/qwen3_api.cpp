@@ -181,7 +181,7 @@ DenseLayout dense_layout(const qwen3_config* c, int op, int B, int S, int cap_hi
 // Generation workspace: per-step buffers, then one region shared by the prefill and the
 // decode steps of the stack.
 struct GenLayout {
-  size_t logits, ids, pos, stack, total;
+  size_t logits, ids, pos, samp, stack, total;
   DenseLayout prefill, decode;
 };
 
@@ -191,6 +191,7 @@ GenLayout gen_layout(const qwen3_config* c, int B, int S, int cap) {
   G.logits = b.take((size_t)B * c->vocab_size * 4);
   G.ids = b.take((size_t)B * 4);
   G.pos = b.take((size_t)B * 4);
+  G.samp = b.take(sample_ws_bytes(B));
   G.stack = b.off;
   G.prefill = dense_layout(c, QWEN3_OP_STACK_PREFILL, B, S, cap);
   G.decode = dense_layout(c, QWEN3_OP_STACK_DECODE, B, 1, cap);
@@ -968,6 +969,8 @@ int qwen3_generate(const qwen3_config* c, const qwen3_model_weights* w, const fl
     if (!(temperature > 0.f)) return fail(QWEN3_EINVAL, "temperature must be >= 0");
     if (!(top_p > 0.f && top_p <= 1.f)) return fail(QWEN3_EINVAL, "top_p must be in (0, 1]");
     if (!uniforms) return fail(QWEN3_EINVAL, "uniforms is NULL (needed when temperature > 0)");
+    if (c->vocab_size > (1 << 18))
+      return fail(QWEN3_EINVAL, "sampling supports vocab_size <= 262144 (got %d)", c->vocab_size);
   }
   // the prompt and every generated token but the last take a cache position
   for (int l = 0; l < c->num_hidden_layers; ++l)
@@ -994,7 +997,7 @@ int qwen3_generate(const qwen3_config* c, const qwen3_model_weights* w, const fl
     if (sampling) {
       ProfScope ps("sample", s);
       CHECK_HIP(sample_rows(logits, V, batch, V, temperature, top_p,
-                            uniforms + (int64_t)i * batch, ids, s));
+                            uniforms + (int64_t)i * batch, ids, ws + G.samp, s));
     }
     CHECK_HIP(gen_feed(ids, out_ids, n_new, i, pos, prompt_len + i, batch, s));
   }

@@ -271,12 +271,14 @@ int qwen3_stack_forward(const qwen3_config *cfg, const qwen3_model_weights *w,
  *     total; r = u * kept mass; the token is the smallest index v whose running kept mass
  *     over tokens <= v exceeds r.  uniforms: device float [n_new][batch] in [0, 1), the
  *     caller's random numbers (u for step i, sequence b at uniforms[i * batch + b]).
+ *     e_v is computed in fp32 and the masses are summed exactly in fixed point (units of
+ *     2^-44, e_v <= 1), so the draw does not depend on the order of any sum.
  *   caches: HOST array [L] of per-layer caches (one capacity, >= prompt_len + n_new - 1,
  *     <= max_position_embeddings); positions 0 .. prompt_len + n_new - 2 are written.
  *   out_ids: device int32 [batch][n_new].
  *   workspace: qwen3_workspace_bytes(cfg, QWEN3_OP_GENERATE, batch, prompt_len) bytes.
- * Errors as for qwen3_stack_forward; EINVAL for temperature < 0, top_p outside (0, 1] or
- * missing uniforms when sampling. */
+ * Errors as for qwen3_stack_forward; EINVAL for temperature < 0, top_p outside (0, 1],
+ * missing uniforms, or vocab_size above 262144 when sampling. */
 int qwen3_generate(const qwen3_config *cfg, const qwen3_model_weights *w, const float *rope,
                    const int32_t *prompt_ids, int32_t batch, int32_t prompt_len, int32_t n_new,
                    const qwen3_kv_layer *caches, float temperature, float top_p,

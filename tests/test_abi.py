@@ -163,15 +163,16 @@ def test_routed_stack_multi_token_and_generation_reject_bad_arguments():
     _expect(lambda: stack(seq_len=200, pos=0x4000), q3.QWEN3_ERANGE, "capacity")
     _expect(lambda: stack(seq_len=8, pos=0x4000), q3.QWEN3_EWORKSPACE, "workspace")
 
-    def gen(temperature=0.5, top_p=0.9, uniforms=0x5000, n_new=4):
+    def gen(temperature=0.5, top_p=0.9, uniforms=0x5000, n_new=4, c=cfg):
         mw, keep = q3.make_model_weights(0x7000, 0x8000, [full, full])
-        q3.qwen3_generate(cfg, mw, 0x3000, 0x6000, 1, 16, n_new, caches, 0x9000, None,
+        q3.qwen3_generate(c, mw, 0x3000, 0x6000, 1, 16, n_new, caches, 0x9000, None,
                           temperature=temperature, top_p=top_p, uniforms=uniforms, stream=0)
 
     _expect(lambda: gen(temperature=-1.0), q3.QWEN3_EINVAL, "temperature")
     _expect(lambda: gen(top_p=1.5), q3.QWEN3_EINVAL, "top_p")
     _expect(lambda: gen(uniforms=None), q3.QWEN3_EINVAL, "uniforms")
     _expect(lambda: gen(n_new=200), q3.QWEN3_ERANGE, "capacity")
+    _expect(lambda: gen(c=dict(cfg, vocab_size=300000)), q3.QWEN3_EINVAL, "vocab_size")
 
 
 def test_block_decode_static_rejects_calls_beyond_its_scratch():

@@ -77,7 +77,7 @@ def test_generate_greedy_matches_oracle(gpu):
 
 def _check_draw(tok, logits, temperature, top_p, u, where):
     """tok must be the oracle's draw on the same logits, or sit within a rounding distance of
-    the drawn boundary (the kernel sums in fp32)."""
+    the drawn boundary (the kernel computes e_v in fp32 and sums them in 2^-44 fixed point)."""
     want, det = oracle.sample(logits, temperature, top_p, [u])
     want = int(want[0])
     if tok == want:
@@ -94,21 +94,13 @@ def _check_draw(tok, logits, temperature, top_p, u, where):
     return False
 
 
-def test_generate_sampling_matches_oracle_sampler(gpu):
-    # The device loop is replayed step by step through qwen3_stack_forward (same kernels,
-    # same order, so the same logits); every draw must be the oracle's draw on those logits
-    # with the same uniform.  The first tokens are also checked against the oracle's own
-    # logits through the greedy path's parity, so the two checks together cover the loop.
+def _replay_draws(gpu, cfg, mw, rope, ids, got, temperature, top_p, uni, cap):
+    """Replays the device loop step by step through qwen3_stack_forward (same kernels, same
+    order, so the same logits) and checks every draw against the oracle's sampler on those
+    logits with the same uniform.  Returns the number of draws equal to the oracle's."""
     import torch
-    cfg = small_cfg(L=2, V=600)
-    B, S, n_new, cap = 3, 19, 6, 64
-    T, top_p = 0.8, 0.9
-    log(f"case generate sampled: B={B} prompt={S} n_new={n_new} T={T} top_p={top_p}")
-    model, mw, keep, rope, ids = _setup(gpu, cfg, 32, B, S, cap)
-    rng = np.random.default_rng(7)
-    uni = rng.random((n_new, B)).astype(np.float32)  # the values the device receives
-    got = _generate(gpu, cfg, mw, rope, ids, n_new, cap, T, top_p, uni)
-
+    B, S = ids.shape
+    n_new = got.shape[1]
     bufs, kvs = _caches(cfg, B, cap, gpu)
     V = cfg["vocab_size"]
     logits = torch.empty((B, V), dtype=torch.float32, device=gpu)
@@ -123,12 +115,44 @@ def test_generate_sampling_matches_oracle_sampler(gpu):
         torch.cuda.synchronize()
         lg = logits.cpu().numpy().astype(np.float64)
         for b in range(B):
-            exact += _check_draw(int(got[b, i]), lg[b], T, top_p, uni[i, b], (i, b))
+            exact += _check_draw(int(got[b, i]), lg[b], temperature, top_p, uni[i, b], (i, b))
         if i + 1 < n_new:
             cur = torch.from_numpy(np.ascontiguousarray(got[:, i])).to(gpu)
             pos = torch.full((B,), S + i, dtype=torch.int32, device=gpu)
             q3.qwen3_stack_forward(cfg, mw, rope, cur, B, 1, 0, pos, kvs, logits,
                                    q3.QWEN3_LOGITS_LAST, None, ws_d)
+    return exact
+
+
+def test_generate_sampling_matches_oracle_sampler(gpu):
+    # Every draw must be the oracle's draw on the GPU's own logits with the same uniform.
+    # The first tokens are also checked against the oracle's own logits through the greedy
+    # path's parity, so the two checks together cover the loop.
+    cfg = small_cfg(L=2, V=600)
+    B, S, n_new, cap = 3, 19, 6, 64
+    T, top_p = 0.8, 0.9
+    log(f"case generate sampled: B={B} prompt={S} n_new={n_new} T={T} top_p={top_p}")
+    model, mw, keep, rope, ids = _setup(gpu, cfg, 32, B, S, cap)
+    rng = np.random.default_rng(7)
+    uni = rng.random((n_new, B)).astype(np.float32)  # the values the device receives
+    got = _generate(gpu, cfg, mw, rope, ids, n_new, cap, T, top_p, uni)
+    exact = _replay_draws(gpu, cfg, mw, rope, ids, got, T, top_p, uni, cap)
+    assert exact >= B * n_new - 1, exact
+
+
+@pytest.mark.parametrize("T,top_p", [(0.7, 0.9), (1.0, 1.0), (1.3, 0.5), (0.05, 0.95)])
+def test_generate_sampling_full_vocabulary(gpu, T, top_p):
+    # The sampler at the full 151,936-token vocabulary: every chunk of every row holds
+    # thousands of tokens, and the nucleus cut falls deep inside the radix histograms.
+    cfg = small_cfg(L=1, V=151936)
+    B, S, n_new, cap = 16, 8, 3, 64
+    log(f"case generate sampled full vocabulary: B={B} prompt={S} n_new={n_new} T={T} "
+        f"top_p={top_p}")
+    model, mw, keep, rope, ids = _setup(gpu, cfg, 34, B, S, cap)
+    rng = np.random.default_rng(9)
+    uni = rng.random((n_new, B)).astype(np.float32)
+    got = _generate(gpu, cfg, mw, rope, ids, n_new, cap, T, top_p, uni)
+    exact = _replay_draws(gpu, cfg, mw, rope, ids, got, T, top_p, uni, cap)
     assert exact >= B * n_new - 1, exact
 
 
