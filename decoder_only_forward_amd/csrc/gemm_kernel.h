@@ -446,11 +446,21 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  // Grouped tiles are often partly filled (an expert's last rows): copies of A rows wholly
+  // past rows_valid and the MFMAs of 32-row groups wholly past it are skipped (those LDS rows
+  // then hold stale data, which only reaches accumulator rows the epilogue never stores).
+  // The waits below count copies per stage, which skipped copies would throw off unless
+  // every wait is for all copies (two stages).
+  static_assert(!GROUPED || T::STAGES == 2, "grouped tiles skip copies: two stages only");
+  auto a_live = [&](int i) { return !GROUPED || RPC * (wave * A_INSTS + i) < rows_valid; };
+  const int tm_live =
+      GROUPED ? max(0, min(T::TM, (rows_valid - wm * T::WM + 31) / 32)) : T::TM;
   auto load_stage = [&](int kt, int st) {
     const int koff = kt * T::BK;
 #pragma unroll
     for (int i = 0; i < A_INSTS; ++i)
-      lds_dma16(aptr[i] + koff, sA + st * (T::BM * T::BK) + (wave * A_INSTS + i) * 512);
+      if (a_live(i))
+        lds_dma16(aptr[i] + koff, sA + st * (T::BM * T::BK) + (wave * A_INSTS + i) * 512);
 #pragma unroll
     for (int i = 0; i < B_INSTS; ++i)
       lds_dma16(bptr[i] + koff, sB + st * (T::BN * T::BK) + (wave * B_INSTS + i) * 512);
@@ -485,6 +495,7 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
     for (int i = 0; i < T::TM; ++i)
 #pragma unroll
       for (int j = 0; j < T::TN; ++j) {
+        if (GROUPED && i >= tm_live) continue;
         if (F16)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(fa[slot][i]),
                                                              as_f16x8(fb[slot][j]), acc[i][j],
