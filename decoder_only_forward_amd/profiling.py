@@ -20,6 +20,7 @@ Usage (after the rocprofv3 runs):
   python -m decoder_only_forward_amd.profiling traffic <fetch_dir> <write_dir> <workload>
          <copy_gib> <command_fetch> <command_write> <traffic.json>
   python -m decoder_only_forward_amd.profiling mfma <out.md> <command> <workload>=<dir> ...
+  python -m decoder_only_forward_amd.profiling counters <out.md> <command> <workload>=<dir> ...
 """
 import csv
 import glob
@@ -42,6 +43,10 @@ KERNELS = {
     "lm_head_gemm": ("gemm_kernel<", _GEMM),
     "moe_gate_up_gemm": ("gemm_kernel<", _GEMM),
     "moe_down_gemm": ("gemm_kernel<", _GEMM),
+    # decode-size products (<= 256 rows): one 16-column block per output slice
+    "decode_qkv_gemm": ("decode_gemm_kernel<1, 6, false>", _GEMM),
+    "decode_gate_up_gemm": ("decode_gemm_kernel<2, 5, false>", _GEMM),
+    "decode_res_gemm": ("decode_gemm_kernel<0, 2, true>", _GEMM),
 }
 
 # Template signatures that single out one GEMM use (fp16 A, B mode, epilogue, grouped).
@@ -256,6 +261,50 @@ def mfma_markdown(runs, command):
     return "\n".join(out)
 
 
+def counter_rows(rocprof_dir):
+    """Per kernel class: dispatches, mean duration and the mean of every collected counter
+    per dispatch (counters summed over the chip's instances)."""
+    per, meta = {}, {}
+    for r in _csv_rows(os.path.join(rocprof_dir, "**", "*counter_collection.csv")):
+        d = per.setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        meta[r["Dispatch_Id"]] = (r["Kernel_Name"],
+                                  int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    groups = {}
+    for k, c in per.items():
+        name, dur = meta[k]
+        g = groups.setdefault(short_name(name), {"n": 0, "dur": 0.0, "c": {}})
+        g["n"] += 1
+        g["dur"] += dur
+        for cn, v in c.items():
+            g["c"][cn] = g["c"].get(cn, 0.0) + v
+    out = [{"kernel": name, "dispatches": g["n"], "avg_us": g["dur"] / g["n"] / 1e3,
+            "total_us": g["dur"] / 1e3,
+            "counters": {cn: v / g["n"] for cn, v in g["c"].items()}}
+           for name, g in groups.items()]
+    out.sort(key=lambda e: -e["total_us"])
+    return out
+
+
+def counters_markdown(runs, command, top=12):
+    out = ["# Memory-hierarchy counters per kernel (rocprofv3)", "",
+           "Command (run from the repository root, once per workload):", "", "```",
+           command, "```", "",
+           "Each counter is the mean per dispatch over the kernel class's dispatches (summed "
+           "over the chip's counter instances).  Counter runs serialise dispatches, so "
+           "durations are a little longer than in the timed benchmark.", ""]
+    for workload, rows in runs:
+        names = sorted({cn for e in rows for cn in e["counters"]})
+        out += [f"## {workload}", "",
+                "| kernel | dispatches | avg us | " + " | ".join(names) + " |",
+                "|---|---:|---:|" + "---:|" * len(names)]
+        for e in rows[:top]:
+            vals = " | ".join(f"{e['counters'].get(cn, 0.0):.4g}" for cn in names)
+            out.append(f"| `{e['kernel']}` | {e['dispatches']} | {e['avg_us']:.1f} | {vals} |")
+        out.append("")
+    return "\n".join(out)
+
+
 def main(argv):
     if argv[0] == "stats":
         d, workload, cmd, out = argv[1:5]
@@ -273,6 +322,11 @@ def main(argv):
             json.dump(table, fh, indent=1, sort_keys=True)
         with open(os.path.splitext(out)[0] + ".md", "w") as fh:
             fh.write(traffic_markdown(table))
+    elif argv[0] == "counters":
+        out, cmd = argv[1:3]
+        runs = [(a.split("=", 1)[0], counter_rows(a.split("=", 1)[1])) for a in argv[3:]]
+        with open(out, "w") as fh:
+            fh.write(counters_markdown(runs, cmd))
     elif argv[0] == "mfma":
         out, cmd = argv[1:3]
         runs = [(a.split("=", 1)[0], mfma_rows(a.split("=", 1)[1])) for a in argv[3:]]
