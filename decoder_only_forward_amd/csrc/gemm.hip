@@ -40,6 +40,7 @@ hipError_t launch_t(Args a, hipStream_t s) {
 constexpr int kDecWaves = 8;
 constexpr int kDecBatch = 4;  // k-steps of 32 loaded per batch
 constexpr int kDecMaxRows = 256;
+constexpr int kSplitMaxN = 2048;  // the split-K reduction handles rows of up to 2048
 
 DEV f32x4_t mfma16h(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a), as_f16x8(b), c, 0, 0, 0);
@@ -169,11 +170,12 @@ GemmPlan gemm_plan(int M, int N, int K, int bmode, int epi, bool grouped) {
     // rows): its k order is that of the larger tiles, so last-position logits equal the
     // corresponding rows of a full pass
     p.tile = epi == E_F32 ? kSkinny : kDecode;
-    // residual projections with few output columns split K over extra blocks; the caller
-    // reduces the partials (fused with the residual add and the following RMSNorm)
+    // residual projections with fewer than 256 blocks of 16 columns split K over extra
+    // blocks; the caller reduces the partials (fused with the residual add and the
+    // following RMSNorm)
     const bool res = epi == E_RES_F32 || epi == E_RESB_F32 || epi == E_RESF_B16;
     const int blocks = (N + 15) / 16 * ((M + 63) / 64);
-    if (p.tile == kDecode && res && blocks < 128) {
+    if (p.tile == kDecode && res && blocks < 256 && N <= kSplitMaxN) {
       const int want = (256 + blocks - 1) / blocks;
       p.k_splits = std::max(1, std::min(want, K / (32 * kDecWaves)));
     }
