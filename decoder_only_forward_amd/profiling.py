@@ -9,8 +9,9 @@ Two kinds of run are summarised (both write CSV with ``--output-format csv``):
   for a plain elementwise copy of known size, run first in the same process
   (``bench.py --copy-gib``), so the figure is in real bytes;
 * matrix-core counters (``--pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F16
-  SQ_BUSY_CYCLES GRBM_GUI_ACTIVE``): per kernel class, the fp16 MFMA work executed (each
-  MOPS unit is 512 flops) and the share of SIMD cycles the matrix cores were busy.
+  SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES GRBM_GUI_ACTIVE``): per kernel class, the
+  fp16 and bf16 MFMA work executed (each MOPS unit is 512 flops) and the share of SIMD
+  cycles the matrix cores were busy.
 
 The traffic table is keyed by profile tag and stamped with a hash of the sources the
 kernel is built from; ``bench.py`` reports it only while those sources are unchanged.
@@ -218,7 +219,8 @@ def mfma_rows(rocprof_dir):
         g = groups.setdefault(name, [0, 0.0, 0.0, 0.0, 0.0])
         g[0] += 1
         g[1] += dur
-        g[2] += c.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) * 512.0
+        g[2] += (c.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) +
+                 c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)) * 512.0
         g[3] += c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
         g[4] += c.get("GRBM_GUI_ACTIVE", 0.0) / xcc
     out = []
@@ -241,7 +243,8 @@ def mfma_markdown(runs, command):
     out = ["# MFMA utilisation per kernel (rocprofv3 matrix-core counters)", "",
            "Command (run from the repository root, once per workload):", "", "```",
            command, "```", "",
-           "Executed flops are SQ_INSTS_VALU_MFMA_MOPS_F16 x 512 per dispatch; the rate is "
+           "Executed flops are (SQ_INSTS_VALU_MFMA_MOPS_F16 + SQ_INSTS_VALU_MFMA_MOPS_BF16) "
+           "x 512 per dispatch (a run without the bf16 counter counts fp16 work only); the rate is "
            "that over the dispatch's own duration; the fraction is of the 2.5 PFLOP/s dense "
            "fp16/bf16 peak (2.4 GHz).  MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES over (one XCD's "
            "GRBM_GUI_ACTIVE x 1024 SIMDs): the share of SIMD cycles the matrix cores were "

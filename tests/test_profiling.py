@@ -83,8 +83,10 @@ def test_counter_rows_average_per_dispatch_and_sum_instances(tmp_path):
 
 def test_mfma_rows_flops_busy_share_and_clock(tmp_path):
     d = str(tmp_path / "m")
-    # one dispatch of 1 us: 1000 MOPS units (512 flops each), 8 XCDs of 2000 active cycles
-    _counters(d, [(1, GEMM, "SQ_INSTS_VALU_MFMA_MOPS_F16", 1000, 0, 1000),
+    # one dispatch of 1 us: 1000 MOPS units (512 flops each; fp16 and bf16 work add up),
+    # 8 XCDs of 2000 active cycles
+    _counters(d, [(1, GEMM, "SQ_INSTS_VALU_MFMA_MOPS_F16", 600, 0, 1000),
+                  (1, GEMM, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 400, 0, 1000),
                   (1, GEMM, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 1000, 0, 1000),
                   (1, GEMM, "GRBM_GUI_ACTIVE", 8 * 2000, 0, 1000)])
     (r,) = profiling.mfma_rows(d)
