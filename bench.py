@@ -389,6 +389,7 @@ def decode_step_bytes(cfg, B, ctx, S=1):
 
 
 def wl_moe(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown):
+    import numpy as np
     cfg = dict(recipes.MOE_2048)
     T = 8192
     router, gu, dn = recipes.moe_device(4, cfg, dev)
@@ -411,13 +412,27 @@ def wl_moe(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown):
     counts = (offsets[1:] - offsets[:-1]).cpu().numpy()
     tile_rows = int(((counts + 255) // 256 * 256).sum())
     total = 2.0 * T * E * H + 2.0 * T * k * 2 * I * H + 2.0 * T * k * I * H
+    # per expert: its rows' share of the 256-row tiles it occupies, and its own roofline time
+    # (its gate|up and down flops at the MFMA peak, or its weights at the HBM peak, whichever
+    # is longer); the sum over experts is the time a perfect kernel would need expert by expert
+    live = counts[counts > 0]
+    row_use = live / ((live + 255) // 256 * 256)
+    t_exp = np.maximum(live * 6.0 * I * H / (PEAK_MFMA_TFLOPS * 1e12),
+                       3.0 * I * H * 2 / (PEAK_HBM_GBS * 1e9))
+    per_expert = {"tile_row_use_min": round(float(row_use.min()), 4),
+                  "tile_row_use_median": round(float(np.median(row_use)), 4),
+                  "below_ridge": int((live * 6.0 * I * H / (PEAK_MFMA_TFLOPS * 1e12) <
+                                      3.0 * I * H * 2 / (PEAK_HBM_GBS * 1e9)).sum()),
+                  "roofline_sum_ms": round(float(t_exp.sum()) * 1e3, 4),
+                  "frac_of_roofline_sum": round(float(t_exp.sum()) * 1e3 / ms, 4)}
     out = {"name": "moe_ffn", "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms,
            "config": {"workload": "moe_ffn_2048x128e_top8", "tokens": T, "hidden": H,
                       "experts": E, "top_k": k, "expert_intermediate": I,
                       "load_max_over_mean": round(float(counts.max() / counts.mean()), 2),
                       "load_min": int(counts.min()), "load_max": int(counts.max()),
                       "experts_below_256_rows": int((counts < 256).sum()),
-                      "grouped_tile_row_use": round(float(counts.sum()) / tile_rows, 4)},
+                      "grouped_tile_row_use": round(float(counts.sum()) / tile_rows, 4),
+                      "per_expert": per_expert},
            "dominant_kernel": dom, "roofline": rf,
            "whole_step_mfma_frac": round(total / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)}
     out.update({k: round(v, 4) for k, v in stats.items()})
