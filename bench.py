@@ -243,9 +243,17 @@ def kernel_breakdown(timer, step, units, steps):
     return res
 
 
-def measure(timer, step, steps, warmup, workload, units, default_tag, breakdown):
+# Products of at most 256 rows run on the decode-size GEMM kernel, whose counter entries
+# carry their own tags (o_proj and down share one instantiation).
+DECODE_SIZE_TAGS = {"qkv_gemm": "decode_qkv_gemm", "gate_up_gemm": "decode_gate_up_gemm",
+                    "o_proj_gemm": "decode_res_gemm", "down_gemm": "decode_res_gemm"}
+
+
+def measure(timer, step, steps, warmup, workload, units, default_tag, breakdown,
+            traffic_tags=None):
     """Breakdown first (short runs), then the timed region with the dominant kernel class
-    (largest time per step) recording its launch events live."""
+    (largest time per step) recording its launch events live.  traffic_tags maps a kernel
+    class to the tag of its counter entry where the two differ."""
     kernels = kernel_breakdown(timer, step, units, min(steps, 3)) if breakdown else None
     tag = default_tag
     if kernels:
@@ -255,7 +263,7 @@ def measure(timer, step, steps, warmup, workload, units, default_tag, breakdown)
     ms, kern = timer.run(step, steps, warmup, tag=tag, launches_per_step=per_step,
                          per_step=stats)
     from decoder_only_forward_amd import profiling
-    traffic = profiling.traffic_for(workload, tag)
+    traffic = profiling.traffic_for(workload, (traffic_tags or {}).get(tag, tag))
     rf = (roofline_mfma if bound == "mfma" else roofline_hbm)(amount, kern["avg_ms"], traffic)
     dom = dict(kern, **({"flops_per_launch": amount} if bound == "mfma"
                         else {"bytes_per_launch": amount}))
@@ -321,7 +329,7 @@ def wl_decode(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, S
         "argmax": ("hbm", 4.0 * B * V, 1),
     }
     ms, dom, rf, kernels, stats = measure(timer, step, steps, warmup, name, units, "attn_decode",
-                                   breakdown)
+                                   breakdown, DECODE_SIZE_TAGS if T <= 256 else None)
     step_bytes = decode_step_bytes(cfg, B, ctx, S)
     out = {"name": name, "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms,
            "config": {"workload": name, "batch": B, "context": ctx,
@@ -472,7 +480,7 @@ def wl_block(torch, q3, recipes, synth, dev, steps, warmup, timer, breakdown, bi
     name = ("block_7b" if big else "block_0p6b") + ("_rope_interleaved" if rope_interleaved else "")
     units = dense_units(cfg, B, S, 1)
     ms, dom, rf, kernels, stats = measure(timer, step, steps, warmup, name, units, "attn_prefill",
-                                   breakdown)
+                                   breakdown, DECODE_SIZE_TAGS if B * S <= 256 else None)
     out = {"name": name, "tokens_per_s": B * S / (ms * 1e-3), "ms_per_step": ms,
            "config": {"workload": name, "batch": B, "seq_len": S, "hidden": H,
                       "heads": f"{nq}q/{nkv}kv x128", "intermediate": cfg["intermediate_size"],
