@@ -121,6 +121,8 @@ struct DenseLayout {
   size_t moe;      // stack with routed layers: the MoE FFN's workspace (layout ml)
   MoeLayout ml;
   size_t kf, vtf;  // prefill: fp16 copies of the new keys / values
+  size_t own_k, own_vt;  // block prefill without a caller cache: a cache of own_cap positions
+  int own_cap;
   size_t total;
   int T, rows_out, attn_splits, attn_chunk, am_chunks, fresh_w_max;
 };
@@ -149,6 +151,11 @@ DenseLayout dense_layout(const qwen3_config* c, int op, int B, int S, int cap_hi
     L.fresh_w_max = ((S + 63 + 63) / 64) * 64;
     L.kf = b.take((size_t)B * nkv * L.fresh_w_max * hd * 2);
     L.vtf = b.take((size_t)B * nkv * L.fresh_w_max * hd * 2);
+  }
+  if (op == QWEN3_OP_BLOCK_PREFILL) {
+    L.own_cap = ((S + 63) / 64) * 64;
+    L.own_k = b.take((size_t)B * nkv * L.own_cap * hd * 2);
+    L.own_vt = b.take((size_t)B * nkv * L.own_cap * hd * 2);
   }
   if (decode) {
     attn_decode_plan(cap_hint, B * attn_decode_groups(S, nq / nkv), nkv, L.attn_splits,
@@ -716,17 +723,34 @@ int qwen3_block_prefill(const qwen3_config* c, const qwen3_layer_weights* w, con
   REQ_PTR(x_in, "x_in");
   REQ_PTR(x_out, "x_out");
   if (x_in == x_out) return fail(QWEN3_EINVAL, "x_in and x_out may not alias");
-  TRY(check_cache(c, cache, "cache", batch));
-  TRY(check_range(c, cache, pos0, seq_len));
   if ((int64_t)batch * seq_len > (1 << 30)) return fail(QWEN3_EINVAL, "too many tokens");
-  DenseLayout L = dense_layout(c, QWEN3_OP_BLOCK_PREFILL, batch, seq_len, cache->capacity);
+  if (cache) {
+    TRY(check_cache(c, cache, "cache", batch));
+    TRY(check_range(c, cache, pos0, seq_len));
+  } else {
+    // no cache: the keys and values of this call only, kept in the workspace
+    if (pos0 != 0) return fail(QWEN3_EINVAL, "cache is NULL: pos0=%d must be 0", pos0);
+    if (seq_len > c->max_position_embeddings)
+      return fail(QWEN3_ERANGE, "seq_len=%d exceeds max_position_embeddings %d", seq_len,
+                  c->max_position_embeddings);
+  }
+  DenseLayout L = dense_layout(c, QWEN3_OP_BLOCK_PREFILL, batch, seq_len,
+                               cache ? cache->capacity : 0);
   if (!aligned16(workspace) || workspace_bytes < L.total)
     return fail(QWEN3_EWORKSPACE, "workspace needs %zu bytes (got %zu)", L.total,
                 workspace_bytes);
+  qwen3_kv_layer own{};
+  if (!cache) {
+    own.k = (char*)workspace + L.own_k;
+    own.vt = (char*)workspace + L.own_vt;
+    own.capacity = L.own_cap;
+    own.regions = batch * c->num_key_value_heads;
+  }
   LayerIO io{};
   io.T = batch * seq_len; io.B = batch; io.S = seq_len; io.pos0 = pos0;
   io.x_bf16 = (const bf16_t*)x_in; io.x_out = (bf16_t*)x_out;
-  return run_layer(c, w, rope, cache, io, (char*)workspace, L, (hipStream_t)stream);
+  return run_layer(c, w, rope, cache ? cache : &own, io, (char*)workspace, L,
+                   (hipStream_t)stream);
 }
 
 }  // extern "C"

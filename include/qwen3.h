@@ -189,8 +189,10 @@ int qwen3_rope_table_init(const qwen3_config *cfg, float *rope, void *stream);
  * read from `cache`, the new keys/values are written into it at [pos0, pos0+seq_len).
  *   x_in, x_out: bf16 [batch][seq_len][H] (may not alias)
  *   rope: table from qwen3_rope_table_init
- *   cache: required (holds the new K/V); pos0 + seq_len <= capacity and
- *          <= max_position_embeddings, else QWEN3_ERANGE. */
+ *   cache: holds the new K/V; pos0 + seq_len <= capacity and <= max_position_embeddings,
+ *          else QWEN3_ERANGE.  NULL: no earlier positions and nothing kept (pos0 must be 0,
+ *          else QWEN3_EINVAL; seq_len <= max_position_embeddings): the call's keys and
+ *          values live in the workspace, which qwen3_workspace_bytes sizes for this. */
 int qwen3_block_prefill(const qwen3_config *cfg, const qwen3_layer_weights *w,
                         const float *rope, const void *x_in, void *x_out, int32_t batch,
                         int32_t seq_len, int32_t pos0, const qwen3_kv_layer *cache,

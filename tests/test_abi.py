@@ -96,6 +96,11 @@ def test_block_prefill_rejects_bad_arguments():
     _expect(lambda: call(batch=2, cache=q3.make_kv_layer(0x10000, 0x20000, 128, regions=15)),
             q3.QWEN3_EINVAL, "regions")
     _expect(lambda: call(), q3.QWEN3_EWORKSPACE, "workspace")
+    # no cache: a prefill from position 0 only, bounded by max_position_embeddings
+    _expect(lambda: call(cache=None, pos0=64), q3.QWEN3_EINVAL, "pos0")
+    _expect(lambda: call(c=big, seq_len=101, cache=None), q3.QWEN3_ERANGE,
+            "max_position_embeddings")
+    _expect(lambda: call(cache=None, seq_len=129), q3.QWEN3_EWORKSPACE, "workspace")
 
 
 def test_moe_rejects_bad_arguments():

@@ -97,6 +97,36 @@ def test_block_prefill_deterministic(gpu):
     np.testing.assert_array_equal(outs[0], outs[1])
 
 
+@pytest.mark.parametrize("B,S", [(2, 150), (1, 40)])
+def test_block_prefill_without_cache_equals_with_cache(gpu, B, S):
+    # With no cache the call keeps its keys and values in the workspace: the output must be
+    # the same bits as with a caller cache (tiled projections at 300 rows, decode-size ones
+    # at 40), and every output row must still match the oracle.
+    import torch
+    cfg = small_cfg()
+    log(f"case block prefill without cache: B={B} S={S}")
+    host = recipes.layer_host(5, cfg, 0)
+    layer = layer_to_dev(host, gpu)
+    xh = synth.normal_bf16(5, recipes.activations_name(), (B, S, 256))
+    x = to_dev_bf16(xh, gpu)
+    rope = _rope(cfg, gpu)
+    ws = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_BLOCK_PREFILL, B, S),
+                     dtype=torch.uint8, device=gpu)
+    cap = ((S + 63) // 64) * 64
+    k, vt = new_cache(B, 2, cap, gpu)
+    with_cache = torch.empty_like(x)
+    q3.qwen3_block_prefill(cfg, layer, rope, x, with_cache, B, S, 0,
+                           q3.make_kv_layer(k, vt, cap), ws)
+    without = torch.empty_like(x)
+    q3.qwen3_block_prefill(cfg, layer, rope, x, without, B, S, 0, None, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_host(without), bf16_host(with_cache))
+    got = synth.bf16_to_f32(bf16_host(without)).astype(np.float64)
+    for b in range(B):
+        ref, _, _ = oracle.block(cfg, host, f64(xh[b]))
+        parity(got[b], ref, f"x_out[{b}] without cache")
+
+
 DECODE_CASES = {
     "small": (dict(), [0, 100, 255, 37], 256),
     "group7": (dict(nq=7, nkv=1), [300, 5], 320),
