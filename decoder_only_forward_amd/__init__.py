@@ -34,8 +34,9 @@ QWEN3_LOGITS_LAST = 2
 
 EXPORTS = ("qwen3_workspace_bytes", "qwen3_rope_table_init", "qwen3_block_prefill",
            "qwen3_block_decode", "qwen3_block_decode_static", "qwen3_moe_ffn",
-           "qwen3_stack_forward", "qwen3_generate", "qwen3_status_string", "qwen3_last_error",
-           "qwen3_profile_begin", "qwen3_profile_end")
+           "qwen3_stack_forward", "qwen3_generate", "qwen3_kv_pack", "qwen3_kv_unpack",
+           "qwen3_status_string", "qwen3_last_error", "qwen3_profile_begin",
+           "qwen3_profile_end")
 
 # qwen3_block_decode_static's device scratch per GPU (QWEN3_STATIC_SCRATCH_BYTES)
 QWEN3_STATIC_SCRATCH_BYTES = 16 << 20
@@ -107,6 +108,10 @@ def lib():
         L.qwen3_generate.restype = ctypes.c_int
         L.qwen3_generate.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, ctypes.c_float,
                                      ctypes.c_float, vp, vp, vp, sz, vp]
+        L.qwen3_kv_pack.restype = ctypes.c_int
+        L.qwen3_kv_pack.argtypes = [vp, vp, vp, i32, i32, vp, vp]
+        L.qwen3_kv_unpack.restype = ctypes.c_int
+        L.qwen3_kv_unpack.argtypes = [vp, vp, i32, i32, vp, vp, vp]
         L.qwen3_status_string.restype = ctypes.c_char_p
         L.qwen3_status_string.argtypes = [ctypes.c_int]
         L.qwen3_last_error.restype = ctypes.c_char_p
@@ -339,6 +344,16 @@ def qwen3_generate(cfg, w, rope, prompt_ids, batch, prompt_len, n_new, caches, o
                                 _ptr(prompt_ids), batch, prompt_len, n_new, arr,
                                 float(temperature), float(top_p), _ptr(uniforms),
                                 _ptr(out_ids), wp, wb, _stream(stream)))
+
+
+def qwen3_kv_pack(cfg, k_plain, v_plain, batch, length, cache, stream=None):
+    _check(lib().qwen3_kv_pack(ctypes.byref(_cfg(cfg)), _ptr(k_plain), _ptr(v_plain), batch,
+                               length, _byref(cache), _stream(stream)))
+
+
+def qwen3_kv_unpack(cfg, cache, batch, length, k_plain, v_plain, stream=None):
+    _check(lib().qwen3_kv_unpack(ctypes.byref(_cfg(cfg)), _byref(cache), batch, length,
+                                 _ptr(k_plain), _ptr(v_plain), _stream(stream)))
 
 
 def qwen3_profile_begin(tag, max_launches):

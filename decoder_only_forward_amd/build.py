@@ -9,7 +9,7 @@ SO = os.path.join(HERE, "libqwen3.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["gemm.hip", "norm_rope.hip", "attention.hip", "argmax.hip", "sample.hip", "moe.hip",
-           "qwen3_api.cpp"]
+           "kv_layout.hip", "qwen3_api.cpp"]
 
 # Per-source extras.  attention.hip: its softmax takes maxima of MFMA results, which are
 # never signalling NaNs; without this the compiler quiets every fmaxf operand first.  The

@@ -111,6 +111,12 @@ hipError_t sample_rows(const float* logits, int64_t row_stride, int rows, int V,
 hipError_t gen_feed(const int32_t* ids, int32_t* out_ids, int n_new, int col, int32_t* pos,
                     int next_pos, int B, hipStream_t s);
 
+// ---- cache layout copies (kv_layout.hip)
+// regions (sequence, kv head) pairs of positions [0, len): plain [regions][len][128] bf16
+// K / V <-> tiled cache regions of cap * 128 (to_tiled: plain -> tiled)
+hipError_t kv_copy(void* k_plain, void* v_plain, void* k_tiled, void* vt_tiled, int regions,
+                   int len, int cap, bool to_tiled, hipStream_t s);
+
 // ---- MoE (moe.hip)
 struct MoeRouteArgs {
   float* logits;  // [T][E]: read, or written when x is set

@@ -710,6 +710,37 @@ int qwen3_rope_table_init(const qwen3_config* c, float* rope, void* stream) {
   return QWEN3_OK;
 }
 
+int qwen3_kv_pack(const qwen3_config* c, const void* k_plain, const void* v_plain,
+                  int32_t batch, int32_t len, const qwen3_kv_layer* cache, void* stream) {
+  g_err.clear();
+  TRY(check_dense_cfg(c));
+  if (batch <= 0) return fail(QWEN3_EINVAL, "batch=%d must be positive", batch);
+  TRY(check_cache(c, cache, "cache", batch));
+  if (len < 0 || len > cache->capacity)
+    return fail(QWEN3_ERANGE, "len=%d outside [0, capacity %d]", len, cache->capacity);
+  if (len > 0 && (!aligned16(k_plain) || !aligned16(v_plain)))
+    return fail(QWEN3_EINVAL, "k_plain / v_plain NULL or not 16-byte aligned");
+  CHECK_HIP(kv_copy(const_cast<void*>(k_plain), const_cast<void*>(v_plain), cache->k, cache->vt,
+                    batch * c->num_key_value_heads, len, cache->capacity, true,
+                    (hipStream_t)stream));
+  return QWEN3_OK;
+}
+
+int qwen3_kv_unpack(const qwen3_config* c, const qwen3_kv_layer* cache, int32_t batch,
+                    int32_t len, void* k_plain, void* v_plain, void* stream) {
+  g_err.clear();
+  TRY(check_dense_cfg(c));
+  if (batch <= 0) return fail(QWEN3_EINVAL, "batch=%d must be positive", batch);
+  TRY(check_cache(c, cache, "cache", batch));
+  if (len < 0 || len > cache->capacity)
+    return fail(QWEN3_ERANGE, "len=%d outside [0, capacity %d]", len, cache->capacity);
+  if (len > 0 && (!aligned16(k_plain) || !aligned16(v_plain)))
+    return fail(QWEN3_EINVAL, "k_plain / v_plain NULL or not 16-byte aligned");
+  CHECK_HIP(kv_copy(k_plain, v_plain, cache->k, cache->vt, batch * c->num_key_value_heads, len,
+                    cache->capacity, false, (hipStream_t)stream));
+  return QWEN3_OK;
+}
+
 int qwen3_block_prefill(const qwen3_config* c, const qwen3_layer_weights* w, const float* rope,
                         const void* x_in, void* x_out, int32_t batch, int32_t seq_len,
                         int32_t pos0, const qwen3_kv_layer* cache, void* workspace,

@@ -180,6 +180,20 @@ size_t qwen3_workspace_bytes(const qwen3_config *cfg, int32_t op, int32_t batch,
  * Values are computed in fp64 on the device and rounded once to fp32. */
 int qwen3_rope_table_init(const qwen3_config *cfg, float *rope, void *stream);
 
+/* Copies between plain K / V tensors of one layer, bf16 [batch][num_key_value_heads][len][128]
+ * (one row of head_dim values per position, the pages' cache tensors: [P3] "prefill 与
+ * decode"), and the tiled cache above.  Positions [0, len) of each (sequence, kv head)
+ * region are copied; the cache's other positions are not touched.
+ *   qwen3_kv_pack:   k_plain, v_plain -> cache
+ *   qwen3_kv_unpack: cache -> k_plain, v_plain
+ * All pointers are device memory, 16-byte aligned (k_plain / v_plain may be NULL when
+ * len is 0); 0 <= len <= capacity (ERANGE otherwise); the cache needs batch *
+ * num_key_value_heads regions.  Enqueued on `stream`. */
+int qwen3_kv_pack(const qwen3_config *cfg, const void *k_plain, const void *v_plain,
+                  int32_t batch, int32_t len, const qwen3_kv_layer *cache, void *stream);
+int qwen3_kv_unpack(const qwen3_config *cfg, const qwen3_kv_layer *cache, int32_t batch,
+                    int32_t len, void *k_plain, void *v_plain, void *stream);
+
 /* One pre-norm decoder block, prefill of `seq_len` new tokens for each of `batch`
  * sequences that all start at absolute position pos0 ([P3] "TransformerBlock",
  * "GQA 注意力", "prefill 与 decode"; [P4] decoder layer):

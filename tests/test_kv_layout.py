@@ -64,3 +64,27 @@ def test_make_kv_layer_records_regions():
         q3.make_kv_layer(k, vt, 64, regions=7)  # more than the tensors hold
     with pytest.raises(ValueError):
         q3.make_kv_layer(0x10000, 0x20000, 64)  # raw pointers must state it
+
+
+def test_kv_pack_rejects_bad_arguments():
+    import pytest
+    from synth import recipes
+    cfg = dict(recipes.QWEN3_0P6B)  # 8 kv heads
+    cache = q3.make_kv_layer(0x10000, 0x20000, 128, regions=16)
+
+    def expect(fn, code, word):
+        with pytest.raises(RuntimeError) as e:
+            fn()
+        msg = str(e.value)
+        assert q3.lib().qwen3_status_string(code).decode() in msg and word in msg, msg
+
+    expect(lambda: q3.qwen3_kv_pack(cfg, 0x4000, 0x5000, 2, 129, cache, stream=0),
+           q3.QWEN3_ERANGE, "len")
+    expect(lambda: q3.qwen3_kv_unpack(cfg, cache, 2, -1, 0x4000, 0x5000, stream=0),
+           q3.QWEN3_ERANGE, "len")
+    expect(lambda: q3.qwen3_kv_pack(cfg, 0x4000, 0x5000, 3, 64, cache, stream=0),
+           q3.QWEN3_EINVAL, "regions")
+    expect(lambda: q3.qwen3_kv_pack(cfg, 0x4008, 0x5000, 2, 64, cache, stream=0),
+           q3.QWEN3_EINVAL, "aligned")
+    expect(lambda: q3.qwen3_kv_unpack(cfg, None, 2, 64, 0x4000, 0x5000, stream=0),
+           q3.QWEN3_EINVAL, "cache")
