@@ -539,6 +539,61 @@ def cpu_baseline(n_tokens):
                       f"oracle, {dt:.1f}s wall"}
 
 
+def cpu_workload_samples(wls):
+    """The oracle (as it stands) beside the other workloads, each on a bounded sample of the
+    same inputs, in that workload's own tokens/s: the whole 128-token 0.6B block, one
+    sequence of the decode step (its 28 layers' caches regenerated, 4096 positions), 256 of
+    the 8192 MoE tokens, and the first 512 rows of the 7B block."""
+    import numpy as np
+    import oracle
+    import synth
+    from synth import recipes
+    oracle.set_threads(len(os.sched_getaffinity(0)))
+    f64 = lambda u: synth.bf16_to_f32(u).astype(np.float64)
+    out = {}
+
+    def rec(w, n, dt, sample):
+        out[w] = {"value": round(n / dt, 3), "unit": "tokens/s", "cores": oracle.get_threads(),
+                  "kind": "oracle", "sample": f"{sample}; fp64 C++ oracle, {dt:.2f}s wall"}
+
+    act = recipes.activations_name()
+    if "block" in wls:
+        cfg = dict(recipes.QWEN3_0P6B)
+        layer = recipes.layer_host(1, cfg, 0)
+        x = synth.normal_bf16(1, act, (1, 128, cfg["hidden_size"]))
+        t0 = time.time()
+        oracle.block(cfg, layer, f64(x[0]))
+        rec("block", 128, time.time() - t0, "the whole workload (1 x 128 tokens, one block)")
+    if "decode" in wls:
+        cfg = dict(recipes.QWEN3_0P6B)
+        L, ctx = cfg["num_hidden_layers"], 4096
+        host = recipes.model_host(recipes.MODEL_SEED_0P6B, cfg)
+        ids = synth.uniform_i32(3, "input.ids", (64, 1), 0, cfg["vocab_size"])
+        ck, cv = zip(*[recipes.kv_host(3, cfg, l, 0, ctx, (cfg["num_key_value_heads"], ctx))
+                       for l in range(L)])
+        t0 = time.time()
+        oracle.stack_decode(cfg, host, ids[0], ctx, list(ck), list(cv))
+        rec("decode", 1, time.time() - t0,
+            "sequence 0 of 64: one new token at position 4096, 28 layers + LM head")
+        del host, ck, cv
+    if "moe" in wls:
+        cfg = dict(recipes.MOE_2048)
+        router, gu, dn = recipes.moe_host(4, cfg)
+        x = synth.normal_bf16(4, act, (8192, cfg["hidden_size"]))[:256]
+        t0 = time.time()
+        oracle.moe_ffn(cfg, router, gu, dn, f64(x))
+        rec("moe", 256, time.time() - t0, "the first 256 of the 8192 tokens")
+        del router, gu, dn
+    if "block7b" in wls:
+        cfg = dict(recipes.QWEN_7B_BLOCK)
+        layer = recipes.layer_host(5, cfg, 0)
+        x = synth.normal_bf16(5, act, (1, 32768, cfg["hidden_size"]))[0, :512]
+        t0 = time.time()
+        oracle.block(cfg, layer, f64(x))
+        rec("block7b", 512, time.time() - t0, "the first 512 of the 32768 rows (causal prefix)")
+    return out
+
+
 # ------------------------------------------------------------------------- main
 
 def device_info():
@@ -648,6 +703,9 @@ def main():
     if args.cpu_tokens > 0 and main_wl == "prefill":
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
+        log("cpu samples of the other workloads (oracle) ...")
+        for w, r in cpu_workload_samples(set(results)).items():
+            results[w]["cpu_baseline"] = r
     line["workloads"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                              for kk, vv in v.items()} for k, v in results.items()}
     print(json.dumps(line), flush=True)
