@@ -53,7 +53,23 @@ MOE_CASES = {
     "e8_k2_bf16_router_norm": (dict(num_experts=8, num_experts_per_tok=2,
                                     moe_intermediate_size=128, hidden_size=256,
                                     router_weights_bf16=1), 170, False),
+    # degenerate loads: one expert takes every token (three 256-row tiles, a ragged last
+    # one) and the other fifteen none; with k = 2 the hot expert is every token's first
+    "e16_k1_one_expert": (dict(num_experts=16, num_experts_per_tok=1, moe_intermediate_size=128,
+                               hidden_size=256), 700, "hot"),
+    "e8_k2_hot_expert": (dict(num_experts=8, num_experts_per_tok=2, moe_intermediate_size=128,
+                              hidden_size=256), 300, "hot"),
 }
+
+
+def _make_hot(router, x):
+    """Expert 0's logit gets +8 on every token (a constant input column of 8 that only its
+    router row reads), far above the others' (about N(0, 0.3))."""
+    router, x = router.copy(), x.copy()
+    router[:, 0] = 0
+    router[0, 0] = synth.f32_to_bf16(np.array([1.0], np.float32))[0]
+    x[:, 0] = synth.f32_to_bf16(np.array([8.0], np.float32))[0]
+    return router, x
 
 
 def _near_bf16_midpoint(logits):
@@ -72,9 +88,13 @@ def test_moe_parity(gpu, name):
     cfg = dict(norm_topk_prob=1, rms_norm_eps=1e-6)
     cfg.update(kw)
     log(f"case moe/{name}: T={T} {kw}")
-    router, gu, dn = recipes.moe_host(31, cfg, skew=skew)
+    router, gu, dn = recipes.moe_host(31, cfg, skew=skew is True)
     x = synth.normal_bf16(31, recipes.activations_name(), (T, cfg["hidden_size"]))
+    if skew == "hot":
+        router, x = _make_hot(router, x)
     g = run_moe(cfg, router, gu, dn, x, gpu)
+    if skew == "hot":
+        assert np.all(g["idx"][:, 0] == 0) and g["offsets"][1] == T, g["offsets"]
     y_ref, idx_ref, w_ref, lg_ref = oracle.moe_ffn(cfg, router, gu, dn, f64(x))
     parity(g["logits"], lg_ref, "router_logits")
     k, E = cfg["num_experts_per_tok"], cfg["num_experts"]
