@@ -223,9 +223,6 @@ int check_dense_cfg(const qwen3_config* c) {
   if (c->num_attention_heads % c->num_key_value_heads)
     return fail(QWEN3_EINVAL, "num_attention_heads=%d is not a multiple of num_key_value_heads=%d",
                 c->num_attention_heads, c->num_key_value_heads);
-  if (c->num_attention_heads / c->num_key_value_heads > 8)
-    return fail(QWEN3_EUNSUPPORTED, "group size %d > 8",
-                c->num_attention_heads / c->num_key_value_heads);
   if (c->max_position_embeddings <= 0)
     return fail(QWEN3_EINVAL, "max_position_embeddings=%d", c->max_position_embeddings);
   if (!(c->rms_norm_eps >= 0.f)) return fail(QWEN3_EINVAL, "rms_norm_eps must be >= 0");

@@ -37,8 +37,9 @@
  *     keep fp16-subnormal precision (absolute error at most 2^-25); larger ones are not
  *     supported.  qwen3_moe_ffn reads its bf16 input x as bf16 matrix-core operands.
  *   - Supported shapes: head_dim == 128; hidden_size and the intermediate sizes
- *     multiples of 64; num_attention_heads a multiple of num_key_value_heads with a
- *     group size of at most 8; MoE: at most 256 experts and 8 experts per token.
+ *     multiples of 64; num_attention_heads a multiple of num_key_value_heads (any group
+ *     size: decode steps serve a group's queries eight per block); MoE: at most 256
+ *     experts and 8 experts per token.
  *
  * KV cache (per layer, caller-owned, bf16), tiled by 32 positions (head_dim = 128):
  *   k  [batch][num_key_value_heads][capacity/32][4][32][32]

@@ -77,8 +77,6 @@ def test_block_prefill_rejects_bad_arguments():
     _expect(lambda: call(c=dict(cfg, head_dim=64)), q3.QWEN3_EUNSUPPORTED, "head_dim")
     _expect(lambda: call(c=dict(cfg, num_key_value_heads=3)), q3.QWEN3_EINVAL,
             "num_key_value_heads")
-    _expect(lambda: call(c=dict(cfg, num_attention_heads=32, num_key_value_heads=2)),
-            q3.QWEN3_EUNSUPPORTED, "group size")
     _expect(lambda: call(c=dict(cfg, rope_interleaved=2)), q3.QWEN3_EINVAL, "rope_interleaved")
     _expect(lambda: call(w=dict(lw, o_proj=0)), q3.QWEN3_EINVAL, "o_proj")
     _expect(lambda: call(w=dict(lw, q_proj=0x1001)), q3.QWEN3_EINVAL, "q_proj")

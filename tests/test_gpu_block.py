@@ -37,6 +37,9 @@ PREFILL_CASES = {
     # longer sequences: several causal row blocks of very different lengths
     "long_sequence": (dict(), 1, 1000, 0),
     "long_group7": (dict(nq=7, nkv=1), 2, 450, 0),
+    # sixteen q heads per kv head (a 64 q / 4 kv model's grouping), tiled and small
+    "group16_tiled": (dict(nq=16, nkv=1), 2, 160, 0),
+    "group16_chunked": (dict(nq=16, nkv=1), 1, 40, 30),
 }
 
 
@@ -130,6 +133,8 @@ def test_block_prefill_without_cache_equals_with_cache(gpu, B, S):
 DECODE_CASES = {
     "small": (dict(), [0, 100, 255, 37], 256),
     "group7": (dict(nq=7, nkv=1), [300, 5], 320),
+    # two 8-query blocks per (sequence, kv head)
+    "group16": (dict(nq=16, nkv=1), [200, 63, 0], 256),
     "interleaved_rope": (dict(rope_interleaved=1), [0, 77, 200], 256),
     "cfg_0p6b": (None, [4096, 1000], 4160),
     # the 7B-shaped block: K = 3584 and 18944 decode products, 7 q heads per kv head

@@ -65,6 +65,7 @@ CASES = {
     "s5_ragged": ([50, 120, 0], 5, 128, {}),
     "s20_tile_gemms": ([7, 64, 33, 90], 20, 128, {}),   # 80 rows: tiled projections
     "g8_three_groups": ([70, 3], 3, 128, dict(nq=8, nkv=1)),  # 24 queries per kv head
+    "g16_six_groups": ([70, 3], 3, 128, dict(nq=16, nkv=1)),  # 48 queries per kv head
 }
 
 
