@@ -65,12 +65,15 @@ def parity(got, ref, what="", max_abs_rel=MAX_ABS_REL_RMS, mean_rel=MEAN_REL, st
 class ParityAccumulator:
     """parity() over a tensor compared in pieces: the error sums and maxima of each piece
     are accumulated and the bar is applied once to the whole tensor (rms and L1 norm of the
-    whole oracle tensor), exactly as one parity() call on the concatenation would."""
+    whole oracle tensor), exactly as one parity() call on the concatenation would.  With
+    stored_bf16 the largest error against the oracle rounded to bf16 is reported as well."""
 
-    def __init__(self, what, max_abs_rel=MAX_ABS_REL_RMS, mean_rel=MEAN_REL):
+    def __init__(self, what, max_abs_rel=MAX_ABS_REL_RMS, mean_rel=MEAN_REL, stored_bf16=False):
         self.what, self.max_abs_rel, self.mean_rel = what, max_abs_rel, mean_rel
+        self.stored_bf16 = stored_bf16
         self.n = 0
         self.sq = self.abs_ref = self.abs_err = self.max_err = 0.0
+        self.max_err_bf16 = 0.0  # against the oracle rounded to bf16 (stored_bf16 only)
 
     def add(self, got, ref):
         got = np.asarray(got, np.float64)
@@ -83,17 +86,24 @@ class ParityAccumulator:
         self.abs_ref += float(np.abs(ref).sum())
         self.abs_err += float(err.sum())
         self.max_err = max(self.max_err, float(err.max()) if err.size else 0.0)
+        if self.stored_bf16 and err.size:
+            rb = synth.bf16_to_f32(synth.f32_to_bf16(ref.astype(np.float32))).astype(np.float64)
+            self.max_err_bf16 = max(self.max_err_bf16, float(np.abs(got - rb).max()))
 
     def check(self):
         rms = float(np.sqrt(self.sq / max(self.n, 1)))
         l1 = self.abs_err / max(self.abs_ref, 1e-300)
         bar = self.max_abs_rel * rms
-        RECORDS.append(dict(test=_current_test(), what=self.what, n=self.n, rms=rms,
-                            max_abs=self.max_err, max_abs_bar=bar, mean_rel=l1,
-                            mean_rel_bar=self.mean_rel))
+        rec = dict(test=_current_test(), what=self.what, n=self.n, rms=rms,
+                   max_abs=self.max_err, max_abs_bar=bar, mean_rel=l1, mean_rel_bar=self.mean_rel)
+        extra = ""
+        if self.stored_bf16:
+            rec["max_abs_vs_bf16_ref"] = self.max_err_bf16
+            extra = f" [vs bf16(oracle) {self.max_err_bf16:.3e}]"
+        RECORDS.append(rec)
         log(f"  parity {self.what}: max_abs={self.max_err:.3e} (bar {bar:.3e}, "
             f"{self.max_err / max(bar, 1e-300):.2f} of it) mean_rel={l1:.3e} "
-            f"(bar {self.mean_rel:.1e}, {l1 / self.mean_rel:.2f}) over {self.n} elements")
+            f"(bar {self.mean_rel:.1e}, {l1 / self.mean_rel:.2f}) over {self.n} elements{extra}")
         assert self.max_err <= bar, f"{self.what}: max_abs {self.max_err} > {bar}"
         assert l1 <= self.mean_rel, f"{self.what}: mean relative error {l1} > {self.mean_rel}"
 

@@ -65,8 +65,8 @@ def test_stack_prefill_4x2048(gpu):
     del model, mw, ws
     host = recipes.model_host(recipes.MODEL_SEED_0P6B, cfg)
     acc_lg = ParityAccumulator("logits[4, 2048, 151936] (all)")
-    acc_k = ParityAccumulator("cache K, 28 layers x 4 x 8 x 2048 x 128 (all)")
-    acc_v = ParityAccumulator("cache V, 28 layers x 4 x 8 x 2048 x 128 (all)")
+    acc_k = ParityAccumulator("cache K, 28 layers x 4 x 8 x 2048 x 128 (all)", stored_bf16=True)
+    acc_v = ParityAccumulator("cache V, 28 layers x 4 x 8 x 2048 x 128 (all)", stored_bf16=True)
     for b in range(B):
         log(f"  oracle prefill of sequence {b} (2048 tokens, 28 layers, all logits) ...")
         ref, ko, vo = oracle.stack_prefill(cfg, host, ids_h[b], want_kv=True)
