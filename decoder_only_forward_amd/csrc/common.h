@@ -18,13 +18,9 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 DEV float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// fp32 -> bf16, round to nearest even; a NaN input stays a (quiet) NaN.
-DEV bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// fp32 -> bf16, round to nearest even; a NaN input stays a (quiet) NaN.  One conversion
+// instruction (v_cvt_pk_bf16_f32), with no per-element branch for the NaN case.
+DEV bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 // two floats -> packed bf16 pair, round to nearest even, NaN stays NaN (v_cvt_pk_bf16_f32)
 DEV uint32_t pack_bf16x2(float lo, float hi) {

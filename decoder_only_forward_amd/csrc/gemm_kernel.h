@@ -34,6 +34,8 @@
 // device tile table; A rows may be gathered through a row-index list.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace gemm {
@@ -187,6 +189,15 @@ DEV void qkrope_epilogue(const Args& p, const f32x16_t (&acc)[T::TM][T::TN], f16
       }
   __syncthreads();
   const int tid = threadIdx.x;
+  // Output row out_row0 + lr is token (s_first + lr) % S of sequence b_first +
+  // (s_first + lr) / S: one division per tile, then a 32-bit one per row (rows < 2^30)
+  const unsigned S_u = (unsigned)e.S;
+  const int b_first = out_row0 / e.S, s_first = out_row0 % e.S;
+  auto seq_of = [&](int lr, int& b, int& s) {
+    const unsigned a = (unsigned)(s_first + lr), q = a / S_u;
+    b = b_first + (int)q;
+    s = (int)(a - q * S_u);
+  };
   if (n0 < p.seg2) {
     const bool is_q = n0 < p.seg1;
     const int head0 = is_q ? n0 / HD : (n0 - p.seg1) / HD;
@@ -209,13 +220,14 @@ DEV void qkrope_epilogue(const Args& p, const f32x16_t (&acc)[T::TM][T::TN], f16
     for (int base = wave * 4 + sub; base < rows_valid; base += NB * STEP) {
       u32x4_t raw[NB][HEADS];
       f32x4_t tc[NB][2], ts[NB][2];
-      int pos_k[NB];
+      int pos_k[NB], b_k[NB];
       bool ok_k[NB];
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         const int lr = min(base + u * STEP, rows_valid - 1);
-        const int64_t t = out_row0 + lr;
-        const int pos = e.pos0 + (int)(t % e.S);
+        int sq;
+        seq_of(lr, b_k[u], sq);
+        const int pos = e.pos0 + sq;
         pos_k[u] = pos;
         ok_k[u] = pos >= 0 && pos < e.cap && pos < e.max_pos;
 #pragma unroll
@@ -235,7 +247,7 @@ DEV void qkrope_epilogue(const Args& p, const f32x16_t (&acc)[T::TM][T::TN], f16
         const int lr = base + u * STEP;
         if (lr >= rows_valid) break;
         const int64_t t = out_row0 + lr;
-        const int b = (int)(t / e.S);
+        const int b = b_k[u];
         const int pos = pos_k[u];
         const bool ok = ok_k[u];
         float c[8], sn[8];
@@ -315,8 +327,8 @@ DEV void qkrope_epilogue(const Args& p, const f32x16_t (&acc)[T::TM][T::TN], f16
     const int c = (item >> 2) % T::BN, r0 = ((item >> 2) / T::BN) * 32 + (item & 3) * 8;
     const int h = head0 + c / HD, d = c % HD;
     if (h >= e.nkv || r0 >= rows_valid) continue;
-    const int64_t t0 = out_row0 + r0;
-    const int b = (int)(t0 / e.S), s0 = (int)(t0 % e.S);
+    int b, s0;
+    seq_of(r0, b, s0);
     const int pos = e.pos0 + s0;
     const int n = min(8, rows_valid - r0);
     float v[8];
@@ -339,8 +351,9 @@ DEV void qkrope_epilogue(const Args& p, const f32x16_t (&acc)[T::TM][T::TN], f16
     } else {
       // rows may cross into the next sequence: place each token by its own (b, s)
       for (int k = 0; k < n; ++k) {
-        const int64_t t = t0 + k;
-        const int bk = (int)(t / e.S), sk = (int)(t % e.S), pk = e.pos0 + sk;
+        int bk, sk;
+        seq_of(r0 + k, bk, sk);
+        const int pk = e.pos0 + sk;
         if (pk < 0 || pk >= e.cap || pk >= e.max_pos) continue;
         const int64_t bh = (int64_t)bk * e.nkv + h;
         e.vt_cache[bh * e.cap * HD + vcache_idx(pk, d)] = f2bf(v[k]);
@@ -565,59 +578,72 @@ __global__ void __launch_bounds__(T::THREADS) gemm_kernel(Args p) {
   // of group g + 1 are loaded before group g is stored, so only the first load latency is
   // exposed.  The output may be the residual buffer itself: each element is read before it
   // is written and distinct elements never overlap.
+  // A lane's 16 elements of a group lie in rows row0 + roff(r) of one column, roff(r) =
+  // 8 (r / 4) + r % 4: in a full tile (every row and column valid, all tiles but the last
+  // row / column of a product) each element is the group's base address plus a row offset
+  // that is the same for every lane, with no bounds logic.  Otherwise rows / columns past
+  // the valid range are clamped to the last valid one for the residual loads (every load in
+  // bounds and unconditional, so they issue back to back) and those elements are not stored.
   constexpr bool RES = EPI == E_RES_F32 || EPI == E_RESB_F32 || EPI == E_RESF_B16;
   constexpr int NG = T::TM * T::TN;
-  // Rows / columns past the valid range are clamped to the last valid one: every load is
-  // in bounds and unconditional (so they issue back to back), and those elements are
-  // never stored.
-  auto load_res = [&](int gi, float* res) {
-    const int i = gi / T::TN, j = gi % T::TN;
-    const int col = min(n0 + wn * T::WN + j * 32 + ccol, p.N - 1);
+  auto walk = [&](auto full_c) {
+    constexpr bool FULL = decltype(full_c)::value;
+    auto load_res = [&](int gi, float* res) {
+      const int i = gi / T::TN, j = gi % T::TN;
+      const int col = FULL ? n0 + wn * T::WN + j * 32 + ccol
+                           : min(n0 + wn * T::WN + j * 32 + ccol, p.N - 1);
+      const int64_t row0 = out_row0 + wm * T::WM + i * 32 + rsub;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int lr = min(wm * T::WM + i * 32 + (r >> 2) * 8 + rsub + (r & 3), rows_valid - 1);
-      const int64_t row = out_row0 + lr;
-      if (EPI == E_RESB_F32) {
-        // the aligned 32-bit word holding this bf16 and its neighbour's
-        const uint32_t w = *(const uint32_t*)((const bf16_t*)p.R + row * p.ldr + (col & ~1));
-        res[r] = __uint_as_float((col & 1) ? (w & 0xffff0000u) : (w << 16));
-      } else {
-        res[r] = ((const float*)p.R)[row * p.ldr + col];
+      for (int r = 0; r < 16; ++r) {
+        const int roff = (r >> 2) * 8 + (r & 3);
+        const int64_t row =
+            FULL ? row0 + roff : out_row0 + min((int)(row0 - out_row0) + roff, rows_valid - 1);
+        if (EPI == E_RESB_F32) {
+          // the aligned 32-bit word holding this bf16 and its neighbour's
+          const uint32_t w = *(const uint32_t*)((const bf16_t*)p.R + row * p.ldr + (col & ~1));
+          res[r] = __uint_as_float((col & 1) ? (w & 0xffff0000u) : (w << 16));
+        } else {
+          res[r] = ((const float*)p.R)[row * p.ldr + col];
+        }
+      }
+    };
+    float res_cur[16], res_next[16];
+    if (RES) load_res(0, res_next);
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const int i = gi / T::TN, j = gi % T::TN;
+      if (RES) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) res_cur[r] = res_next[r];
+        if (gi + 1 < NG) load_res(gi + 1, res_next);
+      }
+      const int col = n0 + wn * T::WN + j * 32 + ccol;
+      if (!FULL && col >= p.N) continue;
+      const int lr0 = wm * T::WM + i * 32 + rsub;
+      const int64_t row0 = out_row0 + lr0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int roff = (r >> 2) * 8 + (r & 3);
+        if (!FULL && lr0 + roff >= rows_valid) continue;
+        const int64_t row = row0 + roff;
+        const float v = acc[i][j][r];
+        if (EPI == E_F32) {
+          // fp32 outputs (logits, MoE slot rows) are far larger than the caches and read
+          // once by a later pass: streaming stores (measured: LM head -1%, MoE down -5%,
+          // and the combine that reads the slot rows -17%)
+          __builtin_nontemporal_store(v, (float*)p.C + row * p.ldc + col);
+        } else if (EPI == E_F16) {
+          ((f16_t*)p.C)[row * p.ldc + col] = f2h(v);
+        } else if (EPI == E_RES_F32 || EPI == E_RESB_F32) {
+          ((float*)p.C)[row * p.ldc + col] = res_cur[r] + v;
+        } else if (EPI == E_RESF_B16) {
+          ((bf16_t*)p.C)[row * p.ldc + col] = f2bf(res_cur[r] + v);
+        }
       }
     }
   };
-  float res_cur[16], res_next[16];
-  if (RES) load_res(0, res_next);
-#pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
-    const int i = gi / T::TN, j = gi % T::TN;
-    if (RES) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) res_cur[r] = res_next[r];
-      if (gi + 1 < NG) load_res(gi + 1, res_next);
-    }
-    const int col = n0 + wn * T::WN + j * 32 + ccol;
-    if (col >= p.N) continue;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int lr = wm * T::WM + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
-      if (lr >= rows_valid) continue;
-      const int64_t row = out_row0 + lr;
-      const float v = acc[i][j][r];
-      if (EPI == E_F32) {
-        // fp32 outputs (logits, MoE slot rows) are far larger than the caches and read
-        // once by a later pass: streaming stores (measured: LM head -1%, MoE down -5%,
-        // and the combine that reads the slot rows -17%)
-        __builtin_nontemporal_store(v, (float*)p.C + row * p.ldc + col);
-      } else if (EPI == E_F16) {
-        ((f16_t*)p.C)[row * p.ldc + col] = f2h(v);
-      } else if (EPI == E_RES_F32 || EPI == E_RESB_F32) {
-        ((float*)p.C)[row * p.ldc + col] = res_cur[r] + v;
-      } else if (EPI == E_RESF_B16) {
-        ((bf16_t*)p.C)[row * p.ldc + col] = f2bf(res_cur[r] + v);
-      }
-    }
-  }
+  if (rows_valid == T::BM && n0 + T::BN <= p.N) walk(std::true_type{});
+  else walk(std::false_type{});
 }
 
 }  // namespace gemm
