@@ -40,6 +40,12 @@ PREFILL_CASES = {
     # sixteen q heads per kv head (a 64 q / 4 kv model's grouping), tiled and small
     "group16_tiled": (dict(nq=16, nkv=1), 2, 160, 0),
     "group16_chunked": (dict(nq=16, nkv=1), 1, 40, 30),
+    # a hidden size that is a multiple of 64 but not of 128: the o_proj and down products end
+    # in a partly filled column tile (and, at 300 rows, a partly filled row tile), so their
+    # residual epilogues take both the full-tile and the bounds-checked path
+    "tiled_h320": (dict(H=320), 2, 150, 0),
+    "tiled_h320_chunked": (dict(H=320), 3, 100, 40),
+    "small_h320": (dict(H=320), 1, 90, 0),
 }
 
 
