@@ -51,11 +51,14 @@ PREFILL_CASES = {
 
 @pytest.mark.parametrize("name", list(PREFILL_CASES))
 def test_block_prefill_parity(gpu, name):
-    import torch
     kw, B, S, pos0 = PREFILL_CASES[name]
     cfg = dict(recipes.QWEN3_0P6B) if kw is None else small_cfg(**kw)
     log(f"case block_prefill/{name}: B={B} S={S} pos0={pos0}")
-    seed = 11
+    _block_prefill_case(gpu, cfg, B, S, pos0)
+
+
+def _block_prefill_case(gpu, cfg, B, S, pos0, seed=11):
+    import torch
     H, nkv = cfg["hidden_size"], cfg["num_key_value_heads"]
     layer = recipes.layer_host(seed, cfg, 0)
     x = synth.normal_bf16(seed, recipes.activations_name(), (B, S, H))
@@ -150,7 +153,6 @@ DECODE_CASES = {
 
 @pytest.mark.parametrize("name", list(DECODE_CASES))
 def test_block_decode_parity(gpu, name):
-    import torch
     kw, positions, cap = DECODE_CASES[name]
     if kw is None:
         cfg = dict(recipes.QWEN3_0P6B)
@@ -159,7 +161,11 @@ def test_block_decode_parity(gpu, name):
     else:
         cfg = small_cfg(**kw)
     log(f"case block_decode/{name}: pos={positions} cap={cap}")
-    seed = 12
+    _block_decode_case(gpu, cfg, positions, cap)
+
+
+def _block_decode_case(gpu, cfg, positions, cap, seed=12):
+    import torch
     B = len(positions)
     H, nkv = cfg["hidden_size"], cfg["num_key_value_heads"]
     layer = recipes.layer_host(seed, cfg, 0)
@@ -202,3 +208,55 @@ def test_block_decode_out_of_range_position_gives_nan_row(gpu):
     torch.cuda.synchronize()
     o = out.float().cpu().numpy()
     assert np.all(np.isfinite(o[0])) and np.all(np.isnan(o[1]))
+
+
+# A seeded sweep over small valid shapes, beyond the hand-picked cases: hidden and
+# intermediate sizes at every multiple of 64 up to 512 / 768, 1-4 kv heads with 1-8 q heads
+# each, ragged lengths, prefills onto a past, both q/k-norm settings and both RoPE pairings;
+# decode steps at ragged positions.  The list is fixed by its seed.
+def _sweep_cfg(rng):
+    nkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 3, 5, 7, 8]))
+    return dict(H=64 * int(rng.integers(1, 9)), nq=nkv * g, nkv=nkv,
+                I=64 * int(rng.integers(1, 13)), qk_norm=int(rng.integers(0, 2)),
+                rope_interleaved=int(rng.integers(0, 2)))
+
+
+def _prefill_sweep(n=16, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        kw = _sweep_cfg(rng)
+        B, S = int(rng.integers(1, 4)), int(rng.integers(1, 300))
+        pos0 = 0 if rng.integers(0, 2) == 0 else int(rng.integers(1, 150))
+        out.append((kw, B, S, pos0))
+    return out
+
+
+def _decode_sweep(n=12, seed=2025):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        kw = _sweep_cfg(rng)
+        cap = 64 * int(rng.integers(1, 9))
+        positions = [int(p) for p in rng.integers(0, cap, size=int(rng.integers(1, 6)))]
+        out.append((kw, positions, cap))
+    return out
+
+
+PREFILL_SWEEP = _prefill_sweep()
+DECODE_SWEEP = _decode_sweep()
+
+
+@pytest.mark.parametrize("i", range(len(PREFILL_SWEEP)))
+def test_block_prefill_shape_sweep(gpu, i):
+    kw, B, S, pos0 = PREFILL_SWEEP[i]
+    log(f"case block_prefill/sweep{i}: {kw} B={B} S={S} pos0={pos0}")
+    _block_prefill_case(gpu, small_cfg(**kw), B, S, pos0, seed=100 + i)
+
+
+@pytest.mark.parametrize("i", range(len(DECODE_SWEEP)))
+def test_block_decode_shape_sweep(gpu, i):
+    kw, positions, cap = DECODE_SWEEP[i]
+    log(f"case block_decode/sweep{i}: {kw} pos={positions} cap={cap}")
+    _block_decode_case(gpu, small_cfg(**kw), positions, cap, seed=200 + i)
