@@ -88,8 +88,12 @@ def test_moe_parity(gpu, name):
     cfg = dict(norm_topk_prob=1, rms_norm_eps=1e-6)
     cfg.update(kw)
     log(f"case moe/{name}: T={T} {kw}")
-    router, gu, dn = recipes.moe_host(31, cfg, skew=skew is True)
-    x = synth.normal_bf16(31, recipes.activations_name(), (T, cfg["hidden_size"]))
+    _moe_case(gpu, cfg, T, skew)
+
+
+def _moe_case(gpu, cfg, T, skew, seed=31):
+    router, gu, dn = recipes.moe_host(seed, cfg, skew=skew is True)
+    x = synth.normal_bf16(seed, recipes.activations_name(), (T, cfg["hidden_size"]))
     if skew == "hot":
         router, x = _make_hot(router, x)
     g = run_moe(cfg, router, gu, dn, x, gpu)
@@ -139,6 +143,34 @@ def test_moe_parity(gpu, name):
     np.testing.assert_allclose(y_at[agree], y_ref[agree], rtol=0, atol=1e-12)
     parity(g["y"], y_at, "y (all tokens, at the GPU's selection)", stored_bf16=True)
 
+
+
+# A seeded sweep over small valid routed layers beyond the hand-picked cases: 2-64 experts,
+# top-1 to top-8, hidden and expert sizes at multiples of 64, 1-600 tokens (expert tiles
+# from empty to several, ragged), renormalised or not.  The list is fixed by its seed.
+def _moe_sweep(n=12, seed=2026):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        E = int(rng.integers(2, 65))
+        kw = dict(num_experts=E, num_experts_per_tok=int(rng.integers(1, min(8, E) + 1)),
+                  hidden_size=64 * int(rng.integers(1, 9)),
+                  moe_intermediate_size=64 * int(rng.integers(1, 7)),
+                  norm_topk_prob=int(rng.integers(0, 2)))
+        out.append((kw, int(rng.integers(1, 601))))
+    return out
+
+
+MOE_SWEEP = _moe_sweep()
+
+
+@pytest.mark.parametrize("i", range(len(MOE_SWEEP)))
+def test_moe_shape_sweep(gpu, i):
+    kw, T = MOE_SWEEP[i]
+    cfg = dict(rms_norm_eps=1e-6)
+    cfg.update(kw)
+    log(f"case moe/sweep{i}: T={T} {kw}")
+    _moe_case(gpu, cfg, T, False, seed=300 + i)
 
 def test_moe_deterministic(gpu):
     kw, T, _ = MOE_CASES["e16_k4_ragged"]
