@@ -132,3 +132,58 @@ def test_prefill_then_decode_matches_longer_prefill(gpu):
     for b in range(B):
         ref = oracle.stack_prefill(cfg, model, ids[b], rows=[S])
         parity(got[b], ref[0], f"prefill+decode logits[b={b}]")
+
+
+# A seeded sweep of whole-stack prefills over small valid shapes: vocabularies of any size
+# (the LM head's last column tile and the argmax chunks ragged), one or two layers, tied or
+# untied head, 1-8 q heads per kv head, ragged B x S.  Every logit is compared, the argmax on
+# the GPU's own logits, and LAST mode bit for bit against ALL's last rows.
+def _stack_sweep(n=8, seed=2027):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        nkv = int(rng.choice([1, 2, 4]))
+        kw = dict(H=64 * int(rng.integers(1, 7)), nq=nkv * int(rng.choice([1, 2, 3, 7, 8])),
+                  nkv=nkv, I=64 * int(rng.integers(1, 9)), L=int(rng.integers(1, 3)),
+                  V=int(rng.integers(64, 3001)), qk_norm=int(rng.integers(0, 2)),
+                  rope_interleaved=int(rng.integers(0, 2)))
+        out.append((kw, int(rng.integers(0, 2)), int(rng.integers(1, 4)),
+                    int(rng.integers(1, 200))))
+    return out
+
+
+STACK_SWEEP = _stack_sweep()
+
+
+@pytest.mark.parametrize("i", range(len(STACK_SWEEP)))
+def test_stack_prefill_shape_sweep(gpu, i):
+    import torch
+    kw, tied, B, S = STACK_SWEEP[i]
+    cfg = small_cfg(**kw)
+    cfg["tie_word_embeddings"] = tied
+    L, V, nkv = cfg["num_hidden_layers"], cfg["vocab_size"], cfg["num_key_value_heads"]
+    log(f"case stack_prefill/sweep{i}: {kw} tied={tied} B={B} S={S}")
+    model = recipes.model_host(400 + i, cfg)
+    mw, keep = _model_dev(model, gpu)
+    ids = synth.uniform_i32(400 + i, "input.ids", (B, S), 0, V)
+    idd = torch.from_numpy(ids).to(gpu)
+    cap = ((S + 63) // 64) * 64
+    ws = torch.empty(q3.qwen3_workspace_bytes(cfg, q3.QWEN3_OP_STACK_PREFILL, B, S),
+                     dtype=torch.uint8, device=gpu)
+    logits = torch.empty((B, S, V), dtype=torch.float32, device=gpu)
+    nxt = torch.empty((B,), dtype=torch.int32, device=gpu)
+    caches = [new_cache(B, nkv, cap, gpu) for _ in range(L)]
+    q3.qwen3_stack_forward(cfg, mw, _rope(cfg, gpu), idd, B, S, 0, None,
+                           [q3.make_kv_layer(k, vt, cap) for k, vt in caches], logits,
+                           q3.QWEN3_LOGITS_ALL, nxt, ws)
+    last = torch.empty((B, V), dtype=torch.float32, device=gpu)
+    caches2 = [new_cache(B, nkv, cap, gpu) for _ in range(L)]
+    q3.qwen3_stack_forward(cfg, mw, _rope(cfg, gpu), idd, B, S, 0, None,
+                           [q3.make_kv_layer(k, vt, cap) for k, vt in caches2], last,
+                           q3.QWEN3_LOGITS_LAST, None, ws)
+    torch.cuda.synchronize()
+    got = logits.cpu().numpy()
+    for b in range(B):
+        parity(got[b], oracle.stack_prefill(cfg, model, ids[b]), f"logits[b={b}]")
+    np.testing.assert_array_equal(nxt.cpu().numpy(), oracle.argmax(got[:, -1, :]))
+    np.testing.assert_array_equal(last.cpu().numpy(), got[:, -1, :])
