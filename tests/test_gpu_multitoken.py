@@ -74,11 +74,15 @@ def test_multi_token_decode_matches_oracle(gpu, name):
     positions, S, cap, over = CASES[name]
     cfg = small_cfg(L=2, V=600, **over)
     log(f"case multi-token decode/{name}: pos={positions} S={S} cap={cap}")
-    model, ids, got, nxt, before, after = _run(gpu, cfg, 51, positions, S, cap,
+    _check_all_rows(gpu, cfg, 51, positions, S, cap)
+
+
+def _check_all_rows(gpu, cfg, seed, positions, S, cap):
+    model, ids, got, nxt, before, after = _run(gpu, cfg, seed, positions, S, cap,
                                                q3.QWEN3_LOGITS_ALL)
     got = got.reshape(len(positions), S, -1)
     for b, p in enumerate(positions):
-        ref = _oracle(cfg, model, 51, ids[b], b, p, cap)
+        ref = _oracle(cfg, model, seed, ids[b], b, p, cap)
         parity(got[b], ref, f"logits[b={b}, pos={p}]")
     np.testing.assert_array_equal(nxt, oracle.argmax(np.ascontiguousarray(got[:, -1, :])))
     # each sequence's new positions were written, nothing else
@@ -88,6 +92,36 @@ def test_multi_token_decode_matches_oracle(gpu, name):
             changed = np.nonzero(kd)[0]
             assert changed.min() >= p and changed.max() < p + S, (l, b, changed)
 
+
+
+# A seeded sweep over small valid shapes: 1-5 sequences at ragged positions with 1-12 new
+# tokens each (at most 60 rows: decode-size products; above 256 rows the tiled ones, covered
+# by the cases above), 1-8 q heads per kv head, hidden and FFN sizes at multiples of 64, one
+# or two layers, any vocabulary size, both norm and RoPE settings.
+def _multitoken_sweep(n=10, seed=2028):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        nkv = int(rng.choice([1, 2, 4]))
+        kw = dict(H=64 * int(rng.integers(1, 7)), nq=nkv * int(rng.choice([1, 2, 3, 7, 8])),
+                  nkv=nkv, I=64 * int(rng.integers(1, 9)), L=int(rng.integers(1, 3)),
+                  V=int(rng.integers(64, 2001)), qk_norm=int(rng.integers(0, 2)),
+                  rope_interleaved=int(rng.integers(0, 2)))
+        cap = 64 * int(rng.integers(1, 5))
+        S = int(rng.integers(1, min(12, cap) + 1))
+        positions = [int(p) for p in rng.integers(0, cap - S + 1, size=int(rng.integers(1, 6)))]
+        out.append((kw, positions, S, cap))
+    return out
+
+
+MULTITOKEN_SWEEP = _multitoken_sweep()
+
+
+@pytest.mark.parametrize("i", range(len(MULTITOKEN_SWEEP)))
+def test_multi_token_decode_shape_sweep(gpu, i):
+    kw, positions, S, cap = MULTITOKEN_SWEEP[i]
+    log(f"case multi-token decode/sweep{i}: {kw} pos={positions} S={S} cap={cap}")
+    _check_all_rows(gpu, small_cfg(**kw), 500 + i, positions, S, cap)
 
 def test_multi_token_decode_last_rows_and_out_of_range(gpu):
     # LAST mode gives each sequence's last new row; a sequence whose last new position is
