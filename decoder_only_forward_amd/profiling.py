@@ -1,6 +1,6 @@
 """Text summaries of rocprofv3 output for the benchmark.
 
-Two kinds of run are summarised (both write CSV with ``--output-format csv``):
+Three kinds of run are summarised (all write CSV with ``--output-format csv``):
 
 * kernel trace with statistics (``--kernel-trace --stats``): per kernel class, the number
   of dispatches, total and average duration;
