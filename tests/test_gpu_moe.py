@@ -59,6 +59,12 @@ MOE_CASES = {
                                hidden_size=256), 700, "hot"),
     "e8_k2_hot_expert": (dict(num_experts=8, num_experts_per_tok=2, moe_intermediate_size=128,
                               hidden_size=256), 300, "hot"),
+    # the limits: 256 experts at top-8 (most experts get a few tokens or none), and top-k
+    # equal to the expert count (every token uses every expert; the weights are the softmax)
+    "e256_k8_max": (dict(num_experts=256, num_experts_per_tok=8, moe_intermediate_size=128,
+                         hidden_size=256), 400, False),
+    "e8_k8_all": (dict(num_experts=8, num_experts_per_tok=8, moe_intermediate_size=128,
+                       hidden_size=192), 257, False),
 }
 
 
