@@ -156,6 +156,20 @@ def test_generate_sampling_full_vocabulary(gpu, T, top_p):
     assert exact >= B * n_new - 1, exact
 
 
+
+def test_generate_sampling_at_the_vocabulary_limit(gpu):
+    # The largest vocabulary the sampler accepts (262,144 tokens: 16,384 per chunk of a row)
+    cfg = small_cfg(L=1, V=262144)
+    B, S, n_new, cap = 4, 8, 2, 64
+    T, top_p = 1.0, 0.9
+    log(f"case generate sampled vocabulary limit: V={cfg['vocab_size']} B={B} n_new={n_new}")
+    model, mw, keep, rope, ids = _setup(gpu, cfg, 35, B, S, cap)
+    rng = np.random.default_rng(10)
+    uni = rng.random((n_new, B)).astype(np.float32)
+    got = _generate(gpu, cfg, mw, rope, ids, n_new, cap, T, top_p, uni)
+    exact = _replay_draws(gpu, cfg, mw, rope, ids, got, T, top_p, uni, cap)
+    assert exact >= B * n_new - 1, exact
+
 def test_generate_sampling_limits(gpu):
     # top_p -> 0 keeps only the largest logit: the draw is the greedy token whatever u is
     cfg = small_cfg(L=2, V=600)
